@@ -1,0 +1,118 @@
+"""fp64 CPU oracle for multi-scale retention (parallel, recurrent and chunkwise forms, GroupNorm).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+may import this package. The GPU library shares no code with it.
+
+The arithmetic lives in oracle.c (plain C, double precision); this module only marshals numpy
+arrays to it. Citations of the pages are in oracle.c beside each function.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, SRC, build
+
+_lib = None
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def load(path: str = LIB):
+    """Load (building first if missing or stale) the oracle shared library."""
+    if not os.path.exists(path) or (path == LIB and os.path.getmtime(SRC) > os.path.getmtime(path)):
+        build(out=path, quiet=True)
+    lib = ctypes.CDLL(path)
+    i, d = ctypes.c_int, ctypes.c_double
+    lib.oracle_recurrent.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_parallel.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_chunkwise.argtypes = [i, i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_groupnorm.argtypes = [i, i, i, i, d, _DP, _DP, _DP, _DP]
+    lib.oracle_threads.restype = i
+    lib.oracle_set_threads.argtypes = [i]
+    for f in (lib.oracle_recurrent, lib.oracle_parallel, lib.oracle_chunkwise, lib.oracle_groupnorm):
+        f.restype = None
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: widen the exact stored values
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_DP)
+
+
+class Oracle:
+    """Callable wrapper around one oracle library (the real one, or a test-built variant)."""
+
+    def __init__(self, lib=None):
+        self.lib = lib if lib is not None else _get()
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        self.lib.oracle_set_threads(int(n))
+
+    @staticmethod
+    def _dims(q, v):
+        B, H, N, dk = q.shape
+        dv = v.shape[-1]
+        return B, H, N, dk, dv
+
+    def recurrent(self, q, k, v, gamma, state_in=None, want_out=True, want_state=True):
+        """Recurrent form. q, k: [B,H,N,dk]; v: [B,H,N,dv]; gamma: [H]. Returns (out, state)."""
+        q, k, v, g, s0 = map(_f64, (q, k, v, gamma, state_in))
+        B, H, N, dk, dv = self._dims(q, v)
+        out = np.zeros((B, H, N, dv)) if want_out else None
+        st = np.zeros((B, H, dk, dv)) if want_state else None
+        self.lib.oracle_recurrent(B, H, N, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out), _ptr(st))
+        return out, st
+
+    def parallel(self, q, k, v, gamma):
+        """Parallel form O = (QK^T (.) D) V. Quadratic in N."""
+        q, k, v, g = map(_f64, (q, k, v, gamma))
+        B, H, N, dk, dv = self._dims(q, v)
+        out = np.zeros((B, H, N, dv))
+        self.lib.oracle_parallel(B, H, N, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out))
+        return out
+
+    def chunkwise(self, q, k, v, gamma, chunk, state_in=None, want_state=True):
+        """Chunkwise recurrent form with chunk length `chunk`. Returns (out, state)."""
+        q, k, v, g, s0 = map(_f64, (q, k, v, gamma, state_in))
+        B, H, N, dk, dv = self._dims(q, v)
+        out = np.zeros((B, H, N, dv))
+        st = np.zeros((B, H, dk, dv)) if want_state else None
+        self.lib.oracle_chunkwise(B, H, N, dk, dv, int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0),
+                                  _ptr(out), _ptr(st))
+        return out, st
+
+    def groupnorm(self, x, eps, weight=None, bias=None):
+        """Per-head GroupNorm over the d_v channels of each (b, h, n) row. x: [B,H,N,dv]."""
+        x, w, b = map(_f64, (x, weight, bias))
+        B, H, N, dv = x.shape
+        y = np.zeros_like(x)
+        self.lib.oracle_groupnorm(B, H, N, dv, float(eps), _ptr(w), _ptr(b), _ptr(x), _ptr(y))
+        return y
+
+    def step(self, q, k, v, gamma, state):
+        """One recurrent decode step. q, k: [B,H,dk]; v: [B,H,dv]; state: [B,H,dk,dv].
+        Returns (out [B,H,dv], new_state)."""
+        q, k, v, s = map(_f64, (q, k, v, state))
+        out, st = self.recurrent(q[:, :, None, :], k[:, :, None, :], v[:, :, None, :], gamma, state_in=s)
+        return out[:, :, 0, :], st
+
+
+def get() -> Oracle:
+    return Oracle()

@@ -1,0 +1,229 @@
+/*
+ * Multi-scale retention: plain fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark may load this library. The GPU library never links it and
+ * shares no code, header or table with it.
+ *
+ * Every function follows the definitions on the pages, written out directly
+ * in double precision with no blocking, fusion or reordering beyond what the
+ * definition states:
+ *
+ *   - abeam.tech RetNet paper summary, section "Technical mechanism",
+ *     subsection "Retention multiplies content-based reference and
+ *     distance-based forgetting": the output at position n weights each
+ *     past value v_m by the content affinity q_n . k_m times the decay
+ *     gamma^(n-m); future positions are masked.
+ *   - same page, subsection "Training in parallel, generation by state
+ *     update": per head, S_n = gamma * S_{n-1} + k_n^T v_n and o_n = q_n S_n.
+ *   - same page, subsection "Chunk recursion for long-sequence training":
+ *     inside a chunk the interactions are computed in parallel, earlier
+ *     chunks arrive through the state matrix, and the state is updated at
+ *     the end of each chunk.
+ *   - mlnews.online "Retentive Network: A Successor to Transformer for
+ *     Large Language Models", bullet summary: each head has its own gamma;
+ *     retention outputs are normalised per head with GroupNorm.
+ *
+ * Tensor layout (all row-major, contiguous, last index fastest):
+ *   q, k: [B][H][N][dk]   v, out: [B][H][N][dv]   state: [B][H][dk][dv]
+ * Positions n are 0-based; o_n includes token n (the decay of the diagonal
+ * term is gamma^0 = 1).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/*
+ * Recurrent form (abeam.tech summary, "Training in parallel, generation by
+ * state update"). For every (b, h), starting from state_in (or zero):
+ *     S <- gamma_h * S + k_n^T v_n      (d_k x d_v rank-1 update)
+ *     o_n = q_n S                       (read after the update)
+ * out and state_out may each be NULL.
+ */
+void oracle_recurrent(int B, int H, int N, int dk, int dv,
+                      const double* q, const double* k, const double* v,
+                      const double* gamma, const double* state_in,
+                      double* out, double* state_out) {
+    /* Output columns j and state columns j depend only on state column j, so the work is
+       split into independent blocks of columns; each element sees the same operations in the
+       same order as in a single pass. */
+    const int CB = 64;
+    const int ncb = (dv + CB - 1) / CB;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long task = 0; task < (long)B * H * ncb; ++task) {
+        const int bh = (int)(task / ncb);
+        const int j0 = (int)(task % ncb) * CB;
+        const int j1 = (j0 + CB < dv) ? j0 + CB : dv;
+        const int w = j1 - j0;
+        const double g = gamma[bh % H];
+        double* S = (double*)malloc((size_t)dk * w * sizeof(double));  /* S[i][j - j0] */
+        for (int i = 0; i < dk; ++i)
+            for (int j = j0; j < j1; ++j)
+                S[(size_t)i * w + (j - j0)] = state_in ? state_in[((size_t)bh * dk + i) * dv + j] : 0.0;
+        for (int n = 0; n < N; ++n) {
+            const double* qn = q + ((size_t)bh * N + n) * dk;
+            const double* kn = k + ((size_t)bh * N + n) * dk;
+            const double* vn = v + ((size_t)bh * N + n) * dv;
+            double* on = out ? out + ((size_t)bh * N + n) * dv : NULL;
+            if (on)
+                for (int j = j0; j < j1; ++j) on[j] = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                double* Si = S + (size_t)i * w;  /* Si[j - j0] holds S[i][j] */
+                for (int j = j0; j < j1; ++j) Si[j - j0] = g * Si[j - j0] + kn[i] * vn[j];
+                if (on)
+                    for (int j = j0; j < j1; ++j) on[j] += qn[i] * Si[j - j0];
+            }
+        }
+        if (state_out)
+            for (int i = 0; i < dk; ++i)
+                for (int j = j0; j < j1; ++j)
+                    state_out[((size_t)bh * dk + i) * dv + j] = S[(size_t)i * w + (j - j0)];
+        free(S);
+    }
+}
+
+/*
+ * Parallel form (abeam.tech summary, "Retention multiplies content-based
+ * reference and distance-based forgetting" and "Training in parallel"):
+ *     o_n = sum_{m <= n} gamma^(n-m) (q_n . k_m) v_m
+ * i.e. O = (Q K^T (.) D) V with D_nm = gamma^(n-m) for n >= m, else 0.
+ * Quadratic in N: for small inputs only.
+ */
+void oracle_parallel(int B, int H, int N, int dk, int dv,
+                     const double* q, const double* k, const double* v,
+                     const double* gamma, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const double g = gamma[bh % H];
+        for (int n = 0; n < N; ++n) {
+            const double* qn = q + ((size_t)bh * N + n) * dk;
+            double* on = out + ((size_t)bh * N + n) * dv;
+            memset(on, 0, (size_t)dv * sizeof(double));
+            for (int m = 0; m <= n; ++m) {
+                const double* km = k + ((size_t)bh * N + m) * dk;
+                const double* vm = v + ((size_t)bh * N + m) * dv;
+                double a = 0.0;
+                for (int i = 0; i < dk; ++i) a += qn[i] * km[i];
+                const double w = pow(g, (double)(n - m)) * a;
+                for (int j = 0; j < dv; ++j) on[j] += w * vm[j];
+            }
+        }
+    }
+}
+
+/*
+ * Chunkwise recurrent form (abeam.tech summary, "Chunk recursion for
+ * long-sequence training"; mlnews abstract: each chunk is encoded in
+ * parallel while the chunks are summarised recurrently).
+ * Chunk c covers positions c*C ... c*C+L-1 with L = C, or N mod C for a
+ * short last chunk. With R the state carried in from earlier chunks
+ * (state_in or zero), for local row j of the chunk:
+ *     o_j = sum_{t <= j} gamma^(j-t) (q_j . k_t) v_t      (inside the chunk)
+ *         + gamma^(j+1) q_j R                             (earlier chunks)
+ * and at the end of the chunk
+ *     R <- gamma^L R + sum_t gamma^(L-1-t) k_t^T v_t.
+ * These are the recurrence unrolled over one chunk.
+ */
+void oracle_chunkwise(int B, int H, int N, int dk, int dv, int C,
+                      const double* q, const double* k, const double* v,
+                      const double* gamma, const double* state_in,
+                      double* out, double* state_out) {
+    const size_t sd = (size_t)dk * dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const double g = gamma[bh % H];
+        double* R = (double*)malloc(sd * sizeof(double));
+        if (state_in) memcpy(R, state_in + (size_t)bh * sd, sd * sizeof(double));
+        else memset(R, 0, sd * sizeof(double));
+        for (int c0 = 0; c0 < N; c0 += C) {
+            const int L = (N - c0 < C) ? (N - c0) : C;
+            if (out) {
+                for (int j = 0; j < L; ++j) {
+                    const double* qj = q + ((size_t)bh * N + c0 + j) * dk;
+                    double* oj = out + ((size_t)bh * N + c0 + j) * dv;
+                    memset(oj, 0, (size_t)dv * sizeof(double));
+                    const double xi = pow(g, (double)(j + 1));
+                    for (int i = 0; i < dk; ++i) {
+                        const double* Ri = R + (size_t)i * dv;
+                        for (int col = 0; col < dv; ++col) oj[col] += xi * qj[i] * Ri[col];
+                    }
+                    for (int t = 0; t <= j; ++t) {
+                        const double* kt = k + ((size_t)bh * N + c0 + t) * dk;
+                        const double* vt = v + ((size_t)bh * N + c0 + t) * dv;
+                        double a = 0.0;
+                        for (int i = 0; i < dk; ++i) a += qj[i] * kt[i];
+                        const double w = pow(g, (double)(j - t)) * a;
+                        for (int col = 0; col < dv; ++col) oj[col] += w * vt[col];
+                    }
+                }
+            }
+            const double gL = pow(g, (double)L);
+            for (size_t e = 0; e < sd; ++e) R[e] *= gL;
+            for (int t = 0; t < L; ++t) {
+                const double* kt = k + ((size_t)bh * N + c0 + t) * dk;
+                const double* vt = v + ((size_t)bh * N + c0 + t) * dv;
+                const double z = pow(g, (double)(L - 1 - t));
+                for (int i = 0; i < dk; ++i) {
+                    double* Ri = R + (size_t)i * dv;
+                    for (int col = 0; col < dv; ++col) Ri[col] += z * kt[i] * vt[col];
+                }
+            }
+        }
+        if (state_out) memcpy(state_out + (size_t)bh * sd, R, sd * sizeof(double));
+        free(R);
+    }
+}
+
+/*
+ * Per-head GroupNorm (mlnews bullet summary: retention outputs are
+ * normalised per head with GroupNorm before the heads are concatenated;
+ * abeam.tech summary, "Multi-scale decay, gate and normalisation").
+ * One group = the d_v channels of one head at one position, so each
+ * row x of x[B][H][N][dv] is normalised on its own:
+ *     mu = mean(x), var = mean((x - mu)^2)   (biased)
+ *     y  = (x - mu) / sqrt(var + eps) * w[h][c] + b[h][c]
+ * weight and bias are [H][dv]; NULL means 1 and 0.
+ */
+void oracle_groupnorm(int B, int H, int N, int dv, double eps,
+                      const double* weight, const double* bias,
+                      const double* x, double* y) {
+    const long rows = (long)B * H * N;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const int h = (int)((r / N) % H);
+        const double* xr = x + (size_t)r * dv;
+        double* yr = y + (size_t)r * dv;
+        double mu = 0.0;
+        for (int c = 0; c < dv; ++c) mu += xr[c];
+        mu /= dv;
+        double var = 0.0;
+        for (int c = 0; c < dv; ++c) var += (xr[c] - mu) * (xr[c] - mu);
+        var /= dv;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int c = 0; c < dv; ++c) {
+            const double w = weight ? weight[(size_t)h * dv + c] : 1.0;
+            const double b = bias ? bias[(size_t)h * dv + c] : 0.0;
+            yr[c] = (xr[c] - mu) * inv * w + b;
+        }
+    }
+}

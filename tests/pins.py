@@ -1,0 +1,237 @@
+"""Pins for the fp64 oracle: checks against facts the pages and mathematics fix, not against the
+oracle itself. Each pin takes an `oracle.Oracle` and raises AssertionError when the oracle is wrong.
+
+They are collected in PINS so that the mutation test can run all of them against oracle builds
+with planted mistakes and require that every planted mistake fails at least one pin.
+
+Sources of truth used here:
+  - a hand-worked 3-token example (tests/golden/hand_worked.json), derived by hand from the
+    recurrence on the abeam.tech RetNet summary ("Training in parallel, generation by state update");
+  - closed forms: with q_n = k_m = 1/sqrt(dk) and v = 1, o_n = (1 - g^(n+1)) / (1 - g) and the
+    final state is (1 - g^N) / (1 - g) / sqrt(dk) everywhere (geometric series);
+  - special cases with textbook answers: g = 1 is causal linear attention O = tril(QK^T) V, a
+    tiny g keeps only the diagonal term (q_n . k_n) v_n;
+  - brute force: a plain Python double sum over (n, m) on tiny inputs;
+  - the pages' claim that the parallel, recurrent and chunkwise forms compute the same result
+    (eulerwa.com "3. RetNet in detail", "How does it work?"; abeam.tech summary, FAQ), and the
+    state hand-over between chunks / steps (abeam.tech, "Chunk recursion for long-sequence
+    training"), checked as split/resume and decode-after-prefill identities;
+  - GroupNorm invariants: each normalised row has mean b_h and variance w_h^2 var/(var+eps).
+"""
+import json
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _qkv(B, H, N, dk, dv, seed):
+    s = 1.0 / np.sqrt(dk)
+    return _rand((B, H, N, dk), seed, s), _rand((B, H, N, dk), seed + 1, s), _rand((B, H, N, dv), seed + 2, s)
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    den = max(np.sqrt(np.mean(b * b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den)
+
+
+# ---------------------------------------------------------------------------------------------
+def pin_hand_worked(o):
+    g = json.load(open(os.path.join(HERE, "golden", "hand_worked.json")))
+    r = g["retention"]
+    q = np.array(r["q"], float)[None, None]
+    k = np.array(r["k"], float)[None, None]
+    v = np.array(r["v"], float)[None, None]
+    gam = [r["gamma"]]
+    want_o, want_s = np.array(r["out"], float), np.array(r["state"], float)
+    out, st = o.recurrent(q, k, v, gam)
+    assert np.array_equal(out[0, 0], want_o), ("recurrent out", out[0, 0])
+    assert np.array_equal(st[0, 0], want_s), ("recurrent state", st[0, 0])
+    out = o.parallel(q, k, v, gam)
+    assert np.array_equal(out[0, 0], want_o), ("parallel out", out[0, 0])
+    for C in (1, 2, 3):
+        out, st = o.chunkwise(q, k, v, gam, C)
+        assert np.array_equal(out[0, 0], want_o), ("chunkwise out", C, out[0, 0])
+        assert np.array_equal(st[0, 0], want_s), ("chunkwise state", C, st[0, 0])
+    gn = g["groupnorm"]
+    x = np.array(gn["x"], float)[None, None]
+    y = o.groupnorm(x, gn["eps"], np.array(gn["weight"], float)[None], np.array(gn["bias"], float)[None])
+    assert np.allclose(y[0, 0, 0], gn["y_row0"], rtol=0, atol=1e-15), ("groupnorm", y)
+
+
+def pin_closed_form(o):
+    for dk, dv in ((64, 48), (8, 3)):
+        for gam in (0.5, 0.9, 0.99):
+            N = 250
+            q = np.full((1, 1, N, dk), 1.0 / np.sqrt(dk))
+            k = q.copy()
+            v = np.ones((1, 1, N, dv))
+            n = np.arange(N, dtype=np.float64)
+            want = ((1.0 - gam ** (n + 1)) / (1.0 - gam))[:, None] * np.ones((1, dv))
+            want_s = (1.0 - gam ** N) / (1.0 - gam) / np.sqrt(dk)
+            out, st = o.recurrent(q, k, v, [gam])
+            assert _rel(out[0, 0], want) < 1e-13, ("recurrent closed form", gam, _rel(out[0, 0], want))
+            assert abs(st - want_s).max() < 1e-12 * want_s, ("recurrent state", gam)
+            out = o.parallel(q, k, v, [gam])
+            assert _rel(out[0, 0], want) < 1e-13, ("parallel closed form", gam)
+            for C in (8, 64, 128):
+                out, st = o.chunkwise(q, k, v, [gam], C)
+                assert _rel(out[0, 0], want) < 1e-13, ("chunkwise closed form", gam, C, _rel(out[0, 0], want))
+                assert abs(st - want_s).max() < 1e-12 * want_s, ("chunkwise state", gam, C)
+            # GroupNorm of a constant row is its bias (zero variance)
+            bias = np.linspace(-1, 1, dv)[None]
+            y = o.groupnorm(out, 1e-5, np.full((1, dv), 3.0), bias)
+            assert np.abs(y[0, 0] - bias).max() < 1e-9, ("groupnorm of constant rows", gam)
+
+
+def pin_gamma_one(o):
+    B, H, N, dk, dv = 1, 2, 40, 5, 7
+    q, k, v = _qkv(B, H, N, dk, dv, 11)
+    gam = [1.0, 1.0]
+    want = np.stack([np.tril(q[0, h] @ k[0, h].T) @ v[0, h] for h in range(H)])[None]
+    want_s = np.stack([k[0, h].T @ v[0, h] for h in range(H)])[None]
+    out, st = o.recurrent(q, k, v, gam)
+    assert _rel(out, want) < 1e-12 and _rel(st, want_s) < 1e-12, "recurrent gamma=1"
+    assert _rel(o.parallel(q, k, v, gam), want) < 1e-12, "parallel gamma=1"
+    out, st = o.chunkwise(q, k, v, gam, 16)
+    assert _rel(out, want) < 1e-12 and _rel(st, want_s) < 1e-12, "chunkwise gamma=1"
+
+
+def pin_tiny_gamma(o):
+    B, H, N, dk, dv = 1, 1, 33, 6, 4
+    q, k, v = _qkv(B, H, N, dk, dv, 21)
+    gam = [1e-30]
+    want = (np.sum(q * k, axis=-1, keepdims=True) * v)
+    out, st = o.recurrent(q, k, v, gam)
+    assert _rel(out, want) < 1e-12, "recurrent tiny gamma"
+    assert _rel(st[0, 0], np.outer(k[0, 0, -1], v[0, 0, -1])) < 1e-12, "recurrent tiny gamma state"
+    assert _rel(o.parallel(q, k, v, gam), want) < 1e-12, "parallel tiny gamma"
+    out, st = o.chunkwise(q, k, v, gam, 8)
+    assert _rel(out, want) < 1e-12, "chunkwise tiny gamma"
+    assert _rel(st[0, 0], np.outer(k[0, 0, -1], v[0, 0, -1])) < 1e-12, "chunkwise tiny gamma state"
+
+
+def _brute(q, k, v, gam, state_in=None):
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    out = np.zeros((B, H, N, dv))
+    for b in range(B):
+        for h in range(H):
+            g = gam[h]
+            for n in range(N):
+                acc = np.zeros(dv)
+                for m in range(n + 1):
+                    acc += (g ** (n - m)) * float(np.dot(q[b, h, n], k[b, h, m])) * v[b, h, m]
+                if state_in is not None:
+                    acc += (g ** (n + 1)) * (q[b, h, n] @ state_in[b, h])
+                out[b, h, n] = acc
+    return out
+
+
+def pin_bruteforce(o):
+    B, H, N, dk, dv = 2, 3, 21, 4, 5
+    q, k, v = _qkv(B, H, N, dk, dv, 31)
+    gam = [0.7, 0.95, 1.0]
+    want = _brute(q, k, v, gam)
+    out, _ = o.recurrent(q, k, v, gam)
+    assert _rel(out, want) < 1e-12, "recurrent vs brute force"
+    assert _rel(o.parallel(q, k, v, gam), want) < 1e-12, "parallel vs brute force"
+    for C in (1, 4, 5, 21, 64):
+        out, _ = o.chunkwise(q, k, v, gam, C)
+        assert _rel(out, want) < 1e-12, ("chunkwise vs brute force", C)
+    # with an initial state: o_n gains g^(n+1) q_n S0
+    s0 = _rand((B, H, dk, dv), 35)
+    want = _brute(q, k, v, gam, s0)
+    out, _ = o.recurrent(q, k, v, gam, state_in=s0)
+    assert _rel(out, want) < 1e-12, "recurrent with state_in vs brute force"
+    for C in (3, 8):
+        out, _ = o.chunkwise(q, k, v, gam, C, state_in=s0)
+        assert _rel(out, want) < 1e-12, ("chunkwise with state_in vs brute force", C)
+
+
+def pin_three_forms(o):
+    for N in (1, 7, 64, 250, 256):
+        q, k, v = _qkv(1, 2, N, 16, 12, 40 + N)
+        gam = [0.9, 1.0 - 2.0 ** -20]
+        a, sa = o.recurrent(q, k, v, gam)
+        p = o.parallel(q, k, v, gam)
+        assert _rel(p, a) < 1e-12, ("parallel vs recurrent", N)
+        for C in (8, 16, 64):
+            c, sc = o.chunkwise(q, k, v, gam, C)
+            assert _rel(c, a) < 1e-12, ("chunkwise vs recurrent", N, C)
+            assert _rel(sc, sa) < 1e-12, ("chunkwise state vs recurrent state", N, C)
+
+
+def pin_split_resume(o):
+    B, H, N, dk, dv = 1, 2, 200, 8, 6
+    q, k, v = _qkv(B, H, N, dk, dv, 51)
+    gam = [0.8, 0.995]
+    full, sfull = o.chunkwise(q, k, v, gam, 32)
+    for n1 in (1, 64, 77, 199):
+        a, sa = o.chunkwise(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], gam, 32)
+        b, sb = o.chunkwise(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], gam, 32, state_in=sa)
+        assert _rel(np.concatenate([a, b], axis=2), full) < 1e-12, ("split/resume out", n1)
+        assert _rel(sb, sfull) < 1e-12, ("split/resume state", n1)
+        ra, rsa = o.recurrent(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], gam)
+        assert _rel(rsa, sa) < 1e-12, ("recurrent prefill state", n1)
+
+
+def pin_decode_after_prefill(o):
+    B, H, N, dk, dv = 2, 2, 130, 8, 16
+    q, k, v = _qkv(B, H, N + 1, dk, dv, 61)
+    gam = [0.9, 0.999]
+    full, sfull = o.chunkwise(q, k, v, gam, 64)
+    _, s = o.chunkwise(q[:, :, :N], k[:, :, :N], v[:, :, :N], gam, 64)
+    out, s2 = o.step(q[:, :, N], k[:, :, N], v[:, :, N], gam, s)
+    assert _rel(out, full[:, :, N]) < 1e-12, "decode after prefill: output"
+    assert _rel(s2, sfull) < 1e-12, "decode after prefill: state"
+
+
+def pin_linearity(o):
+    B, H, N, dk, dv = 1, 2, 50, 6, 5
+    q, k, v1 = _qkv(B, H, N, dk, dv, 71)
+    v2 = _rand((B, H, N, dv), 75)
+    gam = [0.85, 0.97]
+    a, sa = o.chunkwise(q, k, v1, gam, 16)
+    b, sb = o.chunkwise(q, k, v2, gam, 16)
+    c, sc = o.chunkwise(q, k, 2.0 * v1 - 3.0 * v2, gam, 16)
+    assert _rel(c, 2.0 * a - 3.0 * b) < 1e-12 and _rel(sc, 2.0 * sa - 3.0 * sb) < 1e-12, "linear in v"
+    # the state read-out is linear in the initial state with weight g^(n+1)
+    s0 = _rand((B, H, dk, dv), 77)
+    d, _ = o.recurrent(q, k, v1, gam, state_in=s0)
+    ra, _ = o.recurrent(q, k, v1, gam)
+    z = np.zeros_like(v1)
+    e, _ = o.recurrent(q, k, z, gam, state_in=s0)
+    assert _rel(d, ra + e) < 1e-12, "state_in contribution adds"
+    for h, g in enumerate(gam):
+        n = np.arange(N)
+        want = (g ** (n + 1))[:, None] * (q[0, h] @ s0[0, h])
+        assert _rel(e[0, h], want) < 1e-12, ("state_in decays as g^(n+1)", h)
+
+
+def pin_groupnorm(o):
+    B, H, N, dv = 2, 3, 5, 32
+    x = _rand((B, H, N, dv), 81) * np.array([0.01, 1.0, 100.0])[None, :, None, None] + 0.3
+    w = np.array([0.5, 2.0, -1.0])[:, None] * np.ones((1, dv))
+    bias = np.array([1.0, -2.0, 0.25])[:, None] * np.ones((1, dv))
+    eps = 1e-3
+    y = o.groupnorm(x, eps, w, bias)
+    for h in range(H):
+        xr = x[:, h]
+        var = xr.var(axis=-1)
+        yr = y[:, h]
+        assert np.allclose(yr.mean(axis=-1), bias[h, 0], atol=1e-12), ("groupnorm mean", h)
+        assert np.allclose(yr.var(axis=-1), w[h, 0] ** 2 * var / (var + eps), rtol=1e-10), ("groupnorm var", h)
+    # scale invariance up to eps: scaling a row by c changes y only through eps
+    y1 = o.groupnorm(x * 1e3, eps * 1e6, w, bias)
+    assert _rel(y1, y) < 1e-10, "groupnorm scale invariance"
+
+
+PINS = [pin_hand_worked, pin_closed_form, pin_gamma_one, pin_tiny_gamma, pin_bruteforce, pin_three_forms,
+        pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm]

@@ -1,0 +1,59 @@
+"""Plant plausible mistakes in a copy of the oracle source (on the CPU) and check that every one of
+them fails at least one pin: evidence that the pins would catch such a mistake in the oracle."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle.build import build
+from pins import PINS
+
+SRC = open(oracle.SRC).read()
+
+# (name, exact text in oracle.c, replacement)
+MUTANTS = [
+    ("recurrent_no_decay", "Si[j - j0] = g * Si[j - j0] + kn[i] * vn[j];", "Si[j - j0] = Si[j - j0] + kn[i] * vn[j];"),
+    ("recurrent_read_before_update",
+     "for (int j = j0; j < j1; ++j) Si[j - j0] = g * Si[j - j0] + kn[i] * vn[j];\n                if (on)\n"
+     "                    for (int j = j0; j < j1; ++j) on[j] += qn[i] * Si[j - j0];",
+     "if (on)\n                    for (int j = j0; j < j1; ++j) on[j] += qn[i] * Si[j - j0];\n"
+     "                for (int j = j0; j < j1; ++j) Si[j - j0] = g * Si[j - j0] + kn[i] * vn[j];"),
+    ("recurrent_state_in_transposed", "state_in[((size_t)bh * dk + i) * dv + j]", "state_in[((size_t)bh * dv + j) * dk + i]"),
+    ("recurrent_k_q_swapped_roles", "on[j] += qn[i] * Si[j - j0];", "on[j] += kn[i] * Si[j - j0];"),
+    ("parallel_no_diagonal", "for (int m = 0; m <= n; ++m)", "for (int m = 0; m < n; ++m)"),
+    ("parallel_decay_sign", "pow(g, (double)(n - m))", "pow(g, (double)(m - n))"),
+    ("parallel_wrong_key_index", "const double* km = k + ((size_t)bh * N + m) * dk;",
+     "const double* km = k + ((size_t)bh * N + n) * dk;"),
+    ("chunk_xi_off_by_one", "pow(g, (double)(j + 1))", "pow(g, (double)j)"),
+    ("chunk_zeta_off_by_one", "pow(g, (double)(L - 1 - t))", "pow(g, (double)(L - t))"),
+    ("chunk_decay_uses_C_for_tail", "const double gL = pow(g, (double)L);", "const double gL = pow(g, (double)C);"),
+    ("chunk_intra_no_diagonal", "for (int t = 0; t <= j; ++t)", "for (int t = 0; t < j; ++t)"),
+    ("chunk_intra_decay_sign", "pow(g, (double)(j - t))", "pow(g, (double)(t - j))"),
+    ("chunk_ignores_state_in", "if (state_in) memcpy(R,", "if (0) memcpy(R,"),
+    ("chunk_cross_term_dropped", "oj[col] += xi * qj[i] * Ri[col];", "oj[col] += 0.0 * xi * qj[i] * Ri[col];"),
+    ("groupnorm_unbiased_variance", "var /= dv;", "var /= (dv - 1);"),
+    ("groupnorm_eps_outside_sqrt", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    ("groupnorm_wrong_head_index", "const int h = (int)((r / N) % H);", "const int h = (int)(r % H);"),
+    ("groupnorm_bias_not_added", "yr[c] = (xr[c] - mu) * inv * w + b;", "yr[c] = (xr[c] - mu) * inv * w;"),
+]
+
+
+def _fails_some_pin(orc):
+    for pin in PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    assert SRC.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(SRC.replace(old, new))
+    lib = build(str(src), str(tmp_path / "liboracle_mut.so"), quiet=True)
+    orc = oracle.Oracle(oracle.load(lib))
+    caught = _fails_some_pin(orc)
+    assert caught is not None, f"planted mistake {name} passed every pin"
