@@ -1,0 +1,141 @@
+/*
+ * retention.h: C ABI of the MI355X (gfx950) multi-scale retention library.
+ *
+ * Multi-scale retention, per head h with a fixed decay gamma_h (0 < gamma_h <= 1):
+ *   parallel form    O = (Q K^T (.) D) V,  D[n][m] = gamma^(n-m) for n >= m, else 0
+ *   recurrent form   S_n = gamma * S_(n-1) + k_n^T v_n,   o_n = q_n S_n
+ *   chunkwise form   each chunk computed in parallel inside, the state carried between chunks
+ * Sources: abeam.tech RetNet paper summary, section "Technical mechanism" (retention as
+ * content-based reference times distance-based forgetting; training in parallel, generation by
+ * state update; chunk recursion for long-sequence training); mlnews.online "Retentive Network:
+ * A Successor to Transformer for Large Language Models" (three computation paradigms; per-head
+ * decay; per-head GroupNorm of the retention outputs); eulerwa.com "3. RetNet in detail"
+ * ("How does it work?": the three modes compute the same values).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts (row-major, contiguous, last index fastest):
+ *   q, k      [B][H][N][d_k]          v, out   [B][H][N][d_v]
+ *   state     [B][H][d_k][d_v] fp32   (the recurrent state S, one d_k x d_v matrix per head)
+ *   decode-step vectors: q, k [B][H][d_k], v and out [B][H][d_v]
+ * Positions are 0-based and o_n includes token n (diagonal decay gamma^0 = 1). No 1/sqrt(d_k)
+ * scaling is applied: the result is exactly (Q K^T (.) D) V.
+ * Pointers: q, k, v, out, state*, groupnorm weight/bias and workspace are DEVICE pointers owned
+ * by the caller. `gamma` is a HOST pointer to H doubles, read during the call only. The library
+ * never allocates device memory and keeps no state between calls except a thread-local error
+ * string. All device pointers must be 16-byte aligned.
+ * Streams: all work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
+ * call returns without synchronising. Errors found during execution surface at the caller's
+ * next synchronisation.
+ * Errors: every argument is validated on the host before any HIP call. No C++ exception
+ * crosses this boundary. On a non-OK return, retention_last_error() describes the problem.
+ * Determinism: for the same inputs, shapes and chunk, results are bitwise identical from run
+ * to run (fixed reduction orders; no floating-point atomics).
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RETENTION_ABI_VERSION 1
+#define RETENTION_MAX_HEADS 128
+
+typedef enum {
+    RET_OK = 0,
+    RET_ERR_INVALID_ARG = 1,  /* null required pointer, bad dimension, gamma not in (0,1], eps <= 0,
+                                 misaligned pointer, out and state_out both NULL, ...          */
+    RET_ERR_UNSUPPORTED = 2,  /* valid arguments, but no kernel specialisation for them        */
+    RET_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than retention_workspace_bytes()    */
+    RET_ERR_DEVICE = 4        /* a HIP call or kernel launch failed; see retention_last_error  */
+} ret_status;
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
+
+typedef enum { RET_FN_CHUNKWISE = 0, RET_FN_RECURRENT_STEP = 1, RET_FN_PARALLEL = 2 } ret_fn;
+
+/* Problem shape. in_dtype applies to q, k and v; out_dtype to out. */
+typedef struct {
+    int32_t batch, heads, seq_len, d_k, d_v;
+    int32_t in_dtype;   /* ret_dtype */
+    int32_t out_dtype;  /* ret_dtype */
+} ret_shape;
+
+/* Optional per-head GroupNorm epilogue (mlnews.online RetNet page, bullet summary: outputs are
+ * normalised per head before concatenation). One group = the d_v channels of one head at one
+ * position: y = (o - mean) / sqrt(var + eps) * weight[h][c] + bias[h][c], biased variance,
+ * statistics in fp32 from the fp32 pre-norm output. weight/bias: device fp32 [H][d_v], or NULL
+ * for 1 / 0. Pass NULL (or enabled = 0) for no normalisation. */
+typedef struct {
+    int32_t enabled;
+    float eps;           /* > 0 */
+    const float* weight; /* [H][d_v] or NULL */
+    const float* bias;   /* [H][d_v] or NULL */
+} ret_groupnorm;
+
+/*
+ * Chunkwise recurrent form (abeam.tech summary, "Chunk recursion for long-sequence training";
+ * mlnews abstract: chunks encoded in parallel, summarised recurrently).
+ * With chunk length C (positions c*C .. c*C+L-1, L = C or N mod C for the last chunk) and R the
+ * state carried in (state_in, or zero when NULL), for local row j:
+ *   o_j = sum_{t<=j} gamma^(j-t) (q_j . k_t) v_t + gamma^(j+1) q_j R
+ *   R  <- gamma^L R + sum_t gamma^(L-1-t) k_t^T v_t
+ * chunk: 64, 128, 256 or 512 (bf16 inputs); 64 or 128 (fp32 inputs).
+ * state_in: fp32 [B][H][d_k][d_v] or NULL (zero). state_out: fp32, or NULL. state_out may equal
+ * state_in (in place). out may be NULL only when state_out is not NULL (state-only prefill);
+ * out must not alias q, k or v.
+ * Supported: (d_k, d_v) in {(64,64), (256,512)} for bf16; d_k in {64,128,256}, d_v a multiple of
+ * 64 up to 512 for fp32. H <= RETENTION_MAX_HEADS.
+ * Precision (bf16 inputs): products accumulate in fp32; the carried state is fp32 and enters the
+ * matrix cores as a bf16 high part plus a bf16 low part, as does v scaled by its decay.
+ */
+ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk,
+                                   const void* q, const void* k, const void* v,
+                                   const double* gamma, const float* state_in,
+                                   const ret_groupnorm* groupnorm, void* out, float* state_out,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * One recurrent step (abeam.tech summary, "Training in parallel, generation by state update"):
+ *   S <- gamma_h S + k^T v  (in place, fp32),   o = q S  (with the updated S)
+ * shape->seq_len must be 1. q, k: [B][H][d_k]; v: [B][H][d_v]; state: fp32 [B][H][d_k][d_v],
+ * read and written in place; out: [B][H][d_v] (may be NULL to only advance the state).
+ * Supported: d_v a multiple of 4 with d_v / 4 dividing 256 (d_v <= 1024), any d_k >= 1.
+ */
+ret_status retention_recurrent_step(const ret_shape* shape,
+                                    const void* q, const void* k, const void* v,
+                                    const double* gamma, float* state,
+                                    const ret_groupnorm* groupnorm, void* out,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Parallel form (abeam.tech summary, retention as content-based reference times distance-based
+ * forgetting): O = (Q K^T (.) D) V over the whole sequence, causal, no state.
+ * Supported shapes as for the chunkwise form.
+ */
+ret_status retention_parallel_fwd(const ret_shape* shape,
+                                  const void* q, const void* k, const void* v,
+                                  const double* gamma, const ret_groupnorm* groupnorm, void* out,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace the call `fn` needs for this shape, chunk and GroupNorm setting.
+ * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid. */
+size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t gn_enabled);
+
+/* Static description of a status code. */
+const char* retention_status_string(int32_t status);
+
+/* Thread-local detail for the last non-OK return on this thread ("" if none). */
+const char* retention_last_error(void);
+
+/* RETENTION_ABI_VERSION of the built library. */
+int32_t retention_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RETENTION_H */

@@ -1,0 +1,267 @@
+// C-ABI entry points of the retention library (declared in include/retention.h): argument
+// validation on the host before any HIP call, per-head decay constants in fp64, workspace sizing,
+// and dispatch to the kernel launchers. No exception crosses the boundary; errors are returned
+// as ret_status with a thread-local message.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/retention.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ret_status fail(ret_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int32_t dt) { return dt == RET_BF16 ? 2 : 4; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+ret_status check_shape(const ret_shape* s, bool step) {
+    if (!s) return fail(RET_ERR_INVALID_ARG, "shape is NULL");
+    if (s->batch <= 0 || s->heads <= 0 || s->seq_len <= 0 || s->d_k <= 0 || s->d_v <= 0)
+        return fail(RET_ERR_INVALID_ARG, "non-positive dimension (batch %d heads %d seq_len %d d_k %d d_v %d)", s->batch, s->heads,
+                    s->seq_len, s->d_k, s->d_v);
+    if ((s->in_dtype != RET_F32 && s->in_dtype != RET_BF16) || (s->out_dtype != RET_F32 && s->out_dtype != RET_BF16))
+        return fail(RET_ERR_INVALID_ARG, "dtype must be RET_F32 (0) or RET_BF16 (1) (in %d out %d)", s->in_dtype, s->out_dtype);
+    if (step && s->seq_len != 1) return fail(RET_ERR_INVALID_ARG, "recurrent step needs seq_len == 1 (got %d)", s->seq_len);
+    const double elems = (double)s->batch * s->heads * s->seq_len * (double)(s->d_k > s->d_v ? s->d_k : s->d_v);
+    const double states = (double)s->batch * s->heads * (double)s->d_k * s->d_v;
+    if (elems > 9.0e15 || states > 9.0e15) return fail(RET_ERR_INVALID_ARG, "tensor sizes overflow");
+    if (s->heads > RETENTION_MAX_HEADS)
+        return fail(RET_ERR_UNSUPPORTED, "heads %d exceeds RETENTION_MAX_HEADS (%d)", s->heads, RETENTION_MAX_HEADS);
+    return RET_OK;
+}
+
+ret_status check_gamma(const ret_shape* s, const double* gamma, ret::HeadConsts* hc) {
+    if (!gamma) return fail(RET_ERR_INVALID_ARG, "gamma is NULL");
+    for (int h = 0; h < s->heads; ++h) {
+        const double g = gamma[h];
+        if (!(g > 0.0 && g <= 1.0)) return fail(RET_ERR_INVALID_ARG, "gamma[%d] = %g is not in (0, 1]", h, g);
+        hc->gamma[h] = (float)g;
+        hc->log2g[h] = (float)std::log2(g);
+    }
+    for (int h = s->heads; h < ret::kMaxHeads; ++h) {
+        hc->gamma[h] = 1.f;
+        hc->log2g[h] = 0.f;
+    }
+    return RET_OK;
+}
+
+ret_status check_gn(const ret_groupnorm* gn, ret::GnArgs* out) {
+    out->enabled = 0;
+    out->eps = 0.f;
+    out->weight = nullptr;
+    out->bias = nullptr;
+    if (!gn || !gn->enabled) return RET_OK;
+    if (!(gn->eps > 0.f) || !std::isfinite(gn->eps)) return fail(RET_ERR_INVALID_ARG, "groupnorm eps must be finite and > 0");
+    if ((gn->weight && !aligned16(gn->weight)) || (gn->bias && !aligned16(gn->bias)))
+        return fail(RET_ERR_INVALID_ARG, "groupnorm weight/bias must be 16-byte aligned");
+    out->enabled = 1;
+    out->eps = gn->eps;
+    out->weight = gn->weight;
+    out->bias = gn->bias;
+    return RET_OK;
+}
+
+ret_status check_ptr(const void* p, const char* name, bool required) {
+    if (!p) return required ? fail(RET_ERR_INVALID_ARG, "%s is NULL", name) : RET_OK;
+    if (!aligned16(p)) return fail(RET_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return RET_OK;
+}
+
+ret_status device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return RET_OK;
+    return fail(RET_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RET_TRY(x)                         \
+    do {                                   \
+        const ret_status _s = (x);         \
+        if (_s != RET_OK) return _s;       \
+    } while (0)
+
+ret::LaunchArgs base_args(const ret_shape* s, int chunk, const ret::HeadConsts& hc, const ret::GnArgs& gn, void* ws,
+                          size_t wsb, void* stream) {
+    ret::LaunchArgs a{};
+    a.B = s->batch; a.H = s->heads; a.N = s->seq_len; a.DK = s->d_k; a.DV = s->d_v;
+    a.in_bf16 = s->in_dtype == RET_BF16;
+    a.out_bf16 = s->out_dtype == RET_BF16;
+    a.chunk = chunk;
+    a.hc = hc;
+    a.gn = gn;
+    a.ws = ws;
+    a.ws_bytes = wsb;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return a;
+}
+
+size_t chunkwise_ws(const ret_shape* s, int chunk, int gn, int want_out) {
+    if (s->in_dtype == RET_BF16)
+        return ret::chunkwise_bf16_workspace(s->batch, s->heads, s->seq_len, s->d_k, s->d_v, chunk, gn, want_out);
+    return want_out ? ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16) : 0;
+}
+
+size_t parallel_ws(const ret_shape* s, int gn) {
+    if (s->in_dtype == RET_BF16) return 0;
+    return ret::parallel_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16);
+}
+
+ret_status check_ws(size_t need, const void* ws, size_t wsb) {
+    if (need == 0) return RET_OK;
+    if (!ws) return fail(RET_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (!aligned16(ws)) return fail(RET_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (wsb < need) return fail(RET_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", wsb, need);
+    return RET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t retention_abi_version(void) { return RETENTION_ABI_VERSION; }
+
+const char* retention_last_error(void) { return g_err; }
+
+const char* retention_status_string(int32_t status) {
+    switch (status) {
+        case RET_OK: return "RET_OK: success";
+        case RET_ERR_INVALID_ARG: return "RET_ERR_INVALID_ARG: invalid argument";
+        case RET_ERR_UNSUPPORTED: return "RET_ERR_UNSUPPORTED: no kernel for these shapes or dtypes";
+        case RET_ERR_WORKSPACE: return "RET_ERR_WORKSPACE: workspace missing or too small";
+        case RET_ERR_DEVICE: return "RET_ERR_DEVICE: HIP error";
+        default: return "unknown status";
+    }
+}
+
+size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t gn_enabled) {
+    if (check_shape(shape, fn == RET_FN_RECURRENT_STEP) != RET_OK) return (size_t)-1;
+    switch (fn) {
+        case RET_FN_CHUNKWISE:
+            if (chunk <= 0) return (size_t)-1;
+            return chunkwise_ws(shape, chunk, gn_enabled != 0, 1);
+        case RET_FN_RECURRENT_STEP: return 0;
+        case RET_FN_PARALLEL: return parallel_ws(shape, gn_enabled != 0);
+        default: return (size_t)-1;
+    }
+}
+
+ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const void* q, const void* k, const void* v,
+                                   const double* gamma, const float* state_in, const ret_groupnorm* groupnorm, void* out,
+                                   float* state_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    g_err[0] = '\0';
+    RET_TRY(check_shape(shape, false));
+    RET_TRY(check_ptr(q, "q", true));
+    RET_TRY(check_ptr(k, "k", true));
+    RET_TRY(check_ptr(v, "v", true));
+    RET_TRY(check_ptr(state_in, "state_in", false));
+    RET_TRY(check_ptr(out, "out", false));
+    RET_TRY(check_ptr(state_out, "state_out", false));
+    if (!out && !state_out) return fail(RET_ERR_INVALID_ARG, "out and state_out are both NULL");
+    ret::HeadConsts hc;
+    RET_TRY(check_gamma(shape, gamma, &hc));
+    ret::GnArgs gn;
+    RET_TRY(check_gn(groupnorm, &gn));
+    if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+    const bool bf = shape->in_dtype == RET_BF16;
+    if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, shape->d_v, chunk)
+           : !ret::chunkwise_f32_supported(shape->d_k, shape->d_v, chunk))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise: no kernel for %s inputs with d_k %d, d_v %d, chunk %d", bf ? "bf16" : "fp32",
+                    shape->d_k, shape->d_v, chunk);
+    const size_t rows = (size_t)shape->batch * shape->heads * shape->seq_len;
+    const size_t in_sz = elem_size(shape->in_dtype);
+    const size_t out_bytes = rows * shape->d_v * elem_size(shape->out_dtype);
+    if (out && (overlaps(out, out_bytes, q, rows * shape->d_k * in_sz) || overlaps(out, out_bytes, k, rows * shape->d_k * in_sz) ||
+                overlaps(out, out_bytes, v, rows * shape->d_v * in_sz)))
+        return fail(RET_ERR_INVALID_ARG, "out must not alias q, k or v");
+    const size_t st_bytes = (size_t)shape->batch * shape->heads * shape->d_k * shape->d_v * sizeof(float);
+    if (state_out && out && overlaps(out, out_bytes, state_out, st_bytes))
+        return fail(RET_ERR_INVALID_ARG, "out must not alias state_out");
+    if (state_out && state_in && state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes))
+        return fail(RET_ERR_INVALID_ARG, "state_out may equal state_in but must not partly overlap it");
+    if (!out) gn.enabled = 0;
+    const size_t need = chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
+    RET_TRY(check_ws(need, workspace, workspace_bytes));
+
+    ret::LaunchArgs a = base_args(shape, chunk, hc, gn, workspace, workspace_bytes, hip_stream);
+    a.q = q; a.k = k; a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
+    hipError_t e = bf ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a);
+    return device_status(e, "retention_chunkwise_fwd launch");
+}
+
+ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const void* k, const void* v, const double* gamma,
+                                    float* state, const ret_groupnorm* groupnorm, void* out, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
+    g_err[0] = '\0';
+    (void)workspace;
+    (void)workspace_bytes;
+    RET_TRY(check_shape(shape, true));
+    RET_TRY(check_ptr(q, "q", true));
+    RET_TRY(check_ptr(k, "k", true));
+    RET_TRY(check_ptr(v, "v", true));
+    RET_TRY(check_ptr(state, "state", true));
+    RET_TRY(check_ptr(out, "out", false));
+    ret::HeadConsts hc;
+    RET_TRY(check_gamma(shape, gamma, &hc));
+    ret::GnArgs gn;
+    RET_TRY(check_gn(groupnorm, &gn));
+    const int dv = shape->d_v;
+    if (dv % 4 != 0 || dv / 4 > 256 || 256 % (dv / 4) != 0)
+        return fail(RET_ERR_UNSUPPORTED, "recurrent step needs d_v a multiple of 4 with d_v/4 dividing 256 (got %d)", dv);
+    if (shape->d_k > 8192) return fail(RET_ERR_UNSUPPORTED, "recurrent step supports d_k <= 8192 (got %d)", shape->d_k);
+    const size_t bh = (size_t)shape->batch * shape->heads;
+    const size_t st_bytes = bh * shape->d_k * dv * sizeof(float);
+    const size_t out_bytes = bh * dv * elem_size(shape->out_dtype);
+    if (out && overlaps(out, out_bytes, state, st_bytes)) return fail(RET_ERR_INVALID_ARG, "out must not alias state");
+    ret::LaunchArgs a = base_args(shape, 1, hc, gn, nullptr, 0, hip_stream);
+    a.q = q; a.k = k; a.v = v; a.out = out; a.state_out = state;
+    return device_status(ret::launch_recurrent_step(a), "retention_recurrent_step launch");
+}
+
+ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const void* k, const void* v, const double* gamma,
+                                  const ret_groupnorm* groupnorm, void* out, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream) {
+    g_err[0] = '\0';
+    RET_TRY(check_shape(shape, false));
+    RET_TRY(check_ptr(q, "q", true));
+    RET_TRY(check_ptr(k, "k", true));
+    RET_TRY(check_ptr(v, "v", true));
+    RET_TRY(check_ptr(out, "out", true));
+    ret::HeadConsts hc;
+    RET_TRY(check_gamma(shape, gamma, &hc));
+    ret::GnArgs gn;
+    RET_TRY(check_gn(groupnorm, &gn));
+    const bool bf = shape->in_dtype == RET_BF16;
+    if (bf ? !ret::parallel_bf16_supported(shape->d_k, shape->d_v) : !ret::parallel_f32_supported(shape->d_k, shape->d_v))
+        return fail(RET_ERR_UNSUPPORTED, "parallel: no kernel for %s inputs with d_k %d, d_v %d", bf ? "bf16" : "fp32", shape->d_k,
+                    shape->d_v);
+    const size_t rows = (size_t)shape->batch * shape->heads * shape->seq_len;
+    const size_t in_sz = elem_size(shape->in_dtype);
+    const size_t out_bytes = rows * shape->d_v * elem_size(shape->out_dtype);
+    if (overlaps(out, out_bytes, q, rows * shape->d_k * in_sz) || overlaps(out, out_bytes, k, rows * shape->d_k * in_sz) ||
+        overlaps(out, out_bytes, v, rows * shape->d_v * in_sz))
+        return fail(RET_ERR_INVALID_ARG, "out must not alias q, k or v");
+    const size_t need = parallel_ws(shape, gn.enabled);
+    RET_TRY(check_ws(need, workspace, workspace_bytes));
+    ret::LaunchArgs a = base_args(shape, 0, hc, gn, workspace, workspace_bytes, hip_stream);
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    hipError_t e = bf ? ret::launch_parallel_bf16(a) : ret::launch_parallel_f32(a);
+    return device_status(e, "retention_parallel_fwd launch");
+}
+
+}  // extern "C"

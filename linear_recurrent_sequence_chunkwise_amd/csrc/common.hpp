@@ -1,0 +1,136 @@
+// Internal header of the gfx950 retention library: types, MFMA wrappers, LDS transpose reads,
+// decay helpers and the launch-argument block shared by the kernels and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ret {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxHeads = 128;
+constexpr int kWave = 64;
+
+// Per-head decay constants, passed by value as a kernel argument. gamma is the fp32 rounding of
+// the caller's fp64 value; log2g = log2(gamma) computed in fp64 on the host, then rounded.
+struct HeadConsts {
+    float gamma[kMaxHeads];
+    float log2g[kMaxHeads];
+};
+
+struct GnArgs {
+    int enabled;
+    float eps;
+    const float* weight;  // [H][dv] or nullptr
+    const float* bias;    // [H][dv] or nullptr
+};
+
+// Everything a launcher needs; filled and validated by the C-ABI layer.
+struct LaunchArgs {
+    int B, H, N, DK, DV;
+    int in_bf16, out_bf16;
+    int chunk;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;              // may be null (chunkwise state-only)
+    const float* state_in;  // may be null
+    float* state_out;       // may be null; the decode step uses it as its in/out state
+    GnArgs gn;
+    HeadConsts hc;
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+// g^e for a per-head log2(g); exact 1 at e = 0; underflows to 0 for large e.
+__device__ __forceinline__ float decay_pow(float log2g, float e) { return exp2f(e * log2g); }
+
+// 16x16x32 bf16 MFMA, fp32 accumulate. Operand layouts (lane l of 64, checked on gfx950):
+//   A[m][k]: lane holds m = l%16, k = 8*(l/16) + j (j = 0..7)
+//   B[k][n]: lane holds k = 8*(l/16) + j, n = l%16
+//   D[m][n]: lane holds m = 4*(l/16) + i (i = 0..3), n = l%16
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i % 4) of the 4-element
+// rows addressed by lanes 4r + i/4, for r = 0..3 (checked on gfx950).
+__device__ __forceinline__ s16x4 lds_read_tr16(const bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// An MFMA operand whose contraction index runs down the rows of a row-major bf16 matrix X in LDS
+// (X[r][c] at base[r*ld + c]): the fragment for rows r0..r0+31 and columns c0..c0+15, i.e.
+// lane l gets X[r0 + 8*(l/16) + j][c0 + l%16], j = 0..7. Serves as the B operand of X (k = rows)
+// or as the A operand of X^T (m = columns). Two transposing 8-byte reads per lane.
+__device__ __forceinline__ bf16x8 lds_frag_kmajor(const bf16* base, int ld, int r0, int c0, int lane) {
+    const int g = lane >> 4, p = lane & 15;
+    const bf16* a0 = base + (size_t)(r0 + 8 * g + (p >> 2)) * ld + c0 + 4 * (p & 3);
+    s16x4 lo = lds_read_tr16(a0);
+    s16x4 hi = lds_read_tr16(a0 + 4 * ld);
+    bf16x8 r;
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+    const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+    r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
+    r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
+    return r;
+}
+
+// The operand whose contraction index runs along the rows' contiguous dimension: lane l gets
+// X[r0 + l%16][c0 + 8*(l/16) + j], j = 0..7 (one 16-byte read). A operand of X (m = rows) or
+// B operand of X^T (n = rows).
+__device__ __forceinline__ bf16x8 frag_rowmajor(const bf16* base, size_t ld, int r0, int c0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(base + (size_t)(r0 + (lane & 15)) * ld + c0 + 8 * (lane >> 4));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    bf16x8 z;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = (bf16)0.0f;
+    return z;
+}
+
+__device__ __forceinline__ void split_hi_lo(float x, bf16& hi, bf16& lo) {
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+}
+
+template <typename T> __device__ __forceinline__ T from_float(float x);
+template <> __device__ __forceinline__ float from_float<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_float<bf16>(float x) { return (bf16)x; }
+
+template <typename T> __device__ __forceinline__ float to_float(T x) { return (float)x; }
+
+// Sum over the 16 lanes that share l/16 (lanes differing in bits 0..3). Symmetric butterfly:
+// every lane ends with the bitwise-same value.
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+}  // namespace ret
+
+// Launchers (one per kernel family), called by the C-ABI layer after validation.
+namespace ret {
+hipError_t launch_recurrent_step(const LaunchArgs& a);
+hipError_t launch_chunkwise_bf16(const LaunchArgs& a);
+hipError_t launch_parallel_bf16(const LaunchArgs& a);
+hipError_t launch_chunkwise_f32(const LaunchArgs& a);
+hipError_t launch_parallel_f32(const LaunchArgs& a);
+size_t chunkwise_bf16_workspace(int B, int H, int N, int DK, int DV, int chunk, int gn, int want_out);
+size_t chunkwise_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16);
+size_t parallel_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16);
+bool chunkwise_bf16_supported(int DK, int DV, int chunk);
+bool chunkwise_f32_supported(int DK, int DV, int chunk);
+bool parallel_bf16_supported(int DK, int DV);
+bool parallel_f32_supported(int DK, int DV);
+}  // namespace ret

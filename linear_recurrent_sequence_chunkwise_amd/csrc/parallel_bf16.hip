@@ -1,0 +1,213 @@
+// Parallel form of retention on the gfx950 matrix cores, bf16 inputs, fp32 accumulation
+// (abeam.tech RetNet summary, retention as content-based reference times distance-based
+// forgetting; "Training in parallel"): O = (Q K^T (.) D) V, D[n][m] = g^(n-m) for n >= m.
+//
+// One workgroup per (64 query rows, b, h) owns all d_v output columns, so the optional per-head
+// GroupNorm is computed inside it. For each 64-key block up to the diagonal:
+//   - K and V blocks are staged in LDS;
+//   - each wave computes S for its 16 query rows (Q fragments stay in registers), applies the
+//     causal mask and the decay g^(n-m) in registers, and writes P to LDS as a bf16 high part and
+//     a bf16 low part (P spans the whole sequence here, so a single bf16 rounding of P would
+//     dominate the error);
+//   - the four waves, arranged 2 x 2 over (rows, columns), accumulate P V with both parts.
+#include "common.hpp"
+
+namespace ret {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DK, int DV>
+struct ParLds {
+    static constexpr int LK = DK + 8;   // K rows: 16-byte reads
+    static constexpr int LV = DV + 16;  // V rows: transposing reads
+    static constexpr int LP = 64 + 8;   // P rows: 16-byte reads
+    bf16 Ks[64 * LK];
+    bf16 Vs[64 * LV];
+    bf16 Phi[64 * LP];
+    bf16 Plo[64 * LP];
+    float red[2][64];
+};
+
+template <int DK, int DV, typename TOUT, bool GN>
+__global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const bf16* __restrict__ q,
+                                                            const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                            TOUT* __restrict__ out, HeadConsts hc, GnArgs gn) {
+    using Lds = ParLds<DK, DV>;
+    constexpr int LK = Lds::LK, LV = Lds::LV, LP = Lds::LP;
+    constexpr int CT = DV / 32;  // 16-column tiles per wave (each wave owns DV/2 columns)
+    extern __shared__ char smem_raw[];
+    Lds& sm = *reinterpret_cast<Lds*>(smem_raw);
+
+    const int qb = blockIdx.x, bh = blockIdx.y, h = bh % H;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
+    const int wr = w >> 1, wc = w & 1;
+    const int n0 = qb * 64;
+    const float l2g = hc.log2g[h];
+    const bf16* qh = q + (size_t)bh * N * DK;
+    const bf16* kh = k + (size_t)bh * N * DK;
+    const bf16* vh = v + (size_t)bh * N * DV;
+
+    bf16x8 qa[DK / 32];
+    const bool qok = n0 + 16 * w + c16 < N;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) qa[ks] = qok ? frag_rowmajor(qh, DK, n0 + 16 * w, 32 * ks, lane) : zero_bf16x8();
+
+    f32x4 acc[2][CT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = 0; kb <= qb; ++kb) {
+        const int m0 = kb * 64;
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < 64 * (DK / 8); idx += kThreads) {
+            const int r = idx / (DK / 8), sg = idx % (DK / 8);
+            bf16x8 val = zero_bf16x8();
+            if (m0 + r < N) val = *reinterpret_cast<const bf16x8*>(kh + (size_t)(m0 + r) * DK + 8 * sg);
+            *reinterpret_cast<bf16x8*>(&sm.Ks[r * LK + 8 * sg]) = val;
+        }
+        for (int idx = threadIdx.x; idx < 64 * (DV / 8); idx += kThreads) {
+            const int r = idx / (DV / 8), sg = idx % (DV / 8);
+            bf16x8 val = zero_bf16x8();
+            if (m0 + r < N) val = *reinterpret_cast<const bf16x8*>(vh + (size_t)(m0 + r) * DV + 8 * sg);
+            *reinterpret_cast<bf16x8*>(&sm.Vs[r * LV + 8 * sg]) = val;
+        }
+        __syncthreads();
+        // S for query rows n0 + 16w .. +16 against the 4 key tiles of this block
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if (kb < qb || kt <= w) {
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) s = mfma16(qa[ks], frag_rowmajor(sm.Ks, LK, 16 * kt, 32 * ks, lane), s);
+            }
+            const int m = m0 + 16 * kt + c16;
+            bf16 hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + 16 * w + 4 * g4 + i;
+                const float d = n >= m ? decay_pow(l2g, (float)(n - m)) : 0.f;
+                split_hi_lo(s[i] * d, hi[i], lo[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.Phi[(16 * w + 4 * g4 + i) * LP + 16 * kt + c16] = hi[i];
+                sm.Plo[(16 * w + 4 * g4 + i) * LP + 16 * kt + c16] = lo[i];
+            }
+        }
+        __syncthreads();
+        // P V: wave (wr, wc) owns rows 32wr .. +32 and columns wc*DV/2 .. +DV/2
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 ahi[2], alo[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                ahi[rt] = frag_rowmajor(sm.Phi, LP, 32 * wr + 16 * rt, 32 * ks, lane);
+                alo[rt] = frag_rowmajor(sm.Plo, LP, 32 * wr + 16 * rt, 32 * ks, lane);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const bf16x8 b = lds_frag_kmajor(sm.Vs, LV, 32 * ks, wc * (DV / 2) + 16 * ct, lane);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    acc[rt][ct] = mfma16(ahi[rt], b, acc[rt][ct]);
+                    acc[rt][ct] = mfma16(alo[rt], b, acc[rt][ct]);
+                }
+            }
+        }
+    }
+
+    if constexpr (GN) {
+        // row statistics over all DV columns: each wave holds DV/2 of them
+        float mean[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) s += acc[rt][ct][i];
+                s = sum16(s);
+                if (c16 == 0) sm.red[wc][32 * wr + 16 * rt + 4 * g4 + i] = s;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 32 * wr + 16 * rt + 4 * g4 + i;
+                mean[rt][i] = (sm.red[0][r] + sm.red[1][r]) * (1.0f / DV);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const float d = acc[rt][ct][i] - mean[rt][i];
+                    s += d * d;
+                }
+                s = sum16(s);
+                if (c16 == 0) sm.red[wc][32 * wr + 16 * rt + 4 * g4 + i] = s;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 32 * wr + 16 * rt + 4 * g4 + i;
+                const float var = (sm.red[0][r] + sm.red[1][r]) * (1.0f / DV);
+                const float inv = rsqrtf(var + gn.eps);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int c = wc * (DV / 2) + 16 * ct + c16;
+                    const float wv = gn.weight ? gn.weight[(size_t)h * DV + c] : 1.f;
+                    const float bv = gn.bias ? gn.bias[(size_t)h * DV + c] : 0.f;
+                    acc[rt][ct][i] = (acc[rt][ct][i] - mean[rt][i]) * inv * wv + bv;
+                }
+            }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = n0 + 32 * wr + 16 * rt + 4 * g4 + i;
+            if (n < N) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    out[((size_t)bh * N + n) * DV + wc * (DV / 2) + 16 * ct + c16] = from_float<TOUT>(acc[rt][ct][i]);
+            }
+        }
+}
+
+template <int DK, int DV, typename TOUT, bool GN>
+hipError_t launch_typed(const LaunchArgs& a) {
+    const size_t lds = sizeof(ParLds<DK, DV>);
+    const void* kern = reinterpret_cast<const void*>(parallel_kernel<DK, DV, TOUT, GN>);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((parallel_kernel<DK, DV, TOUT, GN>), dim3((a.N + 63) / 64, a.B * a.H), dim3(kThreads), lds, a.stream,
+                       a.H, a.N, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOUT*)a.out, a.hc, a.gn);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_shape(const LaunchArgs& a) {
+    if (a.out_bf16) return a.gn.enabled ? launch_typed<DK, DV, bf16, true>(a) : launch_typed<DK, DV, bf16, false>(a);
+    return a.gn.enabled ? launch_typed<DK, DV, float, true>(a) : launch_typed<DK, DV, float, false>(a);
+}
+
+}  // namespace
+
+bool parallel_bf16_supported(int DK, int DV) { return (DK == 64 && DV == 64) || (DK == 256 && DV == 512); }
+
+hipError_t launch_parallel_bf16(const LaunchArgs& a) {
+    if (a.DK == 64) return launch_shape<64, 64>(a);
+    return launch_shape<256, 512>(a);
+}
+
+}  // namespace ret

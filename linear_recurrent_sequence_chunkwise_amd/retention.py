@@ -1,0 +1,243 @@
+"""Thin ctypes binding of the C ABI in include/retention.h.
+
+Argument marshalling only: every step of the computation runs in the gfx950 kernels of
+libretention.so. torch supplies device memory (outputs, workspace) and the current HIP stream.
+If the library is missing this module raises; there is no fallback of any kind.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libretention.so")
+
+RET_OK, RET_ERR_INVALID_ARG, RET_ERR_UNSUPPORTED, RET_ERR_WORKSPACE, RET_ERR_DEVICE = range(5)
+RET_F32, RET_BF16 = 0, 1
+RET_FN_CHUNKWISE, RET_FN_RECURRENT_STEP, RET_FN_PARALLEL = 0, 1, 2
+
+EXPORTED = [
+    "retention_chunkwise_fwd", "retention_recurrent_step", "retention_parallel_fwd", "retention_workspace_bytes",
+    "retention_status_string", "retention_last_error", "retention_abi_version",
+]
+
+
+class RetShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class RetGroupNorm(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int32), ("eps", ctypes.c_float), ("weight", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p)]
+
+
+class RetentionError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libretention.so and declare its signatures. Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m linear_recurrent_sequence_chunkwise_amd.build` "
+                           "(the retention library has no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)
+    sp, gp = ctypes.POINTER(RetShape), ctypes.POINTER(RetGroupNorm)
+    lib.retention_chunkwise_fwd.argtypes = [sp, i32, vp, vp, vp, dp, vp, gp, vp, vp, vp, sz, vp]
+    lib.retention_recurrent_step.argtypes = [sp, vp, vp, vp, dp, vp, gp, vp, vp, sz, vp]
+    lib.retention_parallel_fwd.argtypes = [sp, vp, vp, vp, dp, gp, vp, vp, sz, vp]
+    for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd):
+        f.restype = ctypes.c_int
+    lib.retention_workspace_bytes.argtypes = [i32, sp, i32, i32]
+    lib.retention_workspace_bytes.restype = sz
+    lib.retention_status_string.argtypes = [i32]
+    lib.retention_status_string.restype = ctypes.c_char_p
+    lib.retention_last_error.argtypes = []
+    lib.retention_last_error.restype = ctypes.c_char_p
+    lib.retention_abi_version.argtypes = []
+    lib.retention_abi_version.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != RET_OK:
+        lib = load_library()
+        raise RetentionError(status, f"{lib.retention_status_string(status).decode()}: "
+                                     f"{lib.retention_last_error().decode()}")
+
+
+@dataclass
+class GroupNorm:
+    """Per-head GroupNorm epilogue: y = (o - mean) / sqrt(var + eps) * weight[h] + bias[h] over d_v."""
+    eps: float = 1e-5
+    weight: Optional[torch.Tensor] = None  # fp32 [H, d_v] on the device, or None
+    bias: Optional[torch.Tensor] = None
+
+    def as_struct(self):
+        for t in (self.weight, self.bias):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError("groupnorm weight/bias must be contiguous fp32 device tensors")
+        return RetGroupNorm(1, float(self.eps), _ptr(self.weight), _ptr(self.bias))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return RET_F32
+    if dt == torch.bfloat16:
+        return RET_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _torch_dtype(code):
+    return torch.bfloat16 if code == RET_BF16 else torch.float32
+
+
+def _gamma(gamma, H):
+    g = [float(x) for x in (gamma.tolist() if hasattr(gamma, "tolist") else gamma)]
+    if len(g) != H:
+        raise ValueError(f"gamma has {len(g)} entries, expected {H}")
+    return (ctypes.c_double * H)(*g)
+
+
+def _stream(dev, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape(B, H, N, dk, dv, in_code, out_code):
+    return RetShape(B, H, N, dk, dv, in_code, out_code)
+
+
+def _check_inputs(q, k, v, ndim):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != ndim:
+            raise ValueError(f"{name} must have {ndim} dimensions")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+
+
+def workspace_bytes(fn, B, H, N, dk, dv, in_dtype, out_dtype, chunk=0, groupnorm=False):
+    lib = load_library()
+    shp = _shape(B, H, N, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype))
+    n = lib.retention_workspace_bytes(fn, ctypes.byref(shp), int(chunk), int(bool(groupnorm)))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid shape for workspace query")
+    return n
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace, workspace.numel() * workspace.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, nbytes
+
+
+def chunkwise_fwd(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None, groupnorm: Optional[GroupNorm] = None,
+                  out=None, state_out=None, out_dtype=torch.float32, want_out=True, want_state=True, workspace=None,
+                  stream=None):
+    """Chunkwise retention forward. q, k: [B,H,N,dk]; v: [B,H,N,dv] (fp32 or bf16, device).
+    Returns (out [B,H,N,dv] of out_dtype or None, state_out fp32 [B,H,dk,dv] or None).
+    state_out may be passed as the same tensor as state_in (in place)."""
+    lib = load_library()
+    _check_inputs(q, k, v, 4)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    in_code = _dtype_code(q.dtype)
+    if out is not None:
+        out_dtype = out.dtype
+    out_code = _dtype_code(out_dtype)
+    if want_out and out is None:
+        out = torch.empty((B, H, N, dv), dtype=out_dtype, device=q.device)
+    if not want_out:
+        out = None
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if not want_state:
+        state_out = None
+    gn = groupnorm.as_struct() if groupnorm is not None else None
+    shp = _shape(B, H, N, dk, dv, in_code, out_code)
+    need = lib.retention_workspace_bytes(RET_FN_CHUNKWISE, ctypes.byref(shp), int(chunk),
+                                         int(gn is not None and out is not None))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # the call itself reports the invalid argument
+    ws, wsb = _workspace(need, q.device, workspace)
+    st = lib.retention_chunkwise_fwd(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H),
+                                     _ptr(state_in), ctypes.byref(gn) if gn is not None else None, _ptr(out),
+                                     _ptr(state_out), _ptr(ws), wsb, _stream(q.device, stream))
+    _check(st)
+    return out, state_out
+
+
+def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optional[GroupNorm] = None, out=None,
+                   out_dtype=torch.float32, want_out=True, stream=None):
+    """One recurrent step: state <- g*state + k^T v (in place), o = q state.
+    q, k: [B,H,dk]; v: [B,H,dv]; state: fp32 [B,H,dk,dv]. Returns o [B,H,dv] (or None)."""
+    lib = load_library()
+    _check_inputs(q, k, v, 3)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if not (state.is_cuda and state.is_contiguous() and state.dtype == torch.float32):
+        raise ValueError("state must be a contiguous fp32 device tensor")
+    if out is not None:
+        out_dtype = out.dtype
+    if want_out and out is None:
+        out = torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
+    if not want_out:
+        out = None
+    gn = groupnorm.as_struct() if groupnorm is not None else None
+    shp = _shape(B, H, 1, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    st = lib.retention_recurrent_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _ptr(state),
+                                      ctypes.byref(gn) if gn is not None else None, _ptr(out), None, 0,
+                                      _stream(q.device, stream))
+    _check(st)
+    return out
+
+
+def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNorm] = None, out=None,
+                 out_dtype=torch.float32, workspace=None, stream=None):
+    """Parallel form O = (Q K^T (.) D) V. Returns out [B,H,N,dv]."""
+    lib = load_library()
+    _check_inputs(q, k, v, 4)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if out is not None:
+        out_dtype = out.dtype
+    else:
+        out = torch.empty((B, H, N, dv), dtype=out_dtype, device=q.device)
+    gn = groupnorm.as_struct() if groupnorm is not None else None
+    shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    need = lib.retention_workspace_bytes(RET_FN_PARALLEL, ctypes.byref(shp), 0, int(gn is not None))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0
+    ws, wsb = _workspace(need, q.device, workspace)
+    st = lib.retention_parallel_fwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H),
+                                    ctypes.byref(gn) if gn is not None else None, _ptr(out), _ptr(ws), wsb,
+                                    _stream(q.device, stream))
+    _check(st)
+    return out

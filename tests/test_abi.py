@@ -1,0 +1,171 @@
+"""C-ABI contract on the CPU: the library loads, exports what include/retention.h declares, and
+rejects invalid arguments on the host before any HIP call (so no GPU is needed here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from linear_recurrent_sequence_chunkwise_amd import retention as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "retention.h")
+
+# fake, 16-byte aligned, far-apart device addresses: validation never dereferences them
+Q, K, V, OUT, ST, WS, GW = (ctypes.c_void_p(i << 36) for i in range(1, 8))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return R.load_library()
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(retention_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert set(syms) == set(R.EXPORTED)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.retention_abi_version() == 1
+    for s in range(5):
+        assert lib.retention_status_string(s).decode().startswith("RET_")
+    assert lib.retention_status_string(99).decode() == "unknown status"
+
+
+def shape(B=1, H=2, N=256, dk=64, dv=64, i=R.RET_BF16, o=R.RET_F32):
+    return R.RetShape(B, H, N, dk, dv, i, o)
+
+
+def gam(vals):
+    return (ctypes.c_double * len(vals))(*vals)
+
+
+def chunk(lib, shp=None, C=64, q=Q, k=K, v=V, g=None, sin=None, gn=None, out=OUT, sout=ST, ws=WS, wsb=1 << 40):
+    shp = shp if shp is not None else shape()
+    g = g if g is not None else gam([0.9] * shp.heads)
+    return lib.retention_chunkwise_fwd(ctypes.byref(shp), C, q, k, v, g, sin, gn, out, sout, ws, wsb, None)
+
+
+def test_null_shape(lib):
+    assert lib.retention_chunkwise_fwd(None, 64, Q, K, V, gam([0.9]), None, None, OUT, ST, WS, 1 << 40, None) == R.RET_ERR_INVALID_ARG
+    assert "shape" in lib.retention_last_error().decode()
+
+
+@pytest.mark.parametrize("field,val", [("batch", 0), ("heads", -1), ("seq_len", 0), ("d_k", 0), ("d_v", -3)])
+def test_bad_dims(lib, field, val):
+    s = shape()
+    setattr(s, field, val)
+    assert chunk(lib, s) == R.RET_ERR_INVALID_ARG
+
+
+def test_bad_dtype(lib):
+    assert chunk(lib, shape(i=7)) == R.RET_ERR_INVALID_ARG
+    assert chunk(lib, shape(o=-1)) == R.RET_ERR_INVALID_ARG
+
+
+def test_too_many_heads(lib):
+    s = shape(H=129)
+    assert chunk(lib, s, g=gam([0.9] * 129)) == R.RET_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v"])
+def test_null_inputs(lib, which):
+    kw = {which: None}
+    assert chunk(lib, **kw) == R.RET_ERR_INVALID_ARG
+    assert which in lib.retention_last_error().decode()
+
+
+def test_misaligned(lib):
+    assert chunk(lib, q=ctypes.c_void_p((1 << 36) + 8)) == R.RET_ERR_INVALID_ARG
+    assert "aligned" in lib.retention_last_error().decode()
+    assert chunk(lib, sout=ctypes.c_void_p((5 << 36) + 4)) == R.RET_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("g", [0.0, -0.5, 1.5, math.nan, math.inf])
+def test_bad_gamma(lib, g):
+    assert chunk(lib, g=gam([0.9, g])) == R.RET_ERR_INVALID_ARG
+    assert "gamma[1]" in lib.retention_last_error().decode()
+
+
+def test_null_gamma(lib):
+    s = shape()
+    assert lib.retention_chunkwise_fwd(ctypes.byref(s), 64, Q, K, V, None, None, None, OUT, ST, WS, 1 << 40, None) == R.RET_ERR_INVALID_ARG
+
+
+def test_no_outputs(lib):
+    assert chunk(lib, out=None, sout=None) == R.RET_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("eps", [0.0, -1e-5, math.nan])
+def test_bad_eps(lib, eps):
+    gn = R.RetGroupNorm(1, eps, None, None)
+    assert chunk(lib, gn=ctypes.byref(gn)) == R.RET_ERR_INVALID_ARG
+
+
+def test_unsupported_chunk_and_dims(lib):
+    assert chunk(lib, C=96) == R.RET_ERR_UNSUPPORTED
+    assert chunk(lib, C=0) == R.RET_ERR_INVALID_ARG
+    assert chunk(lib, shape(dk=48)) == R.RET_ERR_UNSUPPORTED
+    assert chunk(lib, shape(i=R.RET_F32), C=256) == R.RET_ERR_UNSUPPORTED
+    s = shape(dk=64, dv=64)
+    assert lib.retention_parallel_fwd(ctypes.byref(shape(dk=128, dv=64)), Q, K, V, gam([0.9, 0.9]), None, OUT, WS, 1 << 40,
+                                      None) == R.RET_ERR_UNSUPPORTED
+    del s
+
+
+def test_aliasing(lib):
+    assert chunk(lib, out=Q) == R.RET_ERR_INVALID_ARG
+    assert "alias" in lib.retention_last_error().decode()
+    assert chunk(lib, out=ST, sout=ST) == R.RET_ERR_INVALID_ARG
+    partly = ctypes.c_void_p((5 << 36) + 256)
+    assert chunk(lib, sin=ST, sout=partly) == R.RET_ERR_INVALID_ARG
+
+
+def test_workspace(lib):
+    s = shape()
+    need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(s), 64, 0)
+    assert 0 < need < (1 << 40)
+    # bf16 chunkwise holds one bf16 C x C score block per chunk
+    assert need >= 1 * 2 * 4 * 64 * 64 * 2
+    assert chunk(lib, ws=None, wsb=0) == R.RET_ERR_WORKSPACE
+    assert chunk(lib, wsb=need - 1) == R.RET_ERR_WORKSPACE
+    assert "workspace" in lib.retention_last_error().decode()
+    assert lib.retention_workspace_bytes(R.RET_FN_RECURRENT_STEP, ctypes.byref(shape(N=1)), 0, 1) == 0
+    assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, None, 64, 0) == ctypes.c_size_t(-1).value
+    assert lib.retention_workspace_bytes(9, ctypes.byref(s), 64, 0) == ctypes.c_size_t(-1).value
+    gn_need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(s), 64, 1)
+    assert gn_need > need
+
+
+def test_step_validation(lib):
+    def step(shp, state=ST, out=OUT, g=None):
+        g = g if g is not None else gam([0.9] * shp.heads)
+        return lib.retention_recurrent_step(ctypes.byref(shp), Q, K, V, g, state, None, out, None, 0, None)
+    assert step(shape(N=2)) == R.RET_ERR_INVALID_ARG
+    assert step(shape(N=1), state=None) == R.RET_ERR_INVALID_ARG
+    assert step(shape(N=1, dv=6)) == R.RET_ERR_UNSUPPORTED
+    assert step(shape(N=1, dv=4 * 3 * 5)) == R.RET_ERR_UNSUPPORTED
+    assert step(shape(N=1), out=ST) == R.RET_ERR_INVALID_ARG
+    assert step(shape(N=1), g=gam([0.9, 2.0])) == R.RET_ERR_INVALID_ARG
+
+
+def test_error_is_thread_local(lib):
+    import threading
+    assert chunk(lib, C=96) == R.RET_ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.retention_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "chunk" in lib.retention_last_error().decode()

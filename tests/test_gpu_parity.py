@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle, element by element.
+
+Metric (fp64 over the whole compared tensor): max|gpu - oracle| / RMS(oracle).
+Bounds: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32 accumulation.
+The oracle always reads back the exact values the GPU consumed (bf16 widened exactly to fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_sequence_chunkwise_amd import inputs as I
+from linear_recurrent_sequence_chunkwise_amd import retention as R
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    R.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def rel_err(gpu, ref):
+    g = gpu.detach().double().cpu().numpy() if hasattr(gpu, "detach") else np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    den = np.sqrt(np.mean(r * r))
+    return float(np.max(np.abs(g - r)) / den)
+
+
+def dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def report(name, e, tol):
+    print(f"  {name}: err {e:.3e} (bound {tol:g})", flush=True)
+    assert e <= tol, f"{name}: {e:.3e} > {tol:g}"
+
+
+# ---------------------------------------------------------------------------------------------
+# Workload: tiny fp32 (B=1, H=2, N=256, d=64, gamma {0.9, 0.99}, chunk 64): three forms agree
+def test_tiny_fp32_three_forms(orc):
+    w = I.WORKLOADS["retention_b1_h2_n256_d64_f32"]
+    q, k, v = I.make_workload_qkv(w)
+    gam = w.gamma_list()
+    ref, ref_s = orc.recurrent(q, k, v, gam)
+    qd, kd, vd = dev(q, k, v)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, 64)
+    report("chunkwise out", rel_err(o, ref), TOL["f32"])
+    report("chunkwise state", rel_err(s, ref_s), TOL["f32"])
+    report("parallel out", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref), TOL["f32"])
+    st = torch.zeros((1, 2, 64, 64), dtype=torch.float32, device=DEV)
+    outs = [R.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), gam, st)
+            for n in range(w.N)]
+    report("recurrent steps out", rel_err(torch.stack(outs, dim=2), ref), TOL["f32"])
+    report("recurrent steps state", rel_err(st, ref_s), TOL["f32"])
+
+
+@pytest.mark.parametrize("N,C", [(250, 64), (1, 64), (63, 128), (300, 128)])
+def test_fp32_ragged_state_in_groupnorm(orc, N, C):
+    B, H, dk, dv = 2, 3, 64, 128
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "f32", seed=100 + N)
+    s0 = I.make_state(B, H, dk, dv, seed=7, scale=0.05)
+    gam = [0.5, 0.95, 1.0]
+    ref, ref_s = orc.recurrent(q, k, v, gam, state_in=s0)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d)
+    report(f"fp32 N={N} C={C} out", rel_err(o, ref), TOL["f32"])
+    report(f"fp32 N={N} C={C} state", rel_err(s, ref_s), TOL["f32"])
+    gw = torch.randn(H, dv, generator=torch.Generator().manual_seed(3)).float()
+    gb = torch.randn(H, dv, generator=torch.Generator().manual_seed(4)).float()
+    gn = R.GroupNorm(1e-5, gw.to(DEV), gb.to(DEV))
+    ref_gn = orc.groupnorm(ref, 1e-5, gw, gb)
+    o2, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, groupnorm=gn)
+    report(f"fp32 GN N={N} C={C}", rel_err(o2, ref_gn), TOL["f32"])
+    o3, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, groupnorm=gn, out_dtype=torch.bfloat16, want_state=False)
+    # fp32 arithmetic plus one round-to-nearest bf16 store: |error| <= 2^-8 |y| per element
+    bound = 2.0 ** -8 * np.abs(ref_gn).max() / np.sqrt(np.mean(ref_gn ** 2)) + TOL["f32"]
+    report(f"fp32 GN bf16-out N={N}", rel_err(o3, ref_gn), bound)
+    ref_p = orc.parallel(q, k, v, gam)
+    report(f"fp32 parallel N={N}", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref_p), TOL["f32"])
+
+
+# ---------------------------------------------------------------------------------------------
+# Workload: bf16 B=4, H=8, N=2048, d=64, chunk 128, fp32 out
+def test_bf16_small_chunkwise_and_parallel(orc):
+    w = I.WORKLOADS["retention_b4_h8_n2048_d64_bf16"]
+    q, k, v = I.make_workload_qkv(w)
+    gam = w.gamma_list()
+    ref, ref_s = orc.recurrent(q, k, v, gam)
+    qd, kd, vd = dev(q, k, v)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, 128)
+    report("chunkwise out", rel_err(o, ref), TOL["bf16"])
+    report("chunkwise state", rel_err(s, ref_s), TOL["bf16"])
+    report("parallel out", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref), TOL["bf16"])
+    for C in (64, 256, 512):
+        o, s = R.chunkwise_fwd(qd, kd, vd, gam, C)
+        report(f"chunkwise C={C} out", rel_err(o, ref), TOL["bf16"])
+        report(f"chunkwise C={C} state", rel_err(s, ref_s), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
+@pytest.mark.parametrize("N,C", [(1, 64), (37, 64), (250, 128), (700, 256), (1100, 512)])
+def test_bf16_ragged_state_in(orc, dk, dv, N, C):
+    B, H = 1, 4
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=200 + N + dk)
+    s0 = I.make_state(B, H, dk, dv, seed=9, scale=0.02)
+    gam = I.multiscale_gammas(H)
+    ref, ref_s = orc.recurrent(q, k, v, gam, state_in=s0)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d)
+    report(f"bf16 dk={dk} N={N} C={C} out", rel_err(o, ref), TOL["bf16"])
+    report(f"bf16 dk={dk} N={N} C={C} state", rel_err(s, ref_s), TOL["bf16"])
+    # state-only prefill (out = NULL) gives the same state
+    _, s_only = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, want_out=False)
+    report(f"bf16 dk={dk} N={N} C={C} state-only", rel_err(s_only, ref_s), TOL["bf16"])
+    # in-place state: state_out is state_in
+    s_inplace = s0d.clone()
+    R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s_inplace, state_out=s_inplace)
+    report(f"bf16 dk={dk} N={N} C={C} in-place state", rel_err(s_inplace, ref_s), TOL["bf16"])
+
+
+def test_bf16_parallel_layer_shape_groupnorm(orc):
+    B, H, N, dk, dv = 1, 4, 1000, 256, 512
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=31)
+    gam = I.multiscale_gammas(16)[::4]
+    ref = orc.parallel(q, k, v, gam)
+    qd, kd, vd = dev(q, k, v)
+    report("parallel layer-shape out", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref), TOL["bf16"])
+    gw = (1.0 + 0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(5))).float()
+    gb = (0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(6))).float()
+    gn = R.GroupNorm(1e-5, gw.to(DEV), gb.to(DEV))
+    ref_gn = orc.groupnorm(ref, 1e-5, gw, gb)
+    report("parallel GN bf16 out", rel_err(R.parallel_fwd(qd, kd, vd, gam, groupnorm=gn, out_dtype=torch.bfloat16), ref_gn),
+           TOL["bf16"])
+    o, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=gn, out_dtype=torch.bfloat16, want_state=False)
+    report("chunkwise GN affine bf16 out", rel_err(o, ref_gn), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------------------------
+# Workload: 6.7B-layer shape, B=1, H=16, N=8192, dk=256, dv=512, chunk 128, GroupNorm eps 1e-5, bf16 out
+def test_layer_6p7b_chunkwise_groupnorm_full(orc):
+    w = I.WORKLOADS["retention_b1_h16_n8192_dk256_dv512_bf16_gn"]
+    q, k, v = I.make_workload_qkv(w)
+    gam = w.gamma_list()
+    qd, kd, vd = dev(q, k, v)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=R.GroupNorm(w.eps), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, ref_s = orc.recurrent(q, k, v, gam)
+    ref_gn = orc.groupnorm(ref, w.eps)
+    e = rel_err(o, ref_gn)
+    report("6.7B-layer GN bf16 out", e, TOL["bf16"])
+    # Storing even the exact result in bf16 costs up to 2^-8 |y| per element; the kernel's own
+    # error must stay small on top of that floor.
+    floor = rel_err(torch.from_numpy(ref_gn).to(torch.bfloat16), ref_gn)
+    report("6.7B-layer GN bf16 out above the bf16 storage floor", e - floor, 5e-3)
+    report("6.7B-layer state", rel_err(s, ref_s), TOL["bf16"])
+    # same launch without GroupNorm, fp32 out
+    o2, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, want_state=False)
+    report("6.7B-layer no-GN fp32 out", rel_err(o2, ref), TOL["bf16"])
+
+
+def test_chunkwise_bitwise_deterministic():
+    w = I.WORKLOADS["retention_b1_h16_n8192_dk256_dv512_bf16_gn"]
+    q, k, v = dev(*I.make_workload_qkv(w, N=2048))
+    gam = w.gamma_list()
+    outs = [R.chunkwise_fwd(q, k, v, gam, 128, groupnorm=R.GroupNorm(w.eps), out_dtype=torch.bfloat16) for _ in range(3)]
+    for o, s in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(s, outs[0][1])
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        o, s = R.chunkwise_fwd(q, k, v, gam, 128, groupnorm=R.GroupNorm(w.eps), out_dtype=torch.bfloat16)
+    stream.synchronize()
+    assert torch.equal(o, outs[0][0]) and torch.equal(s, outs[0][1])
+
+
+def test_split_resume_and_decode_after_prefill(orc):
+    B, H, N, dk, dv = 1, 16, 1500, 256, 512
+    q, k, v = I.make_qkv(B, H, N + 1, dk, dv, "bf16", seed=41)
+    gam = I.multiscale_gammas(H)
+    ref, ref_s = orc.recurrent(q, k, v, gam)
+    qd, kd, vd = dev(q, k, v)
+    n1 = 700
+    a, sa = R.chunkwise_fwd(qd[:, :, :n1].contiguous(), kd[:, :, :n1].contiguous(), vd[:, :, :n1].contiguous(), gam, 128)
+    b, sb = R.chunkwise_fwd(qd[:, :, n1:N].contiguous(), kd[:, :, n1:N].contiguous(), vd[:, :, n1:N].contiguous(), gam, 256,
+                            state_in=sa)
+    report("split/resume out", rel_err(torch.cat([a, b], dim=2), ref[:, :, :N]), TOL["bf16"])
+    o = R.recurrent_step(qd[:, :, N].contiguous(), kd[:, :, N].contiguous(), vd[:, :, N].contiguous(), gam, sb)
+    report("decode after prefill out", rel_err(o, ref[:, :, N]), TOL["bf16"])
+    report("decode after prefill state", rel_err(sb, ref_s), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------------------------
+# Workload: decode step, 128 sequences x 16 heads, fp32 state 256 x 512 from a chunkwise prefill
+# of 8192 random bf16 tokens, one new token per sequence.
+def test_decode_step_after_8192_prefill(orc):
+    w = I.WORKLOADS["decode_b128_h16_dk256_dv512"]
+    gam = w.gamma_list()
+    B, H, dk, dv, NP = w.B, w.H, w.dk, w.dv, I.DECODE_PREFILL_TOKENS
+    state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    per = 16
+    for b0 in range(0, B, per):
+        qp, kp, vp = I.make_qkv(per, H, NP, dk, dv, "bf16", seed=w.seed * 1000 + b0, device=DEV)
+        R.chunkwise_fwd(qp, kp, vp, gam, 128, state_out=state[b0:b0 + per], want_out=False)
+        if b0 == 0:
+            qs, ks, vs = qp[:2].cpu(), kp[:2].cpu(), vp[:2].cpu()
+        del qp, kp, vp
+    torch.cuda.synchronize()
+    # prefill state on a sample of 2 sequences (all heads) against the oracle
+    _, ref_s = orc.recurrent(qs, ks, vs, gam, want_out=False)
+    report("prefill state (2 of 128 sequences)", rel_err(state[:2], ref_s), TOL["bf16"])
+    # the decode step on the exact fp32 state
+    q, k, v = I.make_qkv(B, H, 1, dk, dv, "bf16", seed=w.seed)
+    q, k, v = q[:, :, 0], k[:, :, 0], v[:, :, 0]
+    before = state.cpu()
+    qd, kd, vd = dev(q, k, v)
+    o = R.recurrent_step(qd, kd, vd, gam, state)
+    ro, rs = orc.step(q, k, v, gam, before)
+    report("decode out", rel_err(o, ro), TOL["bf16"])
+    report("decode state", rel_err(state, rs), TOL["bf16"])
+    # with GroupNorm, bf16 out, on a copy of the original state
+    st2 = before.to(DEV)
+    o2 = R.recurrent_step(qd, kd, vd, gam, st2, groupnorm=R.GroupNorm(1e-5), out_dtype=torch.bfloat16)
+    report("decode GN bf16 out", rel_err(o2, orc.groupnorm(ro[:, :, None, :], 1e-5)[:, :, 0]), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------------------------
+# Workload: long context, B=1, H=16, N=65536, dk=256, dv=512, chunk {64,128,256,512}, fp32 out.
+# The oracle runs on a sample of heads (the fastest- and slowest-decaying); chunk-size invariance
+# is checked on every head.
+def test_long_context_chunk_sweep(orc):
+    w = I.WORKLOADS["retention_b1_h16_n65536_dk256_dv512_bf16"]
+    q, k, v = I.make_workload_qkv(w)
+    gam = w.gamma_list()
+    heads = [0, 15]
+    ref, ref_s = orc.recurrent(q[:, heads], k[:, heads], v[:, heads], [gam[h] for h in heads])
+    qd, kd, vd = dev(q, k, v)
+    del q, k, v
+    first = None
+    for C in w.chunks:
+        o, s = R.chunkwise_fwd(qd, kd, vd, gam, C)
+        report(f"N=65536 C={C} out (heads 0, 15)", rel_err(o[:, heads], ref), TOL["bf16"])
+        report(f"N=65536 C={C} final state (heads 0, 15)", rel_err(s[:, heads], ref_s), TOL["bf16"])
+        if first is None:
+            first = (o[:, :, ::64].double().cpu().numpy(), s.double().cpu().numpy())
+        else:
+            report(f"C={C} vs C={w.chunks[0]} every head (sampled rows)", rel_err(o[:, :, ::64], first[0]), TOL["bf16"])
+            report(f"C={C} vs C={w.chunks[0]} state every head", rel_err(s, first[1]), TOL["bf16"])
+        del o, s
