@@ -1,0 +1,203 @@
+"""Benchmark: chunkwise retention forward at N=8192 (TFLOP/s, tokens/s) and the recurrent decode step
+(GB/s) on one MI355X, printed as one JSON line.
+
+One step = one chunkwise forward of the 6.7B-layer-shaped workload (B=1, H=16, N=8192, d_k=256,
+d_v=512, chunk 128, bf16 inputs, fp32 accumulation, per-head GroupNorm eps 1e-5, bf16 output)
+followed by one decode step of 128 sequences x 16 heads on fp32 256 x 512 states (made by a
+chunkwise prefill of 8192 random bf16 tokens). Inputs are resident in HBM before timing starts.
+
+Timing: W untimed warm-up steps, then K timed steps between device synchronisations; each part of
+each step is bracketed with HIP events recorded on the stream the library launches on.
+
+Counting rules:
+  chunkwise algorithmic FLOPs per (b, h): 2 (d_k + d_v) * causal pairs inside chunks + 4 N d_k d_v
+  decode algorithmic bytes: fp32 state read + write, bf16 q, k, v, fp32 out
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "chunkwise retention fwd TFLOP/s & tokens/s at N=8192; decode-step GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def chunk_flops(B, H, N, dk, dv, C):
+    pairs = 0
+    for c0 in range(0, N, C):
+        L = min(C, N - c0)
+        pairs += L * (L + 1) // 2
+    return B * H * (2 * (dk + dv) * pairs + 4 * N * dk * dv)
+
+
+def chunk_bytes(B, H, N, dk, dv, in_bytes=2, out_bytes=2):
+    return B * H * N * (2 * dk + dv) * in_bytes + B * H * N * dv * out_bytes
+
+
+def decode_bytes(B, H, dk, dv):
+    return B * H * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + dv * 4)
+
+
+def read_counters(name, kernel_sources):
+    """HBM traffic per dispatch from a committed rocprofv3 counter summary, if it was taken on the
+    current kernel source (sha256 recorded in the summary); else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for src in kernel_sources:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the retention path is "
+              "single-GPU: heads and sequences are independent and would shard without communication)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_recurrent_sequence_chunkwise_amd import inputs as I
+    from linear_recurrent_sequence_chunkwise_amd import retention as R
+
+    R.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- chunkwise workload
+    w = I.WORKLOADS["retention_b1_h16_n8192_dk256_dv512_bf16_gn"]
+    C = w.chunks[0]
+    q, k, v = (t.to(dev) for t in I.make_workload_qkv(w))
+    gam = w.gamma_list()
+    gn = R.GroupNorm(w.eps)
+    out = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev)
+    st_out = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws_bytes = R.workspace_bytes(R.RET_FN_CHUNKWISE, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.bfloat16, C, True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    # ---- decode workload: state from a chunkwise prefill of 8192 tokens
+    d = I.WORKLOADS["decode_b128_h16_dk256_dv512"]
+    dgam = d.gamma_list()
+    state = torch.empty((d.B, d.H, d.dk, d.dv), dtype=torch.float32, device=dev)
+    per = 16
+    for b0 in range(0, d.B, per):
+        qp, kp, vp = I.make_qkv(per, d.H, I.DECODE_PREFILL_TOKENS, d.dk, d.dv, "bf16", seed=d.seed * 1000 + b0, device=dev)
+        R.chunkwise_fwd(qp, kp, vp, dgam, 128, state_out=state[b0:b0 + per], want_out=False)
+        del qp, kp, vp
+    qn, kn, vn = (t[:, :, 0].contiguous().to(dev) for t in I.make_qkv(d.B, d.H, 1, d.dk, d.dv, "bf16", seed=d.seed))
+    dout = torch.empty((d.B, d.H, d.dv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("setup done")
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        R.chunkwise_fwd(q, k, v, gam, C, groupnorm=gn, out=out, state_out=st_out, workspace=ws, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        R.recurrent_step(qn, kn, vn, dgam, state, out=dout, stream=stream)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_chunk = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    t_step = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; chunkwise {t_chunk * 1e6:.1f} us, decode {t_dec * 1e6:.1f} us")
+
+    cf = chunk_flops(w.B, w.H, w.N, w.dk, w.dv, C)
+    cb = chunk_bytes(w.B, w.H, w.N, w.dk, w.dv) + 2 * w.B * w.H * w.dk * w.dv * 4  # + state out (fp32) read/written once
+    db = decode_bytes(d.B, d.H, d.dk, d.dv)
+    chunk_tflops = cf / t_chunk / 1e12
+    tokens_per_s = w.B * w.N / t_chunk
+    dec_gbps = db / t_dec / 1e9
+
+    dec_traffic = read_counters("recurrent_step_kernel_decode_b128_h16_dk256_dv512_pmc.txt",
+                                ["linear_recurrent_sequence_chunkwise_amd/csrc/recurrent_step.hip",
+                                 "linear_recurrent_sequence_chunkwise_amd/csrc/common.hpp"])
+    roofline = {"kernel": "recurrent_step_kernel (decode step, 128 x 16 states)", "bound": "hbm",
+                "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": dec_traffic,
+                "algorithmic_bytes_per_launch": db, "avg_launch_us": round(t_dec * 1e6, 2)}
+    ch_traffic = read_counters("chunkwise_layer_b1_h16_n8192_pmc.txt",
+                               ["linear_recurrent_sequence_chunkwise_amd/csrc/chunkwise_bf16.hip",
+                                "linear_recurrent_sequence_chunkwise_amd/csrc/common.hpp"])
+    roofline_chunk = {"kernel": "chunkwise forward call (scores + fused chunk kernels)", "bound": "hbm",
+                      "achieved": round(cb / t_chunk / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(cb / t_chunk / 1e9 / HBM_PEAK_GBPS, 4), "traffic": ch_traffic,
+                      "mfma_bf16_tflops": round(chunk_tflops, 2), "mfma_bf16_peak": BF16_MFMA_PEAK_TFLOPS,
+                      "mfma_frac": round(chunk_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                      "algorithmic_flops_per_launch": cf, "algorithmic_bytes_per_launch": cb,
+                      "avg_launch_us": round(t_chunk * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        threads = orc.threads()
+        qc, kc, vc = I.make_workload_qkv(w)
+        t1 = time.perf_counter()
+        ref, _ = orc.recurrent(qc, kc, vc, gam, want_state=False)
+        orc.groupnorm(ref, w.eps)
+        tc = time.perf_counter() - t1
+        cpu = {"value": round(cf / tc / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole N=8192 layer workload (16 heads x 8192 tokens, recurrent form + GroupNorm, fp64), "
+                         f"{tc:.2f} s; rate counted with the same chunkwise algorithmic FLOPs",
+               "tokens_per_s": round(w.B * w.N / tc, 1)}
+        log(f"oracle: {tc:.2f} s on {threads} threads")
+
+    line = {
+        "metric": METRIC, "value": round(chunk_tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "retention_b1_h16_n8192_dk256_dv512_bf16_gn (chunk 128, GroupNorm, bf16 out) + "
+                               "decode_b128_h16_dk256_dv512 (fp32 state)",
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens_per_s, 1), "chunkwise_us": round(t_chunk * 1e6, 2),
+        "decode_GBps": round(dec_gbps, 1), "decode_us": round(t_dec * 1e6, 2),
+        "decode_tokens_per_s": round(d.B / t_dec, 1),
+        "roofline": roofline if t_dec >= t_chunk else roofline_chunk,
+        "roofline_other": roofline_chunk if t_dec >= t_chunk else roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
