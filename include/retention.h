@@ -123,7 +123,11 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Bytes of device workspace the call `fn` needs for this shape, chunk and GroupNorm setting.
- * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid. */
+ * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid.
+ * Chunkwise with bf16 inputs: the bf16 intra-chunk scores (B*H*ceil(N/chunk)*chunk^2*2 bytes)
+ * when an output is wanted, plus fp32 pre-norm rows (B*H*N*d_v*4 bytes) with GroupNorm. Other
+ * calls: fp32 staging rows when GroupNorm or a bf16 output needs them. The caller owns it; its
+ * contents are scratch and need no initialisation. */
 size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t gn_enabled);
 
 /* Static description of a status code. */

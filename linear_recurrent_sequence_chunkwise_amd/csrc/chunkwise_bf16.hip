@@ -6,23 +6,22 @@
 //     o_j = [(Q K^T (.) D) V]_j + g^(j+1) [Q R]_j,      D[j][t] = g^(j-t) for t <= j
 //     R  <- g^L R + K^T (V (.) zeta),                    zeta_t = g^(L-1-t)
 //
-// Two kernels:
+// Kernels:
 //   chunk_scores_kernel   parallel over (64-row band, chunk, b*h): P = (Q K^T) (.) D on MFMA with the
 //                         decay and causal mask applied in registers, stored as bf16 in the workspace
 //                         (32-key blocks on and below the diagonal). Q and K go through LDS with all
 //                         loads of a block issued together; the next key block is prefetched.
-//   chunk_main_kernel     one workgroup per (b, h, 32-column slice of d_v), walking the sequence in
-//                         32-token stages. Each stage's Q, K, V and P rows are prefetched into
-//                         registers two stages ahead, then written to LDS. Per stage:
-//                           out  = g^(j+1) Q R + P V      (R from the previous chunk, as bf16 hi + lo,
-//                                                         held in registers for the whole chunk)
+//   chunk_ws_kernel       (chunks up to 256, output wanted) one workgroup per (b, h, 32-column slice
+//                         of d_v), walking the sequence in 32-token stages, with state waves and
+//                         output waves (see the kernel):
+//                           out  = g^(j+1) Q R + P V      (R of the previous chunk as bf16 hi + lo)
 //                           R   += K^T (V (.) zeta)       (V (.) zeta as bf16 hi + lo; R fp32 in
 //                                                         accumulators, scaled by g^L at chunk start)
-//                         The optional per-head GroupNorm needs statistics over all d_v columns,
-//                         which 16 workgroups share: they exchange tagged per-row partial
-//                         statistics through global memory (see the kernel), with workgroups
-//                         co-resident through a cooperative launch. The slices of one head sit on
-//                         one XCD to share L2.
+//   chunk_main_kernel     the same per stage with every wave doing both parts (512-token chunks, and
+//                         state-only prefills, which have no output part).
+//   gn_rows_kernel        the optional per-head GroupNorm over d_v, on fp32 pre-norm rows that the
+//                         chunk kernel writes to the workspace.
+// The d_v slices of one head sit on one XCD to share its L2.
 #include "common.hpp"
 
 namespace ret {
@@ -31,11 +30,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kW = 32;     // d_v columns per workgroup
 constexpr int kST = 32;    // tokens per pipeline stage
-constexpr int kRingP = 8;  // GroupNorm partials ring (stages); >= 6 needed for the reuse argument
-constexpr int kRingM = 8;  // GroupNorm merged-statistics ring (stages); >= 4 needed
-constexpr int kRedLag = 2; // the reducer of stage x merges its partials during stage x + kRedLag
-constexpr int kGnLag = 5;  // stage x is normalised and stored during stage x + kGnLag
-constexpr unsigned kSpinLimit = 1u << 24;
 
 // ---------------------------------------------------------------------------------------------
 // P = (Q K^T) (.) D. Grid (C/64 bands, nchunks, B*H). Wave w owns row tile t = 4*band + w and
@@ -116,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scores_kernel(int H, int N, in
 
 // ---------------------------------------------------------------------------------------------
 struct MainParams {
-    int H, N, C, NS, nchunks, nteams_launch, team_base;
+    int H, N, C, NS, nchunks, teams;
     const bf16* q;
     const bf16* k;
     const bf16* v;
@@ -124,10 +118,6 @@ struct MainParams {
     const float* state_in;
     float* state_out;
     void* out;
-    unsigned long long* part;    // [teams][kRingP][NP][32] x 2 tagged words: per-16-column row partials
-    unsigned long long* merged;  // [teams][kRingM][32] x 2 tagged words: (mean, 1/std) per row
-    unsigned* err_flag;
-    GnArgs gn;
 };
 
 template <int DK, int C>
@@ -160,43 +150,25 @@ struct StageRegs {
 };
 
 __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-__device__ __forceinline__ unsigned long long tagged(float x, unsigned tag) {
-    return ((unsigned long long)tag << 32) | __builtin_bit_cast(unsigned, x);
-}
-__device__ __forceinline__ float untag(unsigned long long w) { return __builtin_bit_cast(float, (unsigned)w); }
-__device__ __forceinline__ unsigned long long ld_tagged(const unsigned long long* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_tagged(unsigned long long* p, unsigned long long w) {
-    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Merge two (mean, M2) summaries of n values each. Symmetric in its arguments, so every lane of a
-// butterfly ends with the bitwise-same result.
-__device__ __forceinline__ void merge_eq(float& mean, float& m2, float om, float o2, float n) {
-    const float d = om - mean;
-    m2 = (m2 + o2) + d * d * (n * 0.5f);
-    mean = (mean + om) * 0.5f;
+// Team and slice of this workgroup. Workgroup i runs on XCD i % 8: with a multiple of 8 teams,
+// all slices of a team share i % 8 and therefore one L2.
+__device__ __forceinline__ void team_slice(int teams, int NS, int& team, int& slice) {
+    const int i = blockIdx.x;
+    if (teams % 8 == 0) {
+        team = (i % 8) + 8 * (i / (8 * NS));
+        slice = (i / 8) % NS;
+    } else {
+        team = i / NS;
+        slice = i % NS;
+    }
 }
 
 // One (b, h, d_v slice) per workgroup. Wave w owns R rows [w*DK/4, (w+1)*DK/4) (state update) and,
 // in every 32-token stage, the 16 x 16 output tile (rows 16*(w>>1), columns 16*(w&1)).
-//
-// GroupNorm exchange (no counters, no fences): every value is published as a 64-bit atomic store
-// whose high half is a tag (stage + 1), so a reader knows whether it sees the current stage.
-//   stage g, end:   each wave publishes per-row (mean, M2) of its 16 columns for stage g;
-//   stage g, end:   the slice (g-2) % NS ("reducer") merges all partials of stage g-2 in a fixed
-//                   order and publishes (mean, 1/std) per row;
-//   stage g, end:   every workgroup normalises and stores its stage g-5 tile, using the merged
-//                   statistics it loaded during stage g-1.
-// The loads feeding these steps are issued at the start of a stage, ahead of the prefetch, so that
-// waiting for them never waits for the prefetch; a stale tag (rare) makes the lane re-load until
-// the tag matches.
-template <int DK, int C, typename TOUT, bool GN, bool WANT_OUT>
+template <int DK, int C, typename TOUT, bool WANT_OUT>
 __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, HeadConsts hc) {
     using G = MainGeom<DK, C>;
     constexpr int RTR = DK / 64;  // 16-row R tiles per wave
@@ -212,20 +184,10 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     bf16* VZl = reinterpret_cast<bf16*>(smem + G::OFF_ZL);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
-    // XCD-aware placement: workgroup i runs on XCD i % 8. With a multiple of 8 teams per launch,
-    // all slices of a team share i % 8 and therefore one L2.
-    int team_local, slice;
-    if (p.nteams_launch % 8 == 0) {
-        const int i = blockIdx.x;
-        team_local = (i % 8) + 8 * (i / (8 * p.NS));
-        slice = (i / 8) % p.NS;
-    } else {
-        team_local = blockIdx.x / p.NS;
-        slice = blockIdx.x % p.NS;
-    }
-    const int bh = p.team_base + team_local;
+    int bh, slice;
+    team_slice(p.teams, p.NS, bh, slice);
     const int h = bh % p.H;
-    const int N = p.N, DV = p.NS * kW, NS = p.NS;
+    const int N = p.N, DV = p.NS * kW;
     const float l2g = hc.log2g[h];
     const int col0 = slice * kW;
     const int nchunks = p.nchunks;
@@ -359,142 +321,6 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
         }
     };
 
-    // ---- GroupNorm exchange state (see the comment above the kernel)
-    const int NP = 2 * NS;                 // 16-column partials per row
-    const int LPR = NP < 8 ? NP : 8;       // reducer lanes per row
-    const int PPL = NP < 8 ? 1 : NP / 8;   // partials merged locally per reducer lane (<= 4)
-    unsigned long long* part_team = p.part + (size_t)bh * kRingP * NP * kST * 2;
-    unsigned long long* merged_team = p.merged + (size_t)bh * kRingM * kST * 2;
-    // affine parameters of this lane's output column, loaded once
-    float gw = 1.f, gb = 0.f;
-    if constexpr (GN) {
-        const int c = col0 + 16 * ct_o + c16;
-        if (p.gn.weight) gw = p.gn.weight[(size_t)h * DV + c];
-        if (p.gn.bias) gb = p.gn.bias[(size_t)h * DV + c];
-    }
-    f32x4 pend[kGnLag];  // output tiles of stages g-1 .. g-kGnLag (pend[k] = stage g-1-k)
-#pragma unroll
-    for (int k = 0; k < kGnLag; ++k) pend[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    unsigned long long red_w[4][2];   // reducer: this lane's loaded partials
-    unsigned long long mrg_w[2][2];   // (mean, 1/std) of row 4*g4 + (c16 & 3), for two stages in flight
-    const int rrow = 8 * w + (lane >> 3), rk8 = lane & 7;  // reducer: row and lane within the row
-    const int mrow = 16 * rt_o + 4 * g4 + (c16 & 3);       // row whose merged statistics this lane loads
-
-    auto spin_fail = [&]() __attribute__((always_inline)) { atomicOr(p.err_flag, 1u); };
-    auto reducer_issue = [&](int gr) __attribute__((always_inline)) {
-        const unsigned long long* src = part_team + (size_t)(gr % kRingP) * NP * kST * 2;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pi = (NP < 8 ? rk8 % NP : rk8 + 8 * j);
-            if (j < PPL) {
-                red_w[j][0] = ld_tagged(src + ((size_t)pi * kST + rrow) * 2);
-                red_w[j][1] = ld_tagged(src + ((size_t)pi * kST + rrow) * 2 + 1);
-            }
-        }
-    };
-    auto reducer_finish = [&](int gr) __attribute__((always_inline)) {
-        const unsigned tag = (unsigned)gr + 1u;
-        const unsigned long long* src = part_team + (size_t)(gr % kRingP) * NP * kST * 2;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < PPL) {
-                const int pi = (NP < 8 ? rk8 % NP : rk8 + 8 * j);
-                if ((unsigned)(red_w[j][0] >> 32) != tag || (unsigned)(red_w[j][1] >> 32) != tag) {
-                    unsigned spins = 0;
-                    do {
-                        __builtin_amdgcn_s_sleep(1);
-                        red_w[j][0] = ld_tagged(src + ((size_t)pi * kST + rrow) * 2);
-                        red_w[j][1] = ld_tagged(src + ((size_t)pi * kST + rrow) * 2 + 1);
-                        if (++spins > kSpinLimit) { spin_fail(); break; }
-                    } while ((unsigned)(red_w[j][0] >> 32) != tag || (unsigned)(red_w[j][1] >> 32) != tag);
-                }
-            }
-        }
-        // fixed merge tree: ((p0, p1), (p2, p3)) locally, then across the row's lanes
-        float pm[4], p2[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { pm[j] = untag(red_w[j][0]); p2[j] = untag(red_w[j][1]); }
-        float mean = pm[0], m2 = p2[0], n = 16.f;
-        if (PPL == 4) {
-            merge_eq(pm[0], p2[0], pm[1], p2[1], 16.f);
-            merge_eq(pm[2], p2[2], pm[3], p2[3], 16.f);
-            merge_eq(pm[0], p2[0], pm[2], p2[2], 32.f);
-            mean = pm[0]; m2 = p2[0]; n = 64.f;
-        } else if (PPL == 2) {
-            merge_eq(pm[0], p2[0], pm[1], p2[1], 16.f);
-            mean = pm[0]; m2 = p2[0]; n = 32.f;
-        }
-        for (int off = 1; off < LPR; off <<= 1) {
-            const float om = __shfl_xor(mean, off, 64), o2 = __shfl_xor(m2, off, 64);
-            merge_eq(mean, m2, om, o2, n);
-            n *= 2.f;
-        }
-        if (rk8 == 0) {
-            const float rstd = rsqrtf(m2 / (float)DV + p.gn.eps);
-            unsigned long long* dst = merged_team + (size_t)(gr % kRingM) * kST * 2 + (size_t)rrow * 2;
-            st_tagged(dst, tagged(mean, tag));
-            st_tagged(dst + 1, tagged(rstd, tag));
-        }
-    };
-    auto merged_issue = [&](int gf, int b) __attribute__((always_inline)) {
-        const unsigned long long* src = merged_team + (size_t)(gf % kRingM) * kST * 2 + (size_t)mrow * 2;
-        mrg_w[b][0] = ld_tagged(src);
-        mrg_w[b][1] = ld_tagged(src + 1);
-    };
-    auto finalize = [&](f32x4 a, int gf, int b) __attribute__((always_inline)) {
-        const unsigned tag = (unsigned)gf + 1u;
-        if ((unsigned)(mrg_w[b][0] >> 32) != tag || (unsigned)(mrg_w[b][1] >> 32) != tag) {
-            const unsigned long long* src = merged_team + (size_t)(gf % kRingM) * kST * 2 + (size_t)mrow * 2;
-            unsigned spins = 0;
-            do {
-                __builtin_amdgcn_s_sleep(1);
-                mrg_w[b][0] = ld_tagged(src);
-                mrg_w[b][1] = ld_tagged(src + 1);
-                if (++spins > kSpinLimit) { spin_fail(); break; }
-            } while ((unsigned)(mrg_w[b][0] >> 32) != tag || (unsigned)(mrg_w[b][1] >> 32) != tag);
-        }
-        const float mean_l = untag(mrg_w[b][0]), rstd_l = untag(mrg_w[b][1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mean = __shfl(mean_l, 16 * g4 + i, 64), rstd = __shfl(rstd_l, 16 * g4 + i, 64);
-            a[i] = (a[i] - mean) * rstd * gw + gb;
-        }
-        store_tile(a, gf);
-    };
-    auto publish = [&](const f32x4& a, int g) __attribute__((always_inline)) {
-        const unsigned tag = (unsigned)g + 1u;
-        unsigned long long* dst = part_team + ((size_t)(g % kRingP) * NP + 2 * slice + ct_o) * kST * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mean = sum16(a[i]) * (1.0f / 16.0f);
-            const float d = a[i] - mean;
-            const float m2 = sum16(d * d);
-            if (c16 == 0) {
-                const int rr = 16 * rt_o + 4 * g4 + i;
-                st_tagged(dst + (size_t)rr * 2, tagged(mean, tag));
-                st_tagged(dst + (size_t)rr * 2 + 1, tagged(m2, tag));
-            }
-        }
-    };
-    // GroupNorm bookkeeping for step g (a pipeline stage, or a drain step after the last one). The
-    // loads are issued at the start of a step, before that step's prefetch, so that waiting for them
-    // never waits for the prefetch; merged statistics are used one step after they are loaded.
-    //   reducer of stage g-kRedLag: load its partials now, merge and publish at the end of this step
-    //   merged statistics of stage g-kGnLag+1: load now (buffer b), use next step
-    //   stage g-kGnLag: normalise with the statistics loaded last step (buffer b^1) and store
-    auto gn_issue = [&](int g, int b) __attribute__((always_inline)) {
-        const int gr = g - kRedLag;
-        if (gr >= 0 && gr < total && gr % NS == slice) reducer_issue(gr);
-        const int gm = g - kGnLag + 1;
-        if (gm >= 0 && gm < total) merged_issue(gm, b);
-    };
-    auto gn_finish = [&](int g, int b) __attribute__((always_inline)) {
-        const int gr = g - kRedLag;
-        if (gr >= 0 && gr < total && gr % NS == slice) reducer_finish(gr);
-        const int gf = g - kGnLag;
-        if (gf >= 0 && gf < total) finalize(pend[kGnLag - 1], gf, b ^ 1);
-    };
-
     // ---- one pipeline stage
     auto stage = [&](StageRegs<DK, C>& r, int g) __attribute__((always_inline)) {
         const int ci = g / SPC, s = g % SPC;
@@ -509,7 +335,6 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
                 for (int ct = 0; ct < 2; ++ct) accR[rt][ct] *= gL;
         }
         store_stage(r, s, L);
-        if constexpr (WANT_OUT && GN) gn_issue(g, g & 1);
         load_stage(r, g + 2);
         __syncthreads();  // (B)
         if (s == 0 && WANT_OUT) read_R_frags();
@@ -555,17 +380,7 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
                 }
             }
         }
-        if constexpr (WANT_OUT) {
-            if constexpr (GN) {
-                publish(acc, g);
-                gn_finish(g, g & 1);
-#pragma unroll
-                for (int k = kGnLag - 1; k > 0; --k) pend[k] = pend[k - 1];
-                pend[0] = acc;
-            } else {
-                store_tile(acc, g);
-            }
-        }
+        if constexpr (WANT_OUT) store_tile(acc, g);
         if (chunk_end) {
             __syncthreads();  // (C) all reads of R^T for this chunk are done
             write_R();
@@ -580,15 +395,6 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
         stage(r0, g);
         if (g + 1 < total) stage(r1, g + 1);
     }
-    if constexpr (WANT_OUT && GN) {
-        // drain: the last reductions and normalisations, no compute
-        for (int g = total; g < total + kGnLag; ++g) {
-            gn_issue(g, g & 1);
-            gn_finish(g, g & 1);
-#pragma unroll
-            for (int k = kGnLag - 1; k > 0; --k) pend[k] = pend[k - 1];
-        }
-    }
     if (p.state_out) {
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt)
@@ -602,166 +408,6 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     }
 }
 
-
-// GroupNorm statistics exchange between the workgroups (slices) of one head. Every value is a 64-bit
-// atomic store whose high half is a tag (stage + 1), so a reader can tell whether it sees the
-// current stage; the rings are cleared before each call. No counters, no fences:
-//   stage x, end:            each output wave publishes per-row (mean, M2) of its 16 columns;
-//   stage x + kRedLag, end:  slice x % NS merges all partials of stage x in a fixed order and
-//                            publishes (mean, 1/std) per row;
-//   stage x + kGnLag - 1:    every output wave loads the merged statistics of its rows;
-//   stage x + kGnLag, end:   it normalises and stores its stage-x tile.
-// Loads are issued at the start of a step, before that step's prefetch, so waiting for them never
-// waits for the prefetch; a stale tag (rare) makes the lane re-load until the tag matches.
-// One output wave owns one 16 x 16 tile per stage: rows 16*rt_o .. of the stage, 16 columns.
-template <typename TOUT>
-struct GnExchange {
-    int NS, NP, LPR, PPL, total, slice, part_idx, rt_o, lane, g4, c16, bh, N, DV, col_out, SPC, C;
-    float eps, gw, gb;
-    unsigned long long* part_team;
-    unsigned long long* merged_team;
-    unsigned* err_flag;
-    TOUT* out;
-    unsigned long long red_w[4][2];  // reducer: this lane's loaded partials
-    unsigned long long mrg_a[2], mrg_b[2];  // merged (mean, 1/std) of row mrow, two steps in flight (by parity)
-    int rrow, rk8, mrow;
-
-    __device__ __forceinline__ void init(const MainParams& p, int bh_, int h, int slice_, int wave_in_group, int lane_, int total_,
-                                         int spc, int C_) {
-        NS = p.NS; NP = 2 * NS; LPR = NP < 8 ? NP : 8; PPL = NP < 8 ? 1 : NP / 8;
-        total = total_; slice = slice_; bh = bh_; N = p.N; DV = NS * 32; SPC = spc; C = C_;
-        lane = lane_; g4 = lane >> 4; c16 = lane & 15;
-        rt_o = wave_in_group >> 1;
-        const int ct_o = wave_in_group & 1;
-        part_idx = 2 * slice + ct_o;
-        col_out = slice * 32 + 16 * ct_o + c16;
-        eps = p.gn.eps;
-        gw = p.gn.weight ? p.gn.weight[(size_t)h * DV + col_out] : 1.f;
-        gb = p.gn.bias ? p.gn.bias[(size_t)h * DV + col_out] : 0.f;
-        part_team = p.part + (size_t)bh * kRingP * NP * kST * 2;
-        merged_team = p.merged + (size_t)bh * kRingM * kST * 2;
-        err_flag = p.err_flag;
-        out = reinterpret_cast<TOUT*>(p.out);
-        rrow = 8 * wave_in_group + (lane >> 3);
-        rk8 = lane & 7;
-        mrow = 16 * rt_o + 4 * g4 + (c16 & 3);
-    }
-    __device__ __forceinline__ void store_tile(f32x4 a, int g) const {
-        const int c0 = (g / SPC) * C, s = g % SPC;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = c0 + kST * s + 16 * rt_o + 4 * g4 + i;
-            if (r < N) out[((size_t)bh * N + r) * DV + col_out] = from_float<TOUT>(a[i]);
-        }
-    }
-    __device__ __forceinline__ const unsigned long long* part_at(int g, int pi, int row) const {
-        return part_team + (((size_t)(g % kRingP) * NP + pi) * kST + row) * 2;
-    }
-    __device__ __forceinline__ void publish(f32x4 a, int g) const {
-        const unsigned tag = (unsigned)g + 1u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mean = sum16(a[i]) * (1.0f / 16.0f);
-            const float d = a[i] - mean;
-            const float m2 = sum16(d * d);
-            if (c16 == 0) {
-                unsigned long long* dst = const_cast<unsigned long long*>(part_at(g, part_idx, 16 * rt_o + 4 * g4 + i));
-                st_tagged(dst, tagged(mean, tag));
-                st_tagged(dst + 1, tagged(m2, tag));
-            }
-        }
-    }
-    __device__ __forceinline__ bool is_reducer(int gr) const { return gr >= 0 && gr < total && gr % NS == slice; }
-    __device__ __forceinline__ int red_pi(int j) const { return NP < 8 ? rk8 % NP : rk8 + 8 * j; }
-    __device__ __forceinline__ void reducer_issue(int gr) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (j < PPL) {
-                const unsigned long long* src = part_at(gr, red_pi(j), rrow);
-                red_w[j][0] = ld_tagged(src);
-                red_w[j][1] = ld_tagged(src + 1);
-            }
-    }
-    __device__ __forceinline__ void reducer_finish(int gr) {
-        const unsigned tag = (unsigned)gr + 1u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < PPL && ((unsigned)(red_w[j][0] >> 32) != tag || (unsigned)(red_w[j][1] >> 32) != tag)) {
-                const unsigned long long* src = part_at(gr, red_pi(j), rrow);
-                unsigned spins = 0;
-                do {
-                    __builtin_amdgcn_s_sleep(1);
-                    red_w[j][0] = ld_tagged(src);
-                    red_w[j][1] = ld_tagged(src + 1);
-                    if (++spins > kSpinLimit) { atomicOr(err_flag, 1u); break; }
-                } while ((unsigned)(red_w[j][0] >> 32) != tag || (unsigned)(red_w[j][1] >> 32) != tag);
-            }
-        }
-        // fixed merge tree: ((p0, p1), (p2, p3)) locally, then across the row's lanes
-        float pm[4], p2[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { pm[j] = untag(red_w[j][0]); p2[j] = untag(red_w[j][1]); }
-        float mean = pm[0], m2 = p2[0], n = 16.f;
-        if (PPL == 4) {
-            merge_eq(pm[0], p2[0], pm[1], p2[1], 16.f);
-            merge_eq(pm[2], p2[2], pm[3], p2[3], 16.f);
-            merge_eq(pm[0], p2[0], pm[2], p2[2], 32.f);
-            mean = pm[0]; m2 = p2[0]; n = 64.f;
-        } else if (PPL == 2) {
-            merge_eq(pm[0], p2[0], pm[1], p2[1], 16.f);
-            mean = pm[0]; m2 = p2[0]; n = 32.f;
-        }
-        for (int off = 1; off < LPR; off <<= 1) {
-            const float om = __shfl_xor(mean, off, 64), o2 = __shfl_xor(m2, off, 64);
-            merge_eq(mean, m2, om, o2, n);
-            n *= 2.f;
-        }
-        if (rk8 == 0) {
-            const float rstd = rsqrtf(m2 / (float)DV + eps);
-            unsigned long long* dst = merged_team + ((size_t)(gr % kRingM) * kST + rrow) * 2;
-            st_tagged(dst, tagged(mean, tag));
-            st_tagged(dst + 1, tagged(rstd, tag));
-        }
-    }
-    __device__ __forceinline__ void merged_issue(int gf, int b) {
-        const unsigned long long* src = merged_team + ((size_t)(gf % kRingM) * kST + mrow) * 2;
-        const unsigned long long w0 = ld_tagged(src), w1 = ld_tagged(src + 1);
-        if (b) { mrg_b[0] = w0; mrg_b[1] = w1; } else { mrg_a[0] = w0; mrg_a[1] = w1; }
-    }
-    __device__ __forceinline__ void finalize(f32x4 a, int gf, int b) {
-        const unsigned tag = (unsigned)gf + 1u;
-        unsigned long long w0 = b ? mrg_b[0] : mrg_a[0], w1 = b ? mrg_b[1] : mrg_a[1];
-        if ((unsigned)(w0 >> 32) != tag || (unsigned)(w1 >> 32) != tag) {
-            const unsigned long long* src = merged_team + ((size_t)(gf % kRingM) * kST + mrow) * 2;
-            unsigned spins = 0;
-            do {
-                __builtin_amdgcn_s_sleep(1);
-                w0 = ld_tagged(src);
-                w1 = ld_tagged(src + 1);
-                if (++spins > kSpinLimit) { atomicOr(err_flag, 1u); break; }
-            } while ((unsigned)(w0 >> 32) != tag || (unsigned)(w1 >> 32) != tag);
-        }
-        const float mean_l = untag(w0), rstd_l = untag(w1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mean = __shfl(mean_l, 16 * g4 + i, 64), rstd = __shfl(rstd_l, 16 * g4 + i, 64);
-            a[i] = (a[i] - mean) * rstd * gw + gb;
-        }
-        store_tile(a, gf);
-    }
-    // Step g (a pipeline stage, or a drain step after the last one), with the output-tile ring pend
-    // (pend[k] = tile of stage g-1-k).
-    __device__ __forceinline__ void issue(int g, int b) {
-        if (is_reducer(g - kRedLag)) reducer_issue(g - kRedLag);
-        const int gm = g - kGnLag + 1;
-        if (gm >= 0 && gm < total) merged_issue(gm, b);
-    }
-    __device__ __forceinline__ void finish(int g, int b, const f32x4 (&pend)[kGnLag]) {
-        if (is_reducer(g - kRedLag)) reducer_finish(g - kRedLag);
-        const int gf = g - kGnLag;
-        if (gf >= 0 && gf < total) finalize(pend[kGnLag - 1], gf, b ^ 1);
-    }
-};
 
 // ---------------------------------------------------------------------------------------------
 // Warp-specialised chunk kernel (chunks up to 256): 512 threads = 4 output waves + 4 state waves,
@@ -803,7 +449,7 @@ struct WsRegs {
     bf16x8 v;
 };
 
-template <int DK, int C, typename TOUT, bool GN>
+template <int DK, int C, typename TOUT>
 __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
     using G = WsGeom<DK, C>;
     constexpr int RTR = DK / 64;  // 16-row R tiles per state wave
@@ -826,16 +472,8 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
     const bool state_wave = w >= 4;
     const int wl = w & 3;          // wave index within its group
     const int st = threadIdx.x - 256;  // state-group thread index (valid for state waves)
-    int team_local, slice;
-    if (p.nteams_launch % 8 == 0) {
-        const int i = blockIdx.x;
-        team_local = (i % 8) + 8 * (i / (8 * p.NS));
-        slice = (i / 8) % p.NS;
-    } else {
-        team_local = blockIdx.x / p.NS;
-        slice = blockIdx.x % p.NS;
-    }
-    const int bh = p.team_base + team_local;
+    int bh, slice;
+    team_slice(p.teams, p.NS, bh, slice);
     const int h = bh % p.H;
     const int N = p.N, DV = p.NS * kW;
     const float l2g = hc.log2g[h];
@@ -1019,11 +657,6 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
     } else {
         // ---------------- output waves: 16 x 16 tile of each stage
         bf16x8 rfh[DK / 32], rfl[DK / 32];
-        GnExchange<TOUT> gx;
-        f32x4 pend[kGnLag];
-        if constexpr (GN) gx.init(p, bh, h, slice, wl, lane, total, SPC, C);
-#pragma unroll
-        for (int k = 0; k < kGnLag; ++k) pend[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto store_plain = [&](f32x4 a, int g) __attribute__((always_inline)) {
             const int c0 = (g / SPC) * C, s = g % SPC;
 #pragma unroll
@@ -1047,7 +680,6 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
                 }
                 __syncthreads();
             }
-            if constexpr (GN) gx.issue(g, g & 1);
             const bf16* Qs = Qb(b);
             const bf16* Ps = Pb(b);
             f32x4 qa[4];
@@ -1070,41 +702,69 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = qr[i] * decay_pow(l2g, (float)(kST * s + 16 * rt_o + 4 * g4 + i + 1)) + pv[i];
-            if constexpr (GN) {
-                gx.publish(acc, g);
-                gx.finish(g, g & 1, pend);
-#pragma unroll
-                for (int k = kGnLag - 1; k > 0; --k) pend[k] = pend[k - 1];
-                pend[0] = acc;
-            } else {
-                store_plain(acc, g);
-            }
+            store_plain(acc, g);
             __syncthreads();  // stage g consumed; stage g+1 stored
             if (chunk_end && g + 1 < total) __syncthreads();  // R of this chunk written
-        }
-        if constexpr (GN) {
-            for (int g = total; g < total + kGnLag; ++g) {
-                gx.issue(g, g & 1);
-                gx.finish(g, g & 1, pend);
-#pragma unroll
-                for (int k = kGnLag - 1; k > 0; --k) pend[k] = pend[k - 1];
-            }
         }
     }
 }
 
-__global__ void zero_words_kernel(unsigned* p, size_t n) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+
+// Per-head GroupNorm of fp32 pre-norm rows: one wave per (b, h, n) row of DV <= 512 channels, held
+// in registers (lane l owns channels 4l..4l+3 and 256+4l..256+4l+3). Mean first, then the biased
+// variance from the centred values, so no cancellation; y = (x - mean) / sqrt(var + eps) * w + b.
+template <typename TOUT>
+__global__ __launch_bounds__(256) void gn_rows_kernel(long rows, int H, int N, int DV, const float* __restrict__ x,
+                                                      TOUT* __restrict__ y, GnArgs gn) {
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float* xr = x + (size_t)row * DV;
+    f32x4 xv[2];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = 4 * lane + 256 * i;
+        xv[i] = c < DV ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + c)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        s += (xv[i][0] + xv[i][1]) + (xv[i][2] + xv[i][3]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    const float mean = s / (float)DV;
+    float m2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (4 * lane + 256 * i < DV) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m2 += (xv[i][j] - mean) * (xv[i][j] - mean);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m2 += __shfl_xor(m2, off, 64);
+    const float inv = rsqrtf(m2 / (float)DV + gn.eps);
+    const int h = (int)((row / N) % H);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = 4 * lane + 256 * i;
+        if (c >= DV) continue;
+        f32x4 w = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
+        if (gn.weight) w = *reinterpret_cast<const f32x4*>(gn.weight + (size_t)h * DV + c);
+        if (gn.bias) bb = *reinterpret_cast<const f32x4*>(gn.bias + (size_t)h * DV + c);
+        TOUT o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = from_float<TOUT>((xv[i][j] - mean) * inv * w[j] + bb[j]);
+        TOUT* yr = y + (size_t)row * DV + c;
+        if constexpr (sizeof(TOUT) == 4) *reinterpret_cast<f32x4*>(yr) = f32x4{(float)o[0], (float)o[1], (float)o[2], (float)o[3]};
+        else *reinterpret_cast<bf16x4*>(yr) = bf16x4{o[0], o[1], o[2], o[3]};
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Workspace layout (bytes, each part 256-aligned):
-//   P         B*H*nchunks*C*C bf16                  (only when the output is wanted)
-//   flag      one uint32 error flag                 (only with GroupNorm)
-//   partials  B*H*kRingP*(2*NS)*32 x 2 uint64       (only with GroupNorm)
-//   merged    B*H*kRingM*32 x 2 uint64              (only with GroupNorm)
+//   P     B*H*nchunks*C*C bf16      scores of every chunk (only when the output is wanted)
+//   pre   B*H*N*DV fp32             pre-norm output rows (only with GroupNorm)
 struct WsLayout {
-    size_t p_off, p_bytes, flag_off, part_off, part_bytes, mrg_off, mrg_bytes, total;
+    size_t p_off, p_bytes, pre_off, pre_bytes, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1114,66 +774,30 @@ WsLayout ws_layout(int B, int H, int N, int DV, int C, int gn, int want_out) {
     const size_t nchunks = (size_t)(N + C - 1) / C;
     l.p_off = 0;
     l.p_bytes = want_out ? align256((size_t)B * H * nchunks * C * C * sizeof(bf16)) : 0;
-    l.flag_off = l.p_off + l.p_bytes;
-    const size_t flag_bytes = gn ? 256 : 0;
-    l.part_off = l.flag_off + flag_bytes;
-    l.part_bytes = gn ? align256((size_t)B * H * kRingP * (2 * (DV / kW)) * kST * 2 * sizeof(unsigned long long)) : 0;
-    l.mrg_off = l.part_off + l.part_bytes;
-    l.mrg_bytes = gn ? align256((size_t)B * H * kRingM * kST * 2 * sizeof(unsigned long long)) : 0;
-    l.total = l.mrg_off + l.mrg_bytes;
+    l.pre_off = l.p_off + l.p_bytes;
+    l.pre_bytes = gn && want_out ? align256((size_t)B * H * N * DV * sizeof(float)) : 0;
+    l.total = l.pre_off + l.pre_bytes;
     return l;
 }
 
 // Chunks up to 256 with an output use the warp-specialised kernel; 512-token chunks (whose stage
 // buffers do not fit twice in LDS) and state-only prefills use the single-group kernel.
-template <int DK, int C, bool WANT_OUT>
+template <int C, bool WANT_OUT>
 constexpr bool use_ws() { return WANT_OUT && C <= 256; }
 
-template <int DK, int C, typename TOUT, bool GN, bool WANT_OUT>
-const void* main_kernel_ptr() {
-    if constexpr (use_ws<DK, C, WANT_OUT>()) return reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, GN>);
-    else return reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, GN, WANT_OUT>);
-}
-
-template <int DK, int C, typename TOUT, bool GN, bool WANT_OUT>
-hipError_t launch_main(const LaunchArgs& a, MainParams mp) {
-    constexpr bool ws = use_ws<DK, C, WANT_OUT>();
-    const void* kern = main_kernel_ptr<DK, C, TOUT, GN, WANT_OUT>();
+template <int DK, int C, typename TOUT, bool WANT_OUT>
+hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
+    constexpr bool ws = use_ws<C, WANT_OUT>();
+    const void* kern;
+    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT>);
+    else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT>);
     const size_t dyn = ws ? WsGeom<DK, C>::BYTES : MainGeom<DK, C>::BYTES;
-    const int threads = ws ? 512 : kThreads;
-    const int teams = a.B * a.H;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
-    if (!GN) {
-        mp.team_base = 0;
-        mp.nteams_launch = teams;
-        HeadConsts hc = a.hc;
-        void* args[] = {&mp, &hc};
-        return hipLaunchKernel(kern, dim3(teams * mp.NS), dim3(threads), args, dyn, a.stream);
-    }
-    // GroupNorm: the slices of a head wait for each other's statistics, so they must be
-    // co-resident. Launch cooperatively, in batches of whole teams that fit on the device at once.
-    int dev = 0, ncu = 0, per_cu = 0;
-    e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, dyn);
-    if (e != hipSuccess) return e;
-    const int fit_blocks = ncu * per_cu;
-    int teams_per_launch = fit_blocks / mp.NS;
-    if (teams_per_launch < 1) return hipErrorCooperativeLaunchTooLarge;
-    if (teams_per_launch >= 8) teams_per_launch &= ~7;
-    for (int base = 0; base < teams; base += teams_per_launch) {
-        MainParams lp = mp;
-        lp.team_base = base;
-        lp.nteams_launch = teams - base < teams_per_launch ? teams - base : teams_per_launch;
-        HeadConsts hc = a.hc;
-        void* args[] = {&lp, &hc};
-        e = hipLaunchCooperativeKernel(kern, dim3(lp.nteams_launch * mp.NS), dim3(threads), args, (unsigned)dyn, a.stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    MainParams lp = mp;
+    HeadConsts hc = a.hc;
+    void* args[] = {&lp, &hc};
+    return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 512 : kThreads), args, dyn, a.stream);
 }
 
 template <int DK, int C, typename TOUT>
@@ -1183,31 +807,26 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     const WsLayout l = ws_layout(a.B, a.H, a.N, a.DV, C, a.gn.enabled, want_out);
     char* ws = reinterpret_cast<char*>(a.ws);
     MainParams mp{};
-    mp.H = a.H; mp.N = a.N; mp.C = C; mp.NS = a.DV / kW; mp.nchunks = nchunks;
+    mp.H = a.H; mp.N = a.N; mp.C = C; mp.NS = a.DV / kW; mp.nchunks = nchunks; mp.teams = a.B * a.H;
     mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
-    mp.gn = a.gn;
-    if (a.gn.enabled && want_out) {
-        mp.err_flag = reinterpret_cast<unsigned*>(ws + l.flag_off);
-        mp.part = reinterpret_cast<unsigned long long*>(ws + l.part_off);
-        mp.merged = reinterpret_cast<unsigned long long*>(ws + l.mrg_off);
-        // tags must not match anything left by an earlier call: clear flag, partials and merged
-        const size_t nwords = (l.total - l.flag_off) / sizeof(unsigned);
-        hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((nwords + 1023) / 1024 < 2048 ? (nwords + 1023) / 1024 : 2048)),
-                           dim3(256), 0, a.stream, mp.err_flag, nwords);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (want_out) {
-        hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(C / 64, nchunks, a.B * a.H), dim3(kThreads), 0, a.stream, a.H, a.N, C,
-                           nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), a.hc);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (a.gn.enabled) return launch_main<DK, C, TOUT, true, true>(a, mp);
-        return launch_main<DK, C, TOUT, false, true>(a, mp);
-    }
-    return launch_main<DK, C, TOUT, false, false>(a, mp);
+    if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
+
+    hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(C / 64, nchunks, a.B * a.H), dim3(kThreads), 0, a.stream, a.H, a.N, C,
+                       nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), a.hc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!a.gn.enabled) return launch_main<DK, C, TOUT, true>(a, mp);
+    // GroupNorm: fp32 pre-norm rows into the workspace, then normalise them into out
+    float* pre = reinterpret_cast<float*>(ws + l.pre_off);
+    mp.out = pre;
+    e = launch_main<DK, C, float, true>(a, mp);
+    if (e != hipSuccess) return e;
+    const long rows = (long)a.B * a.H * a.N;
+    hipLaunchKernelGGL(gn_rows_kernel<TOUT>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.stream, rows, a.H, a.N, a.DV,
+                       pre, reinterpret_cast<TOUT*>(a.out), a.gn);
+    return hipGetLastError();
 }
 
 template <int DK, typename TOUT>

@@ -142,7 +142,8 @@ def test_workspace(lib):
     assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, None, 64, 0) == ctypes.c_size_t(-1).value
     assert lib.retention_workspace_bytes(9, ctypes.byref(s), 64, 0) == ctypes.c_size_t(-1).value
     gn_need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(s), 64, 1)
-    assert gn_need > need
+    # GroupNorm adds the fp32 pre-norm rows, normalised by a second kernel
+    assert gn_need >= need + s.batch * s.heads * s.seq_len * s.d_v * 4
 
 
 def test_step_validation(lib):
