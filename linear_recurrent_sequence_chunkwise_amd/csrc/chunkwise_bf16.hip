@@ -12,8 +12,8 @@
 //                         (32-key blocks on and below the diagonal). Q and K go through LDS with all
 //                         loads of a block issued together; the next key block is prefetched.
 //   chunk_ws_kernel       (chunks up to 256, output wanted) one workgroup per (b, h, 32-column slice
-//                         of d_v), walking the sequence in 32-token stages, with state waves and
-//                         output waves (see the kernel):
+//                         of d_v), walking the sequence in 32-token stages, with a loader wave,
+//                         state waves and output waves (see the kernel):
 //                           out  = g^(j+1) Q R + P V      (R of the previous chunk as bf16 hi + lo)
 //                           R   += K^T (V (.) zeta)       (V (.) zeta as bf16 hi + lo; R fp32 in
 //                                                         accumulators, scaled by g^L at chunk start)
@@ -410,68 +410,73 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 
 
 // ---------------------------------------------------------------------------------------------
-// Warp-specialised chunk kernel (chunks up to 256): 512 threads = 4 output waves + 4 state waves,
-// one of each per SIMD, so that loads, LDS traffic and matrix-core work of the two overlap.
-//   state waves  (w = 4..7): prefetch each 32-token stage's Q, K, V and P rows into registers two
-//                stages ahead, store stage g+1 into the idle LDS buffer while stage g is computed,
-//                split V (.) zeta into bf16 hi + lo, and accumulate R += K^T (V (.) zeta) for their
-//                d_k quarter of R (fp32, scaled by g^L at each chunk start).
+// Warp-specialised chunk kernel (chunks up to 256): 576 threads = 4 output waves, 4 state waves and
+// one loader wave, so that loads, LDS traffic and matrix-core work overlap.
+//   loader wave  (w = 8): brings the Q, K and P rows of stage g + NB - 1 from global memory straight
+//                into LDS buffer (g + NB - 1) % NB with buffer-to-LDS loads (no registers, no LDS
+//                write instructions), NB - 1 stages ahead, then waits for the loads of stage g + 1.
+//                It never accesses LDS itself, so the compiler adds no waits for these loads
+//                anywhere else.
+//   state waves  (w = 4..7): per 32-token stage g, accumulate R += K^T (V (.) zeta) for their d_k
+//                quarter of R (fp32, scaled by g^L at each chunk start), and write stage g+1's V rows
+//                and V (.) zeta as bf16 hi + lo (V loaded into registers two stages ahead).
 //   output waves (w = 0..3): per stage, the 16 x 16 tile (rows 16*(w>>1), columns 16*(w&1)) of
-//                g^(j+1) Q R + P V, with R^T (hi + lo) held in registers for the chunk, then the
-//                GroupNorm exchange and the store.
-// At each chunk end the state waves write R as bf16 hi + lo into the Q/K region of the LDS buffer
-// that the finished stage used; the output waves read their fragments from it at the next stage.
+//                g^(j+1) Q R + P V, with R^T (hi + lo) held in registers for the chunk, and its store.
+// Q, K, P and R^T tiles are swizzled (SwzTile). At each chunk end the state waves write R^T as bf16
+// hi + lo into the Q/K region of the buffer that the finished stage used; the output waves read
+// their fragments from it at the next stage, before the loader refills that buffer.
 template <int DK, int C>
 struct WsGeom {
-    static constexpr int LQ = DK + 8, LK = DK + 16, LP = C + 8, LV = kW + 16, LR = DK + 8;
-    static constexpr size_t Q_BYTES = (size_t)kST * LQ * 2;
-    static constexpr size_t K_BYTES = (size_t)kST * LK * 2;
-    static constexpr size_t P_BYTES = (size_t)kST * LP * 2;
+    static constexpr int QRB = DK * 2;            // bytes per Q / K tile row
+    static constexpr int PRB = C * 2;             // bytes per P tile row
+    static constexpr int LV = kW;                 // V and V (.) zeta rows: 32 bf16, dense
+    static constexpr size_t Q_BYTES = (size_t)kST * QRB;
+    static constexpr size_t P_BYTES = (size_t)kST * PRB;
     static constexpr size_t Z_BYTES = (size_t)kST * LV * 2;
-    static constexpr size_t BUF = Q_BYTES + K_BYTES + P_BYTES + 2 * Z_BYTES;  // one stage buffer
+    static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_ZH = OFF_P + P_BYTES, OFF_ZL = OFF_ZH + Z_BYTES;
+    static constexpr size_t BUF = OFF_ZL + Z_BYTES;  // one stage buffer
     // V rows of the chunk, double-buffered by chunk parity: during a chunk's last stage the state
     // waves already store the next chunk's first V rows while the output waves still read these
     static constexpr size_t V_BYTES = (size_t)C * LV * 2;
-    static constexpr size_t OFF_V = 2 * BUF;
+    // three stage buffers when they fit in the 160 KiB of LDS, else two
+    static constexpr int NB = 3 * BUF + 2 * V_BYTES <= 160 * 1024 ? 3 : 2;
+    static constexpr size_t OFF_V = NB * BUF;
     static constexpr size_t BYTES = OFF_V + 2 * V_BYTES;
-    static constexpr size_t R_BYTES = 2 * (size_t)kW * LR * 2;
-    static_assert(R_BYTES <= Q_BYTES + K_BYTES, "R^T must fit in a stage buffer's Q/K region");
-    static constexpr int QCH = kST * DK / 8;
-    static constexpr int QN = QCH / 256;       // Q (and K) chunks per state thread
-    static constexpr int PN = kST * C / 8 / 256;  // P slots per state thread
+    // R^T (kW rows of DK bf16, swizzled like Q) hi part in the Q region, lo part in the K region
+    static_assert((size_t)kW * QRB == Q_BYTES, "R^T hi / lo fill the Q / K regions");
+    static_assert(Q_BYTES % 1024 == 0 && P_BYTES % 1024 == 0, "tiles are filled in whole kilobytes");
+    static constexpr int Q_KB = (int)(Q_BYTES / 1024), P_KB = (int)(P_BYTES / 1024);
+    static constexpr int NDMA = 2 * Q_KB + P_KB;  // buffer-to-LDS loads per stage (loader wave)
+    static_assert(NDMA <= 63, "one stage of loads must fit the vmcnt counter");
 };
 
-template <int DK, int C>
-struct WsRegs {
-    bf16x8 q[WsGeom<DK, C>::QN > 0 ? WsGeom<DK, C>::QN : 1];
-    bf16x8 k[WsGeom<DK, C>::QN > 0 ? WsGeom<DK, C>::QN : 1];
-    bf16x8 p[WsGeom<DK, C>::PN > 0 ? WsGeom<DK, C>::PN : 1];
-    bf16x8 v;
-};
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n), expcnt and lgkmcnt not waited on
+template <int n>
+constexpr int wait_vm() { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Workgroup barrier for LDS hand-offs: this wave's LDS accesses complete (lgkmcnt(0)), then
+// s_barrier. Unlike __syncthreads() it does not wait for outstanding global loads and stores, so
+// prefetches stay in flight across it. The empty asm statements keep the compiler from moving
+// memory accesses across the barrier. Loads into LDS are waited for explicitly by their issuer.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <int DK, int C, typename TOUT>
-__global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
+__global__ __launch_bounds__(576) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
     using G = WsGeom<DK, C>;
+    constexpr int NB = G::NB;
     constexpr int RTR = DK / 64;  // 16-row R tiles per state wave
     constexpr int SPC = C / kST;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    auto Qb = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<bf16*>(smem + b * G::BUF); };
-    auto Kb = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<bf16*>(smem + b * G::BUF + G::Q_BYTES); };
-    auto Pb = [&](int b) __attribute__((always_inline)) {
-        return reinterpret_cast<bf16*>(smem + b * G::BUF + G::Q_BYTES + G::K_BYTES);
-    };
-    auto Zh = [&](int b) __attribute__((always_inline)) {
-        return reinterpret_cast<bf16*>(smem + b * G::BUF + G::Q_BYTES + G::K_BYTES + G::P_BYTES);
-    };
-    auto Zl = [&](int b) __attribute__((always_inline)) {
-        return reinterpret_cast<bf16*>(smem + b * G::BUF + G::Q_BYTES + G::K_BYTES + G::P_BYTES + G::Z_BYTES);
-    };
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    auto buf = [&](int g) __attribute__((always_inline)) { return smem + (g % NB) * G::BUF; };  // buffer of stage g
     auto Vc = [&](int ci) __attribute__((always_inline)) { return reinterpret_cast<bf16*>(smem + G::OFF_V + (ci & 1) * G::V_BYTES); };
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
-    const bool state_wave = w >= 4;
-    const int wl = w & 3;          // wave index within its group
-    const int st = threadIdx.x - 256;  // state-group thread index (valid for state waves)
+    const int wl = w & 3;  // wave index within the output or state group
     int bh, slice;
     team_slice(p.teams, p.NS, bh, slice);
     const int h = bh % p.H;
@@ -483,85 +488,100 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
     const int total = (nchunks - 1) * SPC + (L_last + kST - 1) / kST;
     const int rt_o = wl >> 1, ct_o = wl & 1;
 
+    // Buffer resources: loads past the end of a head's data return zero (tail rows, padding).
     const unsigned q_bytes = (unsigned)((size_t)N * DK * 2), v_bytes = (unsigned)((size_t)N * DV * 2);
     const unsigned p_bytes = (unsigned)((size_t)nchunks * C * C * 2);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)bh * N * DV), 0, v_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
 
-    // ---- state waves: stage loads and stores
-    auto load_stage = [&](WsRegs<DK, C>& r, int g) __attribute__((always_inline)) {
-        const int gg = g < total ? g : total - 1;
-        const int ci = gg / SPC, s = gg % SPC;
-        const int tok0 = ci * C + kST * s;
-#pragma unroll
-        for (int u = 0; u < G::QN; ++u) {
-            const int j = st + 256 * u;
-            const int row = j / (DK / 8), sg = j % (DK / 8);
-            const unsigned off = (unsigned)((tok0 + row) * DK + 8 * sg) * 2u;
-            r.q[u] = buf_load16(rq, off);
-            r.k[u] = buf_load16(rk, off);
-        }
-        {
-            const int row = st >> 2, sg = st & 3;
-            const unsigned off = st < kST * 4 ? (unsigned)((tok0 + row) * DV + col0 + 8 * sg) * 2u : v_bytes;
-            r.v = buf_load16(rv, off);
-        }
-        const int per_row = 4 * (s + 1);
-        const unsigned base = (unsigned)((ci * C + kST * s) * C);
-#pragma unroll
-        for (int u = 0; u < G::PN; ++u) {
-            const int j = st + 256 * u;
-            const int row = j / (C / 8), sg = j % (C / 8);
-            const unsigned off = sg < per_row ? (base + (unsigned)(row * C + 8 * sg)) * 2u : p_bytes;
-            r.p[u] = buf_load16(rp, off);
-        }
-    };
-    auto store_stage = [&](const WsRegs<DK, C>& r, int g, int b) __attribute__((always_inline)) {
-        const int ci = g / SPC, s = g % SPC;
-        const int L = min(C, N - ci * C);
-        bf16* Qs = Qb(b);
-        bf16* Ks = Kb(b);
-        bf16* Ps = Pb(b);
-#pragma unroll
-        for (int u = 0; u < G::QN; ++u) {
-            const int j = st + 256 * u;
-            const int row = j / (DK / 8), sg = j % (DK / 8);
-            *reinterpret_cast<bf16x8*>(Qs + row * G::LQ + 8 * sg) = r.q[u];
-            *reinterpret_cast<bf16x8*>(Ks + row * G::LK + 8 * sg) = r.k[u];
-        }
-        if (st < kST * 4) {
-            const int row = st >> 2, sg = st & 3;
-            *reinterpret_cast<bf16x8*>(Vc(ci) + (kST * s + row) * G::LV + 8 * sg) = r.v;
-            const int t = kST * s + row;
-            const float z = t < L ? decay_pow(l2g, (float)(L - 1 - t)) : 0.f;
-            bf16x8 hi, lo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16 a, c;
-                split_hi_lo((float)r.v[e] * z, a, c);
-                hi[e] = a;
-                lo[e] = c;
-            }
-            *reinterpret_cast<bf16x8*>(Zh(b) + row * G::LV + 8 * sg) = hi;
-            *reinterpret_cast<bf16x8*>(Zl(b) + row * G::LV + 8 * sg) = lo;
-        }
-        const int per_row = 4 * (s + 1);
-#pragma unroll
-        for (int u = 0; u < G::PN; ++u) {
-            const int j = st + 256 * u;
-            const int row = j / (C / 8), sg = j % (C / 8);
-            if (sg < per_row) *reinterpret_cast<bf16x8*>(Ps + row * G::LP + 8 * sg) = r.p[u];
-        }
-    };
-
-    // Barrier sequence, identical for both roles (each role runs its own loop with its own
+    // Barrier sequence, identical for all roles (each role runs its own loop with its own
     // registers): one after the prologue; per stage g: one at a chunk start (s == 0), one at the
     // end of the stage, and one more after a chunk end that is not the last stage.
-    TOUT* out = reinterpret_cast<TOUT*>(p.out);
-    if (state_wave) {
+    if (w == 8) {
+        // ---------------- loader wave
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rp =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
+        // Q, K and P rows of stage g into its buffer; lane l fills bytes [16l, 16l+16) of each
+        // kilobyte. P: only the 32-key steps up to this stage; the rest read as zero, no traffic.
+        auto dma_stage = [&](int g) __attribute__((always_inline)) {
+            const int ci = g / SPC, s = g % SPC;
+            const int tok0 = ci * C + kST * s;
+            char* bq = buf(g);
+#pragma unroll
+            for (int j = 0; j < G::Q_KB; ++j) {
+                const int byte = 1024 * j + 16 * lane, r = byte / G::QRB;
+                const int c = ((byte % G::QRB) >> 4) ^ (r & SwzTile<G::QRB>::M);
+                const unsigned off = (unsigned)(((tok0 + r) * DK + 8 * c) * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(bq + 1024 * j), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(bq + G::OFF_K + 1024 * j), 16, off,
+                                                         0, 0, 0);
+            }
+            const int per_row = 4 * (s + 1);
+            const unsigned base = (unsigned)((ci * C + kST * s) * C);
+#pragma unroll
+            for (int j = 0; j < G::P_KB; ++j) {
+                const int byte = 1024 * j + 16 * lane, r = byte / G::PRB;
+                const int c = ((byte % G::PRB) >> 4) ^ (r & SwzTile<G::PRB>::M);
+                const unsigned off = c < per_row ? (base + (unsigned)(r * C + 8 * c)) * 2u : p_bytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void*)(bq + G::OFF_P + 1024 * j), 16, off,
+                                                         0, 0, 0);
+            }
+        };
+        // prologue: stages 0 .. NB-2
+        dma_stage(0);
+        if (NB == 3 && total > 1) {
+            dma_stage(1);
+            __builtin_amdgcn_s_waitcnt(wait_vm<G::NDMA>());  // stage 0 landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(wait_vm<0>());
+        }
+        lds_barrier();
+        for (int g = 0; g < total; ++g) {
+            const int s = g % SPC;
+            const bool chunk_end = (s == SPC - 1) || (g == total - 1);
+            if (s == 0) lds_barrier();  // the output waves have taken R from the buffer refilled next
+            if (g + NB - 1 < total) {
+                dma_stage(g + NB - 1);
+                if constexpr (NB == 3) __builtin_amdgcn_s_waitcnt(wait_vm<G::NDMA>());  // stage g+1 landed
+                else __builtin_amdgcn_s_waitcnt(wait_vm<0>());
+            } else {
+                __builtin_amdgcn_s_waitcnt(wait_vm<0>());
+            }
+            lds_barrier();  // stage g consumed; stage g+1 in LDS
+            if (chunk_end && g + 1 < total) lds_barrier();
+        }
+    } else if (w >= 4) {
         // ---------------- state waves: R rows [wl*DK/4, (wl+1)*DK/4) x 32 columns, fp32
+        const int st = threadIdx.x - 256;  // 0..255
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)bh * N * DV), 0, v_bytes, 0x00020000);
+        // V rows of stage g: 32 rows x 4 groups of 8 columns, one 16-byte load per thread < 128
+        auto load_v = [&](int g) __attribute__((always_inline)) {
+            const int gg = g < total ? g : total - 1;
+            const int tok0 = (gg / SPC) * C + kST * (gg % SPC);
+            const int row = st >> 2, sg = st & 3;
+            const unsigned off = st < kST * 4 && g < total ? (unsigned)((tok0 + row) * DV + col0 + 8 * sg) * 2u : v_bytes;
+            return buf_load16(rv, off);
+        };
+        auto store_v = [&](const bf16x8& v, int g) __attribute__((always_inline)) {
+            const int ci = g / SPC, s = g % SPC;
+            const int L = min(C, N - ci * C);
+            if (st < kST * 4) {
+                const int row = st >> 2, sg = st & 3;
+                *reinterpret_cast<bf16x8*>(Vc(ci) + (kST * s + row) * G::LV + 8 * sg) = v;
+                const int t = kST * s + row;
+                const float z = t < L ? decay_pow(l2g, (float)(L - 1 - t)) : 0.f;
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bf16 a, c;
+                    split_hi_lo((float)v[e] * z, a, c);
+                    hi[e] = a;
+                    lo[e] = c;
+                }
+                *reinterpret_cast<bf16x8*>(buf(g) + G::OFF_ZH + (row * G::LV + 8 * sg) * 2) = hi;
+                *reinterpret_cast<bf16x8*>(buf(g) + G::OFF_ZL + (row * G::LV + 8 * sg) * 2) = lo;
+            }
+        };
         f32x4 accR[RTR][2];
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt)
@@ -572,9 +592,7 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
                     const int row = wl * (DK / 4) + 16 * rt + 4 * g4 + i;
                     accR[rt][ct][i] = p.state_in ? p.state_in[((size_t)bh * DK + row) * DV + col0 + 16 * ct + c16] : 0.f;
                 }
-        auto write_R = [&](int b) __attribute__((always_inline)) {  // R^T as bf16 hi + lo into buffer b's Q/K region
-            bf16* Rhi = Qb(b);
-            bf16* Rlo = Qb(b) + kW * G::LR;
+        auto write_R = [&](char* b) __attribute__((always_inline)) {  // R^T as bf16 hi + lo into a buffer's Q/K region
 #pragma unroll
             for (int rt = 0; rt < RTR; ++rt)
 #pragma unroll
@@ -588,8 +606,9 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
                         lo[i] = c;
                     }
                     const int col = 16 * ct + c16, row = wl * (DK / 4) + 16 * rt + 4 * g4;
-                    *reinterpret_cast<bf16x4*>(Rhi + col * G::LR + row) = hi;
-                    *reinterpret_cast<bf16x4*>(Rlo + col * G::LR + row) = lo;
+                    const int o = SwzTile<G::QRB>::off(col, row >> 3) + (row & 7) * 2;
+                    *reinterpret_cast<bf16x4*>(b + o) = hi;
+                    *reinterpret_cast<bf16x4*>(b + G::OFF_K + o) = lo;
                 }
         };
         auto scale_R = [&](int L) __attribute__((always_inline)) {
@@ -599,49 +618,47 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) accR[rt][ct] *= gL;
         };
-        // prologue: stage 0 into buffer 0, R_{-1} into buffer 1's Q/K region, loads for stages 1, 2
-        WsRegs<DK, C> r0, r1;  // r0 holds even stages, r1 odd stages
-        load_stage(r0, 0);
-        load_stage(r1, 1);
-        store_stage(r0, 0, 0);
-        write_R(1);
-        load_stage(r0, 2);
+        // prologue: V of stage 0 into LDS, R_{-1} where the output waves look for it at stage 0
+        // (the buffer of stage -1), V of stages 1 and 2 in registers
+        store_v(load_v(0), 0);
+        write_R(buf(NB - 1));
+        bf16x8 va = load_v(1), vb = load_v(2);  // V of stage g+1 for even g (va) and odd g (vb)
         scale_R(min(C, N));
-        __syncthreads();
-        auto stage = [&](WsRegs<DK, C>& rn, int g) __attribute__((always_inline)) {  // rn holds stage g+1
-            const int b = g & 1, s = g % SPC;
+        lds_barrier();
+        auto sstage = [&](int g, bf16x8& vn) __attribute__((always_inline)) {
+            const int s = g % SPC;
             const bool chunk_end = (s == SPC - 1) || (g == total - 1);
-            if (s == 0) __syncthreads();  // the output waves have taken R from buffer b^1
-            const bf16* Ks = Kb(b);
-            bf16x8 bhi[2], blo[2];
+            if (s == 0) lds_barrier();
+            const char* Ks = buf(g) + G::OFF_K;
+            bf16x8 bhi[2], blo[2], ak[RTR];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                bhi[ct] = lds_frag_kmajor(Zh(b), G::LV, 0, 16 * ct, lane);
-                blo[ct] = lds_frag_kmajor(Zl(b), G::LV, 0, 16 * ct, lane);
+                bhi[ct] = lds_frag_kmajor(reinterpret_cast<const bf16*>(buf(g) + G::OFF_ZH), G::LV, 0, 16 * ct, lane);
+                blo[ct] = lds_frag_kmajor(reinterpret_cast<const bf16*>(buf(g) + G::OFF_ZL), G::LV, 0, 16 * ct, lane);
             }
 #pragma unroll
-            for (int rt = 0; rt < RTR; ++rt) {
-                const bf16x8 ak = lds_frag_kmajor(Ks, G::LK, 0, wl * (DK / 4) + 16 * rt, lane);
+            for (int rt = 0; rt < RTR; ++rt) ak[rt] = lds_frag_kmajor_swz<G::QRB>(Ks, 0, wl * (DK / 4) + 16 * rt, lane);
+            if (g + 1 < total) {
+                store_v(vn, g + 1);  // into Vc and stage g+1's buffer (its Q/K/P come from the loader)
+                vn = load_v(g + 3);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RTR; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    accR[rt][ct] = mfma16(ak, bhi[ct], accR[rt][ct]);
-                    accR[rt][ct] = mfma16(ak, blo[ct], accR[rt][ct]);
+                    accR[rt][ct] = mfma16(ak[rt], bhi[ct], accR[rt][ct]);
+                    accR[rt][ct] = mfma16(ak[rt], blo[ct], accR[rt][ct]);
                 }
-            }
-            if (g + 1 < total) {  // stage g+1 into the idle buffer, then loads for stage g+3
-                store_stage(rn, g + 1, b ^ 1);
-                load_stage(rn, g + 3);
-            }
-            __syncthreads();  // stage g consumed; stage g+1 stored
+            lds_barrier();  // stage g consumed; stage g+1 in LDS
             if (chunk_end && g + 1 < total) {
-                write_R(b);  // R of this chunk into buffer b's (now idle) Q/K region
+                write_R(buf(g));  // R of this chunk into stage g's (now idle) Q/K region
                 scale_R(min(C, N - ((g + 1) / SPC) * C));
-                __syncthreads();
+                lds_barrier();
             }
         };
         for (int g = 0; g < total; g += 2) {
-            stage(r1, g);
-            if (g + 1 < total) stage(r0, g + 1);
+            sstage(g, va);
+            if (g + 1 < total) sstage(g + 1, vb);
         }
         if (p.state_out) {
 #pragma unroll
@@ -656,38 +673,30 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
         }
     } else {
         // ---------------- output waves: 16 x 16 tile of each stage
+        TOUT* out = reinterpret_cast<TOUT*>(p.out);
         bf16x8 rfh[DK / 32], rfl[DK / 32];
-        auto store_plain = [&](f32x4 a, int g) __attribute__((always_inline)) {
-            const int c0 = (g / SPC) * C, s = g % SPC;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = c0 + kST * s + 16 * rt_o + 4 * g4 + i;
-                if (r < N) out[((size_t)bh * N + r) * DV + col0 + 16 * ct_o + c16] = from_float<TOUT>(a[i]);
-            }
-        };
-        __syncthreads();
+        lds_barrier();
         for (int g = 0; g < total; ++g) {
-            const int b = g & 1, s = g % SPC;
+            const int s = g % SPC;
             const bool chunk_end = (s == SPC - 1) || (g == total - 1);
             if (s == 0) {
-                // R of the previous chunk sits in buffer b^1's Q/K region until the barrier
-                const bf16* Rhi = Qb(b ^ 1);
-                const bf16* Rlo = Qb(b ^ 1) + kW * G::LR;
+                // R of the previous chunk sits in the Q/K region of stage g-1's buffer until the barrier
+                const char* Rb = buf(g + NB - 1);
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks) {
-                    rfh[ks] = frag_rowmajor(Rhi, G::LR, 16 * ct_o, 32 * ks, lane);
-                    rfl[ks] = frag_rowmajor(Rlo, G::LR, 16 * ct_o, 32 * ks, lane);
+                    rfh[ks] = frag_rowmajor_swz<G::QRB>(Rb, 16 * ct_o, 32 * ks, lane);
+                    rfl[ks] = frag_rowmajor_swz<G::QRB>(Rb + G::OFF_K, 16 * ct_o, 32 * ks, lane);
                 }
-                __syncthreads();
+                lds_barrier();
             }
-            const bf16* Qs = Qb(b);
-            const bf16* Ps = Pb(b);
+            const char* Qs = buf(g);
+            const char* Ps = buf(g) + G::OFF_P;
             f32x4 qa[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) qa[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
-                const bf16x8 a = frag_rowmajor(Qs, G::LQ, 16 * rt_o, 32 * ks, lane);
+                const bf16x8 a = frag_rowmajor_swz<G::QRB>(Qs, 16 * rt_o, 32 * ks, lane);
                 qa[2 * (ks & 1)] = mfma16(a, rfh[ks], qa[2 * (ks & 1)]);
                 qa[2 * (ks & 1) + 1] = mfma16(a, rfl[ks], qa[2 * (ks & 1) + 1]);
             }
@@ -695,20 +704,22 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(MainParams p, HeadConsts 
             f32x4 pv = {0.f, 0.f, 0.f, 0.f};
             const bf16* Vs = Vc(g / SPC);
             for (int ks = 0; ks <= s; ++ks) {
-                const bf16x8 a = frag_rowmajor(Ps, G::LP, 16 * rt_o, 32 * ks, lane);
+                const bf16x8 a = frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane);
                 const bf16x8 bv = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
                 pv = mfma16(a, bv, pv);
             }
-            f32x4 acc;
+            const int c0 = (g / SPC) * C;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = qr[i] * decay_pow(l2g, (float)(kST * s + 16 * rt_o + 4 * g4 + i + 1)) + pv[i];
-            store_plain(acc, g);
-            __syncthreads();  // stage g consumed; stage g+1 stored
-            if (chunk_end && g + 1 < total) __syncthreads();  // R of this chunk written
+            for (int i = 0; i < 4; ++i) {
+                const int j = kST * s + 16 * rt_o + 4 * g4 + i;  // row within the chunk
+                const float acc = qr[i] * decay_pow(l2g, (float)(j + 1)) + pv[i];
+                if (c0 + j < N) out[((size_t)bh * N + c0 + j) * DV + col0 + 16 * ct_o + c16] = from_float<TOUT>(acc);
+            }
+            lds_barrier();  // stage g consumed; stage g+1 in LDS
+            if (chunk_end && g + 1 < total) lds_barrier();  // R of this chunk written
         }
     }
 }
-
 
 // Per-head GroupNorm of fp32 pre-norm rows: one wave per (b, h, n) row of DV <= 512 channels, held
 // in registers (lane l owns channels 4l..4l+3 and 256+4l..256+4l+3). Mean first, then the biased
@@ -791,13 +802,15 @@ hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
     const void* kern;
     if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT>);
     else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT>);
-    const size_t dyn = ws ? WsGeom<DK, C>::BYTES : MainGeom<DK, C>::BYTES;
+    size_t dyn;
+    if constexpr (ws) dyn = WsGeom<DK, C>::BYTES;
+    else dyn = MainGeom<DK, C>::BYTES;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
     MainParams lp = mp;
     HeadConsts hc = a.hc;
     void* args[] = {&lp, &hc};
-    return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 512 : kThreads), args, dyn, a.stream);
+    return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 576 : kThreads), args, dyn, a.stream);
 }
 
 template <int DK, int C, typename TOUT>

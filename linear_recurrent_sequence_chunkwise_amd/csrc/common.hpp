@@ -89,6 +89,40 @@ __device__ __forceinline__ bf16x8 frag_rowmajor(const bf16* base, size_t ld, int
     return *reinterpret_cast<const bf16x8*>(base + (size_t)(r0 + (lane & 15)) * ld + c0 + 8 * (lane >> 4));
 }
 
+// Swizzled LDS tiles: rows of RB bytes (RB a multiple of 128), the 16-byte chunk c of row r stored
+// at byte r*RB + 16*(c ^ (r & M)), M = min(RB/16, 16) - 1. A fragment read of 16 rows at one chunk,
+// or a transposing read of 4 rows x 2 chunks, then touches distinct banks (measured on gfx950:
+// padding rows by 16 bytes instead still conflicts for 16-row reads). A tile is filled 1 KB at a
+// time by buffer-to-LDS loads, lane l of a wave writing bytes [16l, 16l + 16) of its kilobyte.
+template <int RB>
+struct SwzTile {
+    static_assert(RB % 128 == 0, "rows of whole 128-byte lines");
+    static constexpr int M = (RB / 16 < 16 ? RB / 16 : 16) - 1;
+    __device__ static __forceinline__ int off(int r, int c) { return r * RB + 16 * (c ^ (r & M)); }
+};
+
+// frag_rowmajor on a swizzled tile (c0 a multiple of 8).
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_rowmajor_swz(const char* base, int r0, int c0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(base + SwzTile<RB>::off(r0 + (lane & 15), (c0 >> 3) + (lane >> 4)));
+}
+
+// lds_frag_kmajor on a swizzled tile (c0 a multiple of 16).
+template <int RB>
+__device__ __forceinline__ bf16x8 lds_frag_kmajor_swz(const char* base, int r0, int c0, int lane) {
+    const int g = lane >> 4, p = lane & 15;
+    const int row = r0 + 8 * g + (p >> 2), col = c0 + 4 * (p & 3);
+    const int sub = (col & 7) * 2;
+    s16x4 lo = lds_read_tr16(reinterpret_cast<const bf16*>(base + SwzTile<RB>::off(row, col >> 3) + sub));
+    s16x4 hi = lds_read_tr16(reinterpret_cast<const bf16*>(base + SwzTile<RB>::off(row + 4, col >> 3) + sub));
+    bf16x8 r;
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+    const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+    r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
+    r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
+    return r;
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
 #pragma unroll
