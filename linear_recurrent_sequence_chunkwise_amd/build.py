@@ -53,6 +53,12 @@ def build(verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    # every kernel the host code launches must be defined in the library (a host pass that silently
+    # drops a kernel template leaves an undefined symbol that only dlopen would report)
+    res = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in res.stdout.splitlines() if "_ZN3ret" in l]
+    if missing:
+        raise RuntimeError("library references undefined symbols of its own: " + ", ".join(missing[:4]))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -410,13 +410,16 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 
 
 // ---------------------------------------------------------------------------------------------
-// Warp-specialised chunk kernel (chunks up to 256): 576 threads = 4 output waves, 4 state waves and
-// one loader wave, so that loads, LDS traffic and matrix-core work overlap.
-//   loader wave  (w = 8): brings the Q, K and P rows of stage g + NB - 1 from global memory straight
-//                into LDS buffer (g + NB - 1) % NB with buffer-to-LDS loads (no registers, no LDS
-//                write instructions), NB - 1 stages ahead, then waits for the loads of stage g + 1.
-//                It never accesses LDS itself, so the compiler adds no waits for these loads
-//                anywhere else.
+// Warp-specialised chunk kernel (chunks up to 256): 768 threads = 4 output waves, 4 state waves and
+// 4 loader waves (one of each per SIMD), so that loads, LDS traffic and matrix-core work overlap.
+//   loader waves (w = 8..11): bring the Q, K and P rows of stage g + NB - 1 from global memory
+//                straight into LDS buffer (g + NB - 1) % NB with buffer-to-LDS loads (no registers,
+//                no LDS write instructions), NB - 1 stages ahead, then wait for their loads of stage
+//                g + 1. Four waves keep four times the loads in flight that one wave's counter
+//                allows. They also pull the lines of stage g + 4 into L2 with one more load each
+//                into a scratch kilobyte of LDS that nobody reads: the slices of a head run in step,
+//                so without it every slice would wait for the same lines to come from memory. The
+//                loader waves never read LDS, so the compiler adds no waits for these loads.
 //   state waves  (w = 4..7): per 32-token stage g, accumulate R += K^T (V (.) zeta) for their d_k
 //                quarter of R (fp32, scaled by g^L at each chunk start), and write stage g+1's V rows
 //                and V (.) zeta as bf16 hi + lo (V loaded into registers two stages ahead).
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 //                g^(j+1) Q R + P V, with R^T (hi + lo) held in registers for the chunk, and its store.
 // Q, K, P and R^T tiles are swizzled (SwzTile). At each chunk end the state waves write R^T as bf16
 // hi + lo into the Q/K region of the buffer that the finished stage used; the output waves read
-// their fragments from it at the next stage, before the loader refills that buffer.
+// their fragments from it at the next stage, before the loaders refill that buffer.
 template <int DK, int C>
 struct WsGeom {
     static constexpr int QRB = DK * 2;            // bytes per Q / K tile row
@@ -438,16 +441,18 @@ struct WsGeom {
     // V rows of the chunk, double-buffered by chunk parity: during a chunk's last stage the state
     // waves already store the next chunk's first V rows while the output waves still read these
     static constexpr size_t V_BYTES = (size_t)C * LV * 2;
+    static constexpr size_t SCRATCH = 1024;  // target of the L2 warm-up loads
     // three stage buffers when they fit in the 160 KiB of LDS, else two
-    static constexpr int NB = 3 * BUF + 2 * V_BYTES <= 160 * 1024 ? 3 : 2;
+    static constexpr int NB = 3 * BUF + 2 * V_BYTES + SCRATCH <= 160 * 1024 ? 3 : 2;
     static constexpr size_t OFF_V = NB * BUF;
-    static constexpr size_t BYTES = OFF_V + 2 * V_BYTES;
+    static constexpr size_t OFF_SCRATCH = OFF_V + 2 * V_BYTES;
+    static constexpr size_t BYTES = OFF_SCRATCH + SCRATCH;
     // R^T (kW rows of DK bf16, swizzled like Q) hi part in the Q region, lo part in the K region
     static_assert((size_t)kW * QRB == Q_BYTES, "R^T hi / lo fill the Q / K regions");
-    static_assert(Q_BYTES % 1024 == 0 && P_BYTES % 1024 == 0, "tiles are filled in whole kilobytes");
+    static_assert(Q_BYTES % 4096 == 0 && P_BYTES % 4096 == 0, "tiles are split over four loader waves in kilobytes");
     static constexpr int Q_KB = (int)(Q_BYTES / 1024), P_KB = (int)(P_BYTES / 1024);
-    static constexpr int NDMA = 2 * Q_KB + P_KB;  // buffer-to-LDS loads per stage (loader wave)
-    static_assert(NDMA <= 63, "one stage of loads must fit the vmcnt counter");
+    static constexpr int NDMA = (2 * Q_KB + P_KB) / 4;  // buffer-to-LDS loads per stage and loader wave
+    static_assert(NDMA + 2 <= 63, "the loads of one stage must fit the vmcnt counter");
 };
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(n), expcnt and lgkmcnt not waited on
@@ -466,7 +471,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int DK, int C, typename TOUT>
-__global__ __launch_bounds__(576) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
+__global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
     using G = WsGeom<DK, C>;
     constexpr int NB = G::NB;
     constexpr int RTR = DK / 64;  // 16-row R tiles per state wave
@@ -495,45 +500,76 @@ __global__ __launch_bounds__(576) void chunk_ws_kernel(MainParams p, HeadConsts 
     // Barrier sequence, identical for all roles (each role runs its own loop with its own
     // registers): one after the prologue; per stage g: one at a chunk start (s == 0), one at the
     // end of the stage, and one more after a chunk end that is not the last stage.
-    if (w == 8) {
-        // ---------------- loader wave
+    if (w >= 8) {
+        // ---------------- loader waves
+        const int lw = __builtin_amdgcn_readfirstlane(w - 8);  // wave-uniform: one buffer resource per wave
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)bh * N * DV), 0, v_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rp =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
-        // Q, K and P rows of stage g into its buffer; lane l fills bytes [16l, 16l+16) of each
-        // kilobyte. P: only the 32-key steps up to this stage; the rest read as zero, no traffic.
+        // This wave's share (kilobytes j = lw mod 4) of the Q, K and P rows of stage g, into its
+        // buffer; lane l fills bytes [16l, 16l+16) of each kilobyte. P: only the 32-key steps up to
+        // this stage; the rest read as zero, no traffic.
         auto dma_stage = [&](int g) __attribute__((always_inline)) {
             const int ci = g / SPC, s = g % SPC;
             const int tok0 = ci * C + kST * s;
             char* bq = buf(g);
 #pragma unroll
-            for (int j = 0; j < G::Q_KB; ++j) {
+            for (int jj = 0; jj < G::Q_KB / 4; ++jj) {
+                const int j = 4 * jj + lw;
                 const int byte = 1024 * j + 16 * lane, r = byte / G::QRB;
                 const int c = ((byte % G::QRB) >> 4) ^ (r & SwzTile<G::QRB>::M);
                 const unsigned off = (unsigned)(((tok0 + r) * DK + 8 * c) * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(bq + 1024 * j), 16, off, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(bq + G::OFF_K + 1024 * j), 16, off,
-                                                         0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(bq + G::OFF_K + 1024 * j), 16, off, 0, 0, 0);
             }
             const int per_row = 4 * (s + 1);
             const unsigned base = (unsigned)((ci * C + kST * s) * C);
 #pragma unroll
-            for (int j = 0; j < G::P_KB; ++j) {
+            for (int jj = 0; jj < G::P_KB / 4; ++jj) {
+                const int j = 4 * jj + lw;
                 const int byte = 1024 * j + 16 * lane, r = byte / G::PRB;
                 const int c = ((byte % G::PRB) >> 4) ^ (r & SwzTile<G::PRB>::M);
                 const unsigned off = c < per_row ? (base + (unsigned)(r * C + 8 * c)) * 2u : p_bytes;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void*)(bq + G::OFF_P + 1024 * j), 16, off,
-                                                         0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void*)(bq + G::OFF_P + 1024 * j), 16, off, 0, 0, 0);
             }
         };
-        // prologue: stages 0 .. NB-2
+        // L2 warm-up of stage g: one 16-byte load per 128-byte line, this slice's share (lines
+        // i = slice mod NS) of the head's Q (loader 0), K (loader 1) and P (loader 2) lines, and
+        // this slice's own V row segments (loader 3). Lanes without a line load past the end.
+        auto warm = [&](int g) __attribute__((always_inline)) {
+            const int ci = g / SPC, s = g % SPC;
+            const int tok0 = ci * C + kST * s;
+            constexpr int LPR = G::QRB / 128;  // lines per Q (or K) row
+            const int i = slice + p.NS * lane;
+            unsigned off;
+            __amdgpu_buffer_rsrc_t r = rq;
+            if (lw < 2) {
+                off = g < total && i < kST * LPR ? (unsigned)((tok0 + i / LPR) * G::QRB + 128 * (i % LPR)) : q_bytes;
+                if (lw == 1) r = rk;
+            } else if (lw == 2) {
+                const int plr = (kST * (s + 1) * 2 + 127) / 128;  // P lines per row up to this stage
+                off = g < total && i < kST * plr ? (unsigned)(((ci * C + kST * s + i / plr) * C) * 2 + 128 * (i % plr)) : p_bytes;
+                r = rp;
+            } else {
+                off = g < total && lane < kST ? (unsigned)(((tok0 + lane) * DV + col0) * 2) : v_bytes;
+                r = rv;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(smem + G::OFF_SCRATCH), 16, off, 0, 0, 0);
+        };
+        // Wait for this wave's loads of one stage: the loads issued after them are one stage of
+        // loads and two warm-up loads (NB == 3), or one warm-up load (NB == 2).
+        constexpr int kAfter = NB == 3 ? G::NDMA + 2 : 1;
+        // prologue: stages 0 .. NB-2, warm-up of stages NB .. 2NB-2 ... (see the loop)
         dma_stage(0);
+        warm(2);
         if (NB == 3 && total > 1) {
             dma_stage(1);
-            __builtin_amdgcn_s_waitcnt(wait_vm<G::NDMA>());  // stage 0 landed
+            warm(3);
+            __builtin_amdgcn_s_waitcnt(wait_vm<kAfter>());  // stage 0 landed
         } else {
-            __builtin_amdgcn_s_waitcnt(wait_vm<0>());
+            __builtin_amdgcn_s_waitcnt(wait_vm<1>());
         }
         lds_barrier();
         for (int g = 0; g < total; ++g) {
@@ -542,8 +578,8 @@ __global__ __launch_bounds__(576) void chunk_ws_kernel(MainParams p, HeadConsts 
             if (s == 0) lds_barrier();  // the output waves have taken R from the buffer refilled next
             if (g + NB - 1 < total) {
                 dma_stage(g + NB - 1);
-                if constexpr (NB == 3) __builtin_amdgcn_s_waitcnt(wait_vm<G::NDMA>());  // stage g+1 landed
-                else __builtin_amdgcn_s_waitcnt(wait_vm<0>());
+                warm(g + NB + 1);
+                __builtin_amdgcn_s_waitcnt(wait_vm<kAfter>());  // stage g+1 landed
             } else {
                 __builtin_amdgcn_s_waitcnt(wait_vm<0>());
             }
@@ -673,8 +709,14 @@ __global__ __launch_bounds__(576) void chunk_ws_kernel(MainParams p, HeadConsts 
         }
     } else {
         // ---------------- output waves: 16 x 16 tile of each stage
-        TOUT* out = reinterpret_cast<TOUT*>(p.out);
+        // output rows of this head through a buffer resource: stores past row N are dropped
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<TOUT*>(p.out) + (size_t)bh * N * DV), 0, (unsigned)((size_t)N * DV * sizeof(TOUT)), 0x00020000);
         bf16x8 rfh[DK / 32], rfl[DK / 32];
+        // zero the V rows that the state waves do not write before the first stage: all of the
+        // second chunk buffer and the first buffer past stage 0
+        for (int i = threadIdx.x; i < (int)((2 * G::V_BYTES - kST * G::LV * 2) / 16); i += 256)
+            *reinterpret_cast<f32x4*>(smem + G::OFF_V + kST * G::LV * 2 + 16 * i) = f32x4{0.f, 0.f, 0.f, 0.f};
         lds_barrier();
         for (int g = 0; g < total; ++g) {
             const int s = g % SPC;
@@ -691,29 +733,39 @@ __global__ __launch_bounds__(576) void chunk_ws_kernel(MainParams p, HeadConsts 
             }
             const char* Qs = buf(g);
             const char* Ps = buf(g) + G::OFF_P;
+            // the Q fragments first (their read latencies overlap), then the QR chains; the P and V
+            // reads go out while those run
+            bf16x8 qf[DK / 32];
+            const bf16* Vs = Vc(g / SPC);
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = frag_rowmajor_swz<G::QRB>(Qs, 16 * rt_o, 32 * ks, lane);
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 qa[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) qa[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
-                const bf16x8 a = frag_rowmajor_swz<G::QRB>(Qs, 16 * rt_o, 32 * ks, lane);
-                qa[2 * (ks & 1)] = mfma16(a, rfh[ks], qa[2 * (ks & 1)]);
-                qa[2 * (ks & 1) + 1] = mfma16(a, rfl[ks], qa[2 * (ks & 1) + 1]);
+                qa[2 * (ks & 1)] = mfma16(qf[ks], rfh[ks], qa[2 * (ks & 1)]);
+                qa[2 * (ks & 1) + 1] = mfma16(qf[ks], rfl[ks], qa[2 * (ks & 1) + 1]);
             }
-            const f32x4 qr = (qa[0] + qa[2]) + (qa[1] + qa[3]);
+            // P V over every 32-key step of the chunk: P is zero past this stage's keys (its rows are
+            // loaded as zero there), and the V rows there are finite (zeroed at the start, or rows
+            // of an earlier chunk), so the unrolled sum needs no branch
             f32x4 pv = {0.f, 0.f, 0.f, 0.f};
-            const bf16* Vs = Vc(g / SPC);
-            for (int ks = 0; ks <= s; ++ks) {
-                const bf16x8 a = frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane);
-                const bf16x8 bv = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
-                pv = mfma16(a, bv, pv);
-            }
+#pragma unroll
+            for (int ks = 0; ks < SPC; ++ks)
+                pv = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane), pv);
+            const f32x4 qr = (qa[0] + qa[2]) + (qa[1] + qa[3]);
             const int c0 = (g / SPC) * C;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = kST * s + 16 * rt_o + 4 * g4 + i;  // row within the chunk
                 const float acc = qr[i] * decay_pow(l2g, (float)(j + 1)) + pv[i];
-                if (c0 + j < N) out[((size_t)bh * N + c0 + j) * DV + col0 + 16 * ct_o + c16] = from_float<TOUT>(acc);
+                const unsigned off = (unsigned)(((c0 + j) * DV + col0 + 16 * ct_o + c16) * (int)sizeof(TOUT));
+                if constexpr (sizeof(TOUT) == 4)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_float<TOUT>(acc)), ro, off, 0, 0);
             }
             lds_barrier();  // stage g consumed; stage g+1 in LDS
             if (chunk_end && g + 1 < total) lds_barrier();  // R of this chunk written
@@ -810,7 +862,7 @@ hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
     MainParams lp = mp;
     HeadConsts hc = a.hc;
     void* args[] = {&lp, &hc};
-    return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 576 : kThreads), args, dyn, a.stream);
+    return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 768 : kThreads), args, dyn, a.stream);
 }
 
 template <int DK, int C, typename TOUT>

@@ -48,8 +48,9 @@ struct LaunchArgs {
     hipStream_t stream;
 };
 
-// g^e for a per-head log2(g); exact 1 at e = 0; underflows to 0 for large e.
-__device__ __forceinline__ float decay_pow(float log2g, float e) { return exp2f(e * log2g); }
+// g^e for a per-head log2(g), with the hardware exp2 (v_exp_f32, about 1 ulp): exactly 1 at e = 0;
+// results below the normal range flush to 0, which is below anything they are added to here.
+__device__ __forceinline__ float decay_pow(float log2g, float e) { return __builtin_amdgcn_exp2f(e * log2g); }
 
 // 16x16x32 bf16 MFMA, fp32 accumulate. Operand layouts (lane l of 64, checked on gfx950):
 //   A[m][k]: lane holds m = l%16, k = 8*(l/16) + j (j = 0..7)
