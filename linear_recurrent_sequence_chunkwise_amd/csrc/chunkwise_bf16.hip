@@ -32,78 +32,66 @@ constexpr int kW = 32;     // d_v columns per workgroup
 constexpr int kST = 32;    // tokens per pipeline stage
 
 // ---------------------------------------------------------------------------------------------
-// P = (Q K^T) (.) D. Grid (C/64 bands, nchunks, B*H). Wave w owns row tile t = 4*band + w and
-// writes key tiles 0 .. (t|1): for even t the second tile of the diagonal 32-key block is all
-// zero but written, so that the consumer reads whole 32-key steps.
+// P = (Q K^T) (.) D for every chunk, into the workspace as [B*H][nchunks][C][C] bf16. Grid
+// (nchunks, B*H), 256 threads. The MFMAs compute P^T = K Q^T per 16 x 16 tile so that each lane
+// ends with 4 consecutive keys of one row (one 8-byte store). K rows go through LDS in 128-key
+// blocks (buffer-to-LDS loads, swizzled rows); each wave reads the Q fragments of its row tile
+// straight from global memory into registers. Row tile t (16 rows) gets key tiles 0 .. (t|1): the
+// consumer reads whole 32-key steps up to the diagonal one, whose upper part is written as zero.
+// Waves take row tiles in mirrored pairs (t, T-1-t) so that the causal work is balanced.
 template <int DK>
-__global__ __launch_bounds__(kThreads) void chunk_scores_kernel(int H, int N, int C, int nchunks,
-                                                                const bf16* __restrict__ q,
-                                                                const bf16* __restrict__ k,
-                                                                bf16* __restrict__ P, HeadConsts hc) {
-    constexpr int LD = DK + 8;           // 16-byte fragment reads of 16 rows: distinct banks
-    constexpr int NCH = 64 * DK / 8 / kThreads;  // 16-byte chunks per thread for a 64-row block
-    __shared__ bf16 Qs[64 * LD];
-    __shared__ bf16 Ks[2][64 * LD];
-    const int band = blockIdx.x, chunk = blockIdx.y, bh = blockIdx.z, h = bh % H;
+__global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
+                                                           const bf16* __restrict__ k, bf16* __restrict__ P, HeadConsts hc) {
+    constexpr int KB = 128;       // keys per LDS block
+    constexpr int QRB = DK * 2;   // bytes per K row
+    constexpr int NKB = KB * QRB / 1024;  // kilobytes of a K block
+    __shared__ __attribute__((aligned(1024))) char Ks[KB * QRB];
+    const int chunk = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
     const int c0 = chunk * C;
-    const int L = min(C, N - c0);
-    const bf16* qb = q + ((size_t)bh * N + c0) * DK;
-    const bf16* kb = k + ((size_t)bh * N + c0) * DK;
-    bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
     const float l2g = hc.log2g[h];
+    const unsigned q_bytes = (unsigned)((size_t)N * DK * 2);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
+    bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
+    const int T = C / 16;  // row tiles of the chunk
 
-    auto load_block = [&](const bf16* base, int row0, bf16x8* r) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int j = threadIdx.x + kThreads * u;
-            const int row = j / (DK / 8), sg = j % (DK / 8);
-            r[u] = row0 + row < L ? *reinterpret_cast<const bf16x8*>(base + (size_t)(row0 + row) * DK + 8 * sg)
-                                  : zero_bf16x8();
+    for (int kb0 = 0; kb0 < C; kb0 += KB) {
+        // K rows kb0 .. kb0+KB-1 of the chunk (rows past the sequence read as zero)
+        if (kb0 > 0) __syncthreads();  // the previous block's reads are done
+        for (int j = w; j < NKB; j += 4) {
+            const int byte = 1024 * j + 16 * lane, r = byte / QRB;
+            const int c = ((byte % QRB) >> 4) ^ (r & SwzTile<QRB>::M);
+            const unsigned off = (unsigned)(((c0 + kb0 + r) * DK + 8 * c) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + 1024 * j), 16, off, 0, 0, 0);
         }
-    };
-    auto store_block = [&](bf16* dst, const bf16x8* r) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        for (int m = 0; m < T / 4; ++m) {
+            const int t = (m & 1) ? 4 * m + 3 - w : 4 * m + w;  // mirrored within each group of 8
+            const int last = min((t | 1), (kb0 + KB) / 16 - 1);  // last key tile of this block
+            if (last * 16 < kb0) continue;
+            bf16x8 qf[DK / 32];
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int j = threadIdx.x + kThreads * u;
-            const int row = j / (DK / 8), sg = j % (DK / 8);
-            *reinterpret_cast<bf16x8*>(dst + row * LD + 8 * sg) = r[u];
-        }
-    };
-
-    bf16x8 rq[NCH], rk[NCH];
-    load_block(qb, 64 * band, rq);
-    load_block(kb, 0, rk);
-    store_block(Qs, rq);
-    store_block(Ks[0], rk);
-    if (band > 0) load_block(kb, 64, rk);
-    __syncthreads();
-
-    const int t = 4 * band + w;  // row tile of this wave
-    bf16x8 qa[DK / 32];
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) qa[ks] = frag_rowmajor(Qs, LD, 16 * w, 32 * ks, lane);
-
-    for (int kbk = 0; kbk <= band; ++kbk) {
-        const bf16* Kc = Ks[kbk & 1];
-        // key tiles of this block that the row tile needs: up to (t|1)
-        const int last = min(3, (t | 1) - 4 * kbk);
-        for (int kt = 0; kt <= last; ++kt) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) s = mfma16(qa[ks], frag_rowmajor(Kc, LD, 16 * kt, 32 * ks, lane), s);
-            const int key = 64 * kbk + 16 * kt + c16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * t + 4 * g4 + i;
-                const float d = row >= key ? decay_pow(l2g, (float)(row - key)) : 0.f;
-                Pc[(size_t)row * C + key] = (bf16)(s[i] * d);
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const unsigned off = (unsigned)(((c0 + 16 * t + c16) * DK + 32 * ks + 8 * g4) * 2);
+                qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
             }
-        }
-        if (kbk < band) {
-            store_block(Ks[(kbk + 1) & 1], rk);
-            if (kbk + 2 <= band) load_block(kb, 64 * (kbk + 2), rk);
-            __syncthreads();
+            for (int kt = kb0 / 16; kt <= last; ++kt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks)
+                    acc = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qf[ks], acc);
+                // lane: row 16t + c16, keys 16kt + 4g4 + i
+                const int row = 16 * t + c16;
+                bf16x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kt + 4 * g4 + i;
+                    o[i] = (bf16)(row >= key ? acc[i] * decay_pow(l2g, (float)(row - key)) : 0.f);
+                }
+                *reinterpret_cast<bf16x4*>(Pc + (size_t)row * C + 16 * kt + 4 * g4) = o;
+            }
         }
     }
 }
@@ -878,7 +866,7 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
 
-    hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(C / 64, nchunks, a.B * a.H), dim3(kThreads), 0, a.stream, a.H, a.N, C,
+    hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C,
                        nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), a.hc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
