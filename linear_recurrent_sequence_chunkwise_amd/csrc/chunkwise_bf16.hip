@@ -701,6 +701,10 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<TOUT*>(p.out) + (size_t)bh * N * DV), 0, (unsigned)((size_t)N * DV * sizeof(TOUT)), 0x00020000);
         bf16x8 rfh[DK / 32], rfl[DK / 32];
+        // g^(r+1) for this lane's rows r = 16 rt_o + 4 g4 + i of a stage
+        float row_decay[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) row_decay[i] = decay_pow(l2g, (float)(16 * rt_o + 4 * g4 + i + 1));
         // zero the V rows that the state waves do not write before the first stage: all of the
         // second chunk buffer and the first buffer past stage 0
         for (int i = threadIdx.x; i < (int)((2 * G::V_BYTES - kST * G::LV * 2) / 16); i += 256)
@@ -721,12 +725,17 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             }
             const char* Qs = buf(g);
             const char* Ps = buf(g) + G::OFF_P;
-            // the Q fragments first (their read latencies overlap), then the QR chains; the P and V
-            // reads go out while those run
-            bf16x8 qf[DK / 32];
             const bf16* Vs = Vc(g / SPC);
+            // the Q fragments and the first two P V steps' fragments first (their read latencies
+            // overlap), then the QR chains; the other P and V reads go out while those run
+            bf16x8 qf[DK / 32], pf[2], vf[2];
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = frag_rowmajor_swz<G::QRB>(Qs, 16 * rt_o, 32 * ks, lane);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                pf[ks] = frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane);
+                vf[ks] = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
+            }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 qa[4];
 #pragma unroll
@@ -736,19 +745,23 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 qa[2 * (ks & 1)] = mfma16(qf[ks], rfh[ks], qa[2 * (ks & 1)]);
                 qa[2 * (ks & 1) + 1] = mfma16(qf[ks], rfl[ks], qa[2 * (ks & 1) + 1]);
             }
-            // P V over every 32-key step of the chunk: P is zero past this stage's keys (its rows are
-            // loaded as zero there), and the V rows there are finite (zeroed at the start, or rows
-            // of an earlier chunk), so the unrolled sum needs no branch
-            f32x4 pv = {0.f, 0.f, 0.f, 0.f};
+            // P V over every 32-key step of the chunk, in two chains: P is zero past this stage's
+            // keys (its rows are loaded as zero there), and the V rows there are finite (zeroed at
+            // the start, or rows of an earlier chunk), so the unrolled sum needs no branch
+            f32x4 pa[2] = {mfma16(pf[0], vf[0], f32x4{0.f, 0.f, 0.f, 0.f}), mfma16(pf[1], vf[1], f32x4{0.f, 0.f, 0.f, 0.f})};
 #pragma unroll
-            for (int ks = 0; ks < SPC; ++ks)
-                pv = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane), pv);
+            for (int ks = 2; ks < SPC; ++ks)
+                pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane),
+                                    pa[ks & 1]);
             const f32x4 qr = (qa[0] + qa[2]) + (qa[1] + qa[3]);
+            const f32x4 pv = pa[0] + pa[1];
+            // g^(j+1) for row j = 32 s + r of the chunk: g^(32 s) (one per stage) times g^(r+1)
+            const float gs = decay_pow(l2g, (float)(kST * s));
             const int c0 = (g / SPC) * C;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = kST * s + 16 * rt_o + 4 * g4 + i;  // row within the chunk
-                const float acc = qr[i] * decay_pow(l2g, (float)(j + 1)) + pv[i];
+                const float acc = qr[i] * (gs * row_decay[i]) + pv[i];
                 const unsigned off = (unsigned)(((c0 + j) * DV + col0 + 16 * ct_o + c16) * (int)sizeof(TOUT));
                 if constexpr (sizeof(TOUT) == 4)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 0);
