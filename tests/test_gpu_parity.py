@@ -150,6 +150,25 @@ def test_bf16_parallel_layer_shape_groupnorm(orc):
     report("chunkwise GN affine bf16 out", rel_err(o, ref_gn), TOL["bf16"])
 
 
+# GroupNorm fused into the chunk kernel (chunks up to 256; 512 takes the separate pass): every chunk
+# size, fp32 and bf16 out, ragged N, head counts that are not a multiple of 8 (the d_v slices of a
+# head then sit on different XCDs), and a grid of 512 workgroups (more than the GPU holds at once).
+@pytest.mark.parametrize("dk,dv,B,H,N", [(64, 64, 3, 5, 777), (256, 512, 1, 3, 1100), (256, 512, 2, 16, 600)])
+def test_bf16_chunkwise_groupnorm_shapes(orc, dk, dv, B, H, N):
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=300 + N)
+    gam = I.multiscale_gammas(H)
+    ref, _ = orc.recurrent(q, k, v, gam)
+    gw = (1.0 + 0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(7))).float()
+    gb = (0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(8))).float()
+    ref_gn = orc.groupnorm(ref, 1e-5, gw, gb)
+    gn = R.GroupNorm(1e-5, gw.to(DEV), gb.to(DEV))
+    qd, kd, vd = dev(q, k, v)
+    for C in (64, 128, 256, 512):
+        for odt in (torch.float32, torch.bfloat16):
+            o, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, groupnorm=gn, out_dtype=odt, want_state=False)
+            report(f"GN B={B} H={H} N={N} dk={dk} C={C} {str(odt)[6:]} out", rel_err(o, ref_gn), TOL["bf16"])
+
+
 # ---------------------------------------------------------------------------------------------
 # Workload: 6.7B-layer shape, B=1, H=16, N=8192, dk=256, dv=512, chunk 128, GroupNorm eps 1e-5, bf16 out
 def test_layer_6p7b_chunkwise_groupnorm_full(orc):
