@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 1
+#define RETENTION_ABI_VERSION 2
 #define RETENTION_MAX_HEADS 128
 
 typedef enum {
@@ -69,12 +69,18 @@ typedef struct {
  * normalised per head before concatenation). One group = the d_v channels of one head at one
  * position: y = (o - mean) / sqrt(var + eps) * weight[h][c] + bias[h][c], biased variance,
  * statistics in fp32 from the fp32 pre-norm output. weight/bias: device fp32 [H][d_v], or NULL
- * for 1 / 0. Pass NULL (or enabled = 0) for no normalisation. */
+ * for 1 / 0. Pass NULL (or enabled = 0) for no normalisation.
+ * Optional swish gate after it (abeam.tech RetNet summary, "Multi-timescale decay, gate and
+ * normalisation": a Swish gate adds non-linearity, GroupNorm handles the heads' differing
+ * variance): out = swish(g) * y with swish(x) = x * sigmoid(x), g = gate[b][h][n][c], a device
+ * tensor in the input dtype laid out like out ([B][H][d_v] for the decode step), or NULL. A gate
+ * needs enabled = 1 (RET_ERR_INVALID_ARG otherwise). */
 typedef struct {
     int32_t enabled;
     float eps;           /* > 0 */
     const float* weight; /* [H][d_v] or NULL */
     const float* bias;   /* [H][d_v] or NULL */
+    const void* gate;    /* like out, input dtype, or NULL */
 } ret_groupnorm;
 
 /*

@@ -63,19 +63,24 @@ ret_status check_gamma(const ret_shape* s, const double* gamma, ret::HeadConsts*
     return RET_OK;
 }
 
-ret_status check_gn(const ret_groupnorm* gn, ret::GnArgs* out) {
+ret_status check_gn(const ret_groupnorm* gn, int in_bf16, ret::GnArgs* out) {
     out->enabled = 0;
     out->eps = 0.f;
     out->weight = nullptr;
     out->bias = nullptr;
+    out->gate = nullptr;
+    out->gate_bf16 = in_bf16;
+    if (gn && !gn->enabled && gn->gate) return fail(RET_ERR_INVALID_ARG, "a gate needs the GroupNorm epilogue (enabled = 1)");
     if (!gn || !gn->enabled) return RET_OK;
     if (!(gn->eps > 0.f) || !std::isfinite(gn->eps)) return fail(RET_ERR_INVALID_ARG, "groupnorm eps must be finite and > 0");
     if ((gn->weight && !aligned16(gn->weight)) || (gn->bias && !aligned16(gn->bias)))
         return fail(RET_ERR_INVALID_ARG, "groupnorm weight/bias must be 16-byte aligned");
+    if (gn->gate && !aligned16(gn->gate)) return fail(RET_ERR_INVALID_ARG, "gate must be 16-byte aligned");
     out->enabled = 1;
     out->eps = gn->eps;
     out->weight = gn->weight;
     out->bias = gn->bias;
+    out->gate = gn->gate;
     return RET_OK;
 }
 
@@ -176,7 +181,7 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
     ret::HeadConsts hc;
     RET_TRY(check_gamma(shape, gamma, &hc));
     ret::GnArgs gn;
-    RET_TRY(check_gn(groupnorm, &gn));
+    RET_TRY(check_gn(groupnorm, shape->in_dtype == RET_BF16, &gn));
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     const bool bf = shape->in_dtype == RET_BF16;
     if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, shape->d_v, chunk)
@@ -194,7 +199,10 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
         return fail(RET_ERR_INVALID_ARG, "out must not alias state_out");
     if (state_out && state_in && state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes))
         return fail(RET_ERR_INVALID_ARG, "state_out may equal state_in but must not partly overlap it");
-    if (!out) gn.enabled = 0;
+    if (!out) {
+        gn.enabled = 0;
+        gn.gate = nullptr;
+    }
     const size_t need = chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
     RET_TRY(check_ws(need, workspace, workspace_bytes));
 
@@ -219,7 +227,7 @@ ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const
     ret::HeadConsts hc;
     RET_TRY(check_gamma(shape, gamma, &hc));
     ret::GnArgs gn;
-    RET_TRY(check_gn(groupnorm, &gn));
+    RET_TRY(check_gn(groupnorm, shape->in_dtype == RET_BF16, &gn));
     const int dv = shape->d_v;
     if (dv % 4 != 0 || dv / 4 > 256 || 256 % (dv / 4) != 0)
         return fail(RET_ERR_UNSUPPORTED, "recurrent step needs d_v a multiple of 4 with d_v/4 dividing 256 (got %d)", dv);
@@ -245,7 +253,7 @@ ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const v
     ret::HeadConsts hc;
     RET_TRY(check_gamma(shape, gamma, &hc));
     ret::GnArgs gn;
-    RET_TRY(check_gn(groupnorm, &gn));
+    RET_TRY(check_gn(groupnorm, shape->in_dtype == RET_BF16, &gn));
     const bool bf = shape->in_dtype == RET_BF16;
     if (bf ? !ret::parallel_bf16_supported(shape->d_k, shape->d_v) : !ret::parallel_f32_supported(shape->d_k, shape->d_v))
         return fail(RET_ERR_UNSUPPORTED, "parallel: no kernel for %s inputs with d_k %d, d_v %d", bf ? "bf16" : "fp32", shape->d_k,

@@ -776,7 +776,8 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
 
 // Per-head GroupNorm of fp32 pre-norm rows: one wave per (b, h, n) row of DV <= 512 channels, held
 // in registers (lane l owns channels 4l..4l+3 and 256+4l..256+4l+3). Mean first, then the biased
-// variance from the centred values, so no cancellation; y = (x - mean) / sqrt(var + eps) * w + b.
+// variance from the centred values, so no cancellation; y = (x - mean) / sqrt(var + eps) * w + b,
+// times swish(gate) when a (bf16) gate is given.
 template <typename TOUT>
 __global__ __launch_bounds__(256) void gn_rows_kernel(long rows, int H, int N, int DV, const float* __restrict__ x,
                                                       TOUT* __restrict__ y, GnArgs gn) {
@@ -814,9 +815,15 @@ __global__ __launch_bounds__(256) void gn_rows_kernel(long rows, int H, int N, i
         f32x4 w = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
         if (gn.weight) w = *reinterpret_cast<const f32x4*>(gn.weight + (size_t)h * DV + c);
         if (gn.bias) bb = *reinterpret_cast<const f32x4*>(gn.bias + (size_t)h * DV + c);
+        f32x4 gs = {1.f, 1.f, 1.f, 1.f};
+        if (gn.gate) {
+            const bf16x4 g = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(gn.gate) + (size_t)row * DV + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gs[j] = swish((float)g[j]);
+        }
         TOUT o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = from_float<TOUT>((xv[i][j] - mean) * inv * w[j] + bb[j]);
+        for (int j = 0; j < 4; ++j) o[j] = from_float<TOUT>(((xv[i][j] - mean) * inv * w[j] + bb[j]) * gs[j]);
         TOUT* yr = y + (size_t)row * DV + c;
         if constexpr (sizeof(TOUT) == 4) *reinterpret_cast<f32x4*>(yr) = f32x4{(float)o[0], (float)o[1], (float)o[2], (float)o[3]};
         else *reinterpret_cast<bf16x4*>(yr) = bf16x4{o[0], o[1], o[2], o[3]};

@@ -28,6 +28,8 @@ struct GnArgs {
     float eps;
     const float* weight;  // [H][dv] or nullptr
     const float* bias;    // [H][dv] or nullptr
+    const void* gate;     // laid out like the output, input dtype, or nullptr
+    int gate_bf16;
 };
 
 // Everything a launcher needs; filled and validated by the C-ABI layer.
@@ -134,6 +136,17 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 __device__ __forceinline__ void split_hi_lo(float x, bf16& hi, bf16& lo) {
     hi = (bf16)x;
     lo = (bf16)(x - (float)hi);
+}
+
+// Swish gate of the GroupNorm output (abeam.tech RetNet summary, "Multi-timescale decay, gate and
+// normalisation"): x * sigmoid(x), with the hardware exp2 and reciprocal (about 1 ulp each);
+// exp overflow for very negative x gives 0 * x, the limit.
+__device__ __forceinline__ float swish(float x) {
+    return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+// Element i of the gate tensor, in its dtype
+__device__ __forceinline__ float gate_at(const struct GnArgs& gn, size_t i) {
+    return gn.gate_bf16 ? (float)reinterpret_cast<const __bf16*>(gn.gate)[i] : reinterpret_cast<const float*>(gn.gate)[i];
 }
 
 template <typename T> __device__ __forceinline__ T from_float(float x);

@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void parallel_f32_kernel(int H, int N, in
     }
 }
 
-// One wave per (b, h, n) row: y = (x - mean) / sqrt(var + eps) * w + b over DV channels.
+// One wave per (b, h, n) row: y = (x - mean) / sqrt(var + eps) * w + b over DV channels, times
+// swish(gate) when a gate is given.
 template <typename TOUT>
 __global__ __launch_bounds__(kThreads) void groupnorm_rows_kernel(long rows, int H, int N, int DV, const float* __restrict__ x,
                                                                   TOUT* __restrict__ y, GnArgs gn) {
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void groupnorm_rows_kernel(long rows, int
     for (int c = lane; c < DV; c += kWave) {
         const float wv = gn.weight ? gn.weight[(size_t)h * DV + c] : 1.f;
         const float bv = gn.bias ? gn.bias[(size_t)h * DV + c] : 0.f;
-        y[(size_t)row * DV + c] = from_float<TOUT>((xr[c] - mean) * inv * wv + bv);
+        const float gs = gn.gate ? swish(gate_at(gn, (size_t)row * DV + c)) : 1.f;
+        y[(size_t)row * DV + c] = from_float<TOUT>(((xr[c] - mean) * inv * wv + bv) * gs);
     }
 }
 

@@ -178,8 +178,14 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
             const int n = n0 + 32 * wr + 16 * rt + 4 * g4 + i;
             if (n < N) {
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    out[((size_t)bh * N + n) * DV + wc * (DV / 2) + 16 * ct + c16] = from_float<TOUT>(acc[rt][ct][i]);
+                for (int ct = 0; ct < CT; ++ct) {
+                    const size_t e = ((size_t)bh * N + n) * DV + wc * (DV / 2) + 16 * ct + c16;
+                    float val = acc[rt][ct][i];
+                    if constexpr (GN) {
+                        if (gn.gate) val *= swish(gate_at(gn, e));  // the swish gate after GroupNorm
+                    }
+                    out[e] = from_float<TOUT>(val);
+                }
             }
         }
 }

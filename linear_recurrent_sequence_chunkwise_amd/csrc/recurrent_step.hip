@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
                 const float w = gn.weight ? gn.weight[(size_t)h * DV + c] : 1.f;
                 const float b = gn.bias ? gn.bias[(size_t)h * DV + c] : 0.f;
                 o[j] = (o[j] - mean) * inv * w + b;
+                if (gn.gate) o[j] *= swish(gate_at(gn, (size_t)bh * DV + c));  // the swish gate after GroupNorm
             }
         }
     }

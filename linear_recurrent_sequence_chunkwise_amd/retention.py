@@ -32,7 +32,7 @@ class RetShape(ctypes.Structure):
 
 class RetGroupNorm(ctypes.Structure):
     _fields_ = [("enabled", ctypes.c_int32), ("eps", ctypes.c_float), ("weight", ctypes.c_void_p),
-                ("bias", ctypes.c_void_p)]
+                ("bias", ctypes.c_void_p), ("gate", ctypes.c_void_p)]
 
 
 class RetentionError(RuntimeError):
@@ -82,16 +82,21 @@ def _check(status):
 
 @dataclass
 class GroupNorm:
-    """Per-head GroupNorm epilogue: y = (o - mean) / sqrt(var + eps) * weight[h] + bias[h] over d_v."""
+    """Per-head GroupNorm epilogue: y = (o - mean) / sqrt(var + eps) * weight[h] + bias[h] over d_v,
+    then, with a gate, y * swish(gate)."""
     eps: float = 1e-5
     weight: Optional[torch.Tensor] = None  # fp32 [H, d_v] on the device, or None
     bias: Optional[torch.Tensor] = None
+    gate: Optional[torch.Tensor] = None  # shaped like the output, in the input dtype, or None
 
-    def as_struct(self):
+    def as_struct(self, in_dtype, out_shape):
         for t in (self.weight, self.bias):
             if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
                 raise ValueError("groupnorm weight/bias must be contiguous fp32 device tensors")
-        return RetGroupNorm(1, float(self.eps), _ptr(self.weight), _ptr(self.bias))
+        g = self.gate
+        if g is not None and (g.dtype != in_dtype or tuple(g.shape) != tuple(out_shape) or not g.is_contiguous() or not g.is_cuda):
+            raise ValueError(f"gate must be a contiguous {in_dtype} device tensor of shape {tuple(out_shape)}")
+        return RetGroupNorm(1, float(self.eps), _ptr(self.weight), _ptr(self.bias), _ptr(g))
 
 
 def _ptr(t):
@@ -180,7 +185,7 @@ def chunkwise_fwd(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None,
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     if not want_state:
         state_out = None
-    gn = groupnorm.as_struct() if groupnorm is not None else None
+    gn = groupnorm.as_struct(q.dtype, (B, H, N, dv)) if groupnorm is not None else None
     shp = _shape(B, H, N, dk, dv, in_code, out_code)
     need = lib.retention_workspace_bytes(RET_FN_CHUNKWISE, ctypes.byref(shp), int(chunk),
                                          int(gn is not None and out is not None))
@@ -210,7 +215,7 @@ def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optiona
         out = torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
     if not want_out:
         out = None
-    gn = groupnorm.as_struct() if groupnorm is not None else None
+    gn = groupnorm.as_struct(q.dtype, (B, H, dv)) if groupnorm is not None else None
     shp = _shape(B, H, 1, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
     st = lib.retention_recurrent_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _ptr(state),
                                       ctypes.byref(gn) if gn is not None else None, _ptr(out), None, 0,
@@ -230,7 +235,7 @@ def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNo
         out_dtype = out.dtype
     else:
         out = torch.empty((B, H, N, dv), dtype=out_dtype, device=q.device)
-    gn = groupnorm.as_struct() if groupnorm is not None else None
+    gn = groupnorm.as_struct(q.dtype, (B, H, N, dv)) if groupnorm is not None else None
     shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
     need = lib.retention_workspace_bytes(RET_FN_PARALLEL, ctypes.byref(shp), 0, int(gn is not None))
     if need == ctypes.c_size_t(-1).value:

@@ -26,7 +26,7 @@ def load(path: str = LIB):
     lib.oracle_recurrent.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_parallel.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_chunkwise.argtypes = [i, i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
-    lib.oracle_groupnorm.argtypes = [i, i, i, i, d, _DP, _DP, _DP, _DP]
+    lib.oracle_groupnorm.argtypes = [i, i, i, i, d, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_threads.restype = i
     lib.oracle_set_threads.argtypes = [i]
     for f in (lib.oracle_recurrent, lib.oracle_parallel, lib.oracle_chunkwise, lib.oracle_groupnorm):
@@ -98,12 +98,15 @@ class Oracle:
                                   _ptr(out), _ptr(st))
         return out, st
 
-    def groupnorm(self, x, eps, weight=None, bias=None):
-        """Per-head GroupNorm over the d_v channels of each (b, h, n) row. x: [B,H,N,dv]."""
-        x, w, b = map(_f64, (x, weight, bias))
+    def groupnorm(self, x, eps, weight=None, bias=None, gate=None):
+        """Per-head GroupNorm over the d_v channels of each (b, h, n) row, then (if gate, laid out
+        like x, is given) times swish(gate). x: [B,H,N,dv]."""
+        x, w, b, g = map(_f64, (x, weight, bias, gate))
         B, H, N, dv = x.shape
+        if g is not None and g.shape != x.shape:
+            raise ValueError(f"gate shape {g.shape} != {x.shape}")
         y = np.zeros_like(x)
-        self.lib.oracle_groupnorm(B, H, N, dv, float(eps), _ptr(w), _ptr(b), _ptr(x), _ptr(y))
+        self.lib.oracle_groupnorm(B, H, N, dv, float(eps), _ptr(w), _ptr(b), _ptr(g), _ptr(x), _ptr(y))
         return y
 
     def step(self, q, k, v, gamma, state):

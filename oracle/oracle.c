@@ -203,9 +203,13 @@ void oracle_chunkwise(int B, int H, int N, int dk, int dv, int C,
  *     mu = mean(x), var = mean((x - mu)^2)   (biased)
  *     y  = (x - mu) / sqrt(var + eps) * w[h][c] + b[h][c]
  * weight and bias are [H][dv]; NULL means 1 and 0.
+ * Then the swish gate (same abeam.tech section: a Swish gate adds
+ * non-linearity), read here as multiplying the normalised output by
+ * swish(g) = g * sigmoid(g) = g / (1 + exp(-g)) of a given gate tensor g
+ * laid out like x; NULL means no gate.
  */
 void oracle_groupnorm(int B, int H, int N, int dv, double eps,
-                      const double* weight, const double* bias,
+                      const double* weight, const double* bias, const double* gate,
                       const double* x, double* y) {
     const long rows = (long)B * H * N;
 #pragma omp parallel for schedule(static)
@@ -224,6 +228,10 @@ void oracle_groupnorm(int B, int H, int N, int dv, double eps,
             const double w = weight ? weight[(size_t)h * dv + c] : 1.0;
             const double b = bias ? bias[(size_t)h * dv + c] : 0.0;
             yr[c] = (xr[c] - mu) * inv * w + b;
+            if (gate) {
+                const double g = gate[(size_t)r * dv + c];
+                yr[c] *= g / (1.0 + exp(-g));
+            }
         }
     }
 }

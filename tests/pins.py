@@ -63,6 +63,9 @@ def pin_hand_worked(o):
     x = np.array(gn["x"], float)[None, None]
     y = o.groupnorm(x, gn["eps"], np.array(gn["weight"], float)[None], np.array(gn["bias"], float)[None])
     assert np.allclose(y[0, 0, 0], gn["y_row0"], rtol=0, atol=1e-15), ("groupnorm", y)
+    y = o.groupnorm(x, gn["eps"], np.array(gn["weight"], float)[None], np.array(gn["bias"], float)[None],
+                    np.array(gn["gate"], float)[None, None, None])
+    assert np.allclose(y[0, 0, 0], gn["y_gated_row0"], rtol=0, atol=1e-15), ("gated groupnorm", y)
 
 
 def pin_closed_form(o):
@@ -233,5 +236,27 @@ def pin_groupnorm(o):
     assert _rel(y1, y) < 1e-10, "groupnorm scale invariance"
 
 
+def pin_swish_gate(o):
+    """The gate multiplies the affine GroupNorm output by swish(g) = g * sigmoid(g), checked through
+    properties of the logistic function rather than its formula: swish(g) - swish(-g) = g (since
+    sigmoid(g) + sigmoid(-g) = 1), swish(0) = 0, swish(g) -> g for large g and -> 0 for very
+    negative g, and sigmoid(ln 3) = 3/4."""
+    B, H, N, dv = 2, 3, 4, 16
+    x = _rand((B, H, N, dv), 91) + 0.2
+    w = _rand((H, dv), 92) + 1.0
+    bias = _rand((H, dv), 93)
+    eps = 1e-5
+    y0 = o.groupnorm(x, eps, w, bias)
+    g = 4.0 * _rand((B, H, N, dv), 94)
+    diff = o.groupnorm(x, eps, w, bias, g) - o.groupnorm(x, eps, w, bias, -g)
+    assert _rel(diff, y0 * g) < 1e-12, "swish(g) - swish(-g) = g"
+    assert np.all(o.groupnorm(x, eps, w, bias, np.zeros_like(x)) == 0.0), "swish(0) = 0"
+    assert _rel(o.groupnorm(x, eps, w, bias, np.full_like(x, 40.0)), 40.0 * y0) < 1e-15, "swish(40) = 40"
+    assert np.abs(o.groupnorm(x, eps, w, bias, np.full_like(x, -40.0))).max() < 1e-13 * np.abs(y0).max(), "swish(-40) ~ 0"
+    # the gate applies after the affine, bias included: with g = ln 3 everywhere, y = (3/4) ln 3 * y0
+    ln3 = np.log(3.0)
+    assert _rel(o.groupnorm(x, eps, w, bias, np.full_like(x, ln3)), 0.75 * ln3 * y0) < 1e-14, "sigmoid(ln 3) = 3/4"
+
+
 PINS = [pin_hand_worked, pin_closed_form, pin_gamma_one, pin_tiny_gamma, pin_bruteforce, pin_three_forms,
-        pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm]
+        pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm, pin_swish_gate]

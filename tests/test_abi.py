@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.retention_abi_version() == 1
+    assert lib.retention_abi_version() == 2
     for s in range(5):
         assert lib.retention_status_string(s).decode().startswith("RET_")
     assert lib.retention_status_string(99).decode() == "unknown status"
@@ -108,6 +108,16 @@ def test_no_outputs(lib):
 def test_bad_eps(lib, eps):
     gn = R.RetGroupNorm(1, eps, None, None)
     assert chunk(lib, gn=ctypes.byref(gn)) == R.RET_ERR_INVALID_ARG
+
+
+def test_gate_validation(lib):
+    # a gate only follows an enabled GroupNorm, and must be 16-byte aligned
+    gn = R.RetGroupNorm(0, 1e-5, None, None, ctypes.c_void_p(1 << 36))
+    assert chunk(lib, gn=ctypes.byref(gn)) == R.RET_ERR_INVALID_ARG
+    assert "gate" in lib.retention_last_error().decode()
+    gn = R.RetGroupNorm(1, 1e-5, None, None, ctypes.c_void_p((1 << 36) + 8))
+    assert chunk(lib, gn=ctypes.byref(gn)) == R.RET_ERR_INVALID_ARG
+    assert "gate" in lib.retention_last_error().decode()
 
 
 def test_unsupported_chunk_and_dims(lib):

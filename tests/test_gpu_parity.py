@@ -150,9 +150,9 @@ def test_bf16_parallel_layer_shape_groupnorm(orc):
     report("chunkwise GN affine bf16 out", rel_err(o, ref_gn), TOL["bf16"])
 
 
-# GroupNorm fused into the chunk kernel (chunks up to 256; 512 takes the separate pass): every chunk
-# size, fp32 and bf16 out, ragged N, head counts that are not a multiple of 8 (the d_v slices of a
-# head then sit on different XCDs), and a grid of 512 workgroups (more than the GPU holds at once).
+# GroupNorm after the bf16 chunk kernels: every chunk size, fp32 and bf16 out, per-channel affine,
+# ragged N, B > 1, head counts that are not a multiple of 8 (the d_v slices of a head then sit on
+# different XCDs), and a grid of 512 workgroups (more than the GPU holds at once).
 @pytest.mark.parametrize("dk,dv,B,H,N", [(64, 64, 3, 5, 777), (256, 512, 1, 3, 1100), (256, 512, 2, 16, 600)])
 def test_bf16_chunkwise_groupnorm_shapes(orc, dk, dv, B, H, N):
     q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=300 + N)
@@ -167,6 +167,95 @@ def test_bf16_chunkwise_groupnorm_shapes(orc, dk, dv, B, H, N):
         for odt in (torch.float32, torch.bfloat16):
             o, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, groupnorm=gn, out_dtype=odt, want_state=False)
             report(f"GN B={B} H={H} N={N} dk={dk} C={C} {str(odt)[6:]} out", rel_err(o, ref_gn), TOL["bf16"])
+
+
+# The swish gate after GroupNorm, out = swish(g) * GN(o), through every kernel that applies
+# GroupNorm: the bf16 chunkwise pass (chunks 128 and 512), the bf16 parallel kernel, the fp32
+# chunkwise and parallel passes, and the decode step in both input dtypes. Gate inputs g ~ N(0, 1).
+# Bound: the gate multiplies each element, and so its error, by swish(g) (plus about 1e-6 relative
+# from the fp32 gate), so max|out - ref| <= max|swish(g)| * max|ungated out - ungated ref|. The
+# gated error is therefore measured against RMS(ungated ref) * max|swish(g)| and held to the inputs'
+# bound; max|gpu - ref| / RMS(ref) itself is not invariant under an elementwise gate. Each gated
+# output is also compared with the same kernel's ungated output times swish(g) in fp64, which
+# isolates the gate stage. fp32 out throughout; one bf16-out case is checked against the fp32 one.
+def _gate(shape, dtype, seed):
+    return torch.randn(*shape, generator=torch.Generator().manual_seed(seed)).to(dtype)
+
+
+def _swish64(g):
+    g = g.double().cpu()
+    return g / (1.0 + torch.exp(-g))
+
+
+def gated_err(gpu, ref_g, ref_gn, g):
+    r = np.asarray(ref_gn, dtype=np.float64)
+    return rel_err(gpu, ref_g) * np.sqrt(np.mean(np.asarray(ref_g) ** 2)) / (np.sqrt(np.mean(r * r)) * float(_swish64(g).abs().max()))
+
+
+def _gate_stage(name, gated, ungated, g, tol=1e-5):
+    report(f"{name}: gate stage", rel_err(gated, (ungated.double().cpu() * _swish64(g)).numpy()), tol)
+
+
+def test_swish_gate_all_paths(orc):
+    B, H, N, dk, dv = 2, 3, 300, 256, 512
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=401)
+    gam = I.multiscale_gammas(H)
+    g = _gate((B, H, N, dv), torch.bfloat16, 402)
+    gw = (1.0 + 0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(403))).float()
+    gb = (0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(404))).float()
+    ref, _ = orc.recurrent(q, k, v, gam)
+    ref_gn = orc.groupnorm(ref, 1e-5, gw, gb)
+    ref_g = orc.groupnorm(ref, 1e-5, gw, gb, g)
+    qd, kd, vd, gd = dev(q, k, v, g)
+    gn = R.GroupNorm(1e-5, gw.to(DEV), gb.to(DEV), gd)
+    gn0 = R.GroupNorm(1e-5, gw.to(DEV), gb.to(DEV))
+    for C in (128, 512):
+        o, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, groupnorm=gn, want_state=False)
+        report(f"gated chunkwise bf16 C={C}", gated_err(o, ref_g, ref_gn, g), TOL["bf16"])
+        _gate_stage(f"chunkwise bf16 C={C}", o, R.chunkwise_fwd(qd, kd, vd, gam, C, groupnorm=gn0, want_state=False)[0], g)
+    o = R.parallel_fwd(qd, kd, vd, gam, groupnorm=gn)
+    report("gated parallel bf16", gated_err(o, ref_g, ref_gn, g), TOL["bf16"])
+    _gate_stage("parallel bf16", o, R.parallel_fwd(qd, kd, vd, gam, groupnorm=gn0), g)
+    # bf16 out is the fp32 result rounded to nearest (8 significand bits): within 2^-8 of it,
+    # relative, element by element
+    o32, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=gn, want_state=False)
+    ob, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=gn, out_dtype=torch.bfloat16, want_state=False)
+    o32, ob = o32.double().cpu(), ob.double().cpu()
+    report("gated chunkwise bf16 out vs fp32 out rounded", float(((ob - o32).abs() / o32.abs().clamp_min(1e-30)).max()), 2.0 ** -8)
+
+    # fp32 inputs
+    B, H, N, dk, dv = 1, 2, 200, 64, 128
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "f32", seed=405)
+    gam = I.multiscale_gammas(H)
+    g = _gate((B, H, N, dv), torch.float32, 406)
+    ref, _ = orc.recurrent(q, k, v, gam)
+    ref_gn = orc.groupnorm(ref, 1e-5)
+    ref_g = orc.groupnorm(ref, 1e-5, None, None, g)
+    qd, kd, vd, gd = dev(q, k, v, g)
+    gn = R.GroupNorm(1e-5, gate=gd)
+    o, _ = R.chunkwise_fwd(qd, kd, vd, gam, 64, groupnorm=gn, want_state=False)
+    report("gated chunkwise fp32", gated_err(o, ref_g, ref_gn, g), TOL["f32"])
+    _gate_stage("chunkwise fp32", o, R.chunkwise_fwd(qd, kd, vd, gam, 64, groupnorm=R.GroupNorm(1e-5), want_state=False)[0], g)
+    o = R.parallel_fwd(qd, kd, vd, gam, groupnorm=gn)
+    report("gated parallel fp32", gated_err(o, ref_g, ref_gn, g), TOL["f32"])
+    _gate_stage("parallel fp32", o, R.parallel_fwd(qd, kd, vd, gam, groupnorm=R.GroupNorm(1e-5)), g)
+
+    # decode step, bf16 and fp32 inputs
+    for dt, tol in (("bf16", TOL["bf16"]), ("f32", TOL["f32"])):
+        B, H, dk, dv = 4, 3, 256, 512
+        q, k, v = I.make_qkv(B, H, 1, dk, dv, dt, seed=407)
+        q, k, v = q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous()
+        s0 = I.make_state(B, H, dk, dv, seed=408, scale=0.02)
+        gam = I.multiscale_gammas(H)
+        g = _gate((B, H, dv), q.dtype, 409)
+        ro, _ = orc.step(q, k, v, gam, s0)
+        ref_gn = orc.groupnorm(ro[:, :, None, :], 1e-5)[:, :, 0]
+        ref_g = orc.groupnorm(ro[:, :, None, :], 1e-5, None, None, g[:, :, None, :])[:, :, 0]
+        qd, kd, vd, gd, st = dev(q, k, v, g, s0.clone())
+        o = R.recurrent_step(qd, kd, vd, gam, st, groupnorm=R.GroupNorm(1e-5, gate=gd))
+        report(f"gated decode {dt}", gated_err(o, ref_g, ref_gn, g), tol)
+        st0 = dev(s0.clone())[0]
+        _gate_stage(f"decode {dt}", o, R.recurrent_step(qd, kd, vd, gam, st0, groupnorm=R.GroupNorm(1e-5)), g)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -36,6 +36,11 @@ MUTANTS = [
     ("groupnorm_eps_outside_sqrt", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
     ("groupnorm_wrong_head_index", "const int h = (int)((r / N) % H);", "const int h = (int)(r % H);"),
     ("groupnorm_bias_not_added", "yr[c] = (xr[c] - mu) * inv * w + b;", "yr[c] = (xr[c] - mu) * inv * w;"),
+    ("gate_sigmoid_not_swish", "yr[c] *= g / (1.0 + exp(-g));", "yr[c] *= 1.0 / (1.0 + exp(-g));"),
+    ("gate_sigmoid_sign", "yr[c] *= g / (1.0 + exp(-g));", "yr[c] *= g / (1.0 + exp(g));"),
+    ("gate_wrong_index", "const double g = gate[(size_t)r * dv + c];", "const double g = gate[c];"),
+    ("gate_before_bias", "yr[c] = (xr[c] - mu) * inv * w + b;\n            if (gate) {\n                const double g = gate[(size_t)r * dv + c];\n                yr[c] *= g / (1.0 + exp(-g));",
+     "yr[c] = (xr[c] - mu) * inv * w;\n            if (gate) {\n                const double g = gate[(size_t)r * dv + c];\n                yr[c] *= g / (1.0 + exp(-g));\n            }\n            yr[c] += b;\n            {"),
 ]
 
 
