@@ -27,6 +27,8 @@ def load(path: str = LIB):
     lib.oracle_parallel.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_chunkwise.argtypes = [i, i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_groupnorm.argtypes = [i, i, i, i, d, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_recurrent_bwd.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_recurrent_bwd.restype = None
     lib.oracle_threads.restype = i
     lib.oracle_set_threads.argtypes = [i]
     for f in (lib.oracle_recurrent, lib.oracle_parallel, lib.oracle_chunkwise, lib.oracle_groupnorm):
@@ -108,6 +110,17 @@ class Oracle:
         y = np.zeros_like(x)
         self.lib.oracle_groupnorm(B, H, N, dv, float(eps), _ptr(w), _ptr(b), _ptr(g), _ptr(x), _ptr(y))
         return y
+
+    def recurrent_bwd(self, q, k, v, gamma, dout, state_in=None):
+        """Gradients of the recurrent form for dL/dout = dout: (dq, dk, dv, dstate_in), fp64.
+        q, k: [B,H,N,dk]; v, dout: [B,H,N,dv]; state_in: [B,H,dk,dv] or None."""
+        q, k, v, dout, g, s0 = map(_f64, (q, k, v, dout, gamma, state_in))
+        B, H, N, dk, dv = self._dims(q, v)
+        dq, dkk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        ds = np.zeros((B, H, dk, dv))
+        self.lib.oracle_recurrent_bwd(B, H, N, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(dout),
+                                      _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(ds))
+        return dq, dkk, dvv, ds
 
     def step(self, q, k, v, gamma, state):
         """One recurrent decode step. q, k: [B,H,dk]; v: [B,H,dv]; state: [B,H,dk,dv].

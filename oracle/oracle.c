@@ -103,6 +103,68 @@ void oracle_recurrent(int B, int H, int N, int dk, int dv,
 }
 
 /*
+ * Gradients of the recurrent form (the backward pass of training, which is what
+ * the pages measure: abeam.tech summary, "Training in parallel, generation by
+ * state update"). For a loss L with dL/do_n = dout_n, differentiating
+ *     S_n = gamma S_{n-1} + k_n^T v_n,   o_n = q_n S_n   (S_-1 = state_in or 0)
+ * with the reverse-time state
+ *     U_n = gamma U_{n+1} + q_n^T dout_n,   U_N = 0      (d_k x d_v)
+ * gives, for every (b, h),
+ *     dq_n = dout_n S_n^T,   dk_n = U_n v_n^T,   dv_n = k_n U_n,
+ *     dstate_in = gamma U_0.
+ * dq, dk, dv (laid out like q, k, v) and dstate_in ([B][H][dk][dv]) may be NULL.
+ */
+void oracle_recurrent_bwd(int B, int H, int N, int dk, int dv,
+                          const double* q, const double* k, const double* v,
+                          const double* gamma, const double* state_in, const double* dout,
+                          double* dq, double* dkk, double* dvv, double* dstate_in) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < (long)B * H; ++bh) {
+        const double g = gamma[bh % H];
+        double* S = (double*)malloc((size_t)dk * dv * sizeof(double));
+        for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] = state_in ? state_in[(size_t)bh * dk * dv + e] : 0.0;
+        for (int n = 0; n < N; ++n) {
+            const double* kn = k + ((size_t)bh * N + n) * dk;
+            const double* vn = v + ((size_t)bh * N + n) * dv;
+            const double* gn = dout + ((size_t)bh * N + n) * dv;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = g * S[(size_t)i * dv + j] + kn[i] * vn[j];
+            if (dq)
+                for (int i = 0; i < dk; ++i) {
+                    double a = 0.0;
+                    for (int j = 0; j < dv; ++j) a += gn[j] * S[(size_t)i * dv + j];
+                    dq[((size_t)bh * N + n) * dk + i] = a;
+                }
+        }
+        double* U = S;  /* reused: the forward state is no longer needed */
+        for (size_t e = 0; e < (size_t)dk * dv; ++e) U[e] = 0.0;
+        for (int n = N - 1; n >= 0; --n) {
+            const double* qn = q + ((size_t)bh * N + n) * dk;
+            const double* kn = k + ((size_t)bh * N + n) * dk;
+            const double* vn = v + ((size_t)bh * N + n) * dv;
+            const double* gn = dout + ((size_t)bh * N + n) * dv;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) U[(size_t)i * dv + j] = g * U[(size_t)i * dv + j] + qn[i] * gn[j];
+            if (dkk)
+                for (int i = 0; i < dk; ++i) {
+                    double a = 0.0;
+                    for (int j = 0; j < dv; ++j) a += U[(size_t)i * dv + j] * vn[j];
+                    dkk[((size_t)bh * N + n) * dk + i] = a;
+                }
+            if (dvv)
+                for (int j = 0; j < dv; ++j) {
+                    double a = 0.0;
+                    for (int i = 0; i < dk; ++i) a += kn[i] * U[(size_t)i * dv + j];
+                    dvv[((size_t)bh * N + n) * dv + j] = a;
+                }
+        }
+        if (dstate_in)
+            for (size_t e = 0; e < (size_t)dk * dv; ++e) dstate_in[(size_t)bh * dk * dv + e] = g * U[e];
+        free(S);
+    }
+}
+
+/*
  * Parallel form (abeam.tech summary, "Retention multiplies content-based
  * reference and distance-based forgetting" and "Training in parallel"):
  *     o_n = sum_{m <= n} gamma^(n-m) (q_n . k_m) v_m

@@ -258,5 +258,78 @@ def pin_swish_gate(o):
     assert _rel(o.groupnorm(x, eps, w, bias, np.full_like(x, ln3)), 0.75 * ln3 * y0) < 1e-14, "sigmoid(ln 3) = 3/4"
 
 
+def _ip(a, b):
+    return float(np.sum(np.asarray(a) * np.asarray(b)))
+
+
+def pin_backward_adjoint(o):
+    """The output is linear in q (k, v and the state fixed), in k and in v (zero state), and in the
+    state (q, k fixed, v = 0). For a linear map A with gradient A^T dout the adjoint identity
+    <dout, A(d)> = <A^T dout, d> holds for every direction d, so each gradient is fixed by the
+    pinned forward oracle alone."""
+    B, H, N, dk, dv = 2, 2, 37, 5, 4
+    q, k, v = _qkv(B, H, N, dk, dv, 101)
+    s0 = _rand((B, H, dk, dv), 102)
+    dout = _rand((B, H, N, dv), 103)
+    gam = [0.9, 0.5]
+    dq, dk_, dv_, ds = o.recurrent_bwd(q, k, v, gam, dout, state_in=s0)
+    dq0, dk0, dv0, _ = o.recurrent_bwd(q, k, v, gam, dout)
+    d = [_rand(x.shape, 104 + i) for i, x in enumerate((q, k, v, s0))]
+    fwd = lambda qq, kk, vv, ss=None: o.recurrent(qq, kk, vv, gam, state_in=ss)[0]
+    checks = [("dq", _ip(dout, fwd(d[0], k, v, s0)), _ip(dq, d[0])),
+              ("dk", _ip(dout, fwd(q, d[1], v)), _ip(dk0, d[1])),
+              ("dv", _ip(dout, fwd(q, k, d[2])), _ip(dv0, d[2])),
+              ("dstate_in", _ip(dout, fwd(q, k, 0 * v, d[3])), _ip(ds, d[3]))]
+    for name, lhs, rhs in checks:
+        assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1.0), (name, lhs, rhs)
+    # dk and dv do not depend on the state
+    assert _rel(dk_, dk0) < 1e-14 and _rel(dv_, dv0) < 1e-14, "state-independent dk, dv"
+
+
+def pin_backward_fd(o):
+    """Central finite differences of L = <dout, out> in fp64 against single gradient entries."""
+    B, H, N, dk, dv = 1, 2, 9, 3, 2
+    q, k, v = _qkv(B, H, N, dk, dv, 111)
+    s0 = _rand((B, H, dk, dv), 112)
+    dout = _rand((B, H, N, dv), 113)
+    gam = [0.8, 0.99]
+    grads = o.recurrent_bwd(q, k, v, gam, dout, state_in=s0)
+    args = [q, k, v, s0]
+    L = lambda a: _ip(dout, o.recurrent(a[0], a[1], a[2], gam, state_in=a[3])[0])
+    rng = np.random.default_rng(114)
+    h = 1e-4
+    for t in range(4):
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, s)) for s in args[t].shape)
+            ap, am = [x.copy() for x in args], [x.copy() for x in args]
+            ap[t][idx] += h
+            am[t][idx] -= h
+            fd = (L(ap) - L(am)) / (2 * h)
+            assert abs(fd - grads[t][idx]) <= 1e-8 * max(abs(fd), 1.0), ("finite difference", t, idx, fd, grads[t][idx])
+
+
+def pin_backward_bruteforce(o):
+    """The parallel form's derivatives as Python double sums, for a small case:
+    dq_n = sum_{m<=n} g^(n-m) (dout_n . v_m) k_m, dk_m = sum_{n>=m} g^(n-m) (dout_n . v_m) q_n,
+    dv_m = sum_{n>=m} g^(n-m) (q_n . k_m) dout_n, plus dq_n += g^(n+1) dout_n S_in^T."""
+    B, H, N, dk, dv = 1, 1, 11, 3, 2
+    q, k, v = _qkv(B, H, N, dk, dv, 121)
+    s0 = _rand((B, H, dk, dv), 122)
+    dout = _rand((B, H, N, dv), 123)
+    g = 0.7
+    dq, dk_, dv_, ds = o.recurrent_bwd(q, k, v, [g], dout, state_in=s0)
+    Q, K, V, G, S = q[0, 0], k[0, 0], v[0, 0], dout[0, 0], s0[0, 0]
+    for n in range(N):
+        want_q = sum(g ** (n - m) * (G[n] @ V[m]) * K[m] for m in range(n + 1)) + g ** (n + 1) * (S @ G[n])
+        want_k = sum(g ** (m - n) * (G[m] @ V[n]) * Q[m] for m in range(n, N))
+        want_v = sum(g ** (m - n) * (Q[m] @ K[n]) * G[m] for m in range(n, N))
+        assert np.allclose(dq[0, 0, n], want_q, rtol=1e-12, atol=1e-12), ("dq", n)
+        assert np.allclose(dk_[0, 0, n], want_k, rtol=1e-12, atol=1e-12), ("dk", n)
+        assert np.allclose(dv_[0, 0, n], want_v, rtol=1e-12, atol=1e-12), ("dv", n)
+    want_s = sum(g ** (n + 1) * np.outer(Q[n], G[n]) for n in range(N))
+    assert np.allclose(ds[0, 0], want_s, rtol=1e-12, atol=1e-12), "dstate_in"
+
+
 PINS = [pin_hand_worked, pin_closed_form, pin_gamma_one, pin_tiny_gamma, pin_bruteforce, pin_three_forms,
-        pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm, pin_swish_gate]
+        pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm, pin_swish_gate,
+        pin_backward_adjoint, pin_backward_fd, pin_backward_bruteforce]

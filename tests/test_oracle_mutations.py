@@ -36,6 +36,12 @@ MUTANTS = [
     ("groupnorm_eps_outside_sqrt", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
     ("groupnorm_wrong_head_index", "const int h = (int)((r / N) % H);", "const int h = (int)(r % H);"),
     ("groupnorm_bias_not_added", "yr[c] = (xr[c] - mu) * inv * w + b;", "yr[c] = (xr[c] - mu) * inv * w;"),
+    ("bwd_dual_no_decay", "U[(size_t)i * dv + j] = g * U[(size_t)i * dv + j] + qn[i] * gn[j];",
+     "U[(size_t)i * dv + j] = U[(size_t)i * dv + j] + qn[i] * gn[j];"),
+    ("bwd_dstate_no_gamma", "dstate_in[(size_t)bh * dk * dv + e] = g * U[e];", "dstate_in[(size_t)bh * dk * dv + e] = U[e];"),
+    ("bwd_dk_uses_dout", "a += U[(size_t)i * dv + j] * vn[j];", "a += U[(size_t)i * dv + j] * gn[j];"),
+    ("bwd_dv_uses_q", "a += kn[i] * U[(size_t)i * dv + j];", "a += qn[i] * U[(size_t)i * dv + j];"),
+    ("bwd_dq_ignores_state_in", "S[e] = state_in ? state_in[(size_t)bh * dk * dv + e] : 0.0;", "S[e] = 0.0;"),
     ("gate_sigmoid_not_swish", "yr[c] *= g / (1.0 + exp(-g));", "yr[c] *= 1.0 / (1.0 + exp(-g));"),
     ("gate_sigmoid_sign", "yr[c] *= g / (1.0 + exp(-g));", "yr[c] *= g / (1.0 + exp(g));"),
     ("gate_wrong_index", "const double g = gate[(size_t)r * dv + c];", "const double g = gate[c];"),
