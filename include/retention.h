@@ -56,7 +56,7 @@ typedef enum {
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
 
-typedef enum { RET_FN_CHUNKWISE = 0, RET_FN_RECURRENT_STEP = 1, RET_FN_PARALLEL = 2 } ret_fn;
+typedef enum { RET_FN_CHUNKWISE = 0, RET_FN_RECURRENT_STEP = 1, RET_FN_PARALLEL = 2, RET_FN_CHUNKWISE_BWD = 3 } ret_fn;
 
 /* Problem shape. in_dtype applies to q, k and v; out_dtype to out. */
 typedef struct {
@@ -127,6 +127,26 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
                                   const void* q, const void* k, const void* v,
                                   const double* gamma, const ret_groupnorm* groupnorm, void* out,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Backward of the chunkwise form: the gradients of a loss L for dL/dout = dout (abeam.tech
+ * summary, "Training in parallel, generation by state update": differentiating
+ * S_n = gamma S_(n-1) + k_n^T v_n, o_n = q_n S_n with the reverse-time state
+ * U_n = gamma U_(n+1) + q_n^T dout_n gives dq_n = dout_n S_n^T, dk_n = U_n v_n^T, dv_n = k_n U_n
+ * and dstate_in = gamma U_0). The pre-norm output: no GroupNorm or gate.
+ * q, k: [B][H][N][d_k]; v, dout: [B][H][N][d_v], in shape->in_dtype; state_in: fp32
+ * [B][H][d_k][d_v] or NULL (zero). Outputs, each fp32 and each optional: dq, dk like q; dv like v;
+ * dstate_in like state_in. shape->out_dtype must be RET_F32. Outputs must not alias inputs or each
+ * other. chunk and (d_k, d_v) as for retention_chunkwise_fwd; a d_v with no forward kernel of
+ * contraction width d_v runs as two column blocks of d_v / 2.
+ * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): time-reversed copies of q, k,
+ * v and dout, one fp32 output buffer and the workspace of the forward calls.
+ */
+ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
+                                   const void* q, const void* k, const void* v,
+                                   const double* gamma, const float* state_in, const void* dout,
+                                   float* dq, float* dk, float* dv, float* dstate_in,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Bytes of device workspace the call `fn` needs for this shape, chunk and GroupNorm setting.
  * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid.

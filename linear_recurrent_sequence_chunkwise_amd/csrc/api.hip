@@ -162,6 +162,10 @@ size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chu
             return chunkwise_ws(shape, chunk, gn_enabled != 0, 1);
         case RET_FN_RECURRENT_STEP: return 0;
         case RET_FN_PARALLEL: return parallel_ws(shape, gn_enabled != 0);
+        case RET_FN_CHUNKWISE_BWD:
+            if (chunk <= 0) return (size_t)-1;
+            return ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len, shape->d_k,
+                                                shape->d_v, chunk);
         default: return (size_t)-1;
     }
 }
@@ -210,6 +214,52 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
     a.q = q; a.k = k; a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
     hipError_t e = bf ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a);
     return device_status(e, "retention_chunkwise_fwd launch");
+}
+
+ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const void* q, const void* k, const void* v,
+                                   const double* gamma, const float* state_in, const void* dout, float* dq, float* dk, float* dv,
+                                   float* dstate_in, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    g_err[0] = '\0';
+    RET_TRY(check_shape(shape, false));
+    RET_TRY(check_ptr(q, "q", true));
+    RET_TRY(check_ptr(k, "k", true));
+    RET_TRY(check_ptr(v, "v", true));
+    RET_TRY(check_ptr(dout, "dout", true));
+    RET_TRY(check_ptr(state_in, "state_in", false));
+    RET_TRY(check_ptr(dq, "dq", false));
+    RET_TRY(check_ptr(dk, "dk", false));
+    RET_TRY(check_ptr(dv, "dv", false));
+    RET_TRY(check_ptr(dstate_in, "dstate_in", false));
+    if (!dq && !dk && !dv && !dstate_in) return fail(RET_ERR_INVALID_ARG, "dq, dk, dv and dstate_in are all NULL");
+    if (shape->out_dtype != RET_F32) return fail(RET_ERR_UNSUPPORTED, "the gradients are fp32 (out_dtype must be RET_F32)");
+    ret::HeadConsts hc;
+    RET_TRY(check_gamma(shape, gamma, &hc));
+    if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+    const bool bf = shape->in_dtype == RET_BF16;
+    if (!ret::bwd_split(bf, shape->d_k, shape->d_v, chunk))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise backward: no kernels for %s inputs with d_k %d, d_v %d, chunk %d", bf ? "bf16" : "fp32",
+                    shape->d_k, shape->d_v, chunk);
+    const size_t rows = (size_t)shape->batch * shape->heads * shape->seq_len;
+    const size_t in_sz = elem_size(shape->in_dtype);
+    const size_t st_bytes = (size_t)shape->batch * shape->heads * shape->d_k * shape->d_v * sizeof(float);
+    const void* ins[5] = {q, k, v, dout, state_in};
+    const size_t in_b[5] = {rows * shape->d_k * in_sz, rows * shape->d_k * in_sz, rows * shape->d_v * in_sz, rows * shape->d_v * in_sz,
+                            st_bytes};
+    const void* outs[4] = {dq, dk, dv, dstate_in};
+    const size_t out_b[4] = {rows * shape->d_k * 4, rows * shape->d_k * 4, rows * shape->d_v * 4, st_bytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], out_b[i], ins[j], in_b[j])) return fail(RET_ERR_INVALID_ARG, "gradient outputs must not alias the inputs");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_b[i], outs[j], out_b[j])) return fail(RET_ERR_INVALID_ARG, "gradient outputs must not alias each other");
+    }
+    const size_t need = ret::chunkwise_bwd_workspace(bf, shape->batch, shape->heads, shape->seq_len, shape->d_k, shape->d_v, chunk);
+    RET_TRY(check_ws(need, workspace, workspace_bytes));
+    ret::BwdArgs b{};
+    b.base = base_args(shape, chunk, hc, ret::GnArgs{}, workspace, workspace_bytes, hip_stream);
+    b.q = q; b.k = k; b.v = v; b.dout = dout; b.state_in = state_in;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dstate_in = dstate_in;
+    return device_status(ret::launch_chunkwise_bwd(b), "retention_chunkwise_bwd launch");
 }
 
 ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const void* k, const void* v, const double* gamma,

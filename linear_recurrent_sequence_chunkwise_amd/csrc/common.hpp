@@ -167,6 +167,22 @@ __device__ __forceinline__ float sum16(float x) {
 
 }  // namespace ret
 
+// Backward of the chunkwise form: gradients for dL/dout = dout, in fp32.
+namespace ret {
+struct BwdArgs {
+    LaunchArgs base;  // shape, input dtype, chunk, decay constants, workspace, stream
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;       // laid out like v, input dtype
+    const float* state_in;  // may be null
+    float* dq;              // each may be null
+    float* dk;
+    float* dv;
+    float* dstate_in;
+};
+}  // namespace ret
+
 // Launchers (one per kernel family), called by the C-ABI layer after validation.
 namespace ret {
 hipError_t launch_recurrent_step(const LaunchArgs& a);
@@ -181,4 +197,7 @@ bool chunkwise_bf16_supported(int DK, int DV, int chunk);
 bool chunkwise_f32_supported(int DK, int DV, int chunk);
 bool parallel_bf16_supported(int DK, int DV);
 bool parallel_f32_supported(int DK, int DV);
+int bwd_split(int in_bf16, int DK, int DV, int chunk);  // 0: unsupported
+size_t chunkwise_bwd_workspace(int in_bf16, int B, int H, int N, int DK, int DV, int chunk);
+hipError_t launch_chunkwise_bwd(const BwdArgs& b);
 }  // namespace ret

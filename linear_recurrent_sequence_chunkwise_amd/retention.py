@@ -16,10 +16,11 @@ LIB_PATH = os.path.join(_PKG, "libretention.so")
 
 RET_OK, RET_ERR_INVALID_ARG, RET_ERR_UNSUPPORTED, RET_ERR_WORKSPACE, RET_ERR_DEVICE = range(5)
 RET_F32, RET_BF16 = 0, 1
-RET_FN_CHUNKWISE, RET_FN_RECURRENT_STEP, RET_FN_PARALLEL = 0, 1, 2
+RET_FN_CHUNKWISE, RET_FN_RECURRENT_STEP, RET_FN_PARALLEL, RET_FN_CHUNKWISE_BWD = 0, 1, 2, 3
 
 EXPORTED = [
-    "retention_chunkwise_fwd", "retention_recurrent_step", "retention_parallel_fwd", "retention_workspace_bytes",
+    "retention_chunkwise_fwd", "retention_recurrent_step", "retention_parallel_fwd", "retention_chunkwise_bwd",
+    "retention_workspace_bytes",
     "retention_status_string", "retention_last_error", "retention_abi_version",
 ]
 
@@ -58,7 +59,8 @@ def load_library(path: str = LIB_PATH):
     lib.retention_chunkwise_fwd.argtypes = [sp, i32, vp, vp, vp, dp, vp, gp, vp, vp, vp, sz, vp]
     lib.retention_recurrent_step.argtypes = [sp, vp, vp, vp, dp, vp, gp, vp, vp, sz, vp]
     lib.retention_parallel_fwd.argtypes = [sp, vp, vp, vp, dp, gp, vp, vp, sz, vp]
-    for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd):
+    lib.retention_chunkwise_bwd.argtypes = [sp, i32, vp, vp, vp, dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd, lib.retention_chunkwise_bwd):
         f.restype = ctypes.c_int
     lib.retention_workspace_bytes.argtypes = [i32, sp, i32, i32]
     lib.retention_workspace_bytes.restype = sz
@@ -246,3 +248,30 @@ def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNo
                                     _stream(q.device, stream))
     _check(st)
     return out
+
+
+def chunkwise_bwd(q, k, v, gamma: Sequence[float], dout, chunk: int, *, state_in=None, want=("dq", "dk", "dv", "dstate_in"),
+                  workspace=None, stream=None):
+    """Gradients of chunkwise retention for dL/dout = dout (the pre-norm output): fp32 dq, dk, dv
+    (shaped like q, k, v) and dstate_in ([B,H,dk,dv]); the names not in `want` come back None.
+    dout is laid out like v, in the input dtype."""
+    lib = load_library()
+    _check_inputs(q, k, v, 4)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if not (dout.is_cuda and dout.is_contiguous() and dout.dtype == q.dtype and tuple(dout.shape) == tuple(v.shape)):
+        raise ValueError("dout must be a contiguous device tensor shaped and typed like v")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, H, N, dk), **f32) if "dq" in want else None
+    dk_ = torch.empty((B, H, N, dk), **f32) if "dk" in want else None
+    dv_ = torch.empty((B, H, N, dv), **f32) if "dv" in want else None
+    ds = torch.empty((B, H, dk, dv), **f32) if "dstate_in" in want else None
+    shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), RET_F32)
+    need = lib.retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ctypes.byref(shp), int(chunk), 0)
+    if need == ctypes.c_size_t(-1).value:
+        need = 0
+    ws, wsb = _workspace(need, q.device, workspace)
+    st = lib.retention_chunkwise_bwd(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _ptr(state_in),
+                                     _ptr(dout), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(ds), _ptr(ws), wsb, _stream(q.device, stream))
+    _check(st)
+    return dq, dk_, dv_, ds

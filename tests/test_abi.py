@@ -180,3 +180,32 @@ def test_error_is_thread_local(lib):
     t.join()
     assert seen["msg"] == ""
     assert "chunk" in lib.retention_last_error().decode()
+
+
+def bwd(lib, shp=None, C=64, q=Q, k=K, v=V, dout=GW, sin=None, dq=OUT, dk=ST, dv=WS, ds=None, ws=ctypes.c_void_p(9 << 36),
+        wsb=1 << 40):
+    shp = shp if shp is not None else shape()
+    return lib.retention_chunkwise_bwd(ctypes.byref(shp), C, q, k, v, gam([0.9] * shp.heads), sin, dout, dq, dk, dv, ds, ws, wsb,
+                                       None)
+
+
+def test_backward_validation(lib):
+    # every check below fails on the host before any HIP call
+    assert bwd(lib, dout=None) == R.RET_ERR_INVALID_ARG
+    assert "dout" in lib.retention_last_error().decode()
+    assert bwd(lib, dq=None, dk=None, dv=None, ds=None) == R.RET_ERR_INVALID_ARG
+    assert bwd(lib, shape(o=R.RET_BF16)) == R.RET_ERR_UNSUPPORTED
+    assert bwd(lib, C=96) == R.RET_ERR_UNSUPPORTED
+    assert bwd(lib, shape(dk=48)) == R.RET_ERR_UNSUPPORTED
+    assert bwd(lib, dq=Q) == R.RET_ERR_INVALID_ARG  # aliases q
+    assert "alias" in lib.retention_last_error().decode()
+    assert bwd(lib, dk=OUT) == R.RET_ERR_INVALID_ARG  # aliases dq
+    assert bwd(lib, dq=ctypes.c_void_p((1 << 36) * 3 + 8)) == R.RET_ERR_INVALID_ARG  # misaligned
+    assert bwd(lib, ws=None, wsb=0) == R.RET_ERR_WORKSPACE
+    need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(shape()), 64, 0)
+    assert bwd(lib, wsb=need - 1) == R.RET_ERR_WORKSPACE
+    # the workspace holds time-reversed copies of q, k, v and dout and one fp32 output buffer
+    s = shape()
+    rows = s.batch * s.heads * s.seq_len
+    assert need >= rows * (2 * s.d_k + 2 * s.d_v) * 2 + rows * max(s.d_k, s.d_v) * 4
+    assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s), 0, 0) == ctypes.c_size_t(-1).value

@@ -368,3 +368,58 @@ def test_long_context_chunk_sweep(orc):
             report(f"C={C} vs C={w.chunks[0]} every head (sampled rows)", rel_err(o[:, :, ::64], first[0]), TOL["bf16"])
             report(f"C={C} vs C={w.chunks[0]} state every head", rel_err(s, first[1]), TOL["bf16"])
         del o, s
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward: dq, dk, dv and dstate_in of the chunkwise call against the oracle's gradients of the
+# recurrent form, for dL/dout = dout ~ N(0, 1) in the input dtype, with a state_in. (256, 512) runs
+# the dq and dk forwards as two column blocks of d_v.
+def _dout(shape, dtype, seed):
+    return torch.randn(*shape, generator=torch.Generator().manual_seed(seed)).to(dtype)
+
+
+@pytest.mark.parametrize("dt,B,H,N,dk,dv,C", [
+    ("f32", 1, 2, 256, 64, 64, 64), ("f32", 2, 3, 250, 64, 128, 128), ("bf16", 4, 8, 2048, 64, 64, 128),
+    ("bf16", 1, 4, 1000, 256, 512, 128), ("bf16", 1, 3, 700, 256, 512, 256), ("bf16", 1, 2, 1100, 256, 512, 512),
+    ("bf16", 1, 2, 37, 256, 512, 64)])
+def test_chunkwise_backward(orc, dt, B, H, N, dk, dv, C):
+    q, k, v = I.make_qkv(B, H, N, dk, dv, dt, seed=500 + N)
+    dout = _dout((B, H, N, dv), q.dtype, 501 + N)
+    s0 = I.make_state(B, H, dk, dv, seed=502, scale=0.02)
+    gam = [0.9, 0.99] if H == 2 and dt == "f32" else I.multiscale_gammas(H)
+    ref = orc.recurrent_bwd(q, k, v, gam, dout, state_in=s0)
+    qd, kd, vd, dod, s0d = dev(q, k, v, dout, s0)
+    got = R.chunkwise_bwd(qd, kd, vd, gam, dod, C, state_in=s0d)
+    for name, g_, r_ in zip(("dq", "dk", "dv", "dstate_in"), got, ref):
+        report(f"backward {dt} ({dk},{dv}) N={N} C={C} {name}", rel_err(g_, r_), TOL[dt])
+    # without a state: only dq changes, and dstate_in is the same
+    got0 = R.chunkwise_bwd(qd, kd, vd, gam, dod, C, want=("dq", "dstate_in"))
+    ref0 = orc.recurrent_bwd(q, k, v, gam, dout)
+    report(f"backward {dt} N={N} C={C} dq, zero state", rel_err(got0[0], ref0[0]), TOL[dt])
+    assert got0[1] is None and got0[2] is None
+
+
+# The N=8192 layer (B=1, H=16, d_k=256, d_v=512, chunk 128): the oracle on heads 0 and 15, and on
+# every head the adjoint identities <dout, forward(dq-direction)> = <dq, direction> (the output is
+# linear in q, in k and in v), through the GPU forward.
+def test_backward_layer_6p7b(orc):
+    w = I.WORKLOADS["retention_b1_h16_n8192_dk256_dv512_bf16_gn"]
+    q, k, v = I.make_workload_qkv(w)
+    gam = w.gamma_list()
+    dout = _dout(tuple(v.shape), torch.bfloat16, 503)
+    qd, kd, vd, dod = dev(q, k, v, dout)
+    dq, dk, dv, ds = R.chunkwise_bwd(qd, kd, vd, gam, dod, 128)
+    torch.cuda.synchronize()
+    hs = [0, 15]
+    ref = orc.recurrent_bwd(q[:, hs], k[:, hs], v[:, hs], [gam[h] for h in hs], dout[:, hs])
+    for name, g_, r_ in zip(("dq", "dk", "dv", "dstate_in"), (dq, dk, dv, ds), ref):
+        report(f"layer backward {name}, heads 0 and 15", rel_err(g_[:, hs], r_), TOL["bf16"])
+    dirs = [_dout(tuple(t.shape), torch.bfloat16, 504 + i) for i, t in enumerate((q, k, v))]
+    dq_, dk_, dv_ = dev(*dirs)
+    pairs = [("dq", R.chunkwise_fwd(dq_, kd, vd, gam, 128, want_state=False)[0], dq, dq_),
+             ("dk", R.chunkwise_fwd(qd, dk_, vd, gam, 128, want_state=False)[0], dk, dk_),
+             ("dv", R.chunkwise_fwd(qd, kd, dv_, gam, 128, want_state=False)[0], dv, dv_)]
+    for name, fo, grad, d in pairs:
+        lhs = float((dod.double() * fo.double()).sum())
+        rhs = float((grad.double() * d.double()).sum())
+        report(f"layer backward adjoint identity {name}", abs(lhs - rhs) / abs(lhs), TOL["bf16"])
