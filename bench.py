@@ -12,6 +12,13 @@ each step is bracketed with HIP events recorded on the stream the library launch
 Counting rules:
   chunkwise algorithmic FLOPs per (b, h): 2 (d_k + d_v) * causal pairs inside chunks + 4 N d_k d_v
   decode algorithmic bytes: fp32 state read + write, bf16 q, k, v, fp32 out
+  backward algorithmic FLOPs per (b, h): 2 (3 d_k + 2 d_v) * causal pairs + 10 N d_k d_v (the
+    scores Q K^T and dout V^T, their products with K, Q and dout, and per token the five
+    d_k x d_v products dout R^T, U v, U^T k and the two state updates)
+
+Beside the step, outside its timed region: the same chunkwise call with a swish gate after the
+GroupNorm, and the chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout, each timed
+over the same K calls.
 """
 import argparse
 import json
@@ -37,6 +44,27 @@ def chunk_flops(B, H, N, dk, dv, C):
         L = min(C, N - c0)
         pairs += L * (L + 1) // 2
     return B * H * (2 * (dk + dv) * pairs + 4 * N * dk * dv)
+
+
+def backward_flops(B, H, N, dk, dv, C):
+    pairs = 0
+    for c0 in range(0, N, C):
+        L = min(C, N - c0)
+        pairs += L * (L + 1) // 2
+    return B * H * (2 * (3 * dk + 2 * dv) * pairs + 10 * N * dk * dv)
+
+
+def time_calls(fn, n, stream, torch):
+    """Average time of fn() over n calls, with HIP events on the library's stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3
 
 
 def chunk_bytes(B, H, N, dk, dv, in_bytes=2, out_bytes=2):
@@ -179,6 +207,21 @@ def main():
                       "algorithmic_flops_per_launch": cf, "algorithmic_bytes_per_launch": cb,
                       "avg_launch_us": round(t_chunk * 1e6, 2)}
 
+    # ---- the next rows, outside the step: swish gate after GroupNorm, chunkwise backward
+    gate = (torch.randn((w.B, w.H, w.N, w.dv), generator=torch.Generator().manual_seed(7)) * 1.0).to(torch.bfloat16).to(dev)
+    gn_g = R.GroupNorm(w.eps, gate=gate)
+    t_gate = time_calls(lambda: R.chunkwise_fwd(q, k, v, gam, C, groupnorm=gn_g, out=out, state_out=st_out, workspace=ws,
+                                                stream=stream), args.steps, stream, torch)
+    del gate
+    gdo = (torch.randn((w.B, w.H, w.N, w.dv), generator=torch.Generator().manual_seed(8))).to(torch.bfloat16).to(dev)
+    bws = torch.empty(R.workspace_bytes(R.RET_FN_CHUNKWISE_BWD, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.float32, C),
+                      dtype=torch.uint8, device=dev)
+    t_bwd = time_calls(lambda: R.chunkwise_bwd(q, k, v, gam, gdo, C, want=("dq", "dk", "dv"), workspace=bws, stream=stream),
+                       args.steps, stream, torch)
+    del bws, gdo
+    bf = backward_flops(w.B, w.H, w.N, w.dk, w.dv, C)
+    log(f"gated chunkwise {t_gate * 1e6:.1f} us; backward {t_bwd * 1e6:.1f} us")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -207,6 +250,11 @@ def main():
         "decode_tokens_per_s": round(d.B / t_dec, 1),
         "roofline": roofline,
         "roofline_chunkwise": roofline_chunk,
+        "swish_gate": {"chunkwise_gated_us": round(t_gate * 1e6, 2), "gate_extra_us": round((t_gate - t_chunk) * 1e6, 2)},
+        "backward": {"workload": "dq, dk, dv of the chunkwise workload (bf16 dout, fp32 gradients)",
+                     "us": round(t_bwd * 1e6, 2), "tflops": round(bf / t_bwd / 1e12, 3), "algorithmic_flops": bf,
+                     "mfma_frac": round(bf / t_bwd / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "tokens_per_s": round(w.B * w.N / t_bwd, 1)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -10,8 +10,10 @@
 //   dv_m = sum_{n>=m} g^(n-m) (q_n . k_m) dout_n      = rev(forward(rev k, rev q, rev dout))_m
 //   dk_m = sum_{n>=m} g^(n-m) (dout_n . v_m) q_n      = rev(forward(rev v, rev dout, rev q))_m
 //   dstate_in = g U_0, U_0 = sum_n g^n q_n^T dout_n   = g * state_out of the dv forward
-// A forward whose contraction width (d_v here) has no kernel runs as s forwards over column
-// blocks of width d_v / s, whose outputs add (the scores are sums over the contraction index).
+// A forward whose contraction width (d_v here) has no kernel runs over s column blocks of width
+// d_v / s, whose outputs add (the scores are sums over the contraction index). The blocks are
+// stacked along the batch (B' = s B), so one launch covers them with s times the workgroups, and a
+// last pass sums the s outputs.
 // The gradients come out in fp32; the forwards accumulate in fp32 with the operand precision of
 // the forward path (bf16 scores and bf16 hi + lo state and scaled values for bf16 inputs).
 #include "common.hpp"
@@ -21,27 +23,42 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 
-// dst[bh][n][c] = src[bh][rev ? N-1-n : n][c0 + c], c < w (src rows of d elements), 16 bytes
-// per thread. w * sizeof(T) and c0 * sizeof(T) are multiples of 16 (checked by the caller).
+// Up to six copies of the rows of one [BH][N][d] source, read once: output o receives the column
+// block c0 .. c0 + w of every row, time-reversed or not, `copies` times (copies after the first at
+// copy_stride elements), as dst[copy][bh][n][c]. 16 bytes per thread; c0, w and d hold whole
+// 16-byte units (checked by the caller).
+struct RowCopy {
+    void* dst;
+    int c0, w, rev, copies;
+    size_t copy_stride;
+};
+struct RowCopies {
+    RowCopy o[6];
+    int n;
+};
+
 template <typename T>
-__global__ __launch_bounds__(kCopyThreads) void gather_rows_kernel(long BH, int N, int d, int c0, int w, int rev,
-                                                                   const T* __restrict__ src, T* __restrict__ dst) {
+__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(long BH, int N, int d, const T* __restrict__ src, RowCopies cp) {
     constexpr int EV = 16 / (int)sizeof(T);
-    const int vpr = w / EV;  // vectors per output row
+    const int vpr = d / EV;
     const size_t total = (size_t)BH * N * vpr;
     for (size_t i = blockIdx.x * (size_t)kCopyThreads + threadIdx.x; i < total; i += (size_t)gridDim.x * kCopyThreads) {
         const size_t row = i / vpr;
-        const int cv = (int)(i % vpr);
+        const int c = (int)(i % vpr) * EV;
         const long bh = (long)(row / N);
         const int n = (int)(row % N);
-        const int ns = rev ? N - 1 - n : n;
-        const uint4 x = *reinterpret_cast<const uint4*>(src + ((size_t)bh * N + ns) * d + c0 + cv * EV);
-        *reinterpret_cast<uint4*>(dst + row * w + cv * EV) = x;
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * d + c));
+        for (int k = 0; k < cp.n; ++k) {
+            const RowCopy& o = cp.o[k];
+            if (c < o.c0 || c >= o.c0 + o.w) continue;
+            const size_t at = ((size_t)bh * N + (o.rev ? N - 1 - n : n)) * o.w + (c - o.c0);
+            for (int j = 0; j < o.copies; ++j) *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(o.dst) + j * o.copy_stride + at) = x;
+        }
     }
 }
 
 // dst[bh][rev ? N-1-n : n][c0 + c] = src[bh][n][c] (+ the old value when accumulating), fp32,
-// 16 bytes per thread; the reverse of gather_rows_kernel.
+// 16 bytes per thread.
 __global__ __launch_bounds__(kCopyThreads) void scatter_rows_kernel(long BH, int N, int d, int c0, int w, int rev, int accumulate,
                                                                     const float* __restrict__ src, float* __restrict__ dst) {
     const int vpr = w / 4;
@@ -73,6 +90,26 @@ __global__ __launch_bounds__(kCopyThreads) void transpose_state_kernel(long BH, 
     }
 }
 
+// dst[bh][rev ? N-1-n : n][c] = sum over j < s of src[j][bh][n][c] (fp32, rows of d, 16 bytes per
+// thread), the s column-block outputs of a stacked forward added in block order
+__global__ __launch_bounds__(kCopyThreads) void sum_blocks_kernel(long BH, int N, int d, int s, int rev, const float* __restrict__ src,
+                                                                  float* __restrict__ dst) {
+    const int vpr = d / 4;
+    const size_t rows = (size_t)BH * N, total = rows * vpr;
+    for (size_t i = blockIdx.x * (size_t)kCopyThreads + threadIdx.x; i < total; i += (size_t)gridDim.x * kCopyThreads) {
+        const size_t row = i / vpr;
+        const int cv = (int)(i % vpr);
+        const long bh = (long)(row / N);
+        const int n = (int)(row % N);
+        float4 x = *reinterpret_cast<const float4*>(src + row * d + 4 * cv);
+        for (int j = 1; j < s; ++j) {
+            const float4 y = *reinterpret_cast<const float4*>(src + ((size_t)j * rows + row) * d + 4 * cv);
+            x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        }
+        *reinterpret_cast<float4*>(dst + ((size_t)bh * N + (rev ? N - 1 - n : n)) * d + 4 * cv) = x;
+    }
+}
+
 // x[bh][...] *= gamma_h for each of the per-head blocks of `per` elements
 __global__ __launch_bounds__(kCopyThreads) void scale_heads_kernel(long BH, int H, size_t per, HeadConsts hc, float* __restrict__ x) {
     const size_t total = (size_t)BH * per;
@@ -95,45 +132,47 @@ size_t fwd_workspace(int in_bf16, int B, int H, int N, int dk, int dv, int chunk
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace regions, each 256-aligned.
+// Workspace regions, each 256-aligned. With s column blocks, "stacked" buffers hold s copies one
+// after another (the batch of the stacked forward).
 struct BwdLayout {
     int split;  // column blocks of d_v in the dq and dk forwards
-    size_t fwd, rq, rk, rdo, dqo, dqv, rv, rdh, tmp, st, total;
+    size_t fwd, rq, rk, rdo, sa, sb, sc, ta, tb, tc, tmp, st, total;
 };
 
 BwdLayout bwd_layout(int in_bf16, int B, int H, int N, int DK, int DV, int chunk) {
     BwdLayout l{};
     l.split = bwd_split(in_bf16, DK, DV, chunk);
-    const int w = l.split ? DV / l.split : DV;
+    const int s = l.split ? l.split : 1, w = DV / s;
     const size_t rows = (size_t)B * H * N, sz = in_bf16 ? 2 : 4;
     size_t fw = fwd_workspace(in_bf16, B, H, N, DK, DV, chunk);
-    const size_t f2 = fwd_workspace(in_bf16, B, H, N, w, DK, chunk);
+    const size_t f2 = fwd_workspace(in_bf16, s * B, H, N, w, DK, chunk);
     if (f2 > fw) fw = f2;
     size_t o = 0;
     l.fwd = o; o += al(fw);
-    l.rq = o; o += al(rows * DK * sz);                     // rev q
-    l.rk = o; o += al(rows * DK * sz);                     // rev k
-    l.rdo = o; o += al(rows * DV * sz);                    // rev dout
-    l.dqo = o; o += al(l.split > 1 ? rows * w * sz : 0);   // a column block of dout
-    l.dqv = o; o += al(l.split > 1 ? rows * w * sz : 0);   // ... of v
-    l.rv = o; o += al(rows * w * sz);                      // a column block of rev v
-    l.rdh = o; o += al(l.split > 1 ? rows * w * sz : 0);   // ... of rev dout
-    l.tmp = o; o += al(rows * (size_t)(DK > DV ? DK : DV) * 4);
-    l.st = o; o += al((size_t)B * H * w * DK * 4);         // a block of S_in^T
+    l.rq = o; o += al(rows * DK * sz);                  // rev q
+    l.rk = o; o += al(rows * DK * sz);                  // rev k
+    l.rdo = o; o += al(rows * DV * sz);                 // rev dout
+    l.sa = o; o += al(s > 1 ? s * rows * w * sz : 0);   // dq forward: stacked column blocks of dout
+    l.sb = o; o += al(s > 1 ? s * rows * w * sz : 0);   // ... of v
+    l.sc = o; o += al(s > 1 ? s * rows * DK * sz : 0);  // ... k once per block
+    l.ta = o; o += al(s * rows * w * sz);               // dk forward: stacked reversed blocks of v
+    l.tb = o; o += al(s > 1 ? s * rows * w * sz : 0);   // ... of dout
+    l.tc = o; o += al(s > 1 ? s * rows * DK * sz : 0);  // ... rev q once per block
+    const size_t t1 = rows * (size_t)DV * 4, t2 = s * rows * (size_t)DK * 4;
+    l.tmp = o; o += al(t1 > t2 ? t1 : t2);              // fp32 forward output
+    l.st = o; o += al((size_t)s * B * H * w * DK * 4);  // stacked blocks of S_in^T
     l.total = o;
     return l;
 }
 
-template <typename T>
-void gather(const LaunchArgs& a, const void* src, int d, int c0, int w, int rev, void* dst) {
-    const size_t work = (size_t)a.B * a.H * a.N * w / (16 / sizeof(T));
-    hipLaunchKernelGGL(gather_rows_kernel<T>, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)a.B * a.H, a.N, d, c0,
-                       w, rev, reinterpret_cast<const T*>(src), reinterpret_cast<T*>(dst));
-}
-
-void gather_any(const LaunchArgs& a, const void* src, int d, int c0, int w, int rev, void* dst) {
-    if (a.in_bf16) gather<bf16>(a, src, d, c0, w, rev, dst);
-    else gather<float>(a, src, d, c0, w, rev, dst);
+void copy_rows(const LaunchArgs& a, const void* src, int d, const RowCopies& cp) {
+    const size_t work = (size_t)a.B * a.H * a.N * d * (a.in_bf16 ? 2 : 4) / 16;
+    if (a.in_bf16)
+        hipLaunchKernelGGL(copy_rows_kernel<bf16>, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)a.B * a.H, a.N, d,
+                           reinterpret_cast<const bf16*>(src), cp);
+    else
+        hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)a.B * a.H, a.N, d,
+                           reinterpret_cast<const float*>(src), cp);
 }
 
 void scatter(const LaunchArgs& a, const float* src, int d, int c0, int w, int rev, int acc, float* dst) {
@@ -176,38 +215,65 @@ hipError_t launch_chunkwise_bwd(const BwdArgs& b) {
     const LaunchArgs& a = b.base;
     const BwdLayout l = bwd_layout(a.in_bf16, a.B, a.H, a.N, a.DK, a.DV, a.chunk);
     const int DK = a.DK, DV = a.DV, s = l.split, w = DV / s;
+    const size_t rows = (size_t)a.B * a.H * a.N, sz = a.in_bf16 ? 2 : 4;
     char* ws = reinterpret_cast<char*>(a.ws);
     void* fws = ws + l.fwd;
     const size_t fwb = l.rq - l.fwd;
     float* tmp = reinterpret_cast<float*>(ws + l.tmp);
+    LaunchArgs stacked = a;  // the column blocks stacked along the batch
+    stacked.B = s * a.B;
+    auto blk = [&](size_t off, int j, size_t width) { return ws + off + (size_t)j * rows * width * sz; };
+    auto sum_blocks = [&](int d, int rev, float* dst) {
+        const size_t work = rows * d / 4;
+        hipLaunchKernelGGL(sum_blocks_kernel, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)a.B * a.H, a.N, d, s, rev, tmp,
+                           dst);
+    };
     hipError_t e;
-    // reversed operands
-    gather_any(a, b.q, DK, 0, DK, 1, ws + l.rq);
-    gather_any(a, b.k, DK, 0, DK, 1, ws + l.rk);
-    gather_any(a, b.dout, DV, 0, DV, 1, ws + l.rdo);
+    // The operands of every forward, each source read once: reversed q, k and dout (dv forward);
+    // with s > 1 the column blocks of dout and v and s copies of k, stacked (dq forward); reversed
+    // column blocks of v (and with s > 1 of dout) and s copies of rev q, stacked (dk forward).
+    auto rc = [](void* dst, int c0, int w_, int rev, int copies, size_t stride) { return RowCopy{dst, c0, w_, rev, copies, stride}; };
+    const size_t kst = rows * DK;  // element stride of stacked copies
+    const bool sq = s > 1 && b.dq, sk = s > 1 && b.dk;
+    {
+        RowCopies cq{}, ck{}, cd{}, cv{};
+        cq.o[cq.n++] = rc(ws + l.rq, 0, DK, 1, 1, 0);
+        if (sk) cq.o[cq.n++] = rc(ws + l.tc, 0, DK, 1, s, kst);
+        ck.o[ck.n++] = rc(ws + l.rk, 0, DK, 1, 1, 0);
+        if (sq) ck.o[ck.n++] = rc(ws + l.sc, 0, DK, 0, s, kst);
+        cd.o[cd.n++] = rc(ws + l.rdo, 0, DV, 1, 1, 0);
+        for (int j = 0; j < s; ++j) {
+            if (sq) cd.o[cd.n++] = rc(blk(l.sa, j, w), j * w, w, 0, 1, 0);
+            if (sk) cd.o[cd.n++] = rc(blk(l.tb, j, w), j * w, w, 1, 1, 0);
+            if (sq) cv.o[cv.n++] = rc(blk(l.sb, j, w), j * w, w, 0, 1, 0);
+            if (b.dk) cv.o[cv.n++] = rc(blk(l.ta, j, w), j * w, w, 1, 1, 0);
+        }
+        copy_rows(a, b.q, DK, cq);
+        copy_rows(a, b.k, DK, ck);
+        copy_rows(a, b.dout, DV, cd);
+        if (cv.n) copy_rows(a, b.v, DV, cv);
+    }
 
     // dq = sum over column blocks j of forward(dout_j, v_j, k, (S_in^T)_j)
     if (b.dq) {
-        for (int j = 0; j < s; ++j) {
-            const void* qo = b.dout;
-            const void* kv = b.v;
-            if (s > 1) {
-                gather_any(a, b.dout, DV, j * w, w, 0, ws + l.dqo);
-                gather_any(a, b.v, DV, j * w, w, 0, ws + l.dqv);
-                qo = ws + l.dqo;
-                kv = ws + l.dqv;
-            }
-            const float* st = nullptr;
-            if (b.state_in) {
+        const void *qo = b.dout, *kv = b.v, *vk = b.k;
+        if (s > 1) {
+            qo = ws + l.sa;
+            kv = ws + l.sb;
+            vk = ws + l.sc;
+        }
+        const float* st = nullptr;
+        if (b.state_in) {
+            for (int j = 0; j < s; ++j) {
                 const size_t work = (size_t)a.B * a.H * w * DK;
                 hipLaunchKernelGGL(transpose_state_kernel, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)a.B * a.H, DK, DV,
-                                   j * w, w, b.state_in, reinterpret_cast<float*>(ws + l.st));
-                st = reinterpret_cast<const float*>(ws + l.st);
+                                   j * w, w, b.state_in, reinterpret_cast<float*>(ws + l.st) + (size_t)j * a.B * a.H * w * DK);
             }
-            e = forward(a, w, DK, qo, kv, b.k, st, j == 0 ? b.dq : tmp, nullptr, fws, fwb);
-            if (e != hipSuccess) return e;
-            if (j > 0) scatter(a, tmp, DK, 0, DK, 0, 1, b.dq);
+            st = reinterpret_cast<const float*>(ws + l.st);
         }
+        e = forward(stacked, w, DK, qo, kv, vk, st, s > 1 ? tmp : b.dq, nullptr, fws, fwb);
+        if (e != hipSuccess) return e;
+        if (s > 1) sum_blocks(DK, 0, b.dq);
     }
     // dv = rev(forward(rev k, rev q, rev dout)); its final state is U_0
     if (b.dv || b.dstate_in) {
@@ -222,17 +288,14 @@ hipError_t launch_chunkwise_bwd(const BwdArgs& b) {
     }
     // dk = rev(sum over column blocks j of forward(rev v_j, rev dout_j, rev q))
     if (b.dk) {
-        for (int j = 0; j < s; ++j) {
-            gather_any(a, b.v, DV, j * w, w, 1, ws + l.rv);
-            const void* rdo = ws + l.rdo;
-            if (s > 1) {
-                gather_any(a, b.dout, DV, j * w, w, 1, ws + l.rdh);
-                rdo = ws + l.rdh;
-            }
-            e = forward(a, w, DK, ws + l.rv, rdo, ws + l.rq, nullptr, tmp, nullptr, fws, fwb);
-            if (e != hipSuccess) return e;
-            scatter(a, tmp, DK, 0, DK, 1, j > 0, b.dk);
+        const void *qv = ws + l.ta, *kd = ws + l.rdo, *vq = ws + l.rq;
+        if (s > 1) {
+            kd = ws + l.tb;
+            vq = ws + l.tc;
         }
+        e = forward(stacked, w, DK, qv, kd, vq, nullptr, tmp, nullptr, fws, fwb);
+        if (e != hipSuccess) return e;
+        sum_blocks(DK, 1, b.dk);
     }
     return hipGetLastError();
 }

@@ -786,13 +786,17 @@ __global__ __launch_bounds__(256) void gn_rows_kernel(long rows, int H, int N, i
     if (row >= rows) return;
     const float* xr = x + (size_t)row * DV;
     f32x4 xv[2];
+    bf16x4 gv[2];  // the gate's values, loaded together with the rows
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = 4 * lane + 256 * i;
         xv[i] = c < DV ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + c)) : f32x4{0.f, 0.f, 0.f, 0.f};
-        s += (xv[i][0] + xv[i][1]) + (xv[i][2] + xv[i][3]);
+        if (gn.gate && c < DV)
+            gv[i] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(gn.gate) + (size_t)row * DV + c));
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s += (xv[i][0] + xv[i][1]) + (xv[i][2] + xv[i][3]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     const float mean = s / (float)DV;
@@ -817,9 +821,8 @@ __global__ __launch_bounds__(256) void gn_rows_kernel(long rows, int H, int N, i
         if (gn.bias) bb = *reinterpret_cast<const f32x4*>(gn.bias + (size_t)h * DV + c);
         f32x4 gs = {1.f, 1.f, 1.f, 1.f};
         if (gn.gate) {
-            const bf16x4 g = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(gn.gate) + (size_t)row * DV + c);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) gs[j] = swish((float)g[j]);
+            for (int j = 0; j < 4; ++j) gs[j] = swish((float)gv[i][j]);
         }
         TOUT o[4];
 #pragma unroll
