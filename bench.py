@@ -15,6 +15,7 @@ Counting rules:
   backward algorithmic FLOPs per (b, h): 2 (3 d_k + 2 d_v) * causal pairs + 10 N d_k d_v (the
     scores Q K^T and dout V^T, their products with K, Q and dout, and per token the five
     d_k x d_v products dout R^T, U v, U^T k and the two state updates)
+  backward algorithmic bytes: bf16 q, k, v, dout read; fp32 dq, dk, dv written
 
 Beside the step, outside its timed region: the same chunkwise call with a swish gate after the
 GroupNorm, and the chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout, each timed
@@ -220,6 +221,12 @@ def main():
                        args.steps, stream, torch)
     del bws, gdo
     bf = backward_flops(w.B, w.H, w.N, w.dk, w.dv, C)
+    # bf16 q, k, v, dout read; fp32 dq, dk, dv written
+    bb = w.B * w.H * w.N * (2 * w.dk + 2 * w.dv) * 2 + w.B * w.H * w.N * (2 * w.dk + w.dv) * 4
+    bwd_traffic = read_counters("chunkwise_backward_b1_h16_n8192_pmc.txt",
+                                ["linear_recurrent_sequence_chunkwise_amd/csrc/backward.hip",
+                                 "linear_recurrent_sequence_chunkwise_amd/csrc/chunkwise_bf16.hip",
+                                 "linear_recurrent_sequence_chunkwise_amd/csrc/common.hpp"])
     log(f"gated chunkwise {t_gate * 1e6:.1f} us; backward {t_bwd * 1e6:.1f} us")
 
     cpu = None
@@ -254,6 +261,7 @@ def main():
         "backward": {"workload": "dq, dk, dv of the chunkwise workload (bf16 dout, fp32 gradients)",
                      "us": round(t_bwd * 1e6, 2), "tflops": round(bf / t_bwd / 1e12, 3), "algorithmic_flops": bf,
                      "mfma_frac": round(bf / t_bwd / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "algorithmic_bytes": bb, "traffic": bwd_traffic,
                      "tokens_per_s": round(w.B * w.N / t_bwd, 1)},
         "cpu_baseline": cpu,
     }
