@@ -29,6 +29,8 @@ def load(path: str = LIB):
     lib.oracle_groupnorm.argtypes = [i, i, i, i, d, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_recurrent_bwd.argtypes = [i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP]
     lib.oracle_recurrent_bwd.restype = None
+    lib.oracle_rotate.argtypes = [ctypes.c_long, i, i, d, ctypes.c_longlong, i, _DP, _DP]
+    lib.oracle_rotate.restype = None
     lib.oracle_threads.restype = i
     lib.oracle_set_threads.argtypes = [i]
     for f in (lib.oracle_recurrent, lib.oracle_parallel, lib.oracle_chunkwise, lib.oracle_groupnorm):
@@ -121,6 +123,30 @@ class Oracle:
         self.lib.oracle_recurrent_bwd(B, H, N, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(dout),
                                       _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(ds))
         return dq, dkk, dvv, ds
+
+    def rotate(self, x, base=10000.0, offset=0, inverse=False):
+        """Positional rotation of x [..., N, d] (d even): row n turned by (offset + n) * theta_i on
+        feature pairs (2i, 2i+1), theta_i = base^(-2i/d); inverse=True turns the other way."""
+        x = _f64(x)
+        *lead, N, d = x.shape
+        if d % 2:
+            raise ValueError(f"rotation needs an even feature count, got {d}")
+        rows = int(np.prod(lead)) if lead else 1
+        y = np.zeros_like(x)
+        self.lib.oracle_rotate(rows, N, d, float(base), int(offset), -1 if inverse else 1, _ptr(x), _ptr(y))
+        return y
+
+    def recurrent_rot(self, q, k, v, gamma, base=10000.0, offset=0, state_in=None, want_out=True, want_state=True):
+        """Recurrent form on rotated q and k (the rotation first, then the recurrence)."""
+        return self.recurrent(self.rotate(q, base, offset), self.rotate(k, base, offset), v, gamma, state_in,
+                              want_out, want_state)
+
+    def recurrent_rot_bwd(self, q, k, v, gamma, dout, base=10000.0, offset=0, state_in=None):
+        """Gradients of recurrent_rot with respect to the unrotated q and k (and v, state_in): the
+        gradients at the rotated inputs turned back by the inverse rotation (chain rule)."""
+        dq, dk, dv, ds = self.recurrent_bwd(self.rotate(q, base, offset), self.rotate(k, base, offset), v, gamma, dout,
+                                            state_in)
+        return self.rotate(dq, base, offset, inverse=True), self.rotate(dk, base, offset, inverse=True), dv, ds
 
     def step(self, q, k, v, gamma, state):
         """One recurrent decode step. q, k: [B,H,dk]; v: [B,H,dv]; state: [B,H,dk,dv].

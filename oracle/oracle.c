@@ -297,3 +297,37 @@ void oracle_groupnorm(int B, int H, int N, int dv, double eps,
         }
     }
 }
+
+/*
+ * Positional rotation of q and k (abeam.tech summary, "Technical mechanism",
+ * subsection "Retention multiplies content-based reference and
+ * distance-based forgetting": Q and K get a positional rotation after the
+ * projections; eulerwa.com "3. RetNet 상세", list of advantages and the
+ * comparison table: RoPE is the position encoding used with the decay).
+ * The pages give no formula; the reading taken is the rotary position
+ * embedding as published by Su et al. (RoFormer): at absolute position
+ * p = offset + n, each pair of features (2i, 2i+1), i < d/2, is turned by
+ * the angle p * theta_i with theta_i = base^(-2i/d):
+ *     y[2i]   = x[2i] cos(p theta_i) - x[2i+1] sin(p theta_i)
+ *     y[2i+1] = x[2i] sin(p theta_i) + x[2i+1] cos(p theta_i)
+ * x, y: [rows][N][d] (rows = B*H), d even. direction = -1 turns by the
+ * opposite angle (the inverse, which is the transpose: used for gradients).
+ */
+void oracle_rotate(long rows, int N, int d, double base, long long offset, int direction,
+                   const double* x, double* y) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        for (int n = 0; n < N; ++n) {
+            const double p = (double)(offset + n) * (direction < 0 ? -1.0 : 1.0);
+            const double* xn = x + ((size_t)r * N + n) * d;
+            double* yn = y + ((size_t)r * N + n) * d;
+            for (int i = 0; i < d / 2; ++i) {
+                const double theta = pow(base, -2.0 * i / d);
+                const double c = cos(p * theta), s = sin(p * theta);
+                const double a = xn[2 * i], b = xn[2 * i + 1];
+                yn[2 * i] = a * c - b * s;
+                yn[2 * i + 1] = a * s + b * c;
+            }
+        }
+    }
+}

@@ -16,7 +16,11 @@ Sources of truth used here:
     (eulerwa.com "3. RetNet in detail", "How does it work?"; abeam.tech summary, FAQ), and the
     state hand-over between chunks / steps (abeam.tech, "Chunk recursion for long-sequence
     training"), checked as split/resume and decode-after-prefill identities;
-  - GroupNorm invariants: each normalised row has mean b_h and variance w_h^2 var/(var+eps).
+  - GroupNorm invariants: each normalised row has mean b_h and variance w_h^2 var/(var+eps);
+  - the positional rotation: hand-worked rows (tests/golden/rotation_hand_worked.json) and the
+    facts a rotation by p * theta_i must satisfy (position 0 is the identity, pair norms are kept,
+    turning by a then b is turning by a + b, the inverse undoes it), plus the property the
+    rotation is used for: retention scores and outputs depend only on relative positions.
 """
 import json
 import os
@@ -330,6 +334,88 @@ def pin_backward_bruteforce(o):
     assert np.allclose(ds[0, 0], want_s, rtol=1e-12, atol=1e-12), "dstate_in"
 
 
+def pin_rotation_hand_worked(o):
+    import math
+    g = json.load(open(os.path.join(HERE, "golden", "rotation_hand_worked.json")))
+    env = {"__builtins__": {}, "cos": math.cos, "sin": math.sin}
+    for case in g["cases"]:
+        x = np.array(case["x"], float)[None, None]
+        want = np.array([[eval(e, env) for e in row] for row in case["y"]])
+        y = o.rotate(x, case["base"], case["offset"])[0, 0]
+        assert np.allclose(y, want, rtol=0, atol=1e-15), ("rotation hand-worked", case["what"], y, want)
+
+
+def pin_rotation_properties(o):
+    rng = np.random.default_rng(131)
+    x = rng.standard_normal((2, 3, 50, 16))
+    for base, off in ((10000.0, 0), (500.0, 123), (10000.0, 65536)):
+        y = o.rotate(x, base, off)
+        # pair norms are kept
+        nx = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+        ny = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+        assert _rel(ny, nx) < 1e-14, ("pair norms", base, off)
+        # the inverse undoes the rotation
+        assert _rel(o.rotate(y, base, off, inverse=True), x) < 1e-13, ("inverse", base, off)
+    # position 0 is the identity
+    assert np.array_equal(o.rotate(x[:, :, :1], 10000.0, 0), x[:, :, :1]), "position 0"
+    # one row: turning by a, then by b, is turning by a + b
+    r = x[:, :, :1]
+    for a, b in ((1, 2), (37, 1000), (5000, 3)):
+        assert _rel(o.rotate(o.rotate(r, 10000.0, a), 10000.0, b), o.rotate(r, 10000.0, a + b)) < 1e-12, ("compose", a, b)
+    # the scores of rotated q and k depend only on relative positions
+    q, k = rng.standard_normal((1, 1, 40, 16)), rng.standard_normal((1, 1, 40, 16))
+    s0 = o.rotate(q, 10000.0, 0)[0, 0] @ o.rotate(k, 10000.0, 0)[0, 0].T
+    s1 = o.rotate(q, 10000.0, 911)[0, 0] @ o.rotate(k, 10000.0, 911)[0, 0].T
+    assert _rel(s1, s0) < 1e-12, "relative positions"
+    # the score of one pair at positions n and m equals q . R((m - n) theta) k, with k turned alone
+    for n, m in ((7, 3), (30, 0), (12, 12)):
+        want = float(q[0, 0, n] @ o.rotate(k[:, :, m:m + 1], 10000.0, m - n)[0, 0, 0])
+        assert abs(s0[n, m] - want) < 1e-12 * max(1.0, abs(want)), ("relative score", n, m)
+
+
+def pin_rotation_retention(o):
+    B, H, N, dk, dv = 1, 2, 90, 8, 5
+    q, k, v = _qkv(B, H, N, dk, dv, 141)
+    gam = [0.9, 0.995]
+    # outputs with zero start state depend only on relative positions
+    a, _ = o.recurrent_rot(q, k, v, gam, 10000.0, 0)
+    b, _ = o.recurrent_rot(q, k, v, gam, 10000.0, 4097)
+    assert _rel(b, a) < 1e-11, "rotated retention: offset invariance"
+    # ... and the rotation is not a no-op
+    c, _ = o.recurrent(q, k, v, gam)
+    assert _rel(c, a) > 1e-3, "rotation changes the output"
+    # split and resume with the position offset carried
+    full, sfull = o.recurrent_rot(q, k, v, gam, 500.0, 3)
+    for n1 in (1, 40, 89):
+        x, sx = o.recurrent_rot(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], gam, 500.0, 3)
+        y, sy = o.recurrent_rot(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], gam, 500.0, 3 + n1, state_in=sx)
+        assert _rel(np.concatenate([x, y], axis=2), full) < 1e-12, ("rotated split/resume out", n1)
+        assert _rel(sy, sfull) < 1e-12, ("rotated split/resume state", n1)
+
+
+def pin_rotation_backward_fd(o):
+    """Central finite differences of L = <dout, out> through the rotation, against the gradients
+    with respect to the unrotated q and k."""
+    B, H, N, dk, dv = 1, 1, 8, 4, 3
+    q, k, v = _qkv(B, H, N, dk, dv, 151)
+    s0 = _rand((B, H, dk, dv), 152)
+    dout = _rand((B, H, N, dv), 153)
+    gam, base, off = [0.85], 100.0, 5
+    grads = o.recurrent_rot_bwd(q, k, v, gam, dout, base, off, state_in=s0)
+    L = lambda qq, kk: _ip(dout, o.recurrent_rot(qq, kk, v, gam, base, off, state_in=s0)[0])
+    rng = np.random.default_rng(154)
+    h = 1e-4
+    for t in range(2):
+        for _ in range(4):
+            idx = tuple(int(rng.integers(0, s)) for s in q.shape)
+            ap, am = [q.copy(), k.copy()], [q.copy(), k.copy()]
+            ap[t][idx] += h
+            am[t][idx] -= h
+            fd = (L(*ap) - L(*am)) / (2 * h)
+            assert abs(fd - grads[t][idx]) <= 1e-8 * max(abs(fd), 1.0), ("rotated finite difference", t, idx, fd, grads[t][idx])
+
+
 PINS = [pin_hand_worked, pin_closed_form, pin_gamma_one, pin_tiny_gamma, pin_bruteforce, pin_three_forms,
         pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm, pin_swish_gate,
-        pin_backward_adjoint, pin_backward_fd, pin_backward_bruteforce]
+        pin_backward_adjoint, pin_backward_fd, pin_backward_bruteforce, pin_rotation_hand_worked,
+        pin_rotation_properties, pin_rotation_retention, pin_rotation_backward_fd]

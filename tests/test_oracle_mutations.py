@@ -47,6 +47,16 @@ MUTANTS = [
     ("gate_wrong_index", "const double g = gate[(size_t)r * dv + c];", "const double g = gate[c];"),
     ("gate_before_bias", "yr[c] = (xr[c] - mu) * inv * w + b;\n            if (gate) {\n                const double g = gate[(size_t)r * dv + c];\n                yr[c] *= g / (1.0 + exp(-g));",
      "yr[c] = (xr[c] - mu) * inv * w;\n            if (gate) {\n                const double g = gate[(size_t)r * dv + c];\n                yr[c] *= g / (1.0 + exp(-g));\n            }\n            yr[c] += b;\n            {"),
+    ("rot_sin_sign_first", "yn[2 * i] = a * c - b * s;", "yn[2 * i] = a * c + b * s;"),
+    ("rot_turns_backwards", "yn[2 * i] = a * c - b * s;\n                yn[2 * i + 1] = a * s + b * c;",
+     "yn[2 * i] = a * c + b * s;\n                yn[2 * i + 1] = -a * s + b * c;"),
+    ("rot_theta_exponent_halved", "pow(base, -2.0 * i / d)", "pow(base, -1.0 * i / d)"),
+    ("rot_theta_per_feature_count", "pow(base, -2.0 * i / d)", "pow(base, -2.0 * i / (d - 2 > 0 ? d - 2 : 1))"),
+    ("rot_ignores_offset", "(double)(offset + n)", "(double)(n)"),
+    ("rot_position_one_based", "(double)(offset + n)", "(double)(offset + n + 1)"),
+    ("rot_half_split_pairs", "const double a = xn[2 * i], b = xn[2 * i + 1];\n                yn[2 * i] = a * c - b * s;\n                yn[2 * i + 1] = a * s + b * c;",
+     "const double a = xn[i], b = xn[i + d / 2];\n                yn[i] = a * c - b * s;\n                yn[i + d / 2] = a * s + b * c;"),
+    ("rot_inverse_not_negated", "(direction < 0 ? -1.0 : 1.0)", "1.0"),
 ]
 
 
