@@ -18,8 +18,9 @@ Counting rules:
   backward algorithmic bytes: bf16 q, k, v, dout read; fp32 dq, dk, dv written
 
 Beside the step, outside its timed region: the same chunkwise call with a swish gate after the
-GroupNorm, and the chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout, each timed
-over the same K calls.
+GroupNorm, the chunkwise call and the decode step with the positional rotation of q and k, and the
+chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout, each timed over the same K
+calls.
 """
 import argparse
 import json
@@ -66,6 +67,25 @@ def time_calls(fn, n, stream, torch):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n * 1e-3
+
+
+def time_pair(base, variant, n, stream, torch):
+    """Average times of base() and variant(), called alternately n times each with HIP events on the
+    library's stream, so that clock drift over the run affects both alike."""
+    base()
+    variant()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for e in evs:
+        e[0].record(stream)
+        base()
+        e[1].record(stream)
+        variant()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    tb = sum(e[0].elapsed_time(e[1]) for e in evs) / n * 1e-3
+    tv = sum(e[1].elapsed_time(e[2]) for e in evs) / n * 1e-3
+    return tb, tv
 
 
 def chunk_bytes(B, H, N, dk, dv, in_bytes=2, out_bytes=2):
@@ -211,9 +231,23 @@ def main():
     # ---- the next rows, outside the step: swish gate after GroupNorm, chunkwise backward
     gate = (torch.randn((w.B, w.H, w.N, w.dv), generator=torch.Generator().manual_seed(7)) * 1.0).to(torch.bfloat16).to(dev)
     gn_g = R.GroupNorm(w.eps, gate=gate)
-    t_gate = time_calls(lambda: R.chunkwise_fwd(q, k, v, gam, C, groupnorm=gn_g, out=out, state_out=st_out, workspace=ws,
-                                                stream=stream), args.steps, stream, torch)
+    plain = lambda: R.chunkwise_fwd(q, k, v, gam, C, groupnorm=gn, out=out, state_out=st_out, workspace=ws, stream=stream)
+    tb_gate, t_gate = time_pair(plain, lambda: R.chunkwise_fwd(q, k, v, gam, C, groupnorm=gn_g, out=out, state_out=st_out,
+                                                               workspace=ws, stream=stream), args.steps, stream, torch)
     del gate
+    rot = R.Rotation(10000.0, 0)
+    rws = torch.empty(R.workspace_bytes(R.RET_FN_CHUNKWISE, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.bfloat16, C, True,
+                                        rotation=True), dtype=torch.uint8, device=dev)
+    tb_rot, t_rot = time_pair(plain, lambda: R.chunkwise_fwd(q, k, v, gam, C, groupnorm=gn, rotation=rot, out=out,
+                                                             state_out=st_out, workspace=rws, stream=stream),
+                              args.steps, stream, torch)
+    del rws
+    drot = R.Rotation(10000.0, I.DECODE_PREFILL_TOKENS)
+    dws = torch.empty(R.workspace_bytes(R.RET_FN_RECURRENT_STEP, d.B, d.H, 1, d.dk, d.dv, torch.bfloat16, torch.float32, 0,
+                                        rotation=True), dtype=torch.uint8, device=dev)
+    tb_drot, t_drot = time_pair(lambda: R.recurrent_step(qn, kn, vn, dgam, state, out=dout, stream=stream),
+                                lambda: R.recurrent_step(qn, kn, vn, dgam, state, rotation=drot, out=dout, workspace=dws,
+                                                         stream=stream), args.steps, stream, torch)
     gdo = (torch.randn((w.B, w.H, w.N, w.dv), generator=torch.Generator().manual_seed(8))).to(torch.bfloat16).to(dev)
     bws = torch.empty(R.workspace_bytes(R.RET_FN_CHUNKWISE_BWD, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.float32, C),
                       dtype=torch.uint8, device=dev)
@@ -227,7 +261,8 @@ def main():
                                 ["linear_recurrent_sequence_chunkwise_amd/csrc/backward.hip",
                                  "linear_recurrent_sequence_chunkwise_amd/csrc/chunkwise_bf16.hip",
                                  "linear_recurrent_sequence_chunkwise_amd/csrc/common.hpp"])
-    log(f"gated chunkwise {t_gate * 1e6:.1f} us; backward {t_bwd * 1e6:.1f} us")
+    log(f"gated chunkwise {t_gate * 1e6:.1f} us; rotated chunkwise {t_rot * 1e6:.1f} us; rotated decode {t_drot * 1e6:.1f} us; "
+        f"backward {t_bwd * 1e6:.1f} us")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -257,7 +292,9 @@ def main():
         "decode_tokens_per_s": round(d.B / t_dec, 1),
         "roofline": roofline,
         "roofline_chunkwise": roofline_chunk,
-        "swish_gate": {"chunkwise_gated_us": round(t_gate * 1e6, 2), "gate_extra_us": round((t_gate - t_chunk) * 1e6, 2)},
+        "swish_gate": {"chunkwise_gated_us": round(t_gate * 1e6, 2), "gate_extra_us": round((t_gate - tb_gate) * 1e6, 2)},
+        "rotation": {"chunkwise_rotated_us": round(t_rot * 1e6, 2), "rotation_extra_us": round((t_rot - tb_rot) * 1e6, 2),
+                     "decode_rotated_us": round(t_drot * 1e6, 2), "decode_rotation_extra_us": round((t_drot - tb_drot) * 1e6, 2)},
         "backward": {"workload": "dq, dk, dv of the chunkwise workload (bf16 dout, fp32 gradients)",
                      "us": round(t_bwd * 1e6, 2), "tflops": round(bf / t_bwd / 1e12, 3), "algorithmic_flops": bf,
                      "mfma_frac": round(bf / t_bwd / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),

@@ -21,7 +21,8 @@
  * Positions are 0-based and o_n includes token n (diagonal decay gamma^0 = 1). No 1/sqrt(d_k)
  * scaling is applied: the result is exactly (Q K^T (.) D) V.
  * Pointers: q, k, v, out, state*, groupnorm weight/bias and workspace are DEVICE pointers owned
- * by the caller. `gamma` is a HOST pointer to H doubles, read during the call only. The library
+ * by the caller. `gamma` is a HOST pointer to H doubles, and `rotation` and `groupnorm` HOST
+ * pointers to structs; all three are read during the call only. The library
  * never allocates device memory and keeps no state between calls except a thread-local error
  * string. All device pointers must be 16-byte aligned.
  * Streams: all work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 2
+#define RETENTION_ABI_VERSION 3
 #define RETENTION_MAX_HEADS 128
 
 typedef enum {
@@ -57,6 +58,10 @@ typedef enum {
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
 
 typedef enum { RET_FN_CHUNKWISE = 0, RET_FN_RECURRENT_STEP = 1, RET_FN_PARALLEL = 2, RET_FN_CHUNKWISE_BWD = 3 } ret_fn;
+
+/* Flags of retention_workspace_bytes(): the epilogue and prologue settings of the call. */
+#define RET_WS_GROUPNORM 1
+#define RET_WS_ROTATION 2
 
 /* Problem shape. in_dtype applies to q, k and v; out_dtype to out. */
 typedef struct {
@@ -83,6 +88,28 @@ typedef struct {
     const void* gate;    /* like out, input dtype, or NULL */
 } ret_groupnorm;
 
+/* Optional positional rotation of q and k before retention (abeam.tech RetNet summary, "Technical
+ * mechanism": Q and K get a positional rotation after the projections; eulerwa.com "3. RetNet
+ * 상세": RoPE is the position encoding used with the decay). The pages give no formula; this is
+ * the rotary position embedding of Su et al. (RoFormer): at absolute position p = offset + n, each
+ * feature pair (2i, 2i+1) of q_n and of k_n is turned by p * theta_i, theta_i = base^(-2i/d_k):
+ *   (a, b) -> (a cos(p theta_i) - b sin(p theta_i), a sin(p theta_i) + b cos(p theta_i)).
+ * Retention then runs on the rotated q and k, so scores depend on relative positions only.
+ * offset is the absolute position of token 0 of this call (the number of tokens before it, e.g.
+ * the prefill length for a decode step). Needs d_k even (d_k <= 256), base > 0 finite,
+ * 0 <= offset < 2^31 and seq_len < 2^24. Pass NULL (or enabled = 0) for none. The rotated q and k are staged in the
+ * workspace (flag RET_WS_ROTATION of retention_workspace_bytes) in the input dtype; for bf16
+ * inputs they are rounded to bf16 before the matrix cores, as the unrotated ones are.
+ * Angles: the per-pair frequency theta_i / pi and the offset's phase are formed on the host in
+ * double precision; the device adds n times the frequency with an exact two-product and
+ * evaluates sin and cos of pi times the phase in fp32 (error about 1e-6 rad at any allowed
+ * position). */
+typedef struct {
+    int32_t enabled;
+    double base;    /* e.g. 10000 */
+    int64_t offset; /* absolute position of token 0 */
+} ret_rotation;
+
 /*
  * Chunkwise recurrent form (abeam.tech summary, "Chunk recursion for long-sequence training";
  * mlnews abstract: chunks encoded in parallel, summarised recurrently).
@@ -101,7 +128,7 @@ typedef struct {
  */
 ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk,
                                    const void* q, const void* k, const void* v,
-                                   const double* gamma, const float* state_in,
+                                   const double* gamma, const ret_rotation* rotation, const float* state_in,
                                    const ret_groupnorm* groupnorm, void* out, float* state_out,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
@@ -111,10 +138,12 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk,
  * shape->seq_len must be 1. q, k: [B][H][d_k]; v: [B][H][d_v]; state: fp32 [B][H][d_k][d_v],
  * read and written in place; out: [B][H][d_v] (may be NULL to only advance the state).
  * Supported: d_v a multiple of 4 with d_v / 4 dividing 256 (d_v <= 1024), any d_k >= 1.
+ * With a rotation, rotation->offset is the position of this token; the workspace holds the
+ * rotated q and k.
  */
 ret_status retention_recurrent_step(const ret_shape* shape,
                                     const void* q, const void* k, const void* v,
-                                    const double* gamma, float* state,
+                                    const double* gamma, const ret_rotation* rotation, float* state,
                                     const ret_groupnorm* groupnorm, void* out,
                                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
@@ -125,7 +154,8 @@ ret_status retention_recurrent_step(const ret_shape* shape,
  */
 ret_status retention_parallel_fwd(const ret_shape* shape,
                                   const void* q, const void* k, const void* v,
-                                  const double* gamma, const ret_groupnorm* groupnorm, void* out,
+                                  const double* gamma, const ret_rotation* rotation,
+                                  const ret_groupnorm* groupnorm, void* out,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -139,22 +169,28 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
  * dstate_in like state_in. shape->out_dtype must be RET_F32. Outputs must not alias inputs or each
  * other. chunk and (d_k, d_v) as for retention_chunkwise_fwd; a d_v with no forward kernel of
  * contraction width d_v runs as two column blocks of d_v / 2.
+ * With a rotation, dq and dk are the gradients with respect to the unrotated q and k: the
+ * gradients at the rotated inputs turned back by the inverse rotation (its transpose).
  * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): time-reversed copies of q, k,
- * v and dout, one fp32 output buffer and the workspace of the forward calls.
+ * v and dout, one fp32 output buffer and the workspace of the forward calls (plus the rotated q
+ * and k with RET_WS_ROTATION).
  */
 ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
                                    const void* q, const void* k, const void* v,
-                                   const double* gamma, const float* state_in, const void* dout,
+                                   const double* gamma, const ret_rotation* rotation,
+                                   const float* state_in, const void* dout,
                                    float* dq, float* dk, float* dv, float* dstate_in,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Bytes of device workspace the call `fn` needs for this shape, chunk and GroupNorm setting.
+/* Bytes of device workspace the call `fn` needs for this shape, chunk and flags (a bitwise OR of
+ * RET_WS_GROUPNORM when a GroupNorm epilogue is enabled and RET_WS_ROTATION when a rotation is).
  * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid.
  * Chunkwise with bf16 inputs: the bf16 intra-chunk scores (B*H*ceil(N/chunk)*chunk^2*2 bytes)
  * when an output is wanted, plus fp32 pre-norm rows (B*H*N*d_v*4 bytes) with GroupNorm. Other
- * calls: fp32 staging rows when GroupNorm or a bf16 output needs them. The caller owns it; its
- * contents are scratch and need no initialisation. */
-size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t gn_enabled);
+ * calls: fp32 staging rows when GroupNorm or a bf16 output needs them. A rotation adds the
+ * rotated q and k (2*B*H*N*d_k elements of the input dtype, each copy 256-byte aligned) in front.
+ * The caller owns it; its contents are scratch and need no initialisation. */
+size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t flags);
 
 /* Static description of a status code. */
 const char* retention_status_string(int32_t status);

@@ -84,6 +84,64 @@ ret_status check_gn(const ret_groupnorm* gn, int in_bf16, ret::GnArgs* out) {
     return RET_OK;
 }
 
+// Rotation constants per feature pair, in double precision: theta_i / pi split into two floats,
+// and the offset's phase (offset * theta_i / pi mod 2) from an exact two-product and an exact fmod.
+ret_status check_rotation(const ret_rotation* r, const ret_shape* s, ret::RotConsts* rc, bool* on) {
+    *on = false;
+    if (!r || !r->enabled) return RET_OK;
+    if (!(r->base > 0.0) || !std::isfinite(r->base)) return fail(RET_ERR_INVALID_ARG, "rotation base must be finite and > 0");
+    if (r->offset < 0 || r->offset >= (1LL << 31))
+        return fail(RET_ERR_INVALID_ARG, "rotation offset must be in [0, 2^31) (got %lld)", (long long)r->offset);
+    if (s->d_k % 2) return fail(RET_ERR_INVALID_ARG, "rotation needs an even d_k (got %d)", s->d_k);
+    if (s->d_k / 2 > ret::kMaxPairs) return fail(RET_ERR_UNSUPPORTED, "rotation supports d_k <= %d (got %d)", 2 * ret::kMaxPairs, s->d_k);
+    if (s->seq_len >= (1 << 24)) return fail(RET_ERR_UNSUPPORTED, "rotation supports seq_len < 2^24 (got %d)", s->seq_len);
+    const int d = s->d_k;
+    const double off = (double)r->offset;
+    for (int i = 0; i < ret::kMaxPairs; ++i) {
+        if (i >= d / 2) {
+            rc->fhi[i] = rc->flo[i] = rc->ph[i] = 0.f;
+            continue;
+        }
+        const double f = std::pow(r->base, -2.0 * i / d) / M_PI;
+        const float hi = (float)f;
+        rc->fhi[i] = hi;
+        rc->flo[i] = (float)(f - (double)hi);
+        const double p = off * f;
+        const double e = std::fma(off, f, -p);
+        double ph = std::fmod(p, 2.0) + e;
+        ph -= 2.0 * std::floor(0.5 * ph);
+        rc->ph[i] = (float)ph;
+    }
+    *on = true;
+    return RET_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace for the rotated q and k, in front of the call's own workspace.
+size_t rotation_ws(const ret_shape* s) {
+    return 2 * align256((size_t)s->batch * s->heads * s->seq_len * s->d_k * elem_size(s->in_dtype));
+}
+
+// Rotate q and k into the front of the workspace; q, k and the workspace then point at the
+// rotated copies and the rest of the workspace.
+hipError_t stage_rotation(const ret_shape* s, const ret::RotConsts& rc, const void** q, const void** k, void** ws, size_t* wsb,
+                          hipStream_t st) {
+    const size_t A = rotation_ws(s) / 2;
+    char* base = static_cast<char*>(*ws);
+    const long rows = (long)s->batch * s->heads * s->seq_len;
+    const int bf = s->in_dtype == RET_BF16;
+    hipError_t e = ret::launch_rotate(rows, s->seq_len, s->d_k, *q, bf, base, bf, rc, 0, st);
+    if (e != hipSuccess) return e;
+    e = ret::launch_rotate(rows, s->seq_len, s->d_k, *k, bf, base + A, bf, rc, 0, st);
+    if (e != hipSuccess) return e;
+    *q = base;
+    *k = base + A;
+    *ws = base + 2 * A;
+    *wsb -= 2 * A;
+    return hipSuccess;
+}
+
 ret_status check_ptr(const void* p, const char* name, bool required) {
     if (!p) return required ? fail(RET_ERR_INVALID_ARG, "%s is NULL", name) : RET_OK;
     if (!aligned16(p)) return fail(RET_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
@@ -154,25 +212,29 @@ const char* retention_status_string(int32_t status) {
     }
 }
 
-size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t gn_enabled) {
+size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t flags) {
     if (check_shape(shape, fn == RET_FN_RECURRENT_STEP) != RET_OK) return (size_t)-1;
+    if (flags & ~(RET_WS_GROUPNORM | RET_WS_ROTATION)) return (size_t)-1;
+    const bool gn = (flags & RET_WS_GROUPNORM) != 0;
+    const size_t rot = (flags & RET_WS_ROTATION) ? rotation_ws(shape) : 0;
     switch (fn) {
         case RET_FN_CHUNKWISE:
             if (chunk <= 0) return (size_t)-1;
-            return chunkwise_ws(shape, chunk, gn_enabled != 0, 1);
-        case RET_FN_RECURRENT_STEP: return 0;
-        case RET_FN_PARALLEL: return parallel_ws(shape, gn_enabled != 0);
+            return rot + chunkwise_ws(shape, chunk, gn, 1);
+        case RET_FN_RECURRENT_STEP: return rot;
+        case RET_FN_PARALLEL: return rot + parallel_ws(shape, gn);
         case RET_FN_CHUNKWISE_BWD:
             if (chunk <= 0) return (size_t)-1;
-            return ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len, shape->d_k,
-                                                shape->d_v, chunk);
+            return rot + ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len,
+                                                      shape->d_k, shape->d_v, chunk);
         default: return (size_t)-1;
     }
 }
 
 ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const void* q, const void* k, const void* v,
-                                   const double* gamma, const float* state_in, const ret_groupnorm* groupnorm, void* out,
-                                   float* state_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                   const double* gamma, const ret_rotation* rotation, const float* state_in,
+                                   const ret_groupnorm* groupnorm, void* out, float* state_out, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
     g_err[0] = '\0';
     RET_TRY(check_shape(shape, false));
     RET_TRY(check_ptr(q, "q", true));
@@ -186,6 +248,9 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
     RET_TRY(check_gamma(shape, gamma, &hc));
     ret::GnArgs gn;
     RET_TRY(check_gn(groupnorm, shape->in_dtype == RET_BF16, &gn));
+    ret::RotConsts rc;
+    bool rot = false;
+    RET_TRY(check_rotation(rotation, shape, &rc, &rot));
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     const bool bf = shape->in_dtype == RET_BF16;
     if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, shape->d_v, chunk)
@@ -207,9 +272,12 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
         gn.enabled = 0;
         gn.gate = nullptr;
     }
-    const size_t need = chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
+    const size_t need = (rot ? rotation_ws(shape) : 0) + chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
     RET_TRY(check_ws(need, workspace, workspace_bytes));
-
+    if (rot) {
+        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return device_status(e, "retention_chunkwise_fwd rotation launch");
+    }
     ret::LaunchArgs a = base_args(shape, chunk, hc, gn, workspace, workspace_bytes, hip_stream);
     a.q = q; a.k = k; a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
     hipError_t e = bf ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a);
@@ -217,8 +285,9 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
 }
 
 ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const void* q, const void* k, const void* v,
-                                   const double* gamma, const float* state_in, const void* dout, float* dq, float* dk, float* dv,
-                                   float* dstate_in, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                   const double* gamma, const ret_rotation* rotation, const float* state_in, const void* dout,
+                                   float* dq, float* dk, float* dv, float* dstate_in, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
     g_err[0] = '\0';
     RET_TRY(check_shape(shape, false));
     RET_TRY(check_ptr(q, "q", true));
@@ -234,6 +303,9 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const 
     if (shape->out_dtype != RET_F32) return fail(RET_ERR_UNSUPPORTED, "the gradients are fp32 (out_dtype must be RET_F32)");
     ret::HeadConsts hc;
     RET_TRY(check_gamma(shape, gamma, &hc));
+    ret::RotConsts rc;
+    bool rot = false;
+    RET_TRY(check_rotation(rotation, shape, &rc, &rot));
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     const bool bf = shape->in_dtype == RET_BF16;
     if (!ret::bwd_split(bf, shape->d_k, shape->d_v, chunk))
@@ -253,21 +325,30 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const 
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(outs[i], out_b[i], outs[j], out_b[j])) return fail(RET_ERR_INVALID_ARG, "gradient outputs must not alias each other");
     }
-    const size_t need = ret::chunkwise_bwd_workspace(bf, shape->batch, shape->heads, shape->seq_len, shape->d_k, shape->d_v, chunk);
+    const size_t need = (rot ? rotation_ws(shape) : 0) +
+                        ret::chunkwise_bwd_workspace(bf, shape->batch, shape->heads, shape->seq_len, shape->d_k, shape->d_v, chunk);
     RET_TRY(check_ws(need, workspace, workspace_bytes));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    if (rot) {
+        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, st);
+        if (e != hipSuccess) return device_status(e, "retention_chunkwise_bwd rotation launch");
+    }
     ret::BwdArgs b{};
     b.base = base_args(shape, chunk, hc, ret::GnArgs{}, workspace, workspace_bytes, hip_stream);
     b.q = q; b.k = k; b.v = v; b.dout = dout; b.state_in = state_in;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dstate_in = dstate_in;
-    return device_status(ret::launch_chunkwise_bwd(b), "retention_chunkwise_bwd launch");
+    hipError_t e = ret::launch_chunkwise_bwd(b);
+    // gradients at the rotated q and k, turned back by the inverse rotation (in place)
+    const long rrows = (long)shape->batch * shape->heads * shape->seq_len;
+    if (e == hipSuccess && rot && dq) e = ret::launch_rotate(rrows, shape->seq_len, shape->d_k, dq, 0, dq, 0, rc, 1, st);
+    if (e == hipSuccess && rot && dk) e = ret::launch_rotate(rrows, shape->seq_len, shape->d_k, dk, 0, dk, 0, rc, 1, st);
+    return device_status(e, "retention_chunkwise_bwd launch");
 }
 
 ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const void* k, const void* v, const double* gamma,
-                                    float* state, const ret_groupnorm* groupnorm, void* out, void* workspace,
-                                    size_t workspace_bytes, void* hip_stream) {
+                                    const ret_rotation* rotation, float* state, const ret_groupnorm* groupnorm, void* out,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream) {
     g_err[0] = '\0';
-    (void)workspace;
-    (void)workspace_bytes;
     RET_TRY(check_shape(shape, true));
     RET_TRY(check_ptr(q, "q", true));
     RET_TRY(check_ptr(k, "k", true));
@@ -286,14 +367,22 @@ ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const
     const size_t st_bytes = bh * shape->d_k * dv * sizeof(float);
     const size_t out_bytes = bh * dv * elem_size(shape->out_dtype);
     if (out && overlaps(out, out_bytes, state, st_bytes)) return fail(RET_ERR_INVALID_ARG, "out must not alias state");
+    ret::RotConsts rc;
+    bool rot = false;
+    RET_TRY(check_rotation(rotation, shape, &rc, &rot));
+    if (rot) {
+        RET_TRY(check_ws(rotation_ws(shape), workspace, workspace_bytes));
+        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return device_status(e, "retention_recurrent_step rotation launch");
+    }
     ret::LaunchArgs a = base_args(shape, 1, hc, gn, nullptr, 0, hip_stream);
     a.q = q; a.k = k; a.v = v; a.out = out; a.state_out = state;
     return device_status(ret::launch_recurrent_step(a), "retention_recurrent_step launch");
 }
 
 ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const void* k, const void* v, const double* gamma,
-                                  const ret_groupnorm* groupnorm, void* out, void* workspace, size_t workspace_bytes,
-                                  void* hip_stream) {
+                                  const ret_rotation* rotation, const ret_groupnorm* groupnorm, void* out, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
     g_err[0] = '\0';
     RET_TRY(check_shape(shape, false));
     RET_TRY(check_ptr(q, "q", true));
@@ -314,8 +403,15 @@ ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const v
     if (overlaps(out, out_bytes, q, rows * shape->d_k * in_sz) || overlaps(out, out_bytes, k, rows * shape->d_k * in_sz) ||
         overlaps(out, out_bytes, v, rows * shape->d_v * in_sz))
         return fail(RET_ERR_INVALID_ARG, "out must not alias q, k or v");
-    const size_t need = parallel_ws(shape, gn.enabled);
+    ret::RotConsts rc;
+    bool rot = false;
+    RET_TRY(check_rotation(rotation, shape, &rc, &rot));
+    const size_t need = (rot ? rotation_ws(shape) : 0) + parallel_ws(shape, gn.enabled);
     RET_TRY(check_ws(need, workspace, workspace_bytes));
+    if (rot) {
+        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return device_status(e, "retention_parallel_fwd rotation launch");
+    }
     ret::LaunchArgs a = base_args(shape, 0, hc, gn, workspace, workspace_bytes, hip_stream);
     a.q = q; a.k = k; a.v = v; a.out = out;
     hipError_t e = bf ? ret::launch_parallel_bf16(a) : ret::launch_parallel_f32(a);

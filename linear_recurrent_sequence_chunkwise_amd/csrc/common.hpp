@@ -166,6 +166,32 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// Positional rotation (rotary embedding) of q and k: feature pair i of the row at position
+// offset + n turns by (offset + n) * theta_i. Formed on the host in double precision per call:
+// fhi + flo = theta_i / pi (half-turns per position, split into two floats) and
+// ph = (offset * theta_i / pi) mod 2.
+constexpr int kMaxPairs = 128;
+struct RotConsts {
+    float fhi[kMaxPairs];
+    float flo[kMaxPairs];
+    float ph[kMaxPairs];
+};
+
+// sin and cos of the angle of pair (fhi, flo, ph) at local position n (0 <= n < 2^24, exact in
+// fp32). The phase in half-turns is ph + n * (fhi + flo) mod 2: the product n * fhi is split into
+// its rounded value and its exact rounding error (fma), the rounded value is reduced mod 2 exactly,
+// and sincospif gives sin and cos of pi times the phase. Contraction is off so that the split
+// stays exact as written.
+__device__ __forceinline__ void rot_sincos(int n, float fhi, float flo, float ph, float& s, float& c) {
+#pragma clang fp contract(off)
+    const float nf = (float)n;
+    float p = nf * fhi;
+    const float e = __builtin_fmaf(nf, fhi, -p);
+    p = p - 2.f * __builtin_floorf(0.5f * p);
+    const float h = p + (e + __builtin_fmaf(nf, flo, ph));
+    sincospif(h, &s, &c);
+}
+
 }  // namespace ret
 
 // Backward of the chunkwise form: gradients for dL/dout = dout, in fp32.
@@ -201,4 +227,8 @@ bool parallel_f32_supported(int DK, int DV);
 int bwd_split(int in_bf16, int DK, int DV, int chunk);  // 0: unsupported
 size_t chunkwise_bwd_workspace(int in_bf16, int B, int H, int N, int DK, int DV, int chunk);
 hipError_t launch_chunkwise_bwd(const BwdArgs& b);
+// y = rotation of x ([rows][N][d], d even, row r at local position r % N); x and y may be the same
+// buffer. inverse != 0 turns by the opposite angles.
+hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc,
+                         int inverse, hipStream_t stream);
 }  // namespace ret

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libretention.so")
 RET_OK, RET_ERR_INVALID_ARG, RET_ERR_UNSUPPORTED, RET_ERR_WORKSPACE, RET_ERR_DEVICE = range(5)
 RET_F32, RET_BF16 = 0, 1
 RET_FN_CHUNKWISE, RET_FN_RECURRENT_STEP, RET_FN_PARALLEL, RET_FN_CHUNKWISE_BWD = 0, 1, 2, 3
+RET_WS_GROUPNORM, RET_WS_ROTATION = 1, 2
 
 EXPORTED = [
     "retention_chunkwise_fwd", "retention_recurrent_step", "retention_parallel_fwd", "retention_chunkwise_bwd",
@@ -34,6 +35,10 @@ class RetShape(ctypes.Structure):
 class RetGroupNorm(ctypes.Structure):
     _fields_ = [("enabled", ctypes.c_int32), ("eps", ctypes.c_float), ("weight", ctypes.c_void_p),
                 ("bias", ctypes.c_void_p), ("gate", ctypes.c_void_p)]
+
+
+class RetRotation(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int32), ("base", ctypes.c_double), ("offset", ctypes.c_int64)]
 
 
 class RetentionError(RuntimeError):
@@ -55,11 +60,11 @@ def load_library(path: str = LIB_PATH):
                            "(the retention library has no CPU fallback)")
     lib = ctypes.CDLL(path)
     vp, sz, i32, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)
-    sp, gp = ctypes.POINTER(RetShape), ctypes.POINTER(RetGroupNorm)
-    lib.retention_chunkwise_fwd.argtypes = [sp, i32, vp, vp, vp, dp, vp, gp, vp, vp, vp, sz, vp]
-    lib.retention_recurrent_step.argtypes = [sp, vp, vp, vp, dp, vp, gp, vp, vp, sz, vp]
-    lib.retention_parallel_fwd.argtypes = [sp, vp, vp, vp, dp, gp, vp, vp, sz, vp]
-    lib.retention_chunkwise_bwd.argtypes = [sp, i32, vp, vp, vp, dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    sp, gp, rp = ctypes.POINTER(RetShape), ctypes.POINTER(RetGroupNorm), ctypes.POINTER(RetRotation)
+    lib.retention_chunkwise_fwd.argtypes = [sp, i32, vp, vp, vp, dp, rp, vp, gp, vp, vp, vp, sz, vp]
+    lib.retention_recurrent_step.argtypes = [sp, vp, vp, vp, dp, rp, vp, gp, vp, vp, sz, vp]
+    lib.retention_parallel_fwd.argtypes = [sp, vp, vp, vp, dp, rp, gp, vp, vp, sz, vp]
+    lib.retention_chunkwise_bwd.argtypes = [sp, i32, vp, vp, vp, dp, rp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd, lib.retention_chunkwise_bwd):
         f.restype = ctypes.c_int
     lib.retention_workspace_bytes.argtypes = [i32, sp, i32, i32]
@@ -99,6 +104,22 @@ class GroupNorm:
         if g is not None and (g.dtype != in_dtype or tuple(g.shape) != tuple(out_shape) or not g.is_contiguous() or not g.is_cuda):
             raise ValueError(f"gate must be a contiguous {in_dtype} device tensor of shape {tuple(out_shape)}")
         return RetGroupNorm(1, float(self.eps), _ptr(self.weight), _ptr(self.bias), _ptr(g))
+
+
+@dataclass
+class Rotation:
+    """Positional rotation of q and k before retention: feature pair (2i, 2i+1) of the row at
+    absolute position offset + n turns by (offset + n) * base^(-2i/d_k). offset is the position of
+    token 0 of the call (the tokens already processed, e.g. the prefill length for a decode step)."""
+    base: float = 10000.0
+    offset: int = 0
+
+    def as_struct(self):
+        return RetRotation(1, float(self.base), int(self.offset))
+
+
+def _rot(rotation):
+    return ctypes.byref(rotation.as_struct()) if rotation is not None else None
 
 
 def _ptr(t):
@@ -145,10 +166,14 @@ def _check_inputs(q, k, v, ndim):
         raise ValueError("q, k and v must share a dtype")
 
 
-def workspace_bytes(fn, B, H, N, dk, dv, in_dtype, out_dtype, chunk=0, groupnorm=False):
+def _flags(groupnorm, rotation):
+    return (RET_WS_GROUPNORM if groupnorm else 0) | (RET_WS_ROTATION if rotation else 0)
+
+
+def workspace_bytes(fn, B, H, N, dk, dv, in_dtype, out_dtype, chunk=0, groupnorm=False, rotation=False):
     lib = load_library()
     shp = _shape(B, H, N, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype))
-    n = lib.retention_workspace_bytes(fn, ctypes.byref(shp), int(chunk), int(bool(groupnorm)))
+    n = lib.retention_workspace_bytes(fn, ctypes.byref(shp), int(chunk), _flags(groupnorm, rotation))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid shape for workspace query")
     return n
@@ -166,8 +191,8 @@ def _workspace(nbytes, device, workspace):
 
 
 def chunkwise_fwd(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None, groupnorm: Optional[GroupNorm] = None,
-                  out=None, state_out=None, out_dtype=torch.float32, want_out=True, want_state=True, workspace=None,
-                  stream=None):
+                  rotation: Optional[Rotation] = None, out=None, state_out=None, out_dtype=torch.float32, want_out=True,
+                  want_state=True, workspace=None, stream=None):
     """Chunkwise retention forward. q, k: [B,H,N,dk]; v: [B,H,N,dv] (fp32 or bf16, device).
     Returns (out [B,H,N,dv] of out_dtype or None, state_out fp32 [B,H,dk,dv] or None).
     state_out may be passed as the same tensor as state_in (in place)."""
@@ -190,21 +215,23 @@ def chunkwise_fwd(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None,
     gn = groupnorm.as_struct(q.dtype, (B, H, N, dv)) if groupnorm is not None else None
     shp = _shape(B, H, N, dk, dv, in_code, out_code)
     need = lib.retention_workspace_bytes(RET_FN_CHUNKWISE, ctypes.byref(shp), int(chunk),
-                                         int(gn is not None and out is not None))
+                                         _flags(gn is not None and out is not None, rotation is not None))
     if need == ctypes.c_size_t(-1).value:
         need = 0  # the call itself reports the invalid argument
     ws, wsb = _workspace(need, q.device, workspace)
     st = lib.retention_chunkwise_fwd(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H),
-                                     _ptr(state_in), ctypes.byref(gn) if gn is not None else None, _ptr(out),
+                                     _rot(rotation), _ptr(state_in), ctypes.byref(gn) if gn is not None else None, _ptr(out),
                                      _ptr(state_out), _ptr(ws), wsb, _stream(q.device, stream))
     _check(st)
     return out, state_out
 
 
-def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optional[GroupNorm] = None, out=None,
-                   out_dtype=torch.float32, want_out=True, stream=None):
+def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optional[GroupNorm] = None,
+                   rotation: Optional[Rotation] = None, out=None, out_dtype=torch.float32, want_out=True, workspace=None,
+                   stream=None):
     """One recurrent step: state <- g*state + k^T v (in place), o = q state.
-    q, k: [B,H,dk]; v: [B,H,dv]; state: fp32 [B,H,dk,dv]. Returns o [B,H,dv] (or None)."""
+    q, k: [B,H,dk]; v: [B,H,dv]; state: fp32 [B,H,dk,dv]. Returns o [B,H,dv] (or None).
+    With a rotation, rotation.offset is the position of this token."""
     lib = load_library()
     _check_inputs(q, k, v, 3)
     B, H, dk = q.shape
@@ -219,15 +246,19 @@ def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optiona
         out = None
     gn = groupnorm.as_struct(q.dtype, (B, H, dv)) if groupnorm is not None else None
     shp = _shape(B, H, 1, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
-    st = lib.retention_recurrent_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _ptr(state),
-                                      ctypes.byref(gn) if gn is not None else None, _ptr(out), None, 0,
+    need = lib.retention_workspace_bytes(RET_FN_RECURRENT_STEP, ctypes.byref(shp), 0, _flags(False, rotation is not None))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0
+    ws, wsb = _workspace(need, q.device, workspace)
+    st = lib.retention_recurrent_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _rot(rotation),
+                                      _ptr(state), ctypes.byref(gn) if gn is not None else None, _ptr(out), _ptr(ws), wsb,
                                       _stream(q.device, stream))
     _check(st)
     return out
 
 
-def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNorm] = None, out=None,
-                 out_dtype=torch.float32, workspace=None, stream=None):
+def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNorm] = None,
+                 rotation: Optional[Rotation] = None, out=None, out_dtype=torch.float32, workspace=None, stream=None):
     """Parallel form O = (Q K^T (.) D) V. Returns out [B,H,N,dv]."""
     lib = load_library()
     _check_inputs(q, k, v, 4)
@@ -239,22 +270,23 @@ def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNo
         out = torch.empty((B, H, N, dv), dtype=out_dtype, device=q.device)
     gn = groupnorm.as_struct(q.dtype, (B, H, N, dv)) if groupnorm is not None else None
     shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
-    need = lib.retention_workspace_bytes(RET_FN_PARALLEL, ctypes.byref(shp), 0, int(gn is not None))
+    need = lib.retention_workspace_bytes(RET_FN_PARALLEL, ctypes.byref(shp), 0, _flags(gn is not None, rotation is not None))
     if need == ctypes.c_size_t(-1).value:
         need = 0
     ws, wsb = _workspace(need, q.device, workspace)
-    st = lib.retention_parallel_fwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H),
+    st = lib.retention_parallel_fwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _rot(rotation),
                                     ctypes.byref(gn) if gn is not None else None, _ptr(out), _ptr(ws), wsb,
                                     _stream(q.device, stream))
     _check(st)
     return out
 
 
-def chunkwise_bwd(q, k, v, gamma: Sequence[float], dout, chunk: int, *, state_in=None, want=("dq", "dk", "dv", "dstate_in"),
-                  workspace=None, stream=None):
+def chunkwise_bwd(q, k, v, gamma: Sequence[float], dout, chunk: int, *, state_in=None, rotation: Optional[Rotation] = None,
+                  want=("dq", "dk", "dv", "dstate_in"), workspace=None, stream=None):
     """Gradients of chunkwise retention for dL/dout = dout (the pre-norm output): fp32 dq, dk, dv
     (shaped like q, k, v) and dstate_in ([B,H,dk,dv]); the names not in `want` come back None.
-    dout is laid out like v, in the input dtype."""
+    dout is laid out like v, in the input dtype. With a rotation, dq and dk are the gradients with
+    respect to the unrotated q and k."""
     lib = load_library()
     _check_inputs(q, k, v, 4)
     B, H, N, dk = q.shape
@@ -267,11 +299,12 @@ def chunkwise_bwd(q, k, v, gamma: Sequence[float], dout, chunk: int, *, state_in
     dv_ = torch.empty((B, H, N, dv), **f32) if "dv" in want else None
     ds = torch.empty((B, H, dk, dv), **f32) if "dstate_in" in want else None
     shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), RET_F32)
-    need = lib.retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ctypes.byref(shp), int(chunk), 0)
+    need = lib.retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ctypes.byref(shp), int(chunk), _flags(False, rotation is not None))
     if need == ctypes.c_size_t(-1).value:
         need = 0
     ws, wsb = _workspace(need, q.device, workspace)
-    st = lib.retention_chunkwise_bwd(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _ptr(state_in),
+    st = lib.retention_chunkwise_bwd(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H), _rot(rotation),
+                                     _ptr(state_in),
                                      _ptr(dout), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(ds), _ptr(ws), wsb, _stream(q.device, stream))
     _check(st)
     return dq, dk_, dv_, ds

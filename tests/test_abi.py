@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.retention_abi_version() == 2
+    assert lib.retention_abi_version() == 3
     for s in range(5):
         assert lib.retention_status_string(s).decode().startswith("RET_")
     assert lib.retention_status_string(99).decode() == "unknown status"
@@ -48,14 +48,14 @@ def gam(vals):
     return (ctypes.c_double * len(vals))(*vals)
 
 
-def chunk(lib, shp=None, C=64, q=Q, k=K, v=V, g=None, sin=None, gn=None, out=OUT, sout=ST, ws=WS, wsb=1 << 40):
+def chunk(lib, shp=None, C=64, q=Q, k=K, v=V, g=None, sin=None, gn=None, out=OUT, sout=ST, ws=WS, wsb=1 << 40, rot=None):
     shp = shp if shp is not None else shape()
     g = g if g is not None else gam([0.9] * shp.heads)
-    return lib.retention_chunkwise_fwd(ctypes.byref(shp), C, q, k, v, g, sin, gn, out, sout, ws, wsb, None)
+    return lib.retention_chunkwise_fwd(ctypes.byref(shp), C, q, k, v, g, rot, sin, gn, out, sout, ws, wsb, None)
 
 
 def test_null_shape(lib):
-    assert lib.retention_chunkwise_fwd(None, 64, Q, K, V, gam([0.9]), None, None, OUT, ST, WS, 1 << 40, None) == R.RET_ERR_INVALID_ARG
+    assert lib.retention_chunkwise_fwd(None, 64, Q, K, V, gam([0.9]), None, None, None, OUT, ST, WS, 1 << 40, None) == R.RET_ERR_INVALID_ARG
     assert "shape" in lib.retention_last_error().decode()
 
 
@@ -97,7 +97,7 @@ def test_bad_gamma(lib, g):
 
 def test_null_gamma(lib):
     s = shape()
-    assert lib.retention_chunkwise_fwd(ctypes.byref(s), 64, Q, K, V, None, None, None, OUT, ST, WS, 1 << 40, None) == R.RET_ERR_INVALID_ARG
+    assert lib.retention_chunkwise_fwd(ctypes.byref(s), 64, Q, K, V, None, None, None, None, OUT, ST, WS, 1 << 40, None) == R.RET_ERR_INVALID_ARG
 
 
 def test_no_outputs(lib):
@@ -126,7 +126,7 @@ def test_unsupported_chunk_and_dims(lib):
     assert chunk(lib, shape(dk=48)) == R.RET_ERR_UNSUPPORTED
     assert chunk(lib, shape(i=R.RET_F32), C=256) == R.RET_ERR_UNSUPPORTED
     s = shape(dk=64, dv=64)
-    assert lib.retention_parallel_fwd(ctypes.byref(shape(dk=128, dv=64)), Q, K, V, gam([0.9, 0.9]), None, OUT, WS, 1 << 40,
+    assert lib.retention_parallel_fwd(ctypes.byref(shape(dk=128, dv=64)), Q, K, V, gam([0.9, 0.9]), None, None, OUT, WS, 1 << 40,
                                       None) == R.RET_ERR_UNSUPPORTED
     del s
 
@@ -159,7 +159,7 @@ def test_workspace(lib):
 def test_step_validation(lib):
     def step(shp, state=ST, out=OUT, g=None):
         g = g if g is not None else gam([0.9] * shp.heads)
-        return lib.retention_recurrent_step(ctypes.byref(shp), Q, K, V, g, state, None, out, None, 0, None)
+        return lib.retention_recurrent_step(ctypes.byref(shp), Q, K, V, g, None, state, None, out, None, 0, None)
     assert step(shape(N=2)) == R.RET_ERR_INVALID_ARG
     assert step(shape(N=1), state=None) == R.RET_ERR_INVALID_ARG
     assert step(shape(N=1, dv=6)) == R.RET_ERR_UNSUPPORTED
@@ -183,10 +183,10 @@ def test_error_is_thread_local(lib):
 
 
 def bwd(lib, shp=None, C=64, q=Q, k=K, v=V, dout=GW, sin=None, dq=OUT, dk=ST, dv=WS, ds=None, ws=ctypes.c_void_p(9 << 36),
-        wsb=1 << 40):
+        wsb=1 << 40, rot=None):
     shp = shp if shp is not None else shape()
-    return lib.retention_chunkwise_bwd(ctypes.byref(shp), C, q, k, v, gam([0.9] * shp.heads), sin, dout, dq, dk, dv, ds, ws, wsb,
-                                       None)
+    return lib.retention_chunkwise_bwd(ctypes.byref(shp), C, q, k, v, gam([0.9] * shp.heads), rot, sin, dout, dq, dk, dv, ds, ws,
+                                       wsb, None)
 
 
 def test_backward_validation(lib):
@@ -209,3 +209,45 @@ def test_backward_validation(lib):
     rows = s.batch * s.heads * s.seq_len
     assert need >= rows * (2 * s.d_k + 2 * s.d_v) * 2 + rows * max(s.d_k, s.d_v) * 4
     assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s), 0, 0) == ctypes.c_size_t(-1).value
+
+
+def rot(base=10000.0, offset=0, enabled=1):
+    return ctypes.byref(R.RetRotation(enabled, base, offset))
+
+
+@pytest.mark.parametrize("base,offset,err", [(0.0, 0, "base"), (-2.0, 0, "base"), (math.inf, 0, "base"), (math.nan, 0, "base"),
+                                             (10000.0, -1, "offset"), (10000.0, 1 << 31, "offset")])
+def test_rotation_validation(lib, base, offset, err):
+    assert chunk(lib, rot=rot(base, offset)) == R.RET_ERR_INVALID_ARG
+    assert err in lib.retention_last_error().decode()
+
+
+def test_rotation_shapes(lib):
+    # odd d_k cannot be paired; d_k above 256 has no constants slot; disabled rotation is ignored
+    s = shape(dk=63, i=R.RET_F32)
+    assert chunk(lib, s, rot=rot()) == R.RET_ERR_INVALID_ARG
+    assert "even" in lib.retention_last_error().decode()
+    s = R.RetShape(1, 2, 1, 514, 64, R.RET_F32, R.RET_F32)
+    assert lib.retention_recurrent_step(ctypes.byref(s), Q, K, V, gam([0.9, 0.9]), rot(), ST, None, OUT, WS, 1 << 40,
+                                        None) == R.RET_ERR_UNSUPPORTED
+    assert chunk(lib, shape(dk=48), rot=rot(enabled=0)) == R.RET_ERR_UNSUPPORTED  # the d_k check, not the rotation's
+    assert "chunkwise" in lib.retention_last_error().decode()
+    assert bwd(lib, rot=rot(offset=-5)) == R.RET_ERR_INVALID_ARG
+
+
+def test_rotation_workspace(lib):
+    # a rotation stages the rotated q and k (input dtype, each copy 256-byte aligned) in front
+    for fn, C in ((R.RET_FN_CHUNKWISE, 64), (R.RET_FN_PARALLEL, 0), (R.RET_FN_CHUNKWISE_BWD, 64)):
+        s = shape()
+        base = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, 0)
+        with_rot = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION)
+        copy = s.batch * s.heads * s.seq_len * s.d_k * 2
+        assert with_rot == base + 2 * ((copy + 255) // 256 * 256), fn
+    s = shape(N=1)
+    assert lib.retention_workspace_bytes(R.RET_FN_RECURRENT_STEP, ctypes.byref(s), 0, R.RET_WS_ROTATION) == 2 * 256
+    assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(shape()), 64, 4) == ctypes.c_size_t(-1).value
+    # the step checks its workspace only when a rotation is on
+    assert lib.retention_recurrent_step(ctypes.byref(s), Q, K, V, gam([0.9, 0.9]), rot(), ST, None, OUT, None, 0,
+                                        None) == R.RET_ERR_WORKSPACE
+    need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(shape()), 64, R.RET_WS_ROTATION)
+    assert chunk(lib, wsb=need - 1, rot=rot()) == R.RET_ERR_WORKSPACE

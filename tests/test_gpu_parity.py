@@ -423,3 +423,152 @@ def test_backward_layer_6p7b(orc):
         lhs = float((dod.double() * fo.double()).sum())
         rhs = float((grad.double() * d.double()).sum())
         report(f"layer backward adjoint identity {name}", abs(lhs - rhs) / abs(lhs), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------------------------
+# Positional rotation of q and k (rotary reading): every form against the oracle's rotation
+# followed by its recurrence, with position offsets carried across split calls and decode steps.
+def test_rotation_all_forms_fp32(orc):
+    B, H, N, dk, dv, off, base = 2, 3, 250, 64, 128, 37, 10000.0
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "f32", seed=600)
+    s0 = I.make_state(B, H, dk, dv, seed=601, scale=0.05)
+    gam = [0.5, 0.95, 1.0]
+    ref, ref_s = orc.recurrent_rot(q, k, v, gam, base, off, state_in=s0)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    rot = R.Rotation(base, off)
+    for C in (64, 128):
+        o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, rotation=rot)
+        report(f"rotated fp32 chunkwise C={C} out", rel_err(o, ref), TOL["f32"])
+        report(f"rotated fp32 chunkwise C={C} state", rel_err(s, ref_s), TOL["f32"])
+    ref_p, _ = orc.recurrent_rot(q, k, v, gam, base, off)
+    report("rotated fp32 parallel", rel_err(R.parallel_fwd(qd, kd, vd, gam, rotation=rot), ref_p), TOL["f32"])
+    st = s0d.clone()
+    outs = [R.recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(), vd[:, :, n].contiguous(), gam, st,
+                             rotation=R.Rotation(base, off + n)) for n in range(N)]
+    report("rotated fp32 recurrent steps out", rel_err(torch.stack(outs, dim=2), ref), TOL["f32"])
+    report("rotated fp32 recurrent steps state", rel_err(st, ref_s), TOL["f32"])
+    o, _ = R.chunkwise_fwd(qd, kd, vd, gam, 64, state_in=s0d, rotation=rot, groupnorm=R.GroupNorm(1e-5))
+    report("rotated fp32 chunkwise GN", rel_err(o, orc.groupnorm(ref, 1e-5)), TOL["f32"])
+    # the rotation is not a no-op at this size
+    o0, _ = R.chunkwise_fwd(qd, kd, vd, gam, 64, state_in=s0d)
+    assert rel_err(o0, ref) > 1e-2
+
+
+# bf16 inputs: the rotated q and k enter the matrix cores as bf16, so they are rounded once after
+# the rotation (as in any bf16 implementation of the rotary embedding). The asserted check runs the
+# oracle on q and k rotated in fp64 and rounded to bf16 on the CPU (no GPU value involved), at the
+# bf16 bound. Against the exact rotation the error then stays within the triangle-inequality bound
+# tol * RMS(rounded) / RMS(exact) + the rounding's own effect, both computed by the oracle.
+def _rot_bf16(orc, x, base, off):
+    return torch.from_numpy(orc.rotate(x, base, off)).to(torch.float32).to(torch.bfloat16)
+
+
+def rot_report(name, gpu, ref_rounded, ref_exact, tol):
+    report(f"{name} (oracle on rotated operands rounded to bf16)", rel_err(gpu, ref_rounded), tol)
+    rms = lambda a: float(np.sqrt(np.mean(np.asarray(a, dtype=np.float64) ** 2)))
+    bound = tol * rms(ref_rounded) / rms(ref_exact) + rel_err(torch.from_numpy(np.asarray(ref_rounded)), ref_exact)
+    report(f"{name} (exact rotation, derived bound)", rel_err(gpu, ref_exact), bound)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
+@pytest.mark.parametrize("N,C,off", [(37, 64, 0), (700, 256, 1000), (1100, 512, 123457)])
+def test_rotation_bf16_chunkwise(orc, dk, dv, N, C, off):
+    B, H = 1, 4
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=610 + N + dk)
+    s0 = I.make_state(B, H, dk, dv, seed=611, scale=0.02)
+    gam = I.multiscale_gammas(H)
+    qr, kr = _rot_bf16(orc, q, 10000.0, off), _rot_bf16(orc, k, 10000.0, off)
+    ref, ref_s = orc.recurrent(qr, kr, v, gam, state_in=s0)
+    ex, ex_s = orc.recurrent_rot(q, k, v, gam, 10000.0, off, state_in=s0)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, rotation=R.Rotation(10000.0, off))
+    tag = f"rotated bf16 ({dk},{dv}) N={N} C={C} offset {off}"
+    rot_report(f"{tag} out", o, ref, ex, TOL["bf16"])
+    rot_report(f"{tag} state", s, ref_s, ex_s, TOL["bf16"])
+    ref_p, _ = orc.recurrent(qr, kr, v, gam)
+    ex_p, _ = orc.recurrent_rot(q, k, v, gam, 10000.0, off)
+    rot_report(f"rotated bf16 parallel ({dk},{dv}) N={N}", R.parallel_fwd(qd, kd, vd, gam, rotation=R.Rotation(10000.0, off)),
+               ref_p, ex_p, TOL["bf16"])
+
+
+# The N=8192 layer with rotation, GroupNorm and bf16 out (the launch configuration of the
+# benchmark's rotated call), against the oracle on every head; and, at full size, the property the
+# rotation exists for: with zero start state the output does not depend on the position offset
+# (up to the rounding of the rotated operands, which differs between offsets).
+def test_rotation_layer_6p7b(orc):
+    w = I.WORKLOADS["retention_b1_h16_n8192_dk256_dv512_bf16_gn"]
+    q, k, v = I.make_workload_qkv(w)
+    gam = w.gamma_list()
+    qd, kd, vd = dev(q, k, v)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=R.GroupNorm(w.eps), out_dtype=torch.bfloat16,
+                           rotation=R.Rotation(10000.0, 0))
+    o2, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, want_state=False, rotation=R.Rotation(10000.0, 5000))
+    torch.cuda.synchronize()
+    ref, ref_s = orc.recurrent(_rot_bf16(orc, q, 10000.0, 0), _rot_bf16(orc, k, 10000.0, 0), v, gam)
+    ex, ex_s = orc.recurrent_rot(q, k, v, gam, 10000.0, 0)
+    ref_gn = orc.groupnorm(ref, w.eps)
+    rot_report("rotated layer GN bf16 out", o, ref_gn, orc.groupnorm(ex, w.eps), TOL["bf16"])
+    # most of that is the bf16 storage of the normalised output; the kernels' own share is small
+    floor = rel_err(torch.from_numpy(ref_gn).to(torch.bfloat16), ref_gn)
+    report("rotated layer GN bf16 out above the bf16 storage floor", rel_err(o, ref_gn) - floor, 5e-3)
+    rot_report("rotated layer state", s, ref_s, ex_s, TOL["bf16"])
+    ref2, _ = orc.recurrent(_rot_bf16(orc, q, 10000.0, 5000), _rot_bf16(orc, k, 10000.0, 5000), v, gam, want_state=False)
+    rot_report("rotated layer fp32 out at offset 5000 (exact: the offset-0 oracle)", o2, ref2, ex, TOL["bf16"])
+
+
+def test_rotation_split_resume_and_decode(orc):
+    B, H, N, dk, dv = 1, 16, 1500, 256, 512
+    q, k, v = I.make_qkv(B, H, N + 1, dk, dv, "bf16", seed=620)
+    gam = I.multiscale_gammas(H)
+    ref, ref_s = orc.recurrent(_rot_bf16(orc, q, 10000.0, 0), _rot_bf16(orc, k, 10000.0, 0), v, gam)
+    ex, ex_s = orc.recurrent_rot(q, k, v, gam, 10000.0, 0)
+    qd, kd, vd = dev(q, k, v)
+    n1 = 700
+    a, sa = R.chunkwise_fwd(qd[:, :, :n1].contiguous(), kd[:, :, :n1].contiguous(), vd[:, :, :n1].contiguous(), gam, 128,
+                            rotation=R.Rotation(10000.0, 0))
+    b, sb = R.chunkwise_fwd(qd[:, :, n1:N].contiguous(), kd[:, :, n1:N].contiguous(), vd[:, :, n1:N].contiguous(), gam, 256,
+                            state_in=sa, rotation=R.Rotation(10000.0, n1))
+    rot_report("rotated split/resume out", torch.cat([a, b], dim=2), ref[:, :, :N], ex[:, :, :N], TOL["bf16"])
+    o = R.recurrent_step(qd[:, :, N].contiguous(), kd[:, :, N].contiguous(), vd[:, :, N].contiguous(), gam, sb,
+                         rotation=R.Rotation(10000.0, N))
+    rot_report("rotated decode after prefill out", o, ref[:, :, N], ex[:, :, N], TOL["bf16"])
+    rot_report("rotated decode after prefill state", sb, ref_s, ex_s, TOL["bf16"])
+
+
+# The decode workload (128 sequences x 16 heads, 256 x 512 fp32 states) at position 8192.
+def test_rotation_decode_workload(orc):
+    w = I.WORKLOADS["decode_b128_h16_dk256_dv512"]
+    gam = w.gamma_list()
+    B, H, dk, dv = w.B, w.H, w.dk, w.dv
+    state = I.make_state(B, H, dk, dv, seed=630, scale=0.02)
+    q, k, v = I.make_qkv(B, H, 1, dk, dv, "bf16", seed=631)
+    qd, kd, vd, sd = dev(q[:, :, 0], k[:, :, 0], v[:, :, 0], state)
+    o = R.recurrent_step(qd, kd, vd, gam, sd, rotation=R.Rotation(10000.0, I.DECODE_PREFILL_TOKENS))
+    P = I.DECODE_PREFILL_TOKENS
+    ro, rs = orc.step(_rot_bf16(orc, q, 10000.0, P)[:, :, 0], _rot_bf16(orc, k, 10000.0, P)[:, :, 0], v[:, :, 0], gam, state)
+    eo, es = orc.step(orc.rotate(q, 10000.0, P)[:, :, 0], orc.rotate(k, 10000.0, P)[:, :, 0], v[:, :, 0], gam, state)
+    rot_report("rotated decode out", o, ro, eo, TOL["bf16"])
+    rot_report("rotated decode state", sd, rs, es, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dt,B,H,N,dk,dv,C,off", [
+    ("f32", 1, 2, 256, 64, 64, 64, 11), ("bf16", 4, 8, 2048, 64, 64, 128, 0), ("bf16", 1, 4, 1000, 256, 512, 128, 4096)])
+def test_rotation_backward(orc, dt, B, H, N, dk, dv, C, off):
+    q, k, v = I.make_qkv(B, H, N, dk, dv, dt, seed=640 + N)
+    dout = _dout((B, H, N, dv), q.dtype, 641 + N)
+    s0 = I.make_state(B, H, dk, dv, seed=642, scale=0.02)
+    gam = [0.9, 0.99] if H == 2 and dt == "f32" else I.multiscale_gammas(H)
+    ex = orc.recurrent_rot_bwd(q, k, v, gam, dout, 10000.0, off, state_in=s0)
+    if dt == "bf16":
+        # gradients at the rounded rotated operands, turned back by the inverse rotation in fp64
+        gq, gk, gv, gs = orc.recurrent_bwd(_rot_bf16(orc, q, 10000.0, off), _rot_bf16(orc, k, 10000.0, off), v, gam, dout,
+                                           state_in=s0)
+        ref = (orc.rotate(gq, 10000.0, off, inverse=True), orc.rotate(gk, 10000.0, off, inverse=True), gv, gs)
+    qd, kd, vd, dod, s0d = dev(q, k, v, dout, s0)
+    got = R.chunkwise_bwd(qd, kd, vd, gam, dod, C, state_in=s0d, rotation=R.Rotation(10000.0, off))
+    for i, name in enumerate(("dq", "dk", "dv", "dstate_in")):
+        tag = f"rotated backward {dt} ({dk},{dv}) N={N} C={C} offset {off} {name}"
+        if dt == "bf16":
+            rot_report(tag, got[i], ref[i], ex[i], TOL[dt])
+        else:
+            report(tag, rel_err(got[i], ex[i]), TOL[dt])
