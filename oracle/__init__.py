@@ -31,6 +31,10 @@ def load(path: str = LIB):
     lib.oracle_recurrent_bwd.restype = None
     lib.oracle_rotate.argtypes = [ctypes.c_long, i, i, d, ctypes.c_longlong, i, _DP, _DP]
     lib.oracle_rotate.restype = None
+    lib.oracle_rla.argtypes = [i, i, i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, i, _DP, _DP, _DP]
+    lib.oracle_rla.restype = None
+    lib.oracle_rla_phi.argtypes = [ctypes.c_long, i, i, _DP, _DP]
+    lib.oracle_rla_phi.restype = None
     lib.oracle_threads.restype = i
     lib.oracle_set_threads.argtypes = [i]
     for f in (lib.oracle_recurrent, lib.oracle_parallel, lib.oracle_chunkwise, lib.oracle_groupnorm):
@@ -147,6 +151,37 @@ class Oracle:
         dq, dk, dv, ds = self.recurrent_bwd(self.rotate(q, base, offset), self.rotate(k, base, offset), v, gamma, dout,
                                             state_in)
         return self.rotate(dq, base, offset, inverse=True), self.rotate(dk, base, offset, inverse=True), dv, ds
+
+    FMAPS = {"identity": 0, "softmax": 1}
+
+    def rla_phi(self, x, fmap="softmax"):
+        """Feature map of residual linear attention over the last axis (softmax over the features,
+        or the identity)."""
+        x = _f64(x)
+        y = np.zeros_like(x)
+        self.lib.oracle_rla_phi(int(np.prod(x.shape[:-1])), x.shape[-1], self.FMAPS[fmap], _ptr(x), _ptr(y))
+        return y
+
+    def rla(self, q, k, v, window, fmap="softmax", k_prev=None, v_prev=None, prev_len=None, state_in=None):
+        """Residual linear attention over one segment: o_t = phi(q_t) S_(t-w-1), S_t = S_(t-1) +
+        phi(k_t)^T v_t. k_prev, v_prev: the window+1 positions before the segment ([B,H,window+1,d]),
+        of which the last prev_len (default: all) hold tokens, or None; state_in: the state over every
+        earlier token, or None. Returns (out, state_out)."""
+        q, k, v, kp, vp, s0 = map(_f64, (q, k, v, k_prev, v_prev, state_in))
+        if prev_len is None:
+            prev_len = 0 if kp is None else window + 1
+        if not 0 <= prev_len <= window + 1 or (prev_len > 0 and kp is None):
+            raise ValueError("prev_len must be in [0, window + 1], with k_prev and v_prev when positive")
+        B, H, N, dk, dv = self._dims(q, v)
+        if (kp is None) != (vp is None):
+            raise ValueError("k_prev and v_prev come together")
+        if kp is not None and (kp.shape != (B, H, window + 1, dk) or vp.shape != (B, H, window + 1, dv)):
+            raise ValueError("k_prev, v_prev must be [B, H, window + 1, d]")
+        out = np.zeros((B, H, N, dv))
+        st = np.zeros((B, H, dk, dv))
+        self.lib.oracle_rla(B, H, N, dk, dv, int(window), self.FMAPS[fmap], _ptr(q), _ptr(k), _ptr(v), _ptr(kp), _ptr(vp),
+                            int(prev_len), _ptr(s0), _ptr(out), _ptr(st))
+        return out, st
 
     def step(self, q, k, v, gamma, state):
         """One recurrent decode step. q, k: [B,H,dk]; v: [B,H,dv]; state: [B,H,dk,dv].

@@ -331,3 +331,88 @@ void oracle_rotate(long rows, int N, int d, double base, long long offset, int d
         }
     }
 }
+
+/*
+ * Feature map of residual linear attention (mengro1102.github.io RAttention post, section 4, the
+ * RLA formula and its notes: phi is a feature map, softmax-based works best). The page gives no
+ * formula; the reading taken is the softmax over the d features of one row,
+ *     phi(x)_i = exp(x_i) / sum_j exp(x_j),
+ * evaluated as exp(x_i - max x) / sum_j exp(x_j - max x). fmap 0 is the identity.
+ */
+static void rla_phi(int fmap, int d, const double* x, double* y) {
+    if (fmap == 0) {
+        for (int i = 0; i < d; ++i) y[i] = x[i];
+        return;
+    }
+    double m = x[0];
+    for (int i = 1; i < d; ++i) m = x[i] > m ? x[i] : m;
+    double s = 0.0;
+    for (int i = 0; i < d; ++i) {
+        y[i] = exp(x[i] - m);
+        s += y[i];
+    }
+    for (int i = 0; i < d; ++i) y[i] /= s;
+}
+
+void oracle_rla_phi(long rows, int d, int fmap, const double* x, double* y) {
+    for (long r = 0; r < rows; ++r) rla_phi(fmap, d, x + (size_t)r * d, y + (size_t)r * d);
+}
+
+/*
+ * Residual linear attention (same page, section 4, RLA formula):
+ *     S_t = S_(t-1) + phi(k_t)^T v_t,     o_t = phi(q_t) S_(t-w-1)
+ * i.e. the undecayed linear-attention state read w + 1 tokens late, so that o_t sees only the
+ * tokens that have left the sliding window of the last w tokens and t itself.
+ * One call covers positions 0 .. N-1 of a segment. The w + 1 positions before it (-(w+1) .. -1)
+ * are rows 0 .. w of kp, vp ([B][H][w+1][dk], [B][H][w+1][dv]), of which only the last prev_len
+ * hold tokens (positions -prev_len .. -1; the sequence starts after the others; prev_len = 0 and
+ * NULL kp, vp at the start of a sequence), and state_in (or 0) is S_(-w-2), the sum over every
+ * earlier token. With S_(t-w-1) = S_(t-w-2) + phi(k_(t-w-1))^T v_(t-w-1), the state read by o_t gains one
+ * token per step. state_out is the state the last output read, S_(N-w-2): every token that has
+ * left the window. It is the state_in of a following segment whose kp, vp are the last w + 1
+ * tokens of this one (positions N-w-1 .. N-1, which the next segment adds one per step). w >= 0.
+ */
+void oracle_rla(int B, int H, int N, int dk, int dv, int w, int fmap,
+                const double* q, const double* k, const double* v, const double* kp, const double* vp, int prev_len,
+                const double* state_in, double* out, double* state_out) {
+    const int P = w + 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        double* S = (double*)malloc((size_t)dk * dv * sizeof(double));
+        double* fq = (double*)malloc((size_t)dk * sizeof(double));
+        double* fk = (double*)malloc((size_t)dk * sizeof(double));
+        for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] = state_in ? state_in[(size_t)bh * dk * dv + e] : 0.0;
+        for (int t = 0; t < N; ++t) {
+            /* the token at position t - w - 1 joins the state that o_t reads */
+            const int p = t - P;
+            const double* kt = NULL;
+            const double* vt = NULL;
+            if (p < 0) {
+                if (kp && p >= -prev_len) {
+                    kt = kp + ((size_t)bh * P + (p + P)) * dk;
+                    vt = vp + ((size_t)bh * P + (p + P)) * dv;
+                }
+            } else {
+                kt = k + ((size_t)bh * N + p) * dk;
+                vt = v + ((size_t)bh * N + p) * dv;
+            }
+            if (kt) {
+                rla_phi(fmap, dk, kt, fk);
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += fk[i] * vt[j];
+            }
+            rla_phi(fmap, dk, q + ((size_t)bh * N + t) * dk, fq);
+            double* ot = out + ((size_t)bh * N + t) * dv;
+            for (int j = 0; j < dv; ++j) {
+                double a = 0.0;
+                for (int i = 0; i < dk; ++i) a += fq[i] * S[(size_t)i * dv + j];
+                ot[j] = a;
+            }
+        }
+        if (state_out)
+            for (size_t e = 0; e < (size_t)dk * dv; ++e) state_out[(size_t)bh * dk * dv + e] = S[e];
+        free(S);
+        free(fq);
+        free(fk);
+    }
+}

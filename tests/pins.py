@@ -20,7 +20,10 @@ Sources of truth used here:
   - the positional rotation: hand-worked rows (tests/golden/rotation_hand_worked.json) and the
     facts a rotation by p * theta_i must satisfy (position 0 is the identity, pair norms are kept,
     turning by a then b is turning by a + b, the inverse undoes it), plus the property the
-    rotation is used for: retention scores and outputs depend only on relative positions.
+    rotation is used for: retention scores and outputs depend only on relative positions;
+  - residual linear attention: hand-worked segments (tests/golden/rla_hand_worked.json), the
+    masked linear attention it equals (numpy's shifted tril, scipy's softmax), and the segment
+    and decode identities its window and state hand-over must satisfy.
 """
 import json
 import os
@@ -415,7 +418,85 @@ def pin_rotation_backward_fd(o):
             assert abs(fd - grads[t][idx]) <= 1e-8 * max(abs(fd), 1.0), ("rotated finite difference", t, idx, fd, grads[t][idx])
 
 
+def _num(x):
+    import math
+    return {"ln2": math.log(2.0), "ln3": math.log(3.0)}.get(x, x) if isinstance(x, str) else x
+
+
+def _arr(rows):
+    return np.array([[_num(x) for x in r] for r in rows], float)
+
+
+def pin_rla_hand_worked(o):
+    g = json.load(open(os.path.join(HERE, "golden", "rla_hand_worked.json")))
+    for c in g["cases"]:
+        ex = lambda key: _arr(c[key])[None, None] if key in c else None
+        out, st = o.rla(ex("q"), ex("k"), ex("v"), c["window"], c["fmap"], ex("k_prev"), ex("v_prev"), state_in=ex("state_in"))
+        assert np.allclose(out[0, 0], _arr(c["out"]), rtol=0, atol=1e-14), ("rla hand-worked out", c["what"], out[0, 0])
+        assert np.allclose(st[0, 0], _arr(c["state_out"]), rtol=0, atol=1e-14), ("rla hand-worked state", c["what"], st[0, 0])
+    for r in g["softmax_rows"]:
+        y = o.rla_phi(_arr([r["x"]]), "softmax")[0]
+        assert np.allclose(y, r["y"], rtol=0, atol=1e-15), ("softmax feature map", r, y)
+
+
+def pin_rla_masked_attention(o):
+    """With no earlier tokens and zero state, o = tril(phi(Q) phi(K)^T, -(w+1)) V: linear attention
+    with the diagonal and the w tokens before it masked out."""
+    from scipy.special import softmax
+    B, H, N, dk, dv = 1, 2, 40, 6, 5
+    q, k, v = _qkv(B, H, N, dk, dv, 161)
+    q, k = q * 4, k * 4  # a peaked softmax
+    for fmap, phi in (("identity", lambda x: x), ("softmax", lambda x: softmax(x, axis=-1))):
+        for w in (0, 1, 7, 39, 45):
+            out, st = o.rla(q, k, v, w, fmap)
+            for h in range(H):
+                A = np.tril(phi(q[0, h]) @ phi(k[0, h]).T, -(w + 1))
+                assert _rel(out[0, h], A @ v[0, h]) < 1e-12 or np.abs(out[0, h]).max() == 0 == np.abs(A @ v[0, h]).max(), \
+                    ("rla masked attention", fmap, w, h)
+                n_left = max(N - w - 1, 0)
+                want_s = phi(k[0, h, :n_left]).T @ v[0, h, :n_left]
+                assert np.allclose(st[0, h], want_s, rtol=1e-12, atol=1e-13), ("rla state out", fmap, w, h)
+    # softmax rows are positive, sum to 1, and do not change when a constant is added
+    y = o.rla_phi(q, "softmax")
+    assert np.all(y > 0) and np.allclose(y.sum(-1), 1.0, rtol=0, atol=1e-14), "softmax rows"
+    assert _rel(o.rla_phi(q + 3.25, "softmax"), y) < 1e-14, "softmax shift invariance"
+
+
+def pin_rla_segments(o):
+    """Two segments with the window and state handed over equal one pass, also when the first
+    segment is shorter than the window (a partial window, prev_len < w + 1); one-token segments
+    (decode steps) equal one pass."""
+    B, H, N, dk, dv = 1, 2, 60, 5, 4
+    q, k, v = _qkv(B, H, N, dk, dv, 171)
+    s0 = _rand((B, H, dk, dv), 172, 0.1)
+    for fmap in ("identity", "softmax"):
+        for w in (0, 3, 9):
+            full, sfull = o.rla(q, k, v, w, fmap, state_in=s0)
+            P = w + 1
+            for n1 in (2, 9, 30, 59):
+                a, sa = o.rla(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], w, fmap, state_in=s0)
+                # rows before the sequence start hold junk, which must not be read
+                kp, vp = _rand((B, H, P, dk), 173), _rand((B, H, P, dv), 174)
+                L = min(n1, P)
+                kp[:, :, P - L:], vp[:, :, P - L:] = k[:, :, n1 - L:n1], v[:, :, n1 - L:n1]
+                b, sb = o.rla(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], w, fmap, kp, vp, L, state_in=sa)
+                assert _rel(np.concatenate([a, b], axis=2), full) < 1e-12, ("rla split/resume out", fmap, w, n1)
+                assert _rel(sb, sfull) < 1e-12, ("rla split/resume state", fmap, w, n1)
+            # decode: one token per call, the window slid by the caller
+            st, outs = s0, []
+            for t in range(N):
+                kp, vp = _rand((B, H, P, dk), 175 + t), _rand((B, H, P, dv), 176 + t)
+                L = min(t, P)
+                if L:
+                    kp[:, :, P - L:], vp[:, :, P - L:] = k[:, :, t - L:t], v[:, :, t - L:t]
+                ot, st = o.rla(q[:, :, t:t + 1], k[:, :, t:t + 1], v[:, :, t:t + 1], w, fmap, kp, vp, L, state_in=st)
+                outs.append(ot)
+            assert _rel(np.concatenate(outs, axis=2), full) < 1e-12, ("rla decode steps out", fmap, w)
+            assert _rel(st, sfull) < 1e-12, ("rla decode steps state", fmap, w)
+
+
 PINS = [pin_hand_worked, pin_closed_form, pin_gamma_one, pin_tiny_gamma, pin_bruteforce, pin_three_forms,
         pin_split_resume, pin_decode_after_prefill, pin_linearity, pin_groupnorm, pin_swish_gate,
         pin_backward_adjoint, pin_backward_fd, pin_backward_bruteforce, pin_rotation_hand_worked,
-        pin_rotation_properties, pin_rotation_retention, pin_rotation_backward_fd]
+        pin_rotation_properties, pin_rotation_retention, pin_rotation_backward_fd, pin_rla_hand_worked,
+        pin_rla_masked_attention, pin_rla_segments]

@@ -41,7 +41,8 @@ MUTANTS = [
     ("bwd_dstate_no_gamma", "dstate_in[(size_t)bh * dk * dv + e] = g * U[e];", "dstate_in[(size_t)bh * dk * dv + e] = U[e];"),
     ("bwd_dk_uses_dout", "a += U[(size_t)i * dv + j] * vn[j];", "a += U[(size_t)i * dv + j] * gn[j];"),
     ("bwd_dv_uses_q", "a += kn[i] * U[(size_t)i * dv + j];", "a += qn[i] * U[(size_t)i * dv + j];"),
-    ("bwd_dq_ignores_state_in", "S[e] = state_in ? state_in[(size_t)bh * dk * dv + e] : 0.0;", "S[e] = 0.0;"),
+    ("bwd_dq_ignores_state_in", "S[e] = state_in ? state_in[(size_t)bh * dk * dv + e] : 0.0;\n        for (int n = 0; n < N; ++n) {",
+     "S[e] = 0.0;\n        for (int n = 0; n < N; ++n) {"),
     ("gate_sigmoid_not_swish", "yr[c] *= g / (1.0 + exp(-g));", "yr[c] *= 1.0 / (1.0 + exp(-g));"),
     ("gate_sigmoid_sign", "yr[c] *= g / (1.0 + exp(-g));", "yr[c] *= g / (1.0 + exp(g));"),
     ("gate_wrong_index", "const double g = gate[(size_t)r * dv + c];", "const double g = gate[c];"),
@@ -57,6 +58,18 @@ MUTANTS = [
     ("rot_half_split_pairs", "const double a = xn[2 * i], b = xn[2 * i + 1];\n                yn[2 * i] = a * c - b * s;\n                yn[2 * i + 1] = a * s + b * c;",
      "const double a = xn[i], b = xn[i + d / 2];\n                yn[i] = a * c - b * s;\n                yn[i + d / 2] = a * s + b * c;"),
     ("rot_inverse_not_negated", "(direction < 0 ? -1.0 : 1.0)", "1.0"),
+    ("rla_reads_one_token_late", "const int p = t - P;", "const int p = t - P + 1;"),
+    ("rla_reads_one_token_early", "const int p = t - P;", "const int p = t - P - 1;"),
+    ("rla_softmax_unnormalised", "for (int i = 0; i < d; ++i) y[i] /= s;", "(void)s;"),
+    ("rla_softmax_sign", "y[i] = exp(x[i] - m);", "y[i] = exp(m - x[i]);"),
+    ("rla_q_not_mapped", "rla_phi(fmap, dk, q + ((size_t)bh * N + t) * dk, fq);",
+     "rla_phi(0, dk, q + ((size_t)bh * N + t) * dk, fq);"),
+    ("rla_k_not_mapped", "rla_phi(fmap, dk, kt, fk);", "rla_phi(0, dk, kt, fk);"),
+    ("rla_prev_window_ignored", "if (kp && p >= -prev_len) {", "if (0) {"),
+    ("rla_prev_len_ignored", "if (kp && p >= -prev_len) {", "if (kp) {"),
+    ("rla_prev_rows_reversed", "kt = kp + ((size_t)bh * P + (p + P)) * dk;", "kt = kp + ((size_t)bh * P + (-1 - p)) * dk;"),
+    ("rla_ignores_state_in", "S[e] = state_in ? state_in[(size_t)bh * dk * dv + e] : 0.0;\n        for (int t = 0; t < N; ++t) {",
+     "S[e] = 0.0;\n        for (int t = 0; t < N; ++t) {"),
 ]
 
 
