@@ -18,9 +18,10 @@ Counting rules:
   backward algorithmic bytes: bf16 q, k, v, dout read; fp32 dq, dk, dv written
 
 Beside the step, outside its timed region: the same chunkwise call with a swish gate after the
-GroupNorm, the chunkwise call and the decode step with the positional rotation of q and k, and the
-chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout, each timed over the same K
-calls.
+GroupNorm, the chunkwise call and the decode step with the positional rotation of q and k, residual
+linear attention at the same shape (512-token window, softmax feature map; its rate is counted with
+the chunkwise FLOPs), and the chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout,
+each timed over the same K calls.
 """
 import argparse
 import json
@@ -54,6 +55,9 @@ def backward_flops(B, H, N, dk, dv, C):
         L = min(C, N - c0)
         pairs += L * (L + 1) // 2
     return B * H * (2 * (3 * dk + 2 * dv) * pairs + 10 * N * dk * dv)
+
+
+RLA_WINDOW = 512  # the window the RAttention page reports matching full attention with
 
 
 def time_calls(fn, n, stream, torch):
@@ -248,6 +252,13 @@ def main():
     tb_drot, t_drot = time_pair(lambda: R.recurrent_step(qn, kn, vn, dgam, state, out=dout, stream=stream),
                                 lambda: R.recurrent_step(qn, kn, vn, dgam, state, rotation=drot, out=dout, workspace=dws,
                                                          stream=stream), args.steps, stream, torch)
+    # residual linear attention at the layer shape: 512-token window, softmax feature map
+    rla_ws = torch.empty(R.workspace_bytes(R.RET_FN_RLA, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.float32, C),
+                         dtype=torch.uint8, device=dev)
+    rla_out = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
+    t_rla = time_calls(lambda: R.rla_fwd(q, k, v, RLA_WINDOW, C, out=rla_out, state_out=st_out, workspace=rla_ws, stream=stream),
+                       args.steps, stream, torch)
+    del rla_ws, rla_out
     gdo = (torch.randn((w.B, w.H, w.N, w.dv), generator=torch.Generator().manual_seed(8))).to(torch.bfloat16).to(dev)
     bws = torch.empty(R.workspace_bytes(R.RET_FN_CHUNKWISE_BWD, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.float32, C),
                       dtype=torch.uint8, device=dev)
@@ -262,7 +273,7 @@ def main():
                                  "linear_recurrent_sequence_chunkwise_amd/csrc/chunkwise_bf16.hip",
                                  "linear_recurrent_sequence_chunkwise_amd/csrc/common.hpp"])
     log(f"gated chunkwise {t_gate * 1e6:.1f} us; rotated chunkwise {t_rot * 1e6:.1f} us; rotated decode {t_drot * 1e6:.1f} us; "
-        f"backward {t_bwd * 1e6:.1f} us")
+        f"rla {t_rla * 1e6:.1f} us; backward {t_bwd * 1e6:.1f} us")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -295,6 +306,9 @@ def main():
         "swish_gate": {"chunkwise_gated_us": round(t_gate * 1e6, 2), "gate_extra_us": round((t_gate - tb_gate) * 1e6, 2)},
         "rotation": {"chunkwise_rotated_us": round(t_rot * 1e6, 2), "rotation_extra_us": round((t_rot - tb_rot) * 1e6, 2),
                      "decode_rotated_us": round(t_drot * 1e6, 2), "decode_rotation_extra_us": round((t_drot - tb_drot) * 1e6, 2)},
+        "rla": {"workload": f"residual linear attention, B=1 H=16 N=8192 d_k=256 d_v=512, window {RLA_WINDOW}, softmax "
+                            "feature map, chunk 128, fp32 out", "us": round(t_rla * 1e6, 2),
+                "tflops": round(cf / t_rla / 1e12, 3), "tokens_per_s": round(w.B * w.N / t_rla, 1)},
         "backward": {"workload": "dq, dk, dv of the chunkwise workload (bf16 dout, fp32 gradients)",
                      "us": round(t_bwd * 1e6, 2), "tflops": round(bf / t_bwd / 1e12, 3), "algorithmic_flops": bf,
                      "mfma_frac": round(bf / t_bwd / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),

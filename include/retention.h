@@ -57,7 +57,16 @@ typedef enum {
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
 
-typedef enum { RET_FN_CHUNKWISE = 0, RET_FN_RECURRENT_STEP = 1, RET_FN_PARALLEL = 2, RET_FN_CHUNKWISE_BWD = 3 } ret_fn;
+typedef enum {
+    RET_FN_CHUNKWISE = 0,
+    RET_FN_RECURRENT_STEP = 1,
+    RET_FN_PARALLEL = 2,
+    RET_FN_CHUNKWISE_BWD = 3,
+    RET_FN_RLA = 4
+} ret_fn;
+
+/* Feature maps of residual linear attention. */
+typedef enum { RET_FMAP_IDENTITY = 0, RET_FMAP_SOFTMAX = 1 } ret_feature_map;
 
 /* Flags of retention_workspace_bytes(): the epilogue and prologue settings of the call. */
 #define RET_WS_GROUPNORM 1
@@ -181,6 +190,38 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
                                    const float* state_in, const void* dout,
                                    float* dq, float* dk, float* dv, float* dstate_in,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Residual linear attention, RLA (mengro1102.github.io RAttention post, section 4, RLA formula and
+ * notes): the undecayed linear-attention state read w + 1 tokens late,
+ *   S_t = S_(t-1) + phi(k_t)^T v_t,   o_t = phi(q_t) S_(t-w-1)
+ * so that o_t sees only the tokens that have left a sliding window of the last w tokens and t
+ * itself (the window's own attention is out of scope). phi (feature_map): RET_FMAP_SOFTMAX, the
+ * softmax over the d_k features of each row (the page calls the best map softmax-based and gives
+ * no formula), or RET_FMAP_IDENTITY.
+ * One call covers a segment of N tokens, positions 0 .. N-1:
+ *   k_prev, v_prev: [B][H][window+1][d_k] and [B][H][window+1][d_v], the window+1 positions before
+ *     the segment (rows in time order); only the last prev_len rows hold tokens (the sequence
+ *     starts after the others, which are never read). prev_len = 0 at the start of a sequence,
+ *     where k_prev and v_prev may be NULL. 0 <= prev_len <= window + 1.
+ *   state_in: fp32 [B][H][d_k][d_v], the sum of phi(k)^T v over every token before the window
+ *     rows (NULL: zero).
+ *   state_out: the sum over every token that has left the window at the end of the segment, i.e.
+ *     the state the last output read. With the last window+1 tokens as the next k_prev, v_prev, it
+ *     is the next segment's state_in. A decode step is a segment of N = 1 whose k_prev row 0 is the
+ *     token leaving the window; it runs on the decode-step kernel and needs state_out (which may
+ *     equal state_in: the state is then advanced in place).
+ * q, k, v, out: as retention_chunkwise_fwd. window >= 0. d_k <= 256. N > 1 takes the chunkwise
+ * kernels (chunk and (d_k, d_v) as there); N = 1 the decode-step kernel (d_v as there).
+ * Workspace: retention_workspace_bytes(RET_FN_RLA, ...): phi(q), the shifted phi(k) and v in the
+ * input dtype, plus the chunkwise workspace. For bf16 inputs phi(q) and phi(k) are rounded to bf16
+ * before the matrix cores.
+ */
+ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t window, int32_t feature_map,
+                             const void* q, const void* k, const void* v,
+                             const void* k_prev, const void* v_prev, int32_t prev_len,
+                             const float* state_in, void* out, float* state_out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Bytes of device workspace the call `fn` needs for this shape, chunk and flags (a bitwise OR of
  * RET_WS_GROUPNORM when a GroupNorm epilogue is enabled and RET_WS_ROTATION when a rotation is).

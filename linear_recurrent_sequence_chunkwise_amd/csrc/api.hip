@@ -180,6 +180,14 @@ size_t chunkwise_ws(const ret_shape* s, int chunk, int gn, int want_out) {
     return want_out ? ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16) : 0;
 }
 
+// Residual linear attention: phi(q), the shifted phi(k) and v (input dtype, each 256-byte
+// aligned), then the chunkwise workspace for N > 1 (no GroupNorm).
+size_t rla_ws(const ret_shape* s, int chunk) {
+    const size_t rows = (size_t)s->batch * s->heads * s->seq_len, es = elem_size(s->in_dtype);
+    const size_t ops = 2 * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
+    return ops + (s->seq_len > 1 ? chunkwise_ws(s, chunk, 0, 1) : 0);
+}
+
 size_t parallel_ws(const ret_shape* s, int gn) {
     if (s->in_dtype == RET_BF16) return 0;
     return ret::parallel_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16);
@@ -227,6 +235,9 @@ size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chu
             if (chunk <= 0) return (size_t)-1;
             return rot + ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len,
                                                       shape->d_k, shape->d_v, chunk);
+        case RET_FN_RLA:
+            if (shape->seq_len > 1 && chunk <= 0) return (size_t)-1;
+            return rla_ws(shape, chunk);
         default: return (size_t)-1;
     }
 }
@@ -416,6 +427,85 @@ ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const v
     a.q = q; a.k = k; a.v = v; a.out = out;
     hipError_t e = bf ? ret::launch_parallel_bf16(a) : ret::launch_parallel_f32(a);
     return device_status(e, "retention_parallel_fwd launch");
+}
+
+ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t window, int32_t feature_map, const void* q,
+                             const void* k, const void* v, const void* k_prev, const void* v_prev, int32_t prev_len,
+                             const float* state_in, void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+    g_err[0] = '\0';
+    RET_TRY(check_shape(shape, false));
+    RET_TRY(check_ptr(q, "q", true));
+    RET_TRY(check_ptr(k, "k", true));
+    RET_TRY(check_ptr(v, "v", true));
+    RET_TRY(check_ptr(state_in, "state_in", false));
+    RET_TRY(check_ptr(out, "out", false));
+    RET_TRY(check_ptr(state_out, "state_out", false));
+    if (window < 0 || window > (1 << 30)) return fail(RET_ERR_INVALID_ARG, "window must be in [0, 2^30] (got %d)", window);
+    if (feature_map != RET_FMAP_IDENTITY && feature_map != RET_FMAP_SOFTMAX)
+        return fail(RET_ERR_INVALID_ARG, "feature_map must be RET_FMAP_IDENTITY or RET_FMAP_SOFTMAX (got %d)", feature_map);
+    const int P = window + 1;
+    if (prev_len < 0 || prev_len > P) return fail(RET_ERR_INVALID_ARG, "prev_len must be in [0, window + 1] (got %d)", prev_len);
+    RET_TRY(check_ptr(k_prev, "k_prev", prev_len > 0));
+    RET_TRY(check_ptr(v_prev, "v_prev", prev_len > 0));
+    if (!out && !state_out) return fail(RET_ERR_INVALID_ARG, "out and state_out are both NULL");
+    if (shape->d_k > 256) return fail(RET_ERR_UNSUPPORTED, "residual linear attention supports d_k <= 256 (got %d)", shape->d_k);
+    const bool bf = shape->in_dtype == RET_BF16;
+    const int N = shape->seq_len, dv = shape->d_v;
+    if (N == 1) {
+        if (!state_out) return fail(RET_ERR_INVALID_ARG, "a one-token segment (decode step) needs state_out");
+        if (dv % 4 != 0 || dv / 4 > 256 || 256 % (dv / 4) != 0)
+            return fail(RET_ERR_UNSUPPORTED, "a one-token segment needs d_v a multiple of 4 with d_v/4 dividing 256 (got %d)", dv);
+    } else {
+        if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+        if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, dv, chunk) : !ret::chunkwise_f32_supported(shape->d_k, dv, chunk))
+            return fail(RET_ERR_UNSUPPORTED, "residual linear attention: no chunkwise kernel for %s inputs with d_k %d, d_v %d, chunk %d",
+                        bf ? "bf16" : "fp32", shape->d_k, dv, chunk);
+    }
+    const size_t rows = (size_t)shape->batch * shape->heads * N;
+    const size_t es = elem_size(shape->in_dtype);
+    const size_t out_bytes = rows * dv * elem_size(shape->out_dtype);
+    const size_t pk = (size_t)shape->batch * shape->heads * P * shape->d_k * es, pv = (size_t)shape->batch * shape->heads * P * dv * es;
+    if (out && (overlaps(out, out_bytes, q, rows * shape->d_k * es) || overlaps(out, out_bytes, k, rows * shape->d_k * es) ||
+                overlaps(out, out_bytes, v, rows * dv * es) || (prev_len && overlaps(out, out_bytes, k_prev, pk)) ||
+                (prev_len && overlaps(out, out_bytes, v_prev, pv))))
+        return fail(RET_ERR_INVALID_ARG, "out must not alias q, k, v, k_prev or v_prev");
+    const size_t st_bytes = (size_t)shape->batch * shape->heads * shape->d_k * dv * sizeof(float);
+    if (state_out && out && overlaps(out, out_bytes, state_out, st_bytes)) return fail(RET_ERR_INVALID_ARG, "out must not alias state_out");
+    if (state_out && state_in && state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes))
+        return fail(RET_ERR_INVALID_ARG, "state_out may equal state_in but must not partly overlap it");
+    RET_TRY(check_ws(rla_ws(shape, chunk), workspace, workspace_bytes));
+
+    // operands: phi(q), shifted phi(k) and v, in the front of the workspace
+    const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* w = static_cast<char*>(workspace);
+    const size_t Aq = align256(rows * shape->d_k * es), Av = align256(rows * dv * es);
+    ret::RlaPrep r{};
+    r.rows = (long)rows; r.N = N; r.dk = shape->d_k; r.dv = dv; r.P = P; r.prev_len = prev_len; r.fmap = feature_map; r.bf16 = bf;
+    r.q = q; r.k = k; r.v = v; r.kp = k_prev; r.vp = v_prev;
+    r.qo = feature_map == RET_FMAP_IDENTITY ? nullptr : w;
+    r.ko = w + Aq;
+    r.vo = w + 2 * Aq;
+    hipError_t e = ret::launch_rla_prepare(r, st);
+    if (e != hipSuccess) return device_status(e, "retention_rla_fwd prepare launch");
+    ret::HeadConsts hc;
+    for (int h = 0; h < ret::kMaxHeads; ++h) {
+        hc.gamma[h] = 1.f;
+        hc.log2g[h] = 0.f;
+    }
+    ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, w + 2 * Aq + Av, workspace_bytes - (2 * Aq + Av),
+                                  hip_stream);
+    a.q = r.qo ? r.qo : q; a.k = r.ko; a.v = r.vo; a.out = out;
+    if (N == 1) {
+        if (state_in != state_out) {
+            e = ret::launch_copy_state(st_bytes / sizeof(float), state_in, state_out, st);
+            if (e != hipSuccess) return device_status(e, "retention_rla_fwd state copy launch");
+        }
+        a.state_out = state_out;
+        return device_status(ret::launch_recurrent_step(a), "retention_rla_fwd step launch");
+    }
+    a.state_in = state_in; a.state_out = state_out;
+    return device_status(bf ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
 }
 
 }  // extern "C"

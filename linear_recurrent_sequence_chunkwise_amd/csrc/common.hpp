@@ -231,4 +231,16 @@ hipError_t launch_chunkwise_bwd(const BwdArgs& b);
 // buffer. inverse != 0 turns by the opposite angles.
 hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc,
                          int inverse, hipStream_t stream);
+// Residual linear attention operands: qo = phi(q) (qo null: phi is the identity and q is used as
+// is), ko / vo = phi(k) / v shifted by P = window + 1 rows, the first rows from the window rows kp,
+// vp ([rows / N][P][d], of which the last prev_len hold tokens) or zero.
+struct RlaPrep {
+    long rows;  // B * H * N
+    int N, dk, dv, P, prev_len, fmap, bf16;
+    const void *q, *k, *v, *kp, *vp;
+    void *qo, *ko, *vo;
+};
+hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream);
+// dst = src, or zero when src is null (n floats, a multiple of 4, 16-byte aligned).
+hipError_t launch_copy_state(size_t n, const float* src, float* dst, hipStream_t stream);
 }  // namespace ret

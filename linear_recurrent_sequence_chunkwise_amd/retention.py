@@ -16,11 +16,13 @@ LIB_PATH = os.path.join(_PKG, "libretention.so")
 
 RET_OK, RET_ERR_INVALID_ARG, RET_ERR_UNSUPPORTED, RET_ERR_WORKSPACE, RET_ERR_DEVICE = range(5)
 RET_F32, RET_BF16 = 0, 1
-RET_FN_CHUNKWISE, RET_FN_RECURRENT_STEP, RET_FN_PARALLEL, RET_FN_CHUNKWISE_BWD = 0, 1, 2, 3
+RET_FN_CHUNKWISE, RET_FN_RECURRENT_STEP, RET_FN_PARALLEL, RET_FN_CHUNKWISE_BWD, RET_FN_RLA = 0, 1, 2, 3, 4
+RET_FMAP_IDENTITY, RET_FMAP_SOFTMAX = 0, 1
 RET_WS_GROUPNORM, RET_WS_ROTATION = 1, 2
 
 EXPORTED = [
     "retention_chunkwise_fwd", "retention_recurrent_step", "retention_parallel_fwd", "retention_chunkwise_bwd",
+    "retention_rla_fwd",
     "retention_workspace_bytes",
     "retention_status_string", "retention_last_error", "retention_abi_version",
 ]
@@ -65,7 +67,9 @@ def load_library(path: str = LIB_PATH):
     lib.retention_recurrent_step.argtypes = [sp, vp, vp, vp, dp, rp, vp, gp, vp, vp, sz, vp]
     lib.retention_parallel_fwd.argtypes = [sp, vp, vp, vp, dp, rp, gp, vp, vp, sz, vp]
     lib.retention_chunkwise_bwd.argtypes = [sp, i32, vp, vp, vp, dp, rp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd, lib.retention_chunkwise_bwd):
+    lib.retention_rla_fwd.argtypes = [sp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd, lib.retention_chunkwise_bwd,
+              lib.retention_rla_fwd):
         f.restype = ctypes.c_int
     lib.retention_workspace_bytes.argtypes = [i32, sp, i32, i32]
     lib.retention_workspace_bytes.restype = sz
@@ -308,3 +312,45 @@ def chunkwise_bwd(q, k, v, gamma: Sequence[float], dout, chunk: int, *, state_in
                                      _ptr(dout), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(ds), _ptr(ws), wsb, _stream(q.device, stream))
     _check(st)
     return dq, dk_, dv_, ds
+
+
+_FMAPS = {"identity": RET_FMAP_IDENTITY, "softmax": RET_FMAP_SOFTMAX}
+
+
+def rla_fwd(q, k, v, window: int, chunk: int = 128, *, fmap: str = "softmax", k_prev=None, v_prev=None,
+            prev_len: Optional[int] = None, state_in=None, out=None, state_out=None, out_dtype=torch.float32, want_out=True,
+            want_state=True, workspace=None, stream=None):
+    """Residual linear attention over a segment: o_t = phi(q_t) S_(t-window-1), S_t = S_(t-1) +
+    phi(k_t)^T v_t. q, k: [B,H,N,dk]; v: [B,H,N,dv]. k_prev, v_prev: [B,H,window+1,d], the positions
+    before the segment, of which the last prev_len (default: all, or none without them) hold tokens.
+    state_in / state_out: fp32 [B,H,dk,dv], the sum over the tokens that have left the window
+    (state_out may be state_in; a one-token segment needs a state_out). Returns (out, state_out)."""
+    lib = load_library()
+    _check_inputs(q, k, v, 4)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if prev_len is None:
+        prev_len = 0 if k_prev is None else window + 1
+    for name, t, d in (("k_prev", k_prev, dk), ("v_prev", v_prev, dv)):
+        if t is not None and (tuple(t.shape) != (B, H, window + 1, d) or t.dtype != q.dtype or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {q.dtype} tensor of shape {(B, H, window + 1, d)}")
+    if out is not None:
+        out_dtype = out.dtype
+    if want_out and out is None:
+        out = torch.empty((B, H, N, dv), dtype=out_dtype, device=q.device)
+    if not want_out:
+        out = None
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if not want_state:
+        state_out = None
+    shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    need = lib.retention_workspace_bytes(RET_FN_RLA, ctypes.byref(shp), int(chunk), 0)
+    if need == ctypes.c_size_t(-1).value:
+        need = 0
+    ws, wsb = _workspace(need, q.device, workspace)
+    st = lib.retention_rla_fwd(ctypes.byref(shp), int(chunk), int(window), _FMAPS[fmap], _ptr(q), _ptr(k), _ptr(v), _ptr(k_prev),
+                               _ptr(v_prev), int(prev_len), _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws), wsb,
+                               _stream(q.device, stream))
+    _check(st)
+    return out, state_out

@@ -251,3 +251,36 @@ def test_rotation_workspace(lib):
                                         None) == R.RET_ERR_WORKSPACE
     need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(shape()), 64, R.RET_WS_ROTATION)
     assert chunk(lib, wsb=need - 1, rot=rot()) == R.RET_ERR_WORKSPACE
+
+
+def rla(lib, shp=None, C=64, window=3, fmap=R.RET_FMAP_SOFTMAX, kp=None, vp=None, plen=0, sin=None, out=OUT, sout=ST, ws=WS,
+        wsb=1 << 40):
+    shp = shp if shp is not None else shape()
+    return lib.retention_rla_fwd(ctypes.byref(shp), C, window, fmap, Q, K, V, kp, vp, plen, sin, out, sout, ws, wsb, None)
+
+
+def test_rla_validation(lib):
+    # every check below fails on the host before any HIP call
+    assert rla(lib, window=-1) == R.RET_ERR_INVALID_ARG
+    assert "window" in lib.retention_last_error().decode()
+    assert rla(lib, fmap=2) == R.RET_ERR_INVALID_ARG
+    assert rla(lib, plen=5, kp=GW, vp=GW) == R.RET_ERR_INVALID_ARG  # more than window + 1 earlier tokens
+    assert rla(lib, plen=2) == R.RET_ERR_INVALID_ARG  # earlier tokens without their rows
+    assert "k_prev" in lib.retention_last_error().decode()
+    assert rla(lib, out=None, sout=None) == R.RET_ERR_INVALID_ARG
+    assert rla(lib, shape(dk=512, i=R.RET_F32)) == R.RET_ERR_UNSUPPORTED
+    assert rla(lib, C=96) == R.RET_ERR_UNSUPPORTED
+    assert rla(lib, shape(N=1), sout=None) == R.RET_ERR_INVALID_ARG  # a decode step needs its state
+    assert "state_out" in lib.retention_last_error().decode()
+    assert rla(lib, shape(N=1, dv=6)) == R.RET_ERR_UNSUPPORTED
+    assert rla(lib, out=Q) == R.RET_ERR_INVALID_ARG
+    assert rla(lib, plen=4, kp=GW, vp=ctypes.c_void_p(9 << 36), out=GW) == R.RET_ERR_INVALID_ARG  # out aliases k_prev
+    need = lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(shape()), 64, 0)
+    s = shape()
+    rows = s.batch * s.heads * s.seq_len
+    assert need >= rows * (2 * s.d_k + s.d_v) * 2
+    assert rla(lib, wsb=need - 1) == R.RET_ERR_WORKSPACE
+    assert rla(lib, ws=None, wsb=0) == R.RET_ERR_WORKSPACE
+    # a decode step needs only the operands
+    s1 = shape(N=1)
+    assert lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(s1), 0, 0) == 3 * 256

@@ -572,3 +572,184 @@ def test_rotation_backward(orc, dt, B, H, N, dk, dv, C, off):
             rot_report(tag, got[i], ref[i], ex[i], TOL[dt])
         else:
             report(tag, rel_err(got[i], ex[i]), TOL[dt])
+
+
+# ---------------------------------------------------------------------------------------------
+# Residual linear attention: o_t = phi(q_t) S_(t-w-1), S_t = S_(t-1) + phi(k_t)^T v_t, against the
+# oracle's definition. q and k are drawn at 2 sqrt(d_k) times the usual scale (N(0, 4), exact in
+# bf16) so that the softmax feature map is not nearly uniform. With bf16 inputs and the softmax
+# map, phi(q) and phi(k) enter the matrix cores rounded to bf16: the asserted check (A) runs the
+# oracle on phi computed in fp64 and rounded to bf16 on the CPU (then the identity map), and (B)
+# compares against the exact map with the derived bound of rot_report.
+def _rla_inputs(B, H, N, dk, dv, dt, seed, P=None):
+    q, k, v = I.make_qkv(B, H, N, dk, dv, dt, seed=seed)
+    sc = 2.0 * dk ** 0.5
+    q, k = q * sc, k * sc
+    if P is None:
+        return q, k, v
+    kp, vp = I.make_qkv(B, H, P, dk, dv, dt, seed=seed + 1)[1:]
+    return q, k, v, kp * sc, vp
+
+
+def _phi_bf16(orc, x):
+    return torch.from_numpy(orc.rla_phi(x, "softmax")).to(torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmap", ["identity", "softmax"])
+@pytest.mark.parametrize("w,C,plen", [(0, 64, 0), (5, 128, 6), (64, 64, 20), (200, 128, 201), (400, 64, 0)])
+def test_rla_fp32(orc, fmap, w, C, plen):
+    B, H, N, dk, dv = 2, 3, 300, 64, 128
+    q, k, v, kp, vp = _rla_inputs(B, H, N, dk, dv, "f32", 700 + w, P=w + 1)
+    s0 = I.make_state(B, H, dk, dv, seed=701, scale=0.05)
+    ref, ref_s = orc.rla(q, k, v, w, fmap, kp, vp, plen, s0)
+    qd, kd, vd, kpd, vpd, s0d = dev(q, k, v, kp, vp, s0)
+    o, s = R.rla_fwd(qd, kd, vd, w, C, fmap=fmap, k_prev=kpd, v_prev=vpd, prev_len=plen, state_in=s0d)
+    report(f"rla fp32 {fmap} w={w} C={C} prev {plen} out", rel_err(o, ref), TOL["f32"])
+    report(f"rla fp32 {fmap} w={w} C={C} prev {plen} state", rel_err(s, ref_s), TOL["f32"])
+
+
+def _rla_bf16_refs(orc, q, k, v, w, kp, vp, plen, s0):
+    """(A) reference on phi rounded to bf16, (B) exact reference."""
+    ex, ex_s = orc.rla(q, k, v, w, "softmax", kp, vp, plen, s0)
+    ref, ref_s = orc.rla(_phi_bf16(orc, q), _phi_bf16(orc, k), v, w, "identity",
+                         None if kp is None else _phi_bf16(orc, kp), vp, plen, s0)
+    return ref, ref_s, ex, ex_s
+
+
+def _f64np(x):
+    return None if x is None else (x.double().cpu().numpy() if hasattr(x, "double") else np.asarray(x, dtype=np.float64))
+
+
+def rla_bound_report(name, gpu, ref, q_op, k_op, v, w, C, kp_op=None, vp=None, plen=0, s0=None, heads=None):
+    """The chunkwise kernels' arithmetic bound, element by element, for bf16 operands q_op, k_op
+    (the features the kernels consume): the intra-chunk scores are stored in bf16 (relative error
+    <= 2^-8 each, round to nearest), everything else is exact products accumulated in fp32 or
+    carried as bf16 hi + lo pairs (allowed 2^-14 of the absolute sum of all terms). So
+      |gpu - ref| <= 2^-8 sum_(intra-chunk m <= t) |s_tm| |v_m| + 2^-14 (sum_(m <= t) |q_t| |k_m| |v_m| + |q_t| |S_in|)
+    with the keys and values shifted by w + 1 as the call does. The bounds are computed here in fp64
+    from the same operands; the reference is the oracle's. Asserted: max(|gpu - ref| / bound) <= 1.
+    max|err| / RMS(ref) is printed beside it: with peaked features one score can dominate an output
+    element, which then carries that score's bf16 rounding in full."""
+    g, r = _f64np(gpu), _f64np(ref)
+    Qa, Ka, Va, KPa, VPa, S0 = map(_f64np, (q_op, k_op, v, kp_op, vp, s0))
+    B, H, N, dk = Qa.shape
+    dv = Va.shape[-1]
+    P = w + 1
+    worst = 0.0
+    for b in range(B):
+        for h in (heads if heads is not None else range(H)):
+            Ks, Vs = np.zeros((N, dk)), np.zeros((N, dv))
+            src = np.arange(N) - P
+            inseg = src >= 0
+            Ks[inseg], Vs[inseg] = Ka[b, h, src[inseg]], Va[b, h, src[inseg]]
+            prev = (src < 0) & (src >= -plen)
+            if prev.any():
+                Ks[prev], Vs[prev] = KPa[b, h, src[prev] + P], VPa[b, h, src[prev] + P]
+            Rabs = np.abs(S0[b, h]) if S0 is not None else np.zeros((dk, dv))
+            Q = Qa[b, h]
+            for c0 in range(0, N, C):
+                L = min(C, N - c0)
+                Qc, Kc, Vc = Q[c0:c0 + L], Ks[c0:c0 + L], Vs[c0:c0 + L]
+                intra = np.tril(np.abs(Qc @ Kc.T)) @ np.abs(Vc)
+                absall = np.tril(np.abs(Qc) @ np.abs(Kc).T) @ np.abs(Vc) + np.abs(Qc) @ Rabs
+                Rabs = Rabs + np.abs(Kc).T @ np.abs(Vc)
+                err = np.abs(g[b, h, c0:c0 + L] - r[b, h, c0:c0 + L])
+                bound = 2.0 ** -8 * intra + 2.0 ** -14 * absall + 1e-300
+                worst = max(worst, float((err / bound).max()))
+    print(f"  {name}: max|err|/RMS {rel_err(gpu, ref):.3e}", flush=True)
+    report(f"{name}: max(|err| / elementwise bound)", worst, 1.0)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
+@pytest.mark.parametrize("N,C,w", [(37, 64, 0), (700, 256, 63), (1100, 512, 512)])
+def test_rla_bf16(orc, dk, dv, N, C, w):
+    B, H = 1, 4
+    q, k, v, kp, vp = _rla_inputs(B, H, N, dk, dv, "bf16", 710 + N + dk, P=w + 1)
+    s0 = I.make_state(B, H, dk, dv, seed=711, scale=0.02)
+    plen = min(w + 1, 17)
+    ref, ref_s, ex, ex_s = _rla_bf16_refs(orc, q, k, v, w, kp, vp, plen, s0)
+    qd, kd, vd, kpd, vpd, s0d = dev(q, k, v, kp, vp, s0)
+    o, s = R.rla_fwd(qd, kd, vd, w, C, k_prev=kpd, v_prev=vpd, prev_len=plen, state_in=s0d)
+    tag = f"rla bf16 softmax ({dk},{dv}) N={N} C={C} w={w}"
+    rla_bound_report(f"{tag} out", o, ref, _phi_bf16(orc, q), _phi_bf16(orc, k), v, w, C, _phi_bf16(orc, kp), vp, plen, s0)
+    report(f"{tag} state", rel_err(s, ref_s), TOL["bf16"])
+    print(f"  {tag} out vs the exact map: max|err|/RMS {rel_err(o, ex):.3e}; state {rel_err(s, ex_s):.3e}", flush=True)
+    # the identity map: the bf16 operands are the inputs themselves
+    ri, ri_s = orc.rla(q, k, v, w, "identity", kp, vp, plen, s0)
+    oi, si = R.rla_fwd(qd, kd, vd, w, C, fmap="identity", k_prev=kpd, v_prev=vpd, prev_len=plen, state_in=s0d)
+    rla_bound_report(f"rla bf16 identity ({dk},{dv}) N={N} C={C} w={w} out", oi, ri, q, k, v, w, C, kp, vp, plen, s0)
+    report(f"rla bf16 identity ({dk},{dv}) N={N} C={C} w={w} state", rel_err(si, ri_s), TOL["bf16"])
+
+
+def ref_first_state(orc, pq, pk, v, w, n1):
+    """The state after the first n1 tokens (the tokens that left the window), from the oracle."""
+    return orc.rla(pq[:, :, :n1], pk[:, :, :n1], v[:, :, :n1], w, "identity")[1]
+
+
+# Segments and decode: a prefill, a second segment given the first's last window+1 tokens and its
+# state, then decode steps (one-token segments, the window slid by the caller) equal one pass.
+def test_rla_segments_and_decode(orc):
+    B, H, N, dk, dv, w = 1, 16, 1600, 256, 512, 512
+    P = w + 1
+    q, k, v = _rla_inputs(B, H, N, dk, dv, "bf16", 720)
+    ref, ref_s, ex, ex_s = _rla_bf16_refs(orc, q, k, v, w, None, None, 0, None)
+    qd, kd, vd = dev(q, k, v)
+    n1, n2 = 300, 1590  # the first segment is shorter than the window
+    a, sa = R.rla_fwd(qd[:, :, :n1].contiguous(), kd[:, :, :n1].contiguous(), vd[:, :, :n1].contiguous(), w, 128)
+    kp = torch.zeros((B, H, P, dk), dtype=torch.bfloat16, device=DEV)
+    vp = torch.zeros((B, H, P, dv), dtype=torch.bfloat16, device=DEV)
+    kp[:, :, P - n1:], vp[:, :, P - n1:] = kd[:, :, :n1], vd[:, :, :n1]
+    b, sb = R.rla_fwd(qd[:, :, n1:n2].contiguous(), kd[:, :, n1:n2].contiguous(), vd[:, :, n1:n2].contiguous(), w, 256,
+                      k_prev=kp, v_prev=vp, prev_len=n1, state_in=sa)
+    pq, pk = _phi_bf16(orc, q), _phi_bf16(orc, k)
+    # the first segment is shorter than the window: no token has left it, every output is zero
+    assert torch.count_nonzero(a) == 0 and torch.count_nonzero(sa) == 0
+    kpc, vpc = torch.zeros((B, H, P, dk), dtype=torch.bfloat16), torch.zeros((B, H, P, dv), dtype=torch.bfloat16)
+    kpc[:, :, P - n1:], vpc[:, :, P - n1:] = pk[:, :, :n1], v[:, :, :n1]
+    rla_bound_report("rla second segment out (window handed over)", b, ref[:, :, n1:n2], pq[:, :, n1:n2], pk[:, :, n1:n2],
+                     v[:, :, n1:n2], w, 256, kpc, vpc, n1, ref_first_state(orc, pq, pk, v, w, n1), heads=[0, 7, 15])
+    report("rla split/resume state", rel_err(sb, orc.rla(pq[:, :, :n2], pk[:, :, :n2], v[:, :, :n2], w, "identity")[1]),
+           TOL["bf16"])
+    outs = []
+    for t in range(n2, N):
+        kp = kd[:, :, t - P:t].contiguous()
+        vp = vd[:, :, t - P:t].contiguous()
+        o, _ = R.rla_fwd(qd[:, :, t:t + 1].contiguous(), kd[:, :, t:t + 1].contiguous(), vd[:, :, t:t + 1].contiguous(), w, 128,
+                         k_prev=kp, v_prev=vp, state_in=sb, state_out=sb)
+        outs.append(o)
+    # the decode steps run on the decode kernel: fp32 state updates, no bf16 scores
+    report("rla decode steps out", rel_err(torch.cat(outs, dim=2), ref[:, :, n2:]), TOL["bf16"])
+    report("rla decode steps state", rel_err(sb, ref_s), TOL["bf16"])
+    print(f"  rla decode steps out vs the exact map: {rel_err(torch.cat(outs, dim=2), ex[:, :, n2:]):.3e}", flush=True)
+
+
+# The N=8192 layer shape with a 512-token window (the window the page reports for RAttention),
+# softmax map, chunk 128, fp32 out; every head against the oracle.
+def test_rla_layer(orc):
+    w = I.WORKLOADS["retention_b1_h16_n8192_dk256_dv512_bf16_gn"]
+    q, k, v = _rla_inputs(w.B, w.H, w.N, w.dk, w.dv, "bf16", 730)
+    ref, ref_s, ex, ex_s = _rla_bf16_refs(orc, q, k, v, 512, None, None, 0, None)
+    qd, kd, vd = dev(q, k, v)
+    o, s = R.rla_fwd(qd, kd, vd, 512, 128)
+    rla_bound_report("rla layer out (heads 0, 5, 10, 15)", o, ref, _phi_bf16(orc, q), _phi_bf16(orc, k), v, 512, 128,
+                     heads=[0, 5, 10, 15])
+    report("rla layer state", rel_err(s, ref_s), TOL["bf16"])
+    print(f"  rla layer vs the exact map: out {rel_err(o, ex):.3e}, state {rel_err(s, ex_s):.3e}", flush=True)
+
+
+# The decode workload shape: 128 sequences x 16 heads, 256 x 512 fp32 states, one token each with a
+# full window (the leaving token is row 0 of k_prev). The step reads only that row, so a 15-token
+# window keeps the oracle's copies small.
+def test_rla_decode_workload(orc):
+    d = I.WORKLOADS["decode_b128_h16_dk256_dv512"]
+    B, H, dk, dv, w = d.B, d.H, d.dk, d.dv, 15
+    q, k, v = _rla_inputs(B, H, 1, dk, dv, "bf16", 740)
+    kp = (I.make_qkv(B, H, 1, dk, dv, "bf16", seed=741)[1] * (2.0 * dk ** 0.5)).expand(B, H, w + 1, dk).contiguous()
+    vp = I.make_qkv(B, H, 1, dk, dv, "bf16", seed=742)[2].expand(B, H, w + 1, dv).contiguous()
+    state = I.make_state(B, H, dk, dv, seed=743, scale=0.02)
+    ref, ref_s, ex, ex_s = _rla_bf16_refs(orc, q, k, v, w, kp, vp, w + 1, state)
+    qd, kd, vd, kpd, vpd, sd = dev(q, k, v, kp, vp, state)
+    o, s = R.rla_fwd(qd, kd, vd, w, 0, k_prev=kpd, v_prev=vpd, state_in=sd, state_out=sd)
+    report("rla decode workload out", rel_err(o, ref), TOL["bf16"])
+    report("rla decode workload state", rel_err(sd, ref_s), TOL["bf16"])
+    print(f"  rla decode workload vs the exact map: out {rel_err(o, ex):.3e}, state {rel_err(sd, ex_s):.3e}", flush=True)
