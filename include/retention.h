@@ -211,7 +211,8 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
  *     is the next segment's state_in. A decode step is a segment of N = 1 whose k_prev row 0 is the
  *     token leaving the window; it runs on the decode-step kernel and needs state_out (which may
  *     equal state_in: the state is then advanced in place).
- * q, k, v, out: as retention_chunkwise_fwd. window >= 0. d_k <= 256. N > 1 takes the chunkwise
+ * q, k, v, out: as retention_chunkwise_fwd. window >= 0. d_k <= 256, a multiple of 4; a value row (d_v elements of
+ * the input dtype) a multiple of 16 bytes and at most 4 KiB. N > 1 takes the chunkwise
  * kernels (chunk and (d_k, d_v) as there); N = 1 the decode-step kernel (d_v as there).
  * Workspace: retention_workspace_bytes(RET_FN_RLA, ...): phi(q), the shifted phi(k) and v in the
  * input dtype, plus the chunkwise workspace. For bf16 inputs phi(q) and phi(k) are rounded to bf16

@@ -449,7 +449,12 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     RET_TRY(check_ptr(k_prev, "k_prev", prev_len > 0));
     RET_TRY(check_ptr(v_prev, "v_prev", prev_len > 0));
     if (!out && !state_out) return fail(RET_ERR_INVALID_ARG, "out and state_out are both NULL");
-    if (shape->d_k > 256) return fail(RET_ERR_UNSUPPORTED, "residual linear attention supports d_k <= 256 (got %d)", shape->d_k);
+    if (shape->d_k > 256 || shape->d_k % 4)
+        return fail(RET_ERR_UNSUPPORTED, "residual linear attention supports d_k <= 256, a multiple of 4 (got %d)", shape->d_k);
+    const size_t vrow = (size_t)shape->d_v * elem_size(shape->in_dtype);
+    if (vrow % 16 != 0 || vrow > 4096)
+        return fail(RET_ERR_UNSUPPORTED, "residual linear attention needs value rows of a multiple of 16 bytes, at most 4 KiB (d_v %d)",
+                    shape->d_v);
     const bool bf = shape->in_dtype == RET_BF16;
     const int N = shape->seq_len, dv = shape->d_v;
     if (N == 1) {

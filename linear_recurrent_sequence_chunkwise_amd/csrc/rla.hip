@@ -8,70 +8,125 @@
 //
 //   rla_prepare_kernel   one wave per (b*h, n) row: phi(q[n]) (unless phi is the identity, where q
 //                        is used in place), phi of the shifted key row and the shifted value row,
-//                        in the input dtype. d_k <= 256 (4 features per lane in registers); the
-//                        softmax in double precision. HBM-bound.
+//                        in the input dtype. d_k <= 256, a multiple of 4 (4 consecutive features per
+//                        lane, one 8- or 16-byte access); the softmax in double precision.
 // The retention itself runs in the chunkwise kernels (N > 1) or the decode-step kernel (N = 1).
 #include "common.hpp"
 
 namespace ret {
 namespace {
 
-__device__ __forceinline__ double wave_max_d(double x) {
+// Two independent wave reductions at once, so that their shuffles overlap.
+__device__ __forceinline__ void wave_max2(double& a, double& b) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x = fmax(x, __shfl_xor(x, o, 64));
-    return x;
-}
-__device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
-// y = phi(x) over d <= 256 features, lane l holding features l, l + 64, l + 128, l + 192. The
-// softmax runs in double precision (exp(x - max) / sum) and is rounded once to fp32, then to the
-// output dtype: the rounded features then equal the exactly computed ones rounded the same way,
-// except where a value lies within about 1e-16 relative of a rounding boundary.
-template <typename T>
-__device__ __forceinline__ void feature_row(int fmap, int d, const T* x, T* y, int lane) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = lane + 64 * j;
-        v[j] = i < d ? to_float(x[i]) : -INFINITY;
+    for (int o = 1; o < 64; o <<= 1) {
+        const double x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
+        a = fmax(a, x);
+        b = fmax(b, y);
     }
-    if (fmap == 1) {
-        const double m = wave_max_d((double)fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-        double e[4], s = 0.0;
+}
+__device__ __forceinline__ void wave_sum2(double& a, double& b) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            e[j] = lane + 64 * j < d ? exp((double)v[j] - m) : 0.0;
-            s += e[j];
-        }
-        s = wave_sum_d(s);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = (float)(e[j] / s);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = lane + 64 * j;
-        if (i < d) y[i] = from_float<T>(v[j]);
+    for (int o = 1; o < 64; o <<= 1) {
+        const double x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
+        a += x;
+        b += y;
     }
 }
 
+// Features 4l .. 4l+3 of a row of d <= 256 (lane l, one 8- or 16-byte access; d a multiple of 4);
+// -inf past the end or without a row.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> {
+    static __device__ __forceinline__ void load(const bf16* p, float* v) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (float)x[j];
+    }
+    static __device__ __forceinline__ void store(bf16* p, const float* v) {
+        bf16x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (bf16)v[j];
+        *reinterpret_cast<bf16x4*>(p) = x;
+    }
+};
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float* p, float* v) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = x[j];
+    }
+    static __device__ __forceinline__ void store(float* p, const float* v) {
+        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+};
+
 template <typename T>
-__device__ __forceinline__ void copy_row(int d, const T* x, T* y, int lane) {
-    if ((d * sizeof(T)) % 16 == 0) {
-        const int n16 = d * (int)sizeof(T) / 16;
-        for (int c = lane; c < n16; c += 64) reinterpret_cast<u32x4*>(y)[c] = reinterpret_cast<const u32x4*>(x)[c];
+__device__ __forceinline__ void load_row4(const T* x, int d, int lane, float* v) {
+    if (x && 4 * lane < d) {
+        Vec4<T>::load(x + 4 * lane, v);
     } else {
-        for (int i = lane; i < d; i += 64) y[i] = x[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = -INFINITY;
     }
 }
 
 template <typename T>
-__device__ __forceinline__ void zero_row(int d, T* y, int lane) {
-    for (int i = lane; i < d; i += 64) y[i] = from_float<T>(0.f);
+__device__ __forceinline__ void store_row4(T* y, int d, int lane, const float* v) {
+    if (4 * lane < d) Vec4<T>::store(y + 4 * lane, v);
 }
+
+// exp(z) for z <= 0 in double precision: z = n ln 2 + r with ln 2 split in two (Cody and Waite),
+// |r| <= ln 2 / 2, exp(r) by its Taylor series to degree 11 (truncation below 3.1e-15 relative),
+// then scaled by 2^n (ldexp, which flushes to zero below the double range). Relative error below
+// 1e-14 against libm's exp on [-680, 0], ample for rounding the result to fp32 and bf16 as an
+// exactly computed value would be.
+__device__ __forceinline__ double exp_nonpos(double z) {
+    const double n = rint(z * 1.4426950408889634);
+    double r = fma(-n, 6.93147180369123816490e-01, z);  // ln 2, high part (exact product with n)
+    r = fma(-n, 1.90821492927058770002e-10, r);          // ln 2, low part
+    double p = 1.0 / 39916800.0;                         // 1/11!
+    p = fma(p, r, 1.0 / 3628800.0);
+    p = fma(p, r, 1.0 / 362880.0);
+    p = fma(p, r, 1.0 / 40320.0);
+    p = fma(p, r, 1.0 / 5040.0);
+    p = fma(p, r, 1.0 / 720.0);
+    p = fma(p, r, 1.0 / 120.0);
+    p = fma(p, r, 1.0 / 24.0);
+    p = fma(p, r, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
+    p = fma(p, r, 1.0);
+    p = fma(p, r, 1.0);
+    return ldexp(p, (int)fmax(n, -2000.0));
+}
+
+// phi over two rows at once (a: the q row, b: the key row), in place. The softmax runs in double
+// precision, exp(x - max) times the reciprocal of the sum, rounded once to fp32: the rounded
+// features then equal the exactly computed ones rounded the same way, except where a value lies
+// within about 1e-16 relative of a rounding boundary.
+__device__ __forceinline__ void softmax2(int d, int lane, float* a, float* b) {
+    double ma = (double)fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    double mb = (double)fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
+    wave_max2(ma, mb);
+    double ea[4], eb[4], sa = 0.0, sb = 0.0;
+    const bool in = 4 * lane < d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ea[j] = in ? exp_nonpos((double)a[j] - ma) : 0.0;
+        eb[j] = in ? exp_nonpos((double)b[j] - mb) : 0.0;
+        sa += ea[j];
+        sb += eb[j];
+    }
+    wave_sum2(sa, sb);
+    const double ia = 1.0 / sa, ib = 1.0 / sb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a[j] = (float)(ea[j] * ia);
+        b[j] = (float)(eb[j] * ib);
+    }
+}
+
+constexpr int kMaxV16 = 4;  // 16-byte chunks of a value row per lane: d_v * size <= 4 KiB
 
 template <typename T>
 __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int dk, int dv, int P, int prev_len, int fmap,
@@ -82,7 +137,6 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int 
     const int lane = threadIdx.x & 63;
     const long bh = row / N;
     const int n = (int)(row % N);
-    if (qo) feature_row(fmap, dk, q + (size_t)row * dk, qo + (size_t)row * dk, lane);
     const int p = n - P;  // position of the token whose key and value land in row n
     const T* ks = nullptr;
     const T* vs = nullptr;
@@ -93,12 +147,30 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int 
         ks = kp + ((size_t)bh * P + (p + P)) * dk;
         vs = vp + ((size_t)bh * P + (p + P)) * dv;
     }
+    // every load first
+    float fq[4], fk[4];
+    load_row4(qo ? q + (size_t)row * dk : nullptr, dk, lane, fq);
+    load_row4(ks, dk, lane, fk);
+    const int n16 = dv * (int)sizeof(T) / 16;  // whole 16-byte chunks (d_v * size is a multiple of 16)
+    u32x4 vv[kMaxV16];
+#pragma unroll
+    for (int j = 0; j < kMaxV16; ++j) {
+        const int c = lane + 64 * j;
+        vv[j] = (vs && c < n16) ? reinterpret_cast<const u32x4*>(vs)[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (fmap == 1) softmax2(dk, lane, fq, fk);
+    if (qo) store_row4(qo + (size_t)row * dk, dk, lane, fq);
     if (ks) {
-        feature_row(fmap, dk, ks, ko + (size_t)row * dk, lane);
-        copy_row(dv, vs, vo + (size_t)row * dv, lane);
+        store_row4(ko + (size_t)row * dk, dk, lane, fk);
     } else {
-        zero_row(dk, ko + (size_t)row * dk, lane);
-        zero_row(dv, vo + (size_t)row * dv, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fk[j] = 0.f;
+        store_row4(ko + (size_t)row * dk, dk, lane, fk);
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxV16; ++j) {
+        const int c = lane + 64 * j;
+        if (c < n16) reinterpret_cast<u32x4*>(vo + (size_t)row * dv)[c] = vv[j];
     }
 }
 

@@ -269,10 +269,12 @@ def test_rla_validation(lib):
     assert "k_prev" in lib.retention_last_error().decode()
     assert rla(lib, out=None, sout=None) == R.RET_ERR_INVALID_ARG
     assert rla(lib, shape(dk=512, i=R.RET_F32)) == R.RET_ERR_UNSUPPORTED
+    assert rla(lib, shape(N=1, dk=6)) == R.RET_ERR_UNSUPPORTED  # d_k not a multiple of 4
     assert rla(lib, C=96) == R.RET_ERR_UNSUPPORTED
     assert rla(lib, shape(N=1), sout=None) == R.RET_ERR_INVALID_ARG  # a decode step needs its state
     assert "state_out" in lib.retention_last_error().decode()
     assert rla(lib, shape(N=1, dv=6)) == R.RET_ERR_UNSUPPORTED
+    assert rla(lib, shape(N=1, dv=12)) == R.RET_ERR_UNSUPPORTED  # 24-byte bf16 value rows
     assert rla(lib, out=Q) == R.RET_ERR_INVALID_ARG
     assert rla(lib, plen=4, kp=GW, vp=ctypes.c_void_p(9 << 36), out=GW) == R.RET_ERR_INVALID_ARG  # out aliases k_prev
     need = lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(shape()), 64, 0)
