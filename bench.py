@@ -16,9 +16,11 @@ Counting rules:
     scores Q K^T and dout V^T, their products with K, Q and dout, and per token the five
     d_k x d_v products dout R^T, U v, U^T k and the two state updates)
   backward algorithmic bytes: bf16 q, k, v, dout read; fp32 dq, dk, dv written
+  parallel form algorithmic FLOPs per (b, h): 2 (d_k + d_v) N (N + 1) / 2 (every causal pair)
 
 Beside the step, outside its timed region: the same chunkwise call with a swish gate after the
-GroupNorm, the chunkwise call and the decode step with the positional rotation of q and k, residual
+GroupNorm, the parallel form of the same layer, the chunkwise call and the decode step with the
+positional rotation of q and k, residual
 linear attention at the same shape (512-token window, softmax feature map; its rate is counted with
 the chunkwise FLOPs), and the chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout,
 each timed over the same K calls.
@@ -259,6 +261,10 @@ def main():
     t_rla = time_calls(lambda: R.rla_fwd(q, k, v, RLA_WINDOW, C, out=rla_out, state_out=st_out, workspace=rla_ws, stream=stream),
                        args.steps, stream, torch)
     del rla_ws, rla_out
+    # the parallel form of the same layer (quadratic: every causal pair of the 8192 tokens)
+    t_par = time_calls(lambda: R.parallel_fwd(q, k, v, gam, groupnorm=gn, out=out, stream=stream), max(2, args.steps // 4),
+                       stream, torch)
+    par_flops = 2 * (w.dk + w.dv) * w.B * w.H * w.N * (w.N + 1) // 2
     gdo = (torch.randn((w.B, w.H, w.N, w.dv), generator=torch.Generator().manual_seed(8))).to(torch.bfloat16).to(dev)
     bws = torch.empty(R.workspace_bytes(R.RET_FN_CHUNKWISE_BWD, w.B, w.H, w.N, w.dk, w.dv, torch.bfloat16, torch.float32, C),
                       dtype=torch.uint8, device=dev)
@@ -306,6 +312,9 @@ def main():
         "swish_gate": {"chunkwise_gated_us": round(t_gate * 1e6, 2), "gate_extra_us": round((t_gate - tb_gate) * 1e6, 2)},
         "rotation": {"chunkwise_rotated_us": round(t_rot * 1e6, 2), "rotation_extra_us": round((t_rot - tb_rot) * 1e6, 2),
                      "decode_rotated_us": round(t_drot * 1e6, 2), "decode_rotation_extra_us": round((t_drot - tb_drot) * 1e6, 2)},
+        "parallel": {"workload": "parallel form of the chunkwise workload (GroupNorm, bf16 out)", "us": round(t_par * 1e6, 1),
+                     "tflops": round(par_flops / t_par / 1e12, 3), "algorithmic_flops": par_flops,
+                     "mfma_frac": round(par_flops / t_par / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
         "rla": {"workload": f"residual linear attention, B=1 H=16 N=8192 d_k=256 d_v=512, window {RLA_WINDOW}, softmax "
                             "feature map, chunk 128, fp32 out", "us": round(t_rla * 1e6, 2),
                 "tflops": round(cf / t_rla / 1e12, 3), "tokens_per_s": round(w.B * w.N / t_rla, 1)},

@@ -3,12 +3,14 @@
 // forgetting; "Training in parallel"): O = (Q K^T (.) D) V, D[n][m] = g^(n-m) for n >= m.
 //
 // One workgroup per (64 query rows, b, h) owns all d_v output columns, so the optional per-head
-// GroupNorm is computed inside it. For each 64-key block up to the diagonal:
-//   - K and V blocks are staged in LDS;
-//   - each wave computes S for its 16 query rows (Q fragments stay in registers), applies the
-//     causal mask and the decay g^(n-m) in registers, and writes P to LDS as a bf16 high part and
-//     a bf16 low part (P spans the whole sequence here, so a single bf16 rounding of P would
-//     dominate the error);
+// GroupNorm is computed inside it. For each 32-key block up to the diagonal:
+//   - K and V blocks are staged in LDS; the next block's rows are loaded into registers while the
+//     current block is computed, and written to LDS after the block's reads are done;
+//   - each wave computes S^T = K Q^T for its 16 query rows (Q fragments stay in registers and serve
+//     as the B operand), so that each lane holds 4 consecutive keys of one query row; it applies
+//     the causal mask and the decay g^(n-m) in registers and writes P to LDS as a bf16 high part and
+//     a bf16 low part, 8 bytes each (P spans the whole sequence here, so a single bf16 rounding of
+//     P would dominate the error);
 //   - the four waves, arranged 2 x 2 over (rows, columns), accumulate P V with both parts.
 #include "common.hpp"
 
@@ -16,14 +18,15 @@ namespace ret {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kKB = 32;  // keys per block
 
 template <int DK, int DV>
 struct ParLds {
-    static constexpr int LK = DK + 8;   // K rows: 16-byte reads
-    static constexpr int LV = DV + 16;  // V rows: transposing reads
-    static constexpr int LP = 64 + 8;   // P rows: 16-byte reads
-    bf16 Ks[64 * LK];
-    bf16 Vs[64 * LV];
+    static constexpr int LK = DK + 8;    // K rows: 16-byte reads
+    static constexpr int LV = DV + 16;   // V rows: transposing reads
+    static constexpr int LP = kKB + 8;   // P rows: 8-byte writes, 16-byte reads
+    bf16 Ks[kKB * LK];
+    bf16 Vs[kKB * LV];
     bf16 Phi[64 * LP];
     bf16 Plo[64 * LP];
     float red[2][64];
@@ -59,48 +62,68 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = 0; kb <= qb; ++kb) {
-        const int m0 = kb * 64;
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < 64 * (DK / 8); idx += kThreads) {
-            const int r = idx / (DK / 8), sg = idx % (DK / 8);
-            bf16x8 val = zero_bf16x8();
-            if (m0 + r < N) val = *reinterpret_cast<const bf16x8*>(kh + (size_t)(m0 + r) * DK + 8 * sg);
-            *reinterpret_cast<bf16x8*>(&sm.Ks[r * LK + 8 * sg]) = val;
-        }
-        for (int idx = threadIdx.x; idx < 64 * (DV / 8); idx += kThreads) {
-            const int r = idx / (DV / 8), sg = idx % (DV / 8);
-            bf16x8 val = zero_bf16x8();
-            if (m0 + r < N) val = *reinterpret_cast<const bf16x8*>(vh + (size_t)(m0 + r) * DV + 8 * sg);
-            *reinterpret_cast<bf16x8*>(&sm.Vs[r * LV + 8 * sg]) = val;
-        }
-        __syncthreads();
-        // S for query rows n0 + 16w .. +16 against the 4 key tiles of this block
+    const int nkb = min((n0 + 64 + kKB - 1) / kKB, (N + kKB - 1) / kKB);  // key blocks up to the diagonal
+    // K and V rows of the next block, loaded into registers while this block is computed (16-byte
+    // pieces, idx = threadIdx.x + kThreads * j; rows past the sequence read as zero)
+    constexpr int NKR = kKB * (DK / 8) / kThreads, NVR = kKB * (DV / 8) / kThreads;
+    static_assert(kKB * (DK / 8) % kThreads == 0 && kKB * (DV / 8) % kThreads == 0, "whole pieces per thread");
+    bf16x8 kr[NKR], vr[NVR];
+    auto load_block = [&](int kb) __attribute__((always_inline)) {
+        const int m0 = kb * kKB;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int j = 0; j < NKR; ++j) {
+            const int idx = threadIdx.x + kThreads * j, r = idx / (DK / 8), sg = idx % (DK / 8);
+            kr[j] = m0 + r < N ? *reinterpret_cast<const bf16x8*>(kh + (size_t)(m0 + r) * DK + 8 * sg) : zero_bf16x8();
+        }
+#pragma unroll
+        for (int j = 0; j < NVR; ++j) {
+            const int idx = threadIdx.x + kThreads * j, r = idx / (DV / 8), sg = idx % (DV / 8);
+            vr[j] = m0 + r < N ? *reinterpret_cast<const bf16x8*>(vh + (size_t)(m0 + r) * DV + 8 * sg) : zero_bf16x8();
+        }
+    };
+    load_block(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int m0 = kb * kKB;
+        __syncthreads();  // the previous block's LDS reads are done
+#pragma unroll
+        for (int j = 0; j < NKR; ++j) {
+            const int idx = threadIdx.x + kThreads * j, r = idx / (DK / 8), sg = idx % (DK / 8);
+            *reinterpret_cast<bf16x8*>(&sm.Ks[r * LK + 8 * sg]) = kr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NVR; ++j) {
+            const int idx = threadIdx.x + kThreads * j, r = idx / (DV / 8), sg = idx % (DV / 8);
+            *reinterpret_cast<bf16x8*>(&sm.Vs[r * LV + 8 * sg]) = vr[j];
+        }
+        __syncthreads();
+        if (kb + 1 < nkb) load_block(kb + 1);
+        // S^T for the key tiles of this block against query rows n0 + 16w .. +16: lane (g4, c16) ends
+        // with keys m0 + 16kt + 4g4 + i of query row n0 + 16w + c16
+#pragma unroll
+        for (int kt = 0; kt < kKB / 16; ++kt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (kb < qb || kt <= w) {
+            if (m0 + 16 * kt <= n0 + 16 * w + 15) {  // a tile wholly above the diagonal stays zero
 #pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks) s = mfma16(qa[ks], frag_rowmajor(sm.Ks, LK, 16 * kt, 32 * ks, lane), s);
+                for (int ks = 0; ks < DK / 32; ++ks) s = mfma16(frag_rowmajor(sm.Ks, LK, 16 * kt, 32 * ks, lane), qa[ks], s);
             }
-            const int m = m0 + 16 * kt + c16;
-            bf16 hi[4], lo[4];
+            const int n = n0 + 16 * w + c16;
+            bf16x4 hi, lo;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int n = n0 + 16 * w + 4 * g4 + i;
+                const int m = m0 + 16 * kt + 4 * g4 + i;
                 const float d = n >= m ? decay_pow(l2g, (float)(n - m)) : 0.f;
-                split_hi_lo(s[i] * d, hi[i], lo[i]);
+                bf16 a, c;
+                split_hi_lo(s[i] * d, a, c);
+                hi[i] = a;
+                lo[i] = c;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm.Phi[(16 * w + 4 * g4 + i) * LP + 16 * kt + c16] = hi[i];
-                sm.Plo[(16 * w + 4 * g4 + i) * LP + 16 * kt + c16] = lo[i];
-            }
+            *reinterpret_cast<bf16x4*>(&sm.Phi[(16 * w + c16) * LP + 16 * kt + 4 * g4]) = hi;
+            *reinterpret_cast<bf16x4*>(&sm.Plo[(16 * w + c16) * LP + 16 * kt + 4 * g4]) = lo;
         }
         __syncthreads();
         // P V: wave (wr, wc) owns rows 32wr .. +32 and columns wc*DV/2 .. +DV/2
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < kKB / 32; ++ks) {
             bf16x8 ahi[2], alo[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
