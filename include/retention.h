@@ -180,9 +180,10 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
  * contraction width d_v runs as two column blocks of d_v / 2.
  * With a rotation, dq and dk are the gradients with respect to the unrotated q and k: the
  * gradients at the rotated inputs turned back by the inverse rotation (its transpose).
- * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): time-reversed copies of q, k,
- * v and dout, one fp32 output buffer and the workspace of the forward calls (plus the rotated q
- * and k with RET_WS_ROTATION).
+ * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): the workspace of the forward
+ * calls, the fp32 outputs of the column blocks and the blocks of state_in^T (bf16 inputs, whose
+ * forwards read every operand in place); for fp32 inputs also time-reversed and block copies of
+ * q, k, v and dout (plus the rotated q and k with RET_WS_ROTATION).
  */
 ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
                                    const void* q, const void* k, const void* v,

@@ -14,6 +14,10 @@
 // d_v / s, whose outputs add (the scores are sums over the contraction index). The blocks are
 // stacked along the batch (B' = s B), so one launch covers them with s times the workgroups, and a
 // last pass sums the s outputs.
+// bf16 inputs: the forwards read every operand in place (OpAddr: the time reversal, the row stride
+// and column block of a 512-wide operand, the source head of a stacked block) and write dv in
+// place; only the column-block sums pass through the workspace. fp32 inputs: the reversed and
+// stacked operands are copied into the workspace first.
 // The gradients come out in fp32; the forwards accumulate in fp32 with the operand precision of
 // the forward path (bf16 scores and bf16 hi + lo state and scaled values for bf16 inputs).
 #include "common.hpp"
@@ -133,7 +137,7 @@ size_t fwd_workspace(int in_bf16, int B, int H, int N, int dk, int dv, int chunk
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace regions, each 256-aligned. With s column blocks, "stacked" buffers hold s copies one
-// after another (the batch of the stacked forward).
+// after another (the batch of the stacked forward). bf16 inputs need only fwd, tmp and st.
 struct BwdLayout {
     int split;  // column blocks of d_v in the dq and dk forwards
     size_t fwd, rq, rk, rdo, sa, sb, sc, ta, tb, tc, tmp, st, total;
@@ -149,6 +153,14 @@ BwdLayout bwd_layout(int in_bf16, int B, int H, int N, int DK, int DV, int chunk
     if (f2 > fw) fw = f2;
     size_t o = 0;
     l.fwd = o; o += al(fw);
+    if (in_bf16) {                                      // operands read in place
+        const size_t t2 = s > 1 ? s * rows * (size_t)DK * 4 : 0;
+        l.rq = l.rk = l.rdo = l.sa = l.sb = l.sc = l.ta = l.tb = l.tc = o;
+        l.tmp = o; o += al(t2);                         // stacked fp32 outputs of the dq / dk forwards
+        l.st = o; o += al((size_t)s * B * H * w * DK * 4);
+        l.total = o;
+        return l;
+    }
     l.rq = o; o += al(rows * DK * sz);                  // rev q
     l.rk = o; o += al(rows * DK * sz);                  // rev k
     l.rdo = o; o += al(rows * DV * sz);                 // rev dout
@@ -183,8 +195,9 @@ void scatter(const LaunchArgs& a, const float* src, int d, int c0, int w, int re
 
 // one forward on the given operands (d_k = dk, d_v = dv), fp32 out, no GroupNorm
 hipError_t forward(const LaunchArgs& base, int dk, int dv, const void* q, const void* k, const void* v, const float* state_in,
-                   float* out, float* state_out, void* ws, size_t ws_bytes) {
+                   float* out, float* state_out, void* ws, size_t ws_bytes, OpAddr addr = OpAddr{}) {
     LaunchArgs a = base;
+    a.addr = addr;
     a.DK = dk;
     a.DV = dv;
     a.out_bf16 = 0;
@@ -211,7 +224,61 @@ size_t chunkwise_bwd_workspace(int in_bf16, int B, int H, int N, int DK, int DV,
     return bwd_layout(in_bf16, B, H, N, DK, DV, chunk).total;
 }
 
+// bf16: every forward reads its operands in place.
+hipError_t bwd_in_place(const BwdArgs& b) {
+    const LaunchArgs& a = b.base;
+    const BwdLayout l = bwd_layout(1, a.B, a.H, a.N, a.DK, a.DV, a.chunk);
+    const int DK = a.DK, DV = a.DV, s = l.split, w = DV / s, BH = a.B * a.H;
+    const size_t rows = (size_t)BH * a.N;
+    char* ws = reinterpret_cast<char*>(a.ws);
+    void* fws = ws + l.fwd;
+    const size_t fwb = l.tmp - l.fwd;
+    float* tmp = reinterpret_cast<float*>(ws + l.tmp);
+    LaunchArgs stacked = a;  // the column blocks stacked along the batch
+    stacked.B = s * a.B;
+    auto sum_blocks = [&](float* dst) {
+        const size_t work = rows * DK / 4;
+        hipLaunchKernelGGL(sum_blocks_kernel, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)BH, a.N, DK, s, 0, tmp, dst);
+    };
+    hipError_t e;
+    // dq = sum over column blocks j of forward(dout_j, v_j, k, (S_in^T)_j): dout and v rows DV apart,
+    // block j from column j w; k shared by the blocks
+    if (b.dq) {
+        const float* st = nullptr;
+        if (b.state_in) {
+            for (int j = 0; j < s; ++j) {
+                const size_t work = (size_t)BH * w * DK;
+                hipLaunchKernelGGL(transpose_state_kernel, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)BH, DK, DV, j * w,
+                                   w, b.state_in, reinterpret_cast<float*>(ws + l.st) + (size_t)j * BH * w * DK);
+            }
+            st = reinterpret_cast<const float*>(ws + l.st);
+        }
+        e = forward(stacked, w, DK, b.dout, b.v, b.k, st, s > 1 ? tmp : b.dq, nullptr, fws, fwb, OpAddr{0, DV, w, BH});
+        if (e != hipSuccess) return e;
+        if (s > 1) sum_blocks(b.dq);
+    }
+    // dv = rev(forward(rev k, rev q, rev dout)), written in place; its final state is U_0
+    if (b.dv || b.dstate_in) {
+        e = forward(a, DK, DV, b.k, b.q, b.dout, nullptr, b.dv, b.dstate_in, fws, fwb, OpAddr{1, DK, 0, BH});
+        if (e != hipSuccess) return e;
+        if (b.dstate_in) {
+            const size_t per = (size_t)DK * DV;
+            hipLaunchKernelGGL(scale_heads_kernel, dim3(grid_for((size_t)BH * per)), dim3(kCopyThreads), 0, a.stream, (long)BH, a.H, per,
+                               a.hc, b.dstate_in);
+        }
+    }
+    // dk = rev(sum over column blocks j of forward(rev v_j, rev dout_j, rev q)); the reversed
+    // forward writes its rows back in time order
+    if (b.dk) {
+        e = forward(stacked, w, DK, b.v, b.dout, b.q, nullptr, s > 1 ? tmp : b.dk, nullptr, fws, fwb, OpAddr{1, DV, w, BH});
+        if (e != hipSuccess) return e;
+        if (s > 1) sum_blocks(b.dk);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_chunkwise_bwd(const BwdArgs& b) {
+    if (b.base.in_bf16) return bwd_in_place(b);
     const LaunchArgs& a = b.base;
     const BwdLayout l = bwd_layout(a.in_bf16, a.B, a.H, a.N, a.DK, a.DV, a.chunk);
     const int DK = a.DK, DV = a.DV, s = l.split, w = DV / s;

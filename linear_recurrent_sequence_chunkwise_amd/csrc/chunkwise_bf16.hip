@@ -41,7 +41,8 @@ constexpr int kST = 32;    // tokens per pipeline stage
 // Waves take row tiles in mirrored pairs (t, T-1-t) so that the causal work is balanced.
 template <int DK>
 __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
-                                                           const bf16* __restrict__ k, bf16* __restrict__ P, HeadConsts hc) {
+                                                           const bf16* __restrict__ k, bf16* __restrict__ P, HeadConsts hc,
+                                                           int rev, int ldqk, int qcol_blk, int srcBH) {
     constexpr int KB = 128;       // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row
     constexpr int NKB = KB * QRB / 1024;  // kilobytes of a K block
@@ -50,9 +51,13 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
     const int c0 = chunk * C;
     const float l2g = hc.log2g[h];
-    const unsigned q_bytes = (unsigned)((size_t)N * DK * 2);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
+    // rows of this head's q and k (in place: stride ldqk, a column block, reversed); rows past the
+    // sequence fall outside the resource and read as zero
+    const unsigned q_bytes = (unsigned)(((size_t)(N - 1) * ldqk + DK) * 2);
+    const size_t qbase = (size_t)(bh % srcBH) * N * ldqk + (size_t)(bh / srcBH) * qcol_blk;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + qbase), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + qbase), 0, q_bytes, 0x00020000);
+    auto row_of = [&](int t) __attribute__((always_inline)) { return rev ? N - 1 - t : t; };
     bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
     const int T = C / 16;  // row tiles of the chunk
 
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
         for (int j = w; j < NKB; j += 4) {
             const int byte = 1024 * j + 16 * lane, r = byte / QRB;
             const int c = ((byte % QRB) >> 4) ^ (r & SwzTile<QRB>::M);
-            const unsigned off = (unsigned)(((c0 + kb0 + r) * DK + 8 * c) * 2);
+            const unsigned off = (unsigned)((row_of(c0 + kb0 + r) * ldqk + 8 * c) * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + 1024 * j), 16, off, 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
             bf16x8 qf[DK / 32];
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
-                const unsigned off = (unsigned)(((c0 + 16 * t + c16) * DK + 32 * ks + 8 * g4) * 2);
+                const unsigned off = (unsigned)((row_of(c0 + 16 * t + c16) * ldqk + 32 * ks + 8 * g4) * 2);
                 qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
             }
             for (int kt = kb0 / 16; kt <= last; ++kt) {
@@ -99,6 +104,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
 // ---------------------------------------------------------------------------------------------
 struct MainParams {
     int H, N, C, NS, nchunks, teams;
+    int rev, ldqk, qcol_blk, srcBH;  // operand addressing (OpAddr, defaults resolved)
     const bf16* q;
     const bf16* k;
     const bf16* v;
@@ -183,11 +189,16 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     const int total = (nchunks - 1) * SPC + (L_last + kST - 1) / kST;
     const int rt_o = w >> 1, ct_o = w & 1;  // output tile of this wave within a stage
 
-    // Buffer resources: loads past the end of a head's data return zero (tail rows, padding).
-    const unsigned q_bytes = (unsigned)((size_t)N * DK * 2), v_bytes = (unsigned)((size_t)N * DV * 2);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)bh * N * DV), 0, v_bytes, 0x00020000);
+    // Buffer resources: loads past the end of a head's data return zero (tail rows, padding). q, k
+    // and v of source head bh % srcBH (q and k: rows ldqk apart, from a column block; all rows in
+    // reverse with rev).
+    const int ldqk = p.ldqk, src = bh % p.srcBH;
+    auto row_of = [&](int t) __attribute__((always_inline)) { return p.rev ? N - 1 - t : t; };
+    const unsigned q_bytes = (unsigned)(((size_t)(N - 1) * ldqk + DK) * 2), v_bytes = (unsigned)((size_t)N * DV * 2);
+    const size_t qbase = (size_t)src * N * ldqk + (size_t)(bh / p.srcBH) * p.qcol_blk;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qbase), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qbase), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
     const unsigned p_bytes = WANT_OUT ? (unsigned)((size_t)nchunks * C * C * 2) : 0u;
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(WANT_OUT ? p.P + (size_t)bh * nchunks * C * C : p.q), 0, p_bytes, 0x00020000);
@@ -201,13 +212,13 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
         for (int u = 0; u < G::QN; ++u) {
             const int j = threadIdx.x + kThreads * u;
             const int row = j / (DK / 8), sg = j % (DK / 8);
-            const unsigned off = j < G::QCH ? (unsigned)((tok0 + row) * DK + 8 * sg) * 2u : q_bytes;
+            const unsigned off = j < G::QCH ? (unsigned)((row_of(tok0 + row) * ldqk + 8 * sg) * 2) : q_bytes;
             if constexpr (WANT_OUT) r.q[u] = buf_load16(rq, off);
             r.k[u] = buf_load16(rk, off);
         }
         {
             const int row = threadIdx.x >> 2, sg = threadIdx.x & 3;  // 32 rows x 4 chunks of 8 columns
-            const unsigned off = threadIdx.x < kST * 4 ? (unsigned)((tok0 + row) * DV + col0 + 8 * sg) * 2u : v_bytes;
+            const unsigned off = threadIdx.x < kST * 4 ? (unsigned)((row_of(tok0 + row) * DV + col0 + 8 * sg) * 2) : v_bytes;
             r.v = buf_load16(rv, off);
         }
         if constexpr (WANT_OUT) {
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = c0 + kST * s + 16 * rt_o + 4 * g4 + i;
-            if (r < N) out[((size_t)bh * N + r) * DV + col0 + 16 * ct_o + c16] = from_float<TOUT>(a[i]);
+            if (r < N) out[((size_t)bh * N + row_of(r)) * DV + col0 + 16 * ct_o + c16] = from_float<TOUT>(a[i]);
         }
     };
 
@@ -481,8 +492,13 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     const int total = (nchunks - 1) * SPC + (L_last + kST - 1) / kST;
     const int rt_o = wl >> 1, ct_o = wl & 1;
 
-    // Buffer resources: loads past the end of a head's data return zero (tail rows, padding).
-    const unsigned q_bytes = (unsigned)((size_t)N * DK * 2), v_bytes = (unsigned)((size_t)N * DV * 2);
+    // Buffer resources: loads past the end of a head's data return zero (tail rows, padding). q, k
+    // and v of source head bh % srcBH (q and k: rows ldqk apart, from a column block; all rows in
+    // reverse with rev); P, out and the states of head bh.
+    const int ldqk = p.ldqk, src = bh % p.srcBH;
+    auto row_of = [&](int t) __attribute__((always_inline)) { return p.rev ? N - 1 - t : t; };
+    const unsigned q_bytes = (unsigned)(((size_t)(N - 1) * ldqk + DK) * 2), v_bytes = (unsigned)((size_t)N * DV * 2);
+    const size_t qbase = (size_t)src * N * ldqk + (size_t)(bh / p.srcBH) * p.qcol_blk;
     const unsigned p_bytes = (unsigned)((size_t)nchunks * C * C * 2);
 
     // Barrier sequence, identical for all roles (each role runs its own loop with its own
@@ -491,9 +507,9 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     if (w >= 8) {
         // ---------------- loader waves
         const int lw = __builtin_amdgcn_readfirstlane(w - 8);  // wave-uniform: one buffer resource per wave
-        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)bh * N * DK), 0, q_bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)bh * N * DV), 0, v_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qbase), 0, q_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qbase), 0, q_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rp =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
         // This wave's share (kilobytes j = lw mod 4) of the Q, K and P rows of stage g, into its
@@ -508,7 +524,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 const int j = 4 * jj + lw;
                 const int byte = 1024 * j + 16 * lane, r = byte / G::QRB;
                 const int c = ((byte % G::QRB) >> 4) ^ (r & SwzTile<G::QRB>::M);
-                const unsigned off = (unsigned)(((tok0 + r) * DK + 8 * c) * 2);
+                const unsigned off = (unsigned)((row_of(tok0 + r) * ldqk + 8 * c) * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(bq + 1024 * j), 16, off, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(bq + G::OFF_K + 1024 * j), 16, off, 0, 0, 0);
             }
@@ -534,14 +550,14 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             unsigned off;
             __amdgpu_buffer_rsrc_t r = rq;
             if (lw < 2) {
-                off = g < total && i < kST * LPR ? (unsigned)((tok0 + i / LPR) * G::QRB + 128 * (i % LPR)) : q_bytes;
+                off = g < total && i < kST * LPR ? (unsigned)(row_of(tok0 + i / LPR) * ldqk * 2 + 128 * (i % LPR)) : q_bytes;
                 if (lw == 1) r = rk;
             } else if (lw == 2) {
                 const int plr = (kST * (s + 1) * 2 + 127) / 128;  // P lines per row up to this stage
                 off = g < total && i < kST * plr ? (unsigned)(((ci * C + kST * s + i / plr) * C) * 2 + 128 * (i % plr)) : p_bytes;
                 r = rp;
             } else {
-                off = g < total && lane < kST ? (unsigned)(((tok0 + lane) * DV + col0) * 2) : v_bytes;
+                off = g < total && lane < kST ? (unsigned)((row_of(tok0 + lane) * DV + col0) * 2) : v_bytes;
                 r = rv;
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(smem + G::OFF_SCRATCH), 16, off, 0, 0, 0);
@@ -577,13 +593,13 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     } else if (w >= 4) {
         // ---------------- state waves: R rows [wl*DK/4, (wl+1)*DK/4) x 32 columns, fp32
         const int st = threadIdx.x - 256;  // 0..255
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)bh * N * DV), 0, v_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
         // V rows of stage g: 32 rows x 4 groups of 8 columns, one 16-byte load per thread < 128
         auto load_v = [&](int g) __attribute__((always_inline)) {
             const int gg = g < total ? g : total - 1;
             const int tok0 = (gg / SPC) * C + kST * (gg % SPC);
             const int row = st >> 2, sg = st & 3;
-            const unsigned off = st < kST * 4 && g < total ? (unsigned)((tok0 + row) * DV + col0 + 8 * sg) * 2u : v_bytes;
+            const unsigned off = st < kST * 4 && g < total ? (unsigned)((row_of(tok0 + row) * DV + col0 + 8 * sg) * 2) : v_bytes;
             return buf_load16(rv, off);
         };
         auto store_v = [&](const bf16x8& v, int g) __attribute__((always_inline)) {
@@ -762,7 +778,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             for (int i = 0; i < 4; ++i) {
                 const int j = kST * s + 16 * rt_o + 4 * g4 + i;  // row within the chunk
                 const float acc = qr[i] * (gs * row_decay[i]) + pv[i];
-                const unsigned off = (unsigned)(((c0 + j) * DV + col0 + 16 * ct_o + c16) * (int)sizeof(TOUT));
+                const unsigned off = (unsigned)((row_of(c0 + j) * DV + col0 + 16 * ct_o + c16) * (int)sizeof(TOUT));
                 if constexpr (sizeof(TOUT) == 4)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 0);
                 else
@@ -884,13 +900,17 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     char* ws = reinterpret_cast<char*>(a.ws);
     MainParams mp{};
     mp.H = a.H; mp.N = a.N; mp.C = C; mp.NS = a.DV / kW; mp.nchunks = nchunks; mp.teams = a.B * a.H;
+    mp.rev = a.addr.rev;
+    mp.ldqk = a.addr.ldqk ? a.addr.ldqk : DK;
+    mp.qcol_blk = a.addr.qcol_blk;
+    mp.srcBH = a.addr.srcBH ? a.addr.srcBH : a.B * a.H;
     mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
 
     hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C,
-                       nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), a.hc);
+                       nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), a.hc, mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!a.gn.enabled) return launch_main<DK, C, TOUT, true>(a, mp);

@@ -34,10 +34,22 @@ struct GnArgs {
 };
 
 // Everything a launcher needs; filled and validated by the C-ABI layer.
+// Operand addressing of a bf16 chunkwise forward, for callers that read operands in place (the
+// backward). Zero fields mean the defaults: contiguous [B][H][N][d] tensors walked in time order.
+//   rev       token t of the walk is row N-1-t of q, k, v and out
+//   ldqk      elements between consecutive q rows (and k rows); 0: d_k
+//   qcol_blk  the workgroups of stacked head index bh read q and k from column (bh / srcBH) * qcol_blk
+//   srcBH     q, k and v of stacked head index bh are those of head bh % srcBH; 0: B * H
+// P, out and the states are laid out by the stacked head index.
+struct OpAddr {
+    int rev, ldqk, qcol_blk, srcBH;
+};
+
 struct LaunchArgs {
     int B, H, N, DK, DV;
     int in_bf16, out_bf16;
     int chunk;
+    OpAddr addr;  // bf16 chunkwise only
     const void* q;
     const void* k;
     const void* v;

@@ -204,10 +204,14 @@ def test_backward_validation(lib):
     assert bwd(lib, ws=None, wsb=0) == R.RET_ERR_WORKSPACE
     need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(shape()), 64, 0)
     assert bwd(lib, wsb=need - 1) == R.RET_ERR_WORKSPACE
-    # the workspace holds time-reversed copies of q, k, v and dout and one fp32 output buffer
+    # bf16: the forwards read their operands in place; the workspace holds a forward's scores and
+    # the blocks of state_in^T. fp32: also reversed copies of q, k, v and dout and an fp32 output.
     s = shape()
-    rows = s.batch * s.heads * s.seq_len
-    assert need >= rows * (2 * s.d_k + 2 * s.d_v) * 2 + rows * max(s.d_k, s.d_v) * 4
+    assert need >= lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(s), 64, 0) + s.heads * s.d_k * s.d_v * 4
+    s32 = shape(i=R.RET_F32)
+    rows = s32.batch * s32.heads * s32.seq_len
+    need32 = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s32), 64, 0)
+    assert need32 >= rows * (2 * s32.d_k + 2 * s32.d_v) * 4 + rows * max(s32.d_k, s32.d_v) * 4
     assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s), 0, 0) == ctypes.c_size_t(-1).value
 
 
