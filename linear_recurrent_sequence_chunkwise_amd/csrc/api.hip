@@ -131,9 +131,7 @@ hipError_t stage_rotation(const ret_shape* s, const ret::RotConsts& rc, const vo
     char* base = static_cast<char*>(*ws);
     const long rows = (long)s->batch * s->heads * s->seq_len;
     const int bf = s->in_dtype == RET_BF16;
-    hipError_t e = ret::launch_rotate(rows, s->seq_len, s->d_k, *q, bf, base, bf, rc, 0, st);
-    if (e != hipSuccess) return e;
-    e = ret::launch_rotate(rows, s->seq_len, s->d_k, *k, bf, base + A, bf, rc, 0, st);
+    const hipError_t e = ret::launch_rotate2(rows, s->seq_len, s->d_k, *q, base, *k, base + A, bf, bf, rc, 0, st);
     if (e != hipSuccess) return e;
     *q = base;
     *k = base + A;
@@ -351,8 +349,9 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const 
     hipError_t e = ret::launch_chunkwise_bwd(b);
     // gradients at the rotated q and k, turned back by the inverse rotation (in place)
     const long rrows = (long)shape->batch * shape->heads * shape->seq_len;
-    if (e == hipSuccess && rot && dq) e = ret::launch_rotate(rrows, shape->seq_len, shape->d_k, dq, 0, dq, 0, rc, 1, st);
-    if (e == hipSuccess && rot && dk) e = ret::launch_rotate(rrows, shape->seq_len, shape->d_k, dk, 0, dk, 0, rc, 1, st);
+    if (e == hipSuccess && rot && (dq || dk))
+        e = ret::launch_rotate2(rrows, shape->seq_len, shape->d_k, dq ? dq : dk, dq ? dq : dk, dq && dk ? dk : nullptr,
+                                dq && dk ? dk : nullptr, 0, 0, rc, 1, st);
     return device_status(e, "retention_chunkwise_bwd launch");
 }
 

@@ -243,6 +243,9 @@ hipError_t launch_chunkwise_bwd(const BwdArgs& b);
 // buffer. inverse != 0 turns by the opposite angles.
 hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc,
                          int inverse, hipStream_t stream);
+// Two tensors of the same shape in one launch (x0 -> y0, x1 -> y1; x1 may be null).
+hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, int x_bf16, int y_bf16,
+                          const RotConsts& rc, int inverse, hipStream_t stream);
 // Residual linear attention operands: qo = phi(q) (qo null: phi is the identity and q is used as
 // is), ko / vo = phi(k) / v shifted by P = window + 1 rows, the first rows from the window rows kp,
 // vp ([rows / N][P][d], of which the last prev_len hold tokens) or zero.

@@ -56,11 +56,19 @@ template <> struct Vec8<float> {
 // elements before writing them, and no two threads share an element.
 constexpr int RB = 8;
 
+// Two tensors in one launch: units [0, units) turn x0 into y0, units [units, 2 units) x1 into y1
+// (x1 null: one tensor).
 template <typename TI, typename TO, int PAIRS>
-__global__ __launch_bounds__(256) void rotate_kernel(long units, int N, int d, const TI* x, TO* y, RotConsts rc, float sgn) {
+__global__ __launch_bounds__(256) void rotate_kernel(long units, int N, int d, const TI* x0, TO* y0, const TI* x1, TO* y1,
+                                                     RotConsts rc, float sgn) {
     const int per_row = d / (2 * PAIRS);
     const int nblk = (N + RB - 1) / RB;
-    for (long u = (long)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += (long)gridDim.x * blockDim.x) {
+    const long all = x1 ? 2 * units : units;
+    for (long uu = (long)blockIdx.x * blockDim.x + threadIdx.x; uu < all; uu += (long)gridDim.x * blockDim.x) {
+        const bool second = uu >= units;
+        const long u = second ? uu - units : uu;
+        const TI* x = second ? x1 : x0;
+        TO* y = second ? y1 : y0;
         const int i0 = (int)(u % per_row) * PAIRS;  // first pair
         const long blk = u / per_row;
         const long bh = blk / nblk;
@@ -112,30 +120,36 @@ __global__ __launch_bounds__(256) void rotate_kernel(long units, int N, int d, c
 }
 
 template <typename TI, typename TO>
-hipError_t launch_t(long rows, int N, int d, const void* x, void* y, const RotConsts& rc, float sgn, hipStream_t st) {
+hipError_t launch_t(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, const RotConsts& rc, float sgn,
+                    hipStream_t st) {
     const bool vec = d % 8 == 0;
     const long units = rows / N * ((N + RB - 1) / RB) * (long)(d / (vec ? 8 : 2));
-    const long blocks = (units + 255) / 256;
+    const long blocks = ((x1 ? 2 : 1) * units + 255) / 256;
     const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
     if (vec)
-        hipLaunchKernelGGL((rotate_kernel<TI, TO, 4>), dim3(grid), dim3(256), 0, st, units, N, d, static_cast<const TI*>(x),
-                           static_cast<TO*>(y), rc, sgn);
+        hipLaunchKernelGGL((rotate_kernel<TI, TO, 4>), dim3(grid), dim3(256), 0, st, units, N, d, static_cast<const TI*>(x0),
+                           static_cast<TO*>(y0), static_cast<const TI*>(x1), static_cast<TO*>(y1), rc, sgn);
     else
-        hipLaunchKernelGGL((rotate_kernel<TI, TO, 1>), dim3(grid), dim3(256), 0, st, units, N, d, static_cast<const TI*>(x),
-                           static_cast<TO*>(y), rc, sgn);
+        hipLaunchKernelGGL((rotate_kernel<TI, TO, 1>), dim3(grid), dim3(256), 0, st, units, N, d, static_cast<const TI*>(x0),
+                           static_cast<TO*>(y0), static_cast<const TI*>(x1), static_cast<TO*>(y1), rc, sgn);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc, int inverse,
-                         hipStream_t stream) {
+hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, int x_bf16, int y_bf16,
+                          const RotConsts& rc, int inverse, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     const float sgn = inverse ? -1.f : 1.f;
-    if (x_bf16 && y_bf16) return launch_t<bf16, bf16>(rows, N, d, x, y, rc, sgn, stream);
-    if (x_bf16) return launch_t<bf16, float>(rows, N, d, x, y, rc, sgn, stream);
-    if (y_bf16) return launch_t<float, bf16>(rows, N, d, x, y, rc, sgn, stream);
-    return launch_t<float, float>(rows, N, d, x, y, rc, sgn, stream);
+    if (x_bf16 && y_bf16) return launch_t<bf16, bf16>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
+    if (x_bf16) return launch_t<bf16, float>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
+    if (y_bf16) return launch_t<float, bf16>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
+    return launch_t<float, float>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
+}
+
+hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc, int inverse,
+                         hipStream_t stream) {
+    return launch_rotate2(rows, N, d, x, y, nullptr, nullptr, x_bf16, y_bf16, rc, inverse, stream);
 }
 
 }  // namespace ret
