@@ -2,22 +2,24 @@
 // (abeam.tech RetNet summary, retention as content-based reference times distance-based
 // forgetting; "Training in parallel"): O = (Q K^T (.) D) V, D[n][m] = g^(n-m) for n >= m.
 //
-// One workgroup per (64 query rows, b, h) owns all d_v output columns, so the optional per-head
-// GroupNorm is computed inside it. For each 32-key block up to the diagonal:
+// One workgroup of eight waves per (64 query rows, b, h) owns all d_v output columns, so the
+// optional per-head GroupNorm is computed inside it. For each 32-key block up to the diagonal:
 //   - K and V blocks are staged in LDS; the next block's rows are loaded into registers while the
 //     current block is computed, and written to LDS after the block's reads are done;
-//   - each wave computes S^T = K Q^T for its 16 query rows (Q fragments stay in registers and serve
+//   - each wave computes one 16 x 16 tile of S^T = K Q^T (Q fragments stay in registers and serve
 //     as the B operand), so that each lane holds 4 consecutive keys of one query row; it applies
 //     the causal mask and the decay g^(n-m) in registers and writes P to LDS as a bf16 high part and
 //     a bf16 low part, 8 bytes each (P spans the whole sequence here, so a single bf16 rounding of
 //     P would dominate the error);
-//   - the four waves, arranged 2 x 2 over (rows, columns), accumulate P V with both parts.
+//   - the eight waves, arranged 2 x 4 over (rows, column quarters), accumulate P V with both
+//     parts; two waves per SIMD, so that one's LDS and load latencies overlap the other's work.
 #include "common.hpp"
 
 namespace ret {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kKB = 32;  // keys per block
 
 template <int DK, int DV>
@@ -29,22 +31,28 @@ struct ParLds {
     bf16 Vs[kKB * LV];
     bf16 Phi[64 * LP];
     bf16 Plo[64 * LP];
-    float red[2][64];
+    float red[4][64];
 };
 
+// Eight waves, two per SIMD. Scores: wave w computes the 16 x 16 tile S^T of query tile w & 3 and
+// key tile w >> 2 of the block. P V: wave w owns rows 32 (w >> 2) .. +32 and the column quarter
+// (w & 3) * DV / 4 .. +DV/4.
 template <int DK, int DV, typename TOUT, bool GN>
 __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const bf16* __restrict__ q,
                                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                             TOUT* __restrict__ out, HeadConsts hc, GnArgs gn) {
     using Lds = ParLds<DK, DV>;
     constexpr int LK = Lds::LK, LV = Lds::LV, LP = Lds::LP;
-    constexpr int CT = DV / 32;  // 16-column tiles per wave (each wave owns DV/2 columns)
+    constexpr int CQ = DV / 4;   // columns per wave in P V
+    constexpr int CT = CQ / 16;  // 16-column tiles per wave
+    static_assert(CQ % 16 == 0, "d_v must split into four groups of 16-column tiles");
     extern __shared__ char smem_raw[];
     Lds& sm = *reinterpret_cast<Lds*>(smem_raw);
 
     const int qb = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
-    const int wr = w >> 1, wc = w & 1;
+    const int qt = w & 3, kt = w >> 2;  // scores tile
+    const int wr = w >> 2, wc = w & 3;  // P V rows and column quarter
     const int n0 = qb * 64;
     const float l2g = hc.log2g[h];
     const bf16* qh = q + (size_t)bh * N * DK;
@@ -52,9 +60,9 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
     const bf16* vh = v + (size_t)bh * N * DV;
 
     bf16x8 qa[DK / 32];
-    const bool qok = n0 + 16 * w + c16 < N;
+    const bool qok = n0 + 16 * qt + c16 < N;
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) qa[ks] = qok ? frag_rowmajor(qh, DK, n0 + 16 * w, 32 * ks, lane) : zero_bf16x8();
+    for (int ks = 0; ks < DK / 32; ++ks) qa[ks] = qok ? frag_rowmajor(qh, DK, n0 + 16 * qt, 32 * ks, lane) : zero_bf16x8();
 
     f32x4 acc[2][CT];
 #pragma unroll
@@ -64,21 +72,21 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
 
     const int nkb = min((n0 + 64 + kKB - 1) / kKB, (N + kKB - 1) / kKB);  // key blocks up to the diagonal
     // K and V rows of the next block, loaded into registers while this block is computed (16-byte
-    // pieces, idx = threadIdx.x + kThreads * j; rows past the sequence read as zero)
-    constexpr int NKR = kKB * (DK / 8) / kThreads, NVR = kKB * (DV / 8) / kThreads;
-    static_assert(kKB * (DK / 8) % kThreads == 0 && kKB * (DV / 8) % kThreads == 0, "whole pieces per thread");
+    // pieces, idx = threadIdx.x + kThreads * j < pieces; rows past the sequence read as zero)
+    constexpr int KP = kKB * (DK / 8), VP = kKB * (DV / 8);  // 16-byte pieces of a block
+    constexpr int NKR = (KP + kThreads - 1) / kThreads, NVR = (VP + kThreads - 1) / kThreads;
     bf16x8 kr[NKR], vr[NVR];
     auto load_block = [&](int kb) __attribute__((always_inline)) {
         const int m0 = kb * kKB;
 #pragma unroll
         for (int j = 0; j < NKR; ++j) {
             const int idx = threadIdx.x + kThreads * j, r = idx / (DK / 8), sg = idx % (DK / 8);
-            kr[j] = m0 + r < N ? *reinterpret_cast<const bf16x8*>(kh + (size_t)(m0 + r) * DK + 8 * sg) : zero_bf16x8();
+            kr[j] = (idx < KP && m0 + r < N) ? *reinterpret_cast<const bf16x8*>(kh + (size_t)(m0 + r) * DK + 8 * sg) : zero_bf16x8();
         }
 #pragma unroll
         for (int j = 0; j < NVR; ++j) {
             const int idx = threadIdx.x + kThreads * j, r = idx / (DV / 8), sg = idx % (DV / 8);
-            vr[j] = m0 + r < N ? *reinterpret_cast<const bf16x8*>(vh + (size_t)(m0 + r) * DV + 8 * sg) : zero_bf16x8();
+            vr[j] = (idx < VP && m0 + r < N) ? *reinterpret_cast<const bf16x8*>(vh + (size_t)(m0 + r) * DV + 8 * sg) : zero_bf16x8();
         }
     };
     load_block(0);
@@ -88,25 +96,23 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
 #pragma unroll
         for (int j = 0; j < NKR; ++j) {
             const int idx = threadIdx.x + kThreads * j, r = idx / (DK / 8), sg = idx % (DK / 8);
-            *reinterpret_cast<bf16x8*>(&sm.Ks[r * LK + 8 * sg]) = kr[j];
+            if (idx < KP) *reinterpret_cast<bf16x8*>(&sm.Ks[r * LK + 8 * sg]) = kr[j];
         }
 #pragma unroll
         for (int j = 0; j < NVR; ++j) {
             const int idx = threadIdx.x + kThreads * j, r = idx / (DV / 8), sg = idx % (DV / 8);
-            *reinterpret_cast<bf16x8*>(&sm.Vs[r * LV + 8 * sg]) = vr[j];
+            if (idx < VP) *reinterpret_cast<bf16x8*>(&sm.Vs[r * LV + 8 * sg]) = vr[j];
         }
         __syncthreads();
         if (kb + 1 < nkb) load_block(kb + 1);
-        // S^T for the key tiles of this block against query rows n0 + 16w .. +16: lane (g4, c16) ends
-        // with keys m0 + 16kt + 4g4 + i of query row n0 + 16w + c16
-#pragma unroll
-        for (int kt = 0; kt < kKB / 16; ++kt) {
+        // S^T tile: lane (g4, c16) ends with keys m0 + 16kt + 4g4 + i of query row n0 + 16qt + c16
+        {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (m0 + 16 * kt <= n0 + 16 * w + 15) {  // a tile wholly above the diagonal stays zero
+            if (m0 + 16 * kt <= n0 + 16 * qt + 15) {  // a tile wholly above the diagonal stays zero
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks) s = mfma16(frag_rowmajor(sm.Ks, LK, 16 * kt, 32 * ks, lane), qa[ks], s);
             }
-            const int n = n0 + 16 * w + c16;
+            const int n = n0 + 16 * qt + c16;
             bf16x4 hi, lo;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -117,22 +123,21 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
                 hi[i] = a;
                 lo[i] = c;
             }
-            *reinterpret_cast<bf16x4*>(&sm.Phi[(16 * w + c16) * LP + 16 * kt + 4 * g4]) = hi;
-            *reinterpret_cast<bf16x4*>(&sm.Plo[(16 * w + c16) * LP + 16 * kt + 4 * g4]) = lo;
+            *reinterpret_cast<bf16x4*>(&sm.Phi[(16 * qt + c16) * LP + 16 * kt + 4 * g4]) = hi;
+            *reinterpret_cast<bf16x4*>(&sm.Plo[(16 * qt + c16) * LP + 16 * kt + 4 * g4]) = lo;
         }
         __syncthreads();
-        // P V: wave (wr, wc) owns rows 32wr .. +32 and columns wc*DV/2 .. +DV/2
-#pragma unroll
-        for (int ks = 0; ks < kKB / 32; ++ks) {
+        // P V for rows 32wr .. +32, columns wc*CQ .. +CQ
+        {
             bf16x8 ahi[2], alo[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                ahi[rt] = frag_rowmajor(sm.Phi, LP, 32 * wr + 16 * rt, 32 * ks, lane);
-                alo[rt] = frag_rowmajor(sm.Plo, LP, 32 * wr + 16 * rt, 32 * ks, lane);
+                ahi[rt] = frag_rowmajor(sm.Phi, LP, 32 * wr + 16 * rt, 0, lane);
+                alo[rt] = frag_rowmajor(sm.Plo, LP, 32 * wr + 16 * rt, 0, lane);
             }
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const bf16x8 b = lds_frag_kmajor(sm.Vs, LV, 32 * ks, wc * (DV / 2) + 16 * ct, lane);
+                const bf16x8 b = lds_frag_kmajor(sm.Vs, LV, 0, wc * CQ + 16 * ct, lane);
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     acc[rt][ct] = mfma16(ahi[rt], b, acc[rt][ct]);
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
     }
 
     if constexpr (GN) {
-        // row statistics over all DV columns: each wave holds DV/2 of them
+        // row statistics over all DV columns: each wave holds a quarter of them
         float mean[2][4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 32 * wr + 16 * rt + 4 * g4 + i;
-                mean[rt][i] = (sm.red[0][r] + sm.red[1][r]) * (1.0f / DV);
+                mean[rt][i] = ((sm.red[0][r] + sm.red[1][r]) + (sm.red[2][r] + sm.red[3][r])) * (1.0f / DV);
             }
         __syncthreads();
 #pragma unroll
@@ -183,11 +188,11 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 32 * wr + 16 * rt + 4 * g4 + i;
-                const float var = (sm.red[0][r] + sm.red[1][r]) * (1.0f / DV);
+                const float var = ((sm.red[0][r] + sm.red[1][r]) + (sm.red[2][r] + sm.red[3][r])) * (1.0f / DV);
                 const float inv = rsqrtf(var + gn.eps);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const int c = wc * (DV / 2) + 16 * ct + c16;
+                    const int c = wc * CQ + 16 * ct + c16;
                     const float wv = gn.weight ? gn.weight[(size_t)h * DV + c] : 1.f;
                     const float bv = gn.bias ? gn.bias[(size_t)h * DV + c] : 0.f;
                     acc[rt][ct][i] = (acc[rt][ct][i] - mean[rt][i]) * inv * wv + bv;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
             if (n < N) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const size_t e = ((size_t)bh * N + n) * DV + wc * (DV / 2) + 16 * ct + c16;
+                    const size_t e = ((size_t)bh * N + n) * DV + wc * CQ + 16 * ct + c16;
                     float val = acc[rt][ct][i];
                     if constexpr (GN) {
                         if (gn.gate) val *= swish(gate_at(gn, e));  // the swish gate after GroupNorm
