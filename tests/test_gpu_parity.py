@@ -753,3 +753,71 @@ def test_rla_decode_workload(orc):
     report("rla decode workload out", rel_err(o, ref), TOL["bf16"])
     report("rla decode workload state", rel_err(sd, ref_s), TOL["bf16"])
     print(f"  rla decode workload vs the exact map: out {rel_err(o, ex):.3e}, state {rel_err(sd, ex_s):.3e}", flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# Every supported shape against the oracle (small N, ragged, with a state): bf16 chunkwise
+# (d_k in {64, 256} x d_v in {32 .. 512}), fp32 chunkwise (d_k in {64, 128, 256}), the decode step
+# (any d_k, d_v/4 dividing 256) and the backward (whose column-block split depends on the shape).
+@pytest.mark.parametrize("dk", [64, 256])
+@pytest.mark.parametrize("dv", [32, 64, 128, 256, 512])
+def test_bf16_chunkwise_shape_sweep(orc, dk, dv):
+    B, H, N = 1, 2, 300
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=800 + dk + dv)
+    s0 = I.make_state(B, H, dk, dv, seed=801, scale=0.02)
+    gam = [0.9, 0.999]
+    ref, ref_s = orc.recurrent(q, k, v, gam, state_in=s0)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    for C in (64, 128):
+        o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d)
+        report(f"bf16 ({dk},{dv}) C={C} out", rel_err(o, ref), TOL["bf16"])
+        report(f"bf16 ({dk},{dv}) C={C} state", rel_err(s, ref_s), TOL["bf16"])
+    o, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, state_in=s0d, groupnorm=R.GroupNorm(1e-5), want_state=False)
+    report(f"bf16 ({dk},{dv}) GN out", rel_err(o, orc.groupnorm(ref, 1e-5)), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dk", [64, 128, 256])
+@pytest.mark.parametrize("dv", [64, 192, 512])
+def test_fp32_chunkwise_shape_sweep(orc, dk, dv):
+    B, H, N = 1, 2, 200
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "f32", seed=810 + dk + dv)
+    s0 = I.make_state(B, H, dk, dv, seed=811, scale=0.05)
+    gam = [0.8, 0.99]
+    ref, ref_s = orc.recurrent(q, k, v, gam, state_in=s0)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    for C in (64, 128):
+        o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d)
+        report(f"fp32 ({dk},{dv}) C={C} out", rel_err(o, ref), TOL["f32"])
+        report(f"fp32 ({dk},{dv}) C={C} state", rel_err(s, ref_s), TOL["f32"])
+    ref_p, _ = orc.recurrent(q, k, v, gam)
+    report(f"fp32 ({dk},{dv}) parallel", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref_p), TOL["f32"])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(1, 4), (100, 64), (256, 1024), (1000, 8), (64, 16)])
+def test_decode_step_shape_sweep(orc, dt, dk, dv):
+    B, H = 3, 2
+    q, k, v = I.make_qkv(B, H, 1, dk, dv, dt, seed=820 + dk + dv)
+    state = I.make_state(B, H, dk, dv, seed=821, scale=0.05)
+    gam = [0.9, 0.5]
+    qd, kd, vd, sd = dev(q[:, :, 0], k[:, :, 0], v[:, :, 0], state)
+    o = R.recurrent_step(qd, kd, vd, gam, sd)
+    ro, rs = orc.step(q[:, :, 0], k[:, :, 0], v[:, :, 0], gam, state)
+    report(f"decode {dt} ({dk},{dv}) out", rel_err(o, ro), TOL[dt])
+    report(f"decode {dt} ({dk},{dv}) state", rel_err(sd, rs), TOL[dt])
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("bf16", 64, 512), ("bf16", 256, 256), ("bf16", 256, 128), ("bf16", 64, 128),
+                                      ("bf16", 256, 64), ("bf16", 64, 256), ("f32", 128, 128), ("f32", 64, 512),
+                                      ("f32", 256, 64)])
+def test_backward_shape_sweep(orc, dt, dk, dv):
+    B, H, N = 1, 2, 260
+    q, k, v = I.make_qkv(B, H, N, dk, dv, dt, seed=830 + dk + dv)
+    dout = _dout((B, H, N, dv), q.dtype, 831)
+    s0 = I.make_state(B, H, dk, dv, seed=832, scale=0.02)
+    gam = [0.9, 0.99]
+    ref = orc.recurrent_bwd(q, k, v, gam, dout, state_in=s0)
+    qd, kd, vd, dod, s0d = dev(q, k, v, dout, s0)
+    got = R.chunkwise_bwd(qd, kd, vd, gam, dod, 128, state_in=s0d)
+    for name, g_, r_ in zip(("dq", "dk", "dv", "dstate_in"), got, ref):
+        report(f"backward {dt} ({dk},{dv}) {name}", rel_err(g_, r_), TOL[dt])
