@@ -3,7 +3,8 @@
 // forgetting; "Training in parallel"): O = (Q K^T (.) D) V, D[n][m] = g^(n-m) for n >= m.
 //
 // One workgroup of eight waves per (64 query rows, b, h) owns all d_v output columns, so the
-// optional per-head GroupNorm is computed inside it. For each 32-key block up to the diagonal:
+// optional per-head GroupNorm is computed inside it. Workgroups run longest first (query blocks
+// from the end of the sequence), which balances the causal triangle's unequal rows over the CUs. For each 32-key block up to the diagonal:
 //   - K and V blocks are staged in LDS; the next block's rows are loaded into registers while the
 //     current block is computed, and written to LDS after the block's reads are done;
 //   - each wave computes one 16 x 16 tile of S^T = K Q^T (Q fragments stay in registers and serve
@@ -49,7 +50,12 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
     extern __shared__ char smem_raw[];
     Lds& sm = *reinterpret_cast<Lds*>(smem_raw);
 
-    const int qb = blockIdx.x, bh = blockIdx.y, h = bh % H;
+    // Workgroup order: longest first (query block nqb - 1 has the most key blocks), and within one
+    // query block the heads in turn. Workgroup i runs on XCD i % 8, so with B*H a multiple of 8 an
+    // XCD holds the heads bh = XCD (mod 8), and its concurrent workgroups stream the same K and V
+    // blocks through its L2.
+    const int nqb = (N + 63) / 64, BH = gridDim.x / nqb;
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH, h = bh % H;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
     const int qt = w & 3, kt = w >> 2;  // scores tile
     const int wr = w >> 2, wc = w & 3;  // P V rows and column quarter
@@ -224,7 +230,7 @@ hipError_t launch_typed(const LaunchArgs& a) {
     const void* kern = reinterpret_cast<const void*>(parallel_kernel<DK, DV, TOUT, GN>);
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((parallel_kernel<DK, DV, TOUT, GN>), dim3((a.N + 63) / 64, a.B * a.H), dim3(kThreads), lds, a.stream,
+    hipLaunchKernelGGL((parallel_kernel<DK, DV, TOUT, GN>), dim3((a.N + 63) / 64 * a.B * a.H), dim3(kThreads), lds, a.stream,
                        a.H, a.N, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOUT*)a.out, a.hc, a.gn);
     return hipGetLastError();
 }
