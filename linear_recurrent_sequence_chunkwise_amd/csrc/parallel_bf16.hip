@@ -4,16 +4,18 @@
 //
 // One workgroup of eight waves per (64 query rows, b, h) owns all d_v output columns, so the
 // optional per-head GroupNorm is computed inside it. Workgroups run longest first (query blocks
-// from the end of the sequence), which balances the causal triangle's unequal rows over the CUs. For each 32-key block up to the diagonal:
-//   - K and V blocks are staged in LDS; the next block's rows are loaded into registers while the
-//     current block is computed, and written to LDS after the block's reads are done;
+// from the end of the sequence), which balances the causal triangle's unequal rows over the CUs.
+// The keys go by in 32-key blocks up to the diagonal, software-pipelined with one barrier per block:
+//   - K and V blocks come in through unconditional buffer loads into registers one iteration
+//     ahead, and are written to double-buffered, swizzled LDS tiles;
 //   - each wave computes one 16 x 16 tile of S^T = K Q^T (Q fragments stay in registers and serve
 //     as the B operand), so that each lane holds 4 consecutive keys of one query row; it applies
 //     the causal mask and the decay g^(n-m) in registers and writes P to LDS as a bf16 high part and
-//     a bf16 low part, 8 bytes each (P spans the whole sequence here, so a single bf16 rounding of
-//     P would dominate the error);
-//   - the eight waves, arranged 2 x 4 over (rows, column quarters), accumulate P V with both
-//     parts; two waves per SIMD, so that one's LDS and load latencies overlap the other's work.
+//     a bf16 low part (P spans the whole sequence here, so a single bf16 rounding of P would
+//     dominate the error);
+//   - the scores of block kb + 1 are computed in the same iteration as P V of block kb: the eight
+//     waves, arranged 2 x 4 over (rows, column quarters), accumulate P V with both parts; two waves
+//     per SIMD, so that one's LDS and load latencies overlap the other's work.
 #include "common.hpp"
 
 namespace ret {
@@ -25,13 +27,13 @@ constexpr int kKB = 32;  // keys per block
 
 template <int DK, int DV>
 struct ParLds {
-    static constexpr int LK = DK + 8;    // K rows: 16-byte reads
-    static constexpr int LV = DV + 16;   // V rows: transposing reads
-    static constexpr int LP = kKB + 8;   // P rows: 8-byte writes, 16-byte reads
-    bf16 Ks[kKB * LK];
-    bf16 Vs[kKB * LV];
-    bf16 Phi[64 * LP];
-    bf16 Plo[64 * LP];
+    // K and V rows unpadded, their 16-byte chunks swizzled (SwzTile): fragment reads of 16 rows and
+    // transposing reads then touch distinct banks
+    bf16 Ks[2][kKB * DK];  // K blocks kb + 1 and kb + 2 (by parity)
+    bf16 Vs[2][kKB * DV];  // V blocks kb and kb + 1
+    // P of blocks kb and kb + 1: row r holds the 32 high parts then the 32 low parts (128 bytes),
+    // swizzled like K and V
+    bf16 P[2][64 * 2 * kKB];
     float red[4][64];
 };
 
@@ -43,7 +45,9 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
                                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                             TOUT* __restrict__ out, HeadConsts hc, GnArgs gn) {
     using Lds = ParLds<DK, DV>;
-    constexpr int LK = Lds::LK, LV = Lds::LV, LP = Lds::LP;
+    using KT = SwzTile<DK * 2>;
+    using VT = SwzTile<DV * 2>;
+    using PT = SwzTile<4 * kKB>;  // P rows: 32 high then 32 low bf16 parts
     constexpr int CQ = DV / 4;   // columns per wave in P V
     constexpr int CT = CQ / 16;  // 16-column tiles per wave
     static_assert(CQ % 16 == 0, "d_v must split into four groups of 16-column tiles");
@@ -77,80 +81,122 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
         for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nkb = min((n0 + 64 + kKB - 1) / kKB, (N + kKB - 1) / kKB);  // key blocks up to the diagonal
-    // K and V rows of the next block, loaded into registers while this block is computed (16-byte
-    // pieces, idx = threadIdx.x + kThreads * j < pieces; rows past the sequence read as zero)
+    // K and V rows of a block go through registers (16-byte pieces, idx = threadIdx.x + kThreads * j
+    // < pieces; rows past the sequence read as zero): loaded one iteration before they are written
+    // to LDS, so that a whole iteration hides the load latency.
     constexpr int KP = kKB * (DK / 8), VP = kKB * (DV / 8);  // 16-byte pieces of a block
     constexpr int NKR = (KP + kThreads - 1) / kThreads, NVR = (VP + kThreads - 1) / kThreads;
     bf16x8 kr[NKR], vr[NVR];
-    auto load_block = [&](int kb) __attribute__((always_inline)) {
-        const int m0 = kb * kKB;
+    // Buffer loads over the block's rows (the resource ends at the sequence, so rows past N and
+    // pieces past the block read as zero): no branches, so the compiler's load waits stay exact.
+    auto load_k = [&](int kb) __attribute__((always_inline)) {
+        const int m0 = kb * kKB, rows = min(kKB, N - m0);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kh + (size_t)m0 * DK), 0, (unsigned)(rows * DK * 2), 0x00020000);
 #pragma unroll
         for (int j = 0; j < NKR; ++j) {
-            const int idx = threadIdx.x + kThreads * j, r = idx / (DK / 8), sg = idx % (DK / 8);
-            kr[j] = (idx < KP && m0 + r < N) ? *reinterpret_cast<const bf16x8*>(kh + (size_t)(m0 + r) * DK + 8 * sg) : zero_bf16x8();
-        }
-#pragma unroll
-        for (int j = 0; j < NVR; ++j) {
-            const int idx = threadIdx.x + kThreads * j, r = idx / (DV / 8), sg = idx % (DV / 8);
-            vr[j] = (idx < VP && m0 + r < N) ? *reinterpret_cast<const bf16x8*>(vh + (size_t)(m0 + r) * DV + 8 * sg) : zero_bf16x8();
+            const int idx = threadIdx.x + kThreads * j;
+            kr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)(idx * 16), 0, 0));
         }
     };
-    load_block(0);
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int m0 = kb * kKB;
-        __syncthreads();  // the previous block's LDS reads are done
+    auto load_v = [&](int kb) __attribute__((always_inline)) {
+        const int m0 = kb * kKB, rows = min(kKB, N - m0);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vh + (size_t)m0 * DV), 0, (unsigned)(rows * DV * 2), 0x00020000);
+#pragma unroll
+        for (int j = 0; j < NVR; ++j) {
+            const int idx = threadIdx.x + kThreads * j;
+            vr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)(idx * 16), 0, 0));
+        }
+    };
+    auto store_k = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NKR; ++j) {
             const int idx = threadIdx.x + kThreads * j, r = idx / (DK / 8), sg = idx % (DK / 8);
-            if (idx < KP) *reinterpret_cast<bf16x8*>(&sm.Ks[r * LK + 8 * sg]) = kr[j];
+            if (idx < KP) *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(sm.Ks[buf]) + KT::off(r, sg)) = kr[j];
         }
+    };
+    auto store_v = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NVR; ++j) {
             const int idx = threadIdx.x + kThreads * j, r = idx / (DV / 8), sg = idx % (DV / 8);
-            if (idx < VP) *reinterpret_cast<bf16x8*>(&sm.Vs[r * LV + 8 * sg]) = vr[j];
+            if (idx < VP) *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(sm.Vs[buf]) + VT::off(r, sg)) = vr[j];
         }
-        __syncthreads();
-        if (kb + 1 < nkb) load_block(kb + 1);
-        // S^T tile: lane (g4, c16) ends with keys m0 + 16kt + 4g4 + i of query row n0 + 16qt + c16
-        {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (m0 + 16 * kt <= n0 + 16 * qt + 15) {  // a tile wholly above the diagonal stays zero
+    };
+    // S^T tile of block kb: lane (g4, c16) ends with keys m0 + 16kt + 4g4 + i of query row
+    // n0 + 16qt + c16; P = S (.) D goes to LDS as bf16 high and low parts.
+    auto scores = [&](int kb) __attribute__((always_inline)) {
+        const int m0 = kb * kKB, buf = kb & 1;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        if (m0 + 16 * kt <= n0 + 16 * qt + 15) {  // a tile wholly above the diagonal stays zero
+            constexpr int G = DK / 32 < 4 ? DK / 32 : 4;  // K fragments read together
 #pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks) s = mfma16(frag_rowmajor(sm.Ks, LK, 16 * kt, 32 * ks, lane), qa[ks], s);
-            }
-            const int n = n0 + 16 * qt + c16;
-            bf16x4 hi, lo;
+            for (int k0 = 0; k0 < DK / 32; k0 += G) {
+                bf16x8 kf[G];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + 16 * kt + 4 * g4 + i;
-                const float d = n >= m ? decay_pow(l2g, (float)(n - m)) : 0.f;
-                bf16 a, c;
-                split_hi_lo(s[i] * d, a, c);
-                hi[i] = a;
-                lo[i] = c;
+                for (int i = 0; i < G; ++i) kf[i] = frag_rowmajor_swz<DK * 2>(reinterpret_cast<const char*>(sm.Ks[buf]), 16 * kt, 32 * (k0 + i), lane);
+#pragma unroll
+                for (int i = 0; i < G; ++i) s = mfma16(kf[i], qa[k0 + i], s);
             }
-            *reinterpret_cast<bf16x4*>(&sm.Phi[(16 * qt + c16) * LP + 16 * kt + 4 * g4]) = hi;
-            *reinterpret_cast<bf16x4*>(&sm.Plo[(16 * qt + c16) * LP + 16 * kt + 4 * g4]) = lo;
         }
-        __syncthreads();
-        // P V for rows 32wr .. +32, columns wc*CQ .. +CQ
-        {
-            bf16x8 ahi[2], alo[2];
+        const int n = n0 + 16 * qt + c16;
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + 16 * kt + 4 * g4 + i;
+            const float d = n >= m ? decay_pow(l2g, (float)(n - m)) : 0.f;
+            bf16 a, c;
+            split_hi_lo(s[i] * d, a, c);
+            hi[i] = a;
+            lo[i] = c;
+        }
+        char* prow = reinterpret_cast<char*>(sm.P[buf]);
+        const int pr = 16 * qt + c16, pc = 2 * kt + (g4 >> 1), ps = 8 * (g4 & 1);  // row, 16-byte chunk, byte in it
+        *reinterpret_cast<bf16x4*>(prow + PT::off(pr, pc) + ps) = hi;
+        *reinterpret_cast<bf16x4*>(prow + PT::off(pr, pc + kKB / 8) + ps) = lo;
+    };
+    // P V of block kb for rows 32wr .. +32, columns wc*CQ .. +CQ
+    auto pv = [&](int kb) __attribute__((always_inline)) {
+        const int buf = kb & 1;
+        bf16x8 ahi[2], alo[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            ahi[rt] = frag_rowmajor_swz<4 * kKB>(reinterpret_cast<const char*>(sm.P[buf]), 32 * wr + 16 * rt, 0, lane);
+            alo[rt] = frag_rowmajor_swz<4 * kKB>(reinterpret_cast<const char*>(sm.P[buf]), 32 * wr + 16 * rt, kKB, lane);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const bf16x8 b = lds_frag_kmajor_swz<DV * 2>(reinterpret_cast<const char*>(sm.Vs[buf]), 0, wc * CQ + 16 * ct, lane);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                ahi[rt] = frag_rowmajor(sm.Phi, LP, 32 * wr + 16 * rt, 0, lane);
-                alo[rt] = frag_rowmajor(sm.Plo, LP, 32 * wr + 16 * rt, 0, lane);
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const bf16x8 b = lds_frag_kmajor(sm.Vs, LV, 0, wc * CQ + 16 * ct, lane);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    acc[rt][ct] = mfma16(ahi[rt], b, acc[rt][ct]);
-                    acc[rt][ct] = mfma16(alo[rt], b, acc[rt][ct]);
-                }
+                acc[rt][ct] = mfma16(ahi[rt], b, acc[rt][ct]);
+                acc[rt][ct] = mfma16(alo[rt], b, acc[rt][ct]);
             }
         }
+    };
+
+    // Software pipeline, one barrier per block. Entering iteration kb, LDS holds K(kb+1), V(kb) and
+    // P(kb), and the registers hold K(kb+2) and V(kb+1). Iteration kb writes those registers to the
+    // buffers that iteration kb-1 finished reading, loads K(kb+3) and V(kb+2), and computes the
+    // scores of block kb+1 together with P V of block kb.
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (nkb > 1) load_k(1);
+    if (nkb > 1) load_v(1);
+    __syncthreads();
+    scores(0);
+    if (nkb > 1) store_k(1);
+    if (nkb > 2) load_k(2);
+    for (int kb = 0; kb < nkb; ++kb) {
+        __syncthreads();  // iteration kb-1's reads and writes are done and visible
+        if (kb + 2 < nkb) store_k(kb & 1);
+        if (kb + 1 < nkb) store_v((kb + 1) & 1);
+        if (kb + 3 < nkb) load_k(kb + 3);
+        if (kb + 2 < nkb) load_v(kb + 2);
+        if (kb + 1 < nkb) scores(kb + 1);
+        pv(kb);
     }
 
     if constexpr (GN) {
