@@ -821,3 +821,18 @@ def test_backward_shape_sweep(orc, dt, dk, dv):
     got = R.chunkwise_bwd(qd, kd, vd, gam, dod, 128, state_in=s0d)
     for name, g_, r_ in zip(("dq", "dk", "dv", "dstate_in"), got, ref):
         report(f"backward {dt} ({dk},{dv}) {name}", rel_err(g_, r_), TOL[dt])
+
+
+# The parallel kernel's pipeline prologue and tail at one, two and three key blocks, and B*H that
+# is not a multiple of 8 (the workgroup order interleaves heads).
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
+@pytest.mark.parametrize("N", [1, 17, 32, 33, 64, 65, 96, 97, 130])
+def test_bf16_parallel_short_sequences(orc, dk, dv, N):
+    B, H = 1, 3
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=900 + N + dk)
+    gam = [0.5, 0.9, 0.999]
+    ref = orc.parallel(q, k, v, gam)
+    qd, kd, vd = dev(q, k, v)
+    report(f"parallel bf16 ({dk},{dv}) N={N}", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref), TOL["bf16"])
+    o = R.parallel_fwd(qd, kd, vd, gam, groupnorm=R.GroupNorm(1e-5), out_dtype=torch.bfloat16)
+    report(f"parallel bf16 GN ({dk},{dv}) N={N}", rel_err(o, orc.groupnorm(ref, 1e-5)), TOL["bf16"])
