@@ -227,7 +227,9 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
 
 /* Bytes of device workspace the call `fn` needs for this shape, chunk and flags (a bitwise OR of
  * RET_WS_GROUPNORM when a GroupNorm epilogue is enabled and RET_WS_ROTATION when a rotation is).
- * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid.
+ * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid or no kernel
+ * supports the shape, chunk and flags (the call itself would return RET_ERR_UNSUPPORTED; residual
+ * linear attention takes no rotation).
  * Chunkwise with bf16 inputs: the bf16 intra-chunk scores (B*H*ceil(N/chunk)*chunk^2*2 bytes)
  * when an output is wanted, plus fp32 pre-norm rows (B*H*N*d_v*4 bytes) with GroupNorm. Other
  * calls: fp32 staging rows when GroupNorm or a bf16 output needs them. A rotation adds the

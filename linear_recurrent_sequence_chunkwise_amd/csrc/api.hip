@@ -218,9 +218,32 @@ const char* retention_status_string(int32_t status) {
     }
 }
 
+// Whether a kernel exists for call fn at this shape, chunk and rotation setting: the same tests as
+// the entry points make (which also report the reason).
+bool shape_supported(int32_t fn, const ret_shape* s, int chunk, bool rot) {
+    const bool bf = s->in_dtype == RET_BF16;
+    const int dk = s->d_k, dv = s->d_v;
+    if (rot && (dk % 2 || dk / 2 > ret::kMaxPairs)) return false;
+    const bool step_ok = dv % 4 == 0 && dv / 4 <= 256 && 256 % (dv / 4) == 0;
+    switch (fn) {
+        case RET_FN_CHUNKWISE: return bf ? ret::chunkwise_bf16_supported(dk, dv, chunk) : ret::chunkwise_f32_supported(dk, dv, chunk);
+        case RET_FN_RECURRENT_STEP: return step_ok && dk <= 8192;
+        case RET_FN_PARALLEL: return bf ? ret::parallel_bf16_supported(dk, dv) : ret::parallel_f32_supported(dk, dv);
+        case RET_FN_CHUNKWISE_BWD: return ret::bwd_split(bf, dk, dv, chunk) != 0;
+        case RET_FN_RLA: {
+            const size_t vrow = (size_t)dv * elem_size(s->in_dtype);
+            if (rot || dk > 256 || dk % 4 || vrow % 16 != 0 || vrow > 4096) return false;
+            if (s->seq_len == 1) return step_ok;
+            return bf ? ret::chunkwise_bf16_supported(dk, dv, chunk) : ret::chunkwise_f32_supported(dk, dv, chunk);
+        }
+        default: return false;
+    }
+}
+
 size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t flags) {
     if (check_shape(shape, fn == RET_FN_RECURRENT_STEP) != RET_OK) return (size_t)-1;
     if (flags & ~(RET_WS_GROUPNORM | RET_WS_ROTATION)) return (size_t)-1;
+    if (!shape_supported(fn, shape, chunk, (flags & RET_WS_ROTATION) != 0)) return (size_t)-1;
     const bool gn = (flags & RET_WS_GROUPNORM) != 0;
     const size_t rot = (flags & RET_WS_ROTATION) ? rotation_ws(shape) : 0;
     switch (fn) {

@@ -179,7 +179,7 @@ def workspace_bytes(fn, B, H, N, dk, dv, in_dtype, out_dtype, chunk=0, groupnorm
     shp = _shape(B, H, N, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype))
     n = lib.retention_workspace_bytes(fn, ctypes.byref(shp), int(chunk), _flags(groupnorm, rotation))
     if n == ctypes.c_size_t(-1).value:
-        raise ValueError("invalid shape for workspace query")
+        raise ValueError("workspace query: invalid arguments, or no kernel for this shape, chunk and flags")
     return n
 
 

@@ -290,3 +290,25 @@ def test_rla_validation(lib):
     # a decode step needs only the operands
     s1 = shape(N=1)
     assert lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(s1), 0, 0) == 3 * 256
+
+
+def test_workspace_query_unsupported_shapes(lib):
+    """The query answers (size_t)-1 exactly where the call would return RET_ERR_UNSUPPORTED."""
+    bad = ctypes.c_size_t(-1).value
+    q = lambda fn, shp, C=64, fl=0: lib.retention_workspace_bytes(fn, ctypes.byref(shp), C, fl)
+    assert q(R.RET_FN_CHUNKWISE, shape(dk=128)) == bad  # bf16 chunk kernels: d_k 64 or 256
+    assert q(R.RET_FN_CHUNKWISE, shape(dk=128, i=R.RET_F32)) != bad
+    assert q(R.RET_FN_CHUNKWISE, shape(), C=96) == bad
+    assert q(R.RET_FN_CHUNKWISE_BWD, shape(dv=32)) == bad  # no column split of d_v = 32 for the swapped forwards
+    assert q(R.RET_FN_CHUNKWISE_BWD, shape(dv=128)) != bad
+    assert q(R.RET_FN_PARALLEL, shape(dk=128, dv=128)) == bad
+    assert q(R.RET_FN_PARALLEL, shape(dk=128, dv=128, i=R.RET_F32)) != bad
+    assert q(R.RET_FN_RECURRENT_STEP, shape(N=1, dv=12), 0) == bad
+    assert q(R.RET_FN_RECURRENT_STEP, shape(N=1, dv=16), 0) == 0
+    assert q(R.RET_FN_CHUNKWISE, shape(dk=64, i=R.RET_F32), 64, R.RET_WS_ROTATION) != bad
+    assert q(R.RET_FN_RECURRENT_STEP, shape(N=1, dk=7, dv=16), 0, R.RET_WS_ROTATION) == bad  # odd d_k
+    assert q(R.RET_FN_RLA, shape(), 64, R.RET_WS_ROTATION) == bad  # no rotation for residual linear attention
+    assert q(R.RET_FN_RLA, shape(N=1, dv=12), 0) == bad
+    # each rejected shape is one the call itself rejects
+    assert bwd(lib, shape(dv=32)) == R.RET_ERR_UNSUPPORTED
+    assert chunk(lib, shape(dk=128)) == R.RET_ERR_UNSUPPORTED
