@@ -215,8 +215,10 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
  * q, k, v, out: as retention_chunkwise_fwd. window >= 0. d_k <= 256, a multiple of 4; a value row (d_v elements of
  * the input dtype) a multiple of 16 bytes and at most 4 KiB. N > 1 takes the chunkwise
  * kernels (chunk and (d_k, d_v) as there); N = 1 the decode-step kernel (d_v as there).
- * Workspace: retention_workspace_bytes(RET_FN_RLA, ...): phi(q), the shifted phi(k) and v in the
- * input dtype, plus the chunkwise workspace. For bf16 inputs phi(q) and phi(k) are rounded to bf16
+ * Workspace: retention_workspace_bytes(RET_FN_RLA, ...): phi(q), the shifted phi(k) and room for
+ * the shifted v in the input dtype, plus the chunkwise workspace. Only the first
+ * min(ceil((window + 1) / 32) * 32, N) shifted value rows of each head are written there; the
+ * kernels read the later ones from v itself. For bf16 inputs phi(q) and phi(k) are rounded to bf16
  * before the matrix cores.
  */
 ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t window, int32_t feature_map,

@@ -2,6 +2,7 @@
 // validation on the host before any HIP call, per-head decay constants in fp64, workspace sizing,
 // and dispatch to the kernel launchers. No exception crosses the boundary; errors are returned
 // as ret_status with a thread-local message.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -513,6 +514,9 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     r.qo = feature_map == RET_FMAP_IDENTITY ? nullptr : w;
     r.ko = w + Aq;
     r.vo = w + 2 * Aq;
+    // shifted value rows in the workspace only up to vsplit (w + 1 rounded up to a 32-token stage,
+    // at most N); the chunkwise kernels read the later rows from v, w + 1 rows back
+    r.vsplit = (int)std::min<long long>(((long long)P + 31) / 32 * 32, N);
     hipError_t e = ret::launch_rla_prepare(r, st);
     if (e != hipSuccess) return device_status(e, "retention_rla_fwd prepare launch");
     ret::HeadConsts hc;
@@ -522,7 +526,13 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     }
     ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, w + 2 * Aq + Av, workspace_bytes - (2 * Aq + Av),
                                   hip_stream);
-    a.q = r.qo ? r.qo : q; a.k = r.ko; a.v = r.vo; a.out = out;
+    a.q = r.qo ? r.qo : q; a.k = r.ko; a.out = out;
+    if (r.vsplit == N) {
+        a.v = r.vo;  // every value row is in the prefix buffer (laid out like v)
+    } else {
+        a.v = v;
+        a.vs = ret::VShift{r.vo, r.vsplit, P};
+    }
     if (N == 1) {
         if (state_in != state_out) {
             e = ret::launch_copy_state(st_bytes / sizeof(float), state_in, state_out, st);

@@ -102,12 +102,23 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
 }
 
 // ---------------------------------------------------------------------------------------------
+// The buffer resource of the value rows of one stage (VShift): the prefix buffer of head src when
+// pre, else v of head src. Built from selected scalars, so that it stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t value_rsrc(bool pre, const bf16* v, const bf16* vpre, int src, int N, int vsplit,
+                                                             int DV) {
+    const bf16* base = pre ? vpre + (size_t)src * vsplit * DV : v + (size_t)src * N * DV;
+    const unsigned bytes = (unsigned)((size_t)(pre ? vsplit : N) * DV * 2);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+}
+
 struct MainParams {
     int H, N, C, NS, nchunks, teams;
     int rev, ldqk, qcol_blk, srcBH;  // operand addressing (OpAddr, defaults resolved)
+    int vsplit, vshift;              // value rows through VShift (vsplit = 0: plain)
     const bf16* q;
     const bf16* k;
     const bf16* v;
+    const bf16* vpre;
     const bf16* P;
     const float* state_in;
     float* state_out;
@@ -162,7 +173,8 @@ __device__ __forceinline__ void team_slice(int teams, int NS, int& team, int& sl
 
 // One (b, h, d_v slice) per workgroup. Wave w owns R rows [w*DK/4, (w+1)*DK/4) (state update) and,
 // in every 32-token stage, the 16 x 16 output tile (rows 16*(w>>1), columns 16*(w&1)).
-template <int DK, int C, typename TOUT, bool WANT_OUT>
+// VSH: value rows through VShift (residual linear attention); the plain instantiation has none of it.
+template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH>
 __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, HeadConsts hc) {
     using G = MainGeom<DK, C>;
     constexpr int RTR = DK / 64;  // 16-row R tiles per wave
@@ -199,6 +211,9 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
+    // value rows below vsplit come from the prefix buffer, the others from v shifted by vshift rows;
+    // a stage lies wholly on one side
+    const unsigned vp_bytes = (unsigned)((size_t)p.vsplit * DV * 2);
     const unsigned p_bytes = WANT_OUT ? (unsigned)((size_t)nchunks * C * C * 2) : 0u;
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(WANT_OUT ? p.P + (size_t)bh * nchunks * C * C : p.q), 0, p_bytes, 0x00020000);
@@ -218,8 +233,15 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
         }
         {
             const int row = threadIdx.x >> 2, sg = threadIdx.x & 3;  // 32 rows x 4 chunks of 8 columns
-            const unsigned off = threadIdx.x < kST * 4 ? (unsigned)((row_of(tok0 + row) * DV + col0 + 8 * sg) * 2) : v_bytes;
-            r.v = buf_load16(rv, off);
+            if constexpr (VSH) {
+                const bool pre = __builtin_amdgcn_readfirstlane((int)(tok0 < p.vsplit)) != 0;  // wave-uniform: a scalar resource
+                const int t = tok0 + row, vr = pre ? t : row_of(t) - p.vshift;
+                const unsigned off = threadIdx.x < kST * 4 && t < N ? (unsigned)((vr * DV + col0 + 8 * sg) * 2) : (pre ? vp_bytes : v_bytes);
+                r.v = buf_load16(value_rsrc(pre, p.v, p.vpre, src, N, p.vsplit, DV), off);
+            } else {
+                const unsigned off = threadIdx.x < kST * 4 ? (unsigned)((row_of(tok0 + row) * DV + col0 + 8 * sg) * 2) : v_bytes;
+                r.v = buf_load16(rv, off);
+            }
         }
         if constexpr (WANT_OUT) {
             const int per_row = 4 * (s + 1);  // 16-byte chunks needed per row: keys [0, 32(s+1))
@@ -469,7 +491,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int C, typename TOUT>
+template <int DK, int C, typename TOUT, bool VSH>
 __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
     using G = WsGeom<DK, C>;
     constexpr int NB = G::NB;
@@ -498,6 +520,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     const int ldqk = p.ldqk, src = bh % p.srcBH;
     auto row_of = [&](int t) __attribute__((always_inline)) { return p.rev ? N - 1 - t : t; };
     const unsigned q_bytes = (unsigned)(((size_t)(N - 1) * ldqk + DK) * 2), v_bytes = (unsigned)((size_t)N * DV * 2);
+    const unsigned vp_bytes = (unsigned)((size_t)p.vsplit * DV * 2);  // value rows below vsplit (VShift)
     const size_t qbase = (size_t)src * N * ldqk + (size_t)(bh / p.srcBH) * p.qcol_blk;
     const unsigned p_bytes = (unsigned)((size_t)nchunks * C * C * 2);
 
@@ -556,6 +579,11 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 const int plr = (kST * (s + 1) * 2 + 127) / 128;  // P lines per row up to this stage
                 off = g < total && i < kST * plr ? (unsigned)(((ci * C + kST * s + i / plr) * C) * 2 + 128 * (i % plr)) : p_bytes;
                 r = rp;
+            } else if constexpr (VSH) {
+                const bool pre = __builtin_amdgcn_readfirstlane((int)(tok0 < p.vsplit)) != 0;  // wave-uniform: a scalar resource
+                const int t = tok0 + lane, vr = pre ? t : row_of(t) - p.vshift;
+                off = g < total && lane < kST && t < N ? (unsigned)((vr * DV + col0) * 2) : (pre ? vp_bytes : v_bytes);
+                r = value_rsrc(pre, p.v, p.vpre, src, N, p.vsplit, DV);
             } else {
                 off = g < total && lane < kST ? (unsigned)((row_of(tok0 + lane) * DV + col0) * 2) : v_bytes;
                 r = rv;
@@ -594,13 +622,22 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
         // ---------------- state waves: R rows [wl*DK/4, (wl+1)*DK/4) x 32 columns, fp32
         const int st = threadIdx.x - 256;  // 0..255
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
-        // V rows of stage g: 32 rows x 4 groups of 8 columns, one 16-byte load per thread < 128
+        // V rows of stage g: 32 rows x 4 groups of 8 columns, one 16-byte load per thread < 128 (rows
+        // below vsplit from the prefix buffer, the others from v shifted by vshift rows)
         auto load_v = [&](int g) __attribute__((always_inline)) {
             const int gg = g < total ? g : total - 1;
             const int tok0 = (gg / SPC) * C + kST * (gg % SPC);
             const int row = st >> 2, sg = st & 3;
-            const unsigned off = st < kST * 4 && g < total ? (unsigned)((row_of(tok0 + row) * DV + col0 + 8 * sg) * 2) : v_bytes;
-            return buf_load16(rv, off);
+            if constexpr (VSH) {
+                const bool pre = __builtin_amdgcn_readfirstlane((int)(tok0 < p.vsplit)) != 0;  // wave-uniform: a scalar resource
+                const int t = tok0 + row, vr = pre ? t : row_of(t) - p.vshift;
+                const unsigned off =
+                    st < kST * 4 && g < total && t < N ? (unsigned)((vr * DV + col0 + 8 * sg) * 2) : (pre ? vp_bytes : v_bytes);
+                return buf_load16(value_rsrc(pre, p.v, p.vpre, src, N, p.vsplit, DV), off);
+            } else {
+                const unsigned off = st < kST * 4 && g < total ? (unsigned)((row_of(tok0 + row) * DV + col0 + 8 * sg) * 2) : v_bytes;
+                return buf_load16(rv, off);
+            }
         };
         auto store_v = [&](const bf16x8& v, int g) __attribute__((always_inline)) {
             const int ci = g / SPC, s = g % SPC;
@@ -875,12 +912,12 @@ WsLayout ws_layout(int B, int H, int N, int DV, int C, int gn, int want_out) {
 template <int C, bool WANT_OUT>
 constexpr bool use_ws() { return WANT_OUT && C <= 256; }
 
-template <int DK, int C, typename TOUT, bool WANT_OUT>
-hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
+template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH>
+hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
     constexpr bool ws = use_ws<C, WANT_OUT>();
     const void* kern;
-    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT>);
-    else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT>);
+    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH>);
+    else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT, VSH>);
     size_t dyn;
     if constexpr (ws) dyn = WsGeom<DK, C>::BYTES;
     else dyn = MainGeom<DK, C>::BYTES;
@@ -890,6 +927,12 @@ hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
     HeadConsts hc = a.hc;
     void* args[] = {&lp, &hc};
     return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 768 : kThreads), args, dyn, a.stream);
+}
+
+// value rows through VShift only in the instantiations that need it
+template <int DK, int C, typename TOUT, bool WANT_OUT>
+hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
+    return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true>(a, mp) : launch_main_v<DK, C, TOUT, WANT_OUT, false>(a, mp);
 }
 
 template <int DK, int C, typename TOUT>
@@ -905,6 +948,7 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.qcol_blk = a.addr.qcol_blk;
     mp.srcBH = a.addr.srcBH ? a.addr.srcBH : a.B * a.H;
     mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
+    mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;
     mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);

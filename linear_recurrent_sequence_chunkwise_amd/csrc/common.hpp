@@ -45,11 +45,20 @@ struct OpAddr {
     int rev, ldqk, qcol_blk, srcBH;
 };
 
+// Value rows read with a shift (chunkwise kernels; residual linear attention): row t of the value
+// operand is row t of pre (laid out [B*H][split][DV]) for t < split, and row t - shift of v for
+// t >= split. split is a multiple of 32 (a stage) or N, and split >= shift. split = 0: plain v.
+struct VShift {
+    const void* pre;
+    int split, shift;
+};
+
 struct LaunchArgs {
     int B, H, N, DK, DV;
     int in_bf16, out_bf16;
     int chunk;
     OpAddr addr;  // bf16 chunkwise only
+    VShift vs;    // chunkwise only
     const void* q;
     const void* k;
     const void* v;
@@ -252,6 +261,7 @@ hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, con
 struct RlaPrep {
     long rows;  // B * H * N
     int N, dk, dv, P, prev_len, fmap, bf16;
+    int vsplit;  // shifted value rows written per head ([B*H][vsplit][dv] at vo)
     const void *q, *k, *v, *kp, *vp;
     void *qo, *ko, *vo;
 };

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(int H, int N, int D
                                                              const float* __restrict__ q, const float* __restrict__ k,
                                                              const float* __restrict__ v, const float* __restrict__ state_in,
                                                              float* __restrict__ state_out, float* __restrict__ out,
-                                                             HeadConsts hc) {
+                                                             HeadConsts hc, const float* __restrict__ vpre, int vsplit, int vshift) {
     extern __shared__ float smem[];
     const int nsl = DV / kCols;
     const int bh = blockIdx.x / nsl, slice = blockIdx.x % nsl, h = bh % H;
@@ -33,6 +33,10 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(int H, int N, int D
     const float* qh = q + (size_t)bh * N * DK;
     const float* kh = k + (size_t)bh * N * DK;
     const float* vh = v + (size_t)bh * N * DV;
+    // value row t: row t of the prefix buffer below vsplit, else row t - vshift of v (VShift)
+    auto vat = [&](int t) __attribute__((always_inline)) {
+        return t < vsplit ? vpre[((size_t)bh * vsplit + t) * DV + c] : vh[(size_t)(t - vshift) * DV + c];
+    };
 
     for (int i = rgp; i < DK; i += 4) R[i * kCols + col] = state_in ? state_in[((size_t)bh * DK + i) * DV + c] : 0.f;
     __syncthreads();
@@ -57,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(int H, int N, int D
                 float inter = 0.f;
                 for (int i = 0; i < DK; ++i) inter += qj[i] * R[i * kCols + col];
                 float intra = 0.f;
-                for (int t = 0; t <= j; ++t) intra += S[j * C + t] * vh[(size_t)(c0 + t) * DV + c];
+                for (int t = 0; t <= j; ++t) intra += S[j * C + t] * vat(c0 + t);
                 out[((size_t)bh * N + c0 + j) * DV + c] = intra + decay_pow(l2g, (float)(j + 1)) * inter;
             }
             __syncthreads();  // R is read above and rewritten below
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(int H, int N, int D
         for (int i = rgp; i < DK; i += 4) {
             float acc = 0.f;
             for (int t = 0; t < L; ++t)
-                acc += decay_pow(l2g, (float)(L - 1 - t)) * kh[(size_t)(c0 + t) * DK + i] * vh[(size_t)(c0 + t) * DV + c];
+                acc += decay_pow(l2g, (float)(L - 1 - t)) * kh[(size_t)(c0 + t) * DK + i] * vat(c0 + t);
             R[i * kCols + col] = gL * R[i * kCols + col] + acc;
         }
         __syncthreads();
@@ -195,7 +199,8 @@ hipError_t launch_chunkwise_f32(const LaunchArgs& a) {
                                        (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chunk_f32_kernel, dim3(a.B * a.H * (a.DV / kCols)), dim3(kThreads), lds, a.stream, a.H, a.N, a.DK, a.DV,
-                       a.chunk, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.state_in, a.state_out, pre, a.hc);
+                       a.chunk, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.state_in, a.state_out, pre, a.hc,
+                       (const float*)a.vs.pre, a.vs.split, a.vs.shift);
     e = hipGetLastError();
     if (e != hipSuccess || !stage) return e;
     return finish(a, pre);

@@ -7,10 +7,13 @@
 // row (the page's "softmax-based" feature map).
 //
 //   rla_prepare_kernel   one wave per (b*h, n) row: phi(q[n]) (unless phi is the identity, where q
-//                        is used in place), phi of the shifted key row and the shifted value row,
-//                        in the input dtype. d_k <= 256, a multiple of 4 (4 consecutive features per
-//                        lane, one 8- or 16-byte access); the softmax in double precision.
-// The retention itself runs in the chunkwise kernels (N > 1) or the decode-step kernel (N = 1).
+//                        is used in place) and phi of the shifted key row, in the input dtype; the
+//                        shifted value row only for n below a split (w + 1 rounded up to a 32-token
+//                        stage, at most N), into a prefix buffer. d_k <= 256, a multiple of 4 (4
+//                        consecutive features per lane, one 8- or 16-byte access); the softmax in
+//                        double precision.
+// The retention itself runs in the chunkwise kernels (N > 1), which read value rows at and past the
+// split from v itself, shifted by w + 1 rows (VShift), or the decode-step kernel (N = 1).
 #include "common.hpp"
 
 namespace ret {
@@ -130,8 +133,8 @@ constexpr int kMaxV16 = 4;  // 16-byte chunks of a value row per lane: d_v * siz
 
 template <typename T>
 __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int dk, int dv, int P, int prev_len, int fmap,
-                                                          const T* q, const T* k, const T* v, const T* kp, const T* vp, T* qo,
-                                                          T* ko, T* vo) {
+                                                          int vsplit, const T* q, const T* k, const T* v, const T* kp,
+                                                          const T* vp, T* qo, T* ko, T* vo) {
     const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;  // the whole wave leaves together
     const int lane = threadIdx.x & 63;
@@ -151,12 +154,14 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int 
     float fq[4], fk[4];
     load_row4(qo ? q + (size_t)row * dk : nullptr, dk, lane, fq);
     load_row4(ks, dk, lane, fk);
+    // the shifted value row only below vsplit (the chunk kernels read the later rows from v itself)
+    const bool vrow = n < vsplit;
     const int n16 = dv * (int)sizeof(T) / 16;  // whole 16-byte chunks (d_v * size is a multiple of 16)
     u32x4 vv[kMaxV16];
 #pragma unroll
     for (int j = 0; j < kMaxV16; ++j) {
         const int c = lane + 64 * j;
-        vv[j] = (vs && c < n16) ? reinterpret_cast<const u32x4*>(vs)[c] : u32x4{0u, 0u, 0u, 0u};
+        vv[j] = (vrow && vs && c < n16) ? reinterpret_cast<const u32x4*>(vs)[c] : u32x4{0u, 0u, 0u, 0u};
     }
     if (fmap == 1) softmax2(dk, lane, fq, fk);
     if (qo) store_row4(qo + (size_t)row * dk, dk, lane, fq);
@@ -167,10 +172,12 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int 
         for (int j = 0; j < 4; ++j) fk[j] = 0.f;
         store_row4(ko + (size_t)row * dk, dk, lane, fk);
     }
+    if (vrow) {
 #pragma unroll
-    for (int j = 0; j < kMaxV16; ++j) {
-        const int c = lane + 64 * j;
-        if (c < n16) reinterpret_cast<u32x4*>(vo + (size_t)row * dv)[c] = vv[j];
+        for (int j = 0; j < kMaxV16; ++j) {
+            const int c = lane + 64 * j;
+            if (c < n16) reinterpret_cast<u32x4*>(vo + ((size_t)bh * vsplit + n) * dv)[c] = vv[j];
+        }
     }
 }
 
@@ -188,11 +195,13 @@ hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream) {
     const unsigned grid = (unsigned)((rows + 3) / 4);
     if (r.bf16)
         hipLaunchKernelGGL(rla_prepare_kernel<bf16>, dim3(grid), dim3(256), 0, stream, rows, r.N, r.dk, r.dv, r.P, r.prev_len, r.fmap,
+                           r.vsplit,
                            static_cast<const bf16*>(r.q), static_cast<const bf16*>(r.k), static_cast<const bf16*>(r.v),
                            static_cast<const bf16*>(r.kp), static_cast<const bf16*>(r.vp), static_cast<bf16*>(r.qo),
                            static_cast<bf16*>(r.ko), static_cast<bf16*>(r.vo));
     else
         hipLaunchKernelGGL(rla_prepare_kernel<float>, dim3(grid), dim3(256), 0, stream, rows, r.N, r.dk, r.dv, r.P, r.prev_len, r.fmap,
+                           r.vsplit,
                            static_cast<const float*>(r.q), static_cast<const float*>(r.k), static_cast<const float*>(r.v),
                            static_cast<const float*>(r.kp), static_cast<const float*>(r.vp), static_cast<float*>(r.qo),
                            static_cast<float*>(r.ko), static_cast<float*>(r.vo));
