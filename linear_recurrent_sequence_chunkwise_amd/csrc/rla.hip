@@ -19,18 +19,44 @@
 namespace ret {
 namespace {
 
-// Two independent wave reductions at once, so that their shuffles overlap.
-__device__ __forceinline__ void wave_max2(double& a, double& b) {
+// A lane move within each row of 16 lanes (DPP; all 64 lanes active): quad_perm [1,0,3,2] (lane
+// xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror (lane i of 8 from 7 - i), row_mirror (lane i
+// of 16 from 15 - i). After the two quad steps every lane of a quad holds the same value, so the
+// mirrors pair each lane with the other quad (half-row) as xor 4 (xor 8) would.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
+    const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Two independent wave reductions at once, so that their moves overlap: four DPP steps within rows
+// of 16 lanes, then two shuffles across rows. Every lane ends with the same value (each step adds
+// or compares the same two operands in every lane).
+__device__ __forceinline__ void wave_max2(float& a, float& b) {
+    a = fmaxf(a, dpp_f<0xB1>(a)); b = fmaxf(b, dpp_f<0xB1>(b));
+    a = fmaxf(a, dpp_f<0x4E>(a)); b = fmaxf(b, dpp_f<0x4E>(b));
+    a = fmaxf(a, dpp_f<0x141>(a)); b = fmaxf(b, dpp_f<0x141>(b));
+    a = fmaxf(a, dpp_f<0x140>(a)); b = fmaxf(b, dpp_f<0x140>(b));
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
-        a = fmax(a, x);
-        b = fmax(b, y);
+    for (int o = 16; o < 64; o <<= 1) {
+        const float x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
+        a = fmaxf(a, x);
+        b = fmaxf(b, y);
     }
 }
 __device__ __forceinline__ void wave_sum2(double& a, double& b) {
+    a += dpp_d<0xB1>(a); b += dpp_d<0xB1>(b);
+    a += dpp_d<0x4E>(a); b += dpp_d<0x4E>(b);
+    a += dpp_d<0x141>(a); b += dpp_d<0x141>(b);
+    a += dpp_d<0x140>(a); b += dpp_d<0x140>(b);
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
+    for (int o = 16; o < 64; o <<= 1) {
         const double x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
         a += x;
         b += y;
@@ -79,44 +105,46 @@ __device__ __forceinline__ void store_row4(T* y, int d, int lane, const float* v
     if (4 * lane < d) Vec4<T>::store(y + 4 * lane, v);
 }
 
-// exp(z) for z <= 0 in double precision: z = n ln 2 + r with ln 2 split in two (Cody and Waite),
-// |r| <= ln 2 / 2, exp(r) by its Taylor series to degree 11 (truncation below 3.1e-15 relative),
-// then scaled by 2^n (ldexp, which flushes to zero below the double range). Relative error below
-// 1e-14 against libm's exp on [-680, 0], ample for rounding the result to fp32 and bf16 as an
-// exactly computed value would be.
-__device__ __forceinline__ double exp_nonpos(double z) {
-    const double n = rint(z * 1.4426950408889634);
-    double r = fma(-n, 6.93147180369123816490e-01, z);  // ln 2, high part (exact product with n)
-    r = fma(-n, 1.90821492927058770002e-10, r);          // ln 2, low part
-    double p = 1.0 / 39916800.0;                         // 1/11!
-    p = fma(p, r, 1.0 / 3628800.0);
-    p = fma(p, r, 1.0 / 362880.0);
-    p = fma(p, r, 1.0 / 40320.0);
-    p = fma(p, r, 1.0 / 5040.0);
-    p = fma(p, r, 1.0 / 720.0);
+// 2^(j/32), j = 0 .. 31, rounded to double (computed to 60 digits)
+__constant__ double kExp2Frac[32] = {1.0, 1.0218971486541166, 1.0442737824274138, 1.0671404006768237, 1.0905077326652577, 1.1143867425958924, 1.1387886347566916, 1.1637248587775775, 1.189207115002721, 1.215247359980469, 1.241857812073484, 1.2690509571917332, 1.2968395546510096, 1.3252366431597413, 1.3542555469368927, 1.383909881963832, 1.4142135623730951, 1.4451808069770467, 1.4768261459394993, 1.5091644275934228, 1.5422108254079407, 1.5759808451078865, 1.6104903319492543, 1.645755478153965, 1.681792830507429, 1.718619298122478, 1.7562521603732995, 1.7947090750031072, 1.8340080864093424, 1.8741676341103, 1.9152065613971474, 1.9571441241754002};
+
+// exp(z) for z <= 0 in double precision: z = (32 m + j) ln2/32 + r with ln2/32 split in two (Cody
+// and Waite; n = 32 m + j times the high part is exact for |n| < 2^21), |r| <= ln2/64, exp(r) by its
+// Taylor series to degree 6 (truncation below 4e-18 relative), times 2^(j/32) from the table in
+// LDS, scaled by 2^m (ldexp, which flushes to zero below the double range). z is clamped at -746,
+// below which exp is zero in double precision. Measured against libm's exp on [-700, 0]: relative
+// error below 4e-16.
+__device__ __forceinline__ double exp_nonpos(double z, const double* tab) {
+    z = fmax(z, -746.0);
+    const double n = rint(z * 46.166241308446828);             // 32 / ln 2
+    double r = fma(-n, 6.93147180369123816490e-01 / 32, z);     // ln 2 / 32, high part
+    r = fma(-n, 1.90821492927058770002e-10 / 32, r);            // ln 2 / 32, low part
+    double p = 1.0 / 720.0;
     p = fma(p, r, 1.0 / 120.0);
     p = fma(p, r, 1.0 / 24.0);
     p = fma(p, r, 1.0 / 6.0);
     p = fma(p, r, 0.5);
     p = fma(p, r, 1.0);
     p = fma(p, r, 1.0);
-    return ldexp(p, (int)fmax(n, -2000.0));
+    const int ni = (int)n;  // in [-34500, 0]
+    return ldexp(p * tab[ni & 31], ni >> 5);
 }
 
 // phi over two rows at once (a: the q row, b: the key row), in place. The softmax runs in double
 // precision, exp(x - max) times the reciprocal of the sum, rounded once to fp32: the rounded
 // features then equal the exactly computed ones rounded the same way, except where a value lies
 // within about 1e-16 relative of a rounding boundary.
-__device__ __forceinline__ void softmax2(int d, int lane, float* a, float* b) {
-    double ma = (double)fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-    double mb = (double)fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
-    wave_max2(ma, mb);
+__device__ __forceinline__ void softmax2(int d, int lane, float* a, float* b, const double* tab) {
+    float fa = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));  // the maximum of fp32 values is exact in fp32
+    float fb = fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
+    wave_max2(fa, fb);
+    const double ma = fa, mb = fb;
     double ea[4], eb[4], sa = 0.0, sb = 0.0;
     const bool in = 4 * lane < d;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        ea[j] = in ? exp_nonpos((double)a[j] - ma) : 0.0;
-        eb[j] = in ? exp_nonpos((double)b[j] - mb) : 0.0;
+        ea[j] = in ? exp_nonpos((double)a[j] - ma, tab) : 0.0;
+        eb[j] = in ? exp_nonpos((double)b[j] - mb, tab) : 0.0;
         sa += ea[j];
         sb += eb[j];
     }
@@ -135,6 +163,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int dk, int dv, int P, int prev_len, int fmap,
                                                           int vsplit, const T* q, const T* k, const T* v, const T* kp,
                                                           const T* vp, T* qo, T* ko, T* vo) {
+    __shared__ double tab[32];
+    if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Frac[threadIdx.x];
+    __syncthreads();
     const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;  // the whole wave leaves together
     const int lane = threadIdx.x & 63;
@@ -163,7 +194,7 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int 
         const int c = lane + 64 * j;
         vv[j] = (vrow && vs && c < n16) ? reinterpret_cast<const u32x4*>(vs)[c] : u32x4{0u, 0u, 0u, 0u};
     }
-    if (fmap == 1) softmax2(dk, lane, fq, fk);
+    if (fmap == 1) softmax2(dk, lane, fq, fk, tab);
     if (qo) store_row4(qo + (size_t)row * dk, dk, lane, fq);
     if (ks) {
         store_row4(ko + (size_t)row * dk, dk, lane, fk);
