@@ -24,6 +24,11 @@ positional rotation of q and k, residual
 linear attention at the same shape (512-token window, softmax feature map; its rate is counted with
 the chunkwise FLOPs), and the chunkwise backward (dq, dk, dv) of the same workload with a bf16 dout,
 each timed over the same K calls.
+
+Also reported: the median and minimum per-call times of the step's two parts; the chunkwise call
+with a cold cache (512 MiB written before each call); the long-context workload (N=65536, chunk 64
+to 512, fp32 out); this GPU's own peaks from hand-written probes (bf16 MFMA rate, HBM read and copy
+rates; the roofline fractions stay against the published peaks); the host CPU model for the oracle.
 """
 import argparse
 import json
@@ -102,6 +107,64 @@ def decode_bytes(B, H, dk, dv):
     return B * H * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + dv * 4)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measured_peaks(torch, dev, stream):
+    """This GPU's own peaks from the hand-written probes (probe/peak_probe.hip): dense bf16 MFMA rate
+    (every wave issuing independent 16x16x32 MFMA chains, 8 waves per SIMD) and HBM rates (a 4 GiB
+    read; a 1 GiB device copy, read + write). Each is the best of 3 timed launches. The roofline
+    fractions stay against the published peaks; these say how much of them the chip reaches."""
+    import ctypes
+    path = os.path.join(ROOT, "linear_recurrent_sequence_chunkwise_amd", "probe", "libpeakprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nthr = lib.probe_threads()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    blocks, iters = 256 * 8, 2048
+    out = torch.empty(blocks * nthr, dtype=torch.float32, device=dev)
+    t = best(lambda: lib.probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp))
+    mfma_tflops = blocks * 4 * iters * 16 * 16384 / t / 1e12
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    rblocks = 256 * 16
+    rout = torch.empty(rblocks * nthr, dtype=torch.float32, device=dev)
+    t = best(lambda: lib.probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks, ctypes.c_void_p(rout.data_ptr()), sp))
+    read_gbps = nbytes / t / 1e9
+    src, dst = buf[: (1 << 28)], torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    t = best(lambda: dst.copy_(src))
+    copy_gbps = 2 * (1 << 30) / t / 1e9
+    del buf, dst, out, rout
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_read_GBps": round(read_gbps, 1),
+            "hbm_copy_GBps": round(copy_gbps, 1),
+            "how": "probe/peak_probe.hip: bf16 16x16x32 MFMA chains (2048 workgroups x 4 waves x 2048 trips x 16 MFMAs); "
+                   "4 GiB non-temporal read; 1 GiB torch device copy counted as read + write; best of 3"}
+
+
 def read_counters(name, kernel_sources):
     """HBM traffic per dispatch from a committed rocprofv3 counter summary, if it was taken on the
     current kernel source (sha256 recorded in the summary); else None."""
@@ -131,6 +194,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--peaks", action="store_true", help="only run the peak probes and print their JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     args = ap.parse_args()
@@ -156,6 +220,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n, "copies": 3}))
+        return
+
+    if args.peaks:
+        print(json.dumps(measured_peaks(torch, dev, stream)), flush=True)
         return
 
     # ---- chunkwise workload
@@ -205,6 +273,12 @@ def main():
     t_chunk = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
     t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
     t_step = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    per_chunk = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+    per_dec = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in evs)
+    timing = {"chunkwise_us": {"mean": round(t_chunk * 1e6, 2), "median": round(per_chunk[len(per_chunk) // 2], 2),
+                               "min": round(per_chunk[0], 2)},
+              "decode_us": {"mean": round(t_dec * 1e6, 2), "median": round(per_dec[len(per_dec) // 2], 2),
+                            "min": round(per_dec[0], 2)}}
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; chunkwise {t_chunk * 1e6:.1f} us, decode {t_dec * 1e6:.1f} us")
 
     cf = chunk_flops(w.B, w.H, w.N, w.dk, w.dv, C)
@@ -281,6 +355,45 @@ def main():
     log(f"gated chunkwise {t_gate * 1e6:.1f} us; rotated chunkwise {t_rot * 1e6:.1f} us; rotated decode {t_drot * 1e6:.1f} us; "
         f"rla {t_rla * 1e6:.1f} us; backward {t_bwd * 1e6:.1f} us")
 
+    # cold cache: 512 MiB written before each call evicts the 256 MB MALL (and the L2s); events
+    # around the chunkwise call only
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plain()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    cold.sort()
+    timing["chunkwise_cold_us"] = {"mean": round(sum(cold) / len(cold), 2), "median": round(cold[len(cold) // 2], 2),
+                                   "min": round(cold[0], 2)}
+
+    # long context: N = 65536, chunk 64 .. 512, fp32 out (no GroupNorm), one call timed per chunk size
+    # after a warm-up call, over max(3, K / 4) calls
+    lc = I.WORKLOADS["retention_b1_h16_n65536_dk256_dv512_bf16"]
+    # drawn on the device (the same distribution; 1e9 values would take the host tens of seconds)
+    lq, lk, lv = I.make_qkv(lc.B, lc.H, lc.N, lc.dk, lc.dv, "bf16", seed=lc.seed, device=dev)
+    lout = torch.empty((lc.B, lc.H, lc.N, lc.dv), dtype=torch.float32, device=dev)
+    lst = torch.empty((lc.B, lc.H, lc.dk, lc.dv), dtype=torch.float32, device=dev)
+    long_ctx = {"workload": "B=1 H=16 N=65536 d_k=256 d_v=512, bf16 in (drawn on the device), fp32 out, no GroupNorm",
+                "by_chunk": {}}
+    for lC in lc.chunks:
+        lws = torch.empty(R.workspace_bytes(R.RET_FN_CHUNKWISE, lc.B, lc.H, lc.N, lc.dk, lc.dv, torch.bfloat16, torch.float32, lC),
+                          dtype=torch.uint8, device=dev)
+        t_l = time_calls(lambda: R.chunkwise_fwd(lq, lk, lv, lc.gamma_list(), lC, out=lout, state_out=lst, workspace=lws,
+                                                 stream=stream), max(3, args.steps // 4), stream, torch)
+        lf = chunk_flops(lc.B, lc.H, lc.N, lc.dk, lc.dv, lC)
+        long_ctx["by_chunk"][str(lC)] = {"us": round(t_l * 1e6, 1), "tflops": round(lf / t_l / 1e12, 2),
+                                         "tokens_per_s": round(lc.B * lc.N / t_l, 1)}
+        del lws
+    del lq, lk, lv, lout, lst
+    peaks = measured_peaks(torch, dev, stream)
+    log(f"cold chunkwise median {timing['chunkwise_cold_us']['median']:.1f} us; long context {long_ctx['by_chunk']}; peaks {peaks}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -299,7 +412,8 @@ def main():
                "sample": f"the whole N=8192 layer workload (16 heads x 8192 tokens, recurrent form + GroupNorm, fp64), "
                          f"{passes} passes in {total:.1f} s, {tc:.2f} s each; rate counted with the same chunkwise "
                          "algorithmic FLOPs",
-               "tokens_per_s": round(w.B * w.N / tc, 1)}
+               "tokens_per_s": round(w.B * w.N / tc, 1), "affinity_cores": len(os.sched_getaffinity(0)),
+               "cpu_model": cpu_model()}
         log(f"oracle: {passes} passes, {tc:.2f} s each on {threads} threads")
 
     line = {
@@ -328,6 +442,9 @@ def main():
                      "mfma_frac": round(bf / t_bwd / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "algorithmic_bytes": bb, "traffic": bwd_traffic,
                      "tokens_per_s": round(w.B * w.N / t_bwd, 1)},
+        "timing": timing,
+        "long_context": long_ctx,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
