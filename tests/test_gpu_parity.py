@@ -836,3 +836,29 @@ def test_bf16_parallel_short_sequences(orc, dk, dv, N):
     report(f"parallel bf16 ({dk},{dv}) N={N}", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref), TOL["bf16"])
     o = R.parallel_fwd(qd, kd, vd, gam, groupnorm=R.GroupNorm(1e-5), out_dtype=torch.bfloat16)
     report(f"parallel bf16 GN ({dk},{dv}) N={N}", rel_err(o, orc.groupnorm(ref, 1e-5)), TOL["bf16"])
+
+
+# Residual linear attention without an output (a state-only segment: the single-group chunk kernel
+# with the value rows read in place past the prefix) against the oracle's state and the state of
+# the call with an output; window rows from an earlier segment, a state_in, and windows on both
+# sides of N (vsplit < N reads v in place; vsplit = N reads only the prefix buffer).
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,w,C", [(700, 40, 64), (700, 40, 512), (300, 400, 128), (1000, 100, 256)])
+def test_rla_state_only(orc, dt, N, w, C):
+    B, H, dk, dv = 1, 3, 64, 128 if dt == "f32" else 64
+    if dt == "f32":
+        C = min(C, 128)  # the fp32 chunk kernel takes chunks of 64 and 128
+    P = w + 1
+    q, k, v, kp, vp = _rla_inputs(B, H, N, dk, dv, dt, 760 + N + w, P=P)
+    s0 = I.make_state(B, H, dk, dv, seed=761, scale=0.02)
+    plen = min(P, 25)
+    qd, kd, vd, kpd, vpd, s0d = dev(q, k, v, kp, vp, s0)
+    _, s_only = R.rla_fwd(qd, kd, vd, w, C, fmap="identity", k_prev=kpd, v_prev=vpd, prev_len=plen, state_in=s0d,
+                          want_out=False)
+    o, s_full = R.rla_fwd(qd, kd, vd, w, C, fmap="identity", k_prev=kpd, v_prev=vpd, prev_len=plen, state_in=s0d)
+    ref_o, ref_s = orc.rla(q, k, v, w, "identity", kp, vp, plen, s0)
+    report(f"rla state-only {dt} N={N} w={w} C={C} state", rel_err(s_only, ref_s), TOL[dt])
+    report(f"rla state-only {dt} N={N} w={w} C={C} state vs the call with an output", rel_err(s_only, s_full.double().cpu().numpy()),
+           TOL[dt])
+    if dt == "f32":  # bf16 outputs carry the bf16 scores; test_rla_bf16 holds them to the derived bound
+        report(f"rla {dt} N={N} w={w} C={C} out", rel_err(o, ref_o), TOL[dt])
