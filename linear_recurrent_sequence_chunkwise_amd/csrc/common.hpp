@@ -256,8 +256,10 @@ hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, voi
 hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, int x_bf16, int y_bf16,
                           const RotConsts& rc, int inverse, hipStream_t stream);
 // Residual linear attention operands: qo = phi(q) (qo null: phi is the identity and q is used as
-// is), ko / vo = phi(k) / v shifted by P = window + 1 rows, the first rows from the window rows kp,
-// vp ([rows / N][P][d], of which the last prev_len hold tokens) or zero.
+// is), ko = phi(k) shifted by P = window + 1 rows, and vo = the first vsplit rows of v shifted the
+// same way ([rows / N][vsplit][dv]; the chunk kernels read the later rows from v, see VShift); the
+// first P rows come from the window rows kp, vp ([rows / N][P][d], of which the last prev_len hold
+// tokens) or are zero.
 struct RlaPrep {
     long rows;  // B * H * N
     int N, dk, dv, P, prev_len, fmap, bf16;
