@@ -282,7 +282,7 @@ def main():
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; chunkwise {t_chunk * 1e6:.1f} us, decode {t_dec * 1e6:.1f} us")
 
     cf = chunk_flops(w.B, w.H, w.N, w.dk, w.dv, C)
-    cb = chunk_bytes(w.B, w.H, w.N, w.dk, w.dv) + 2 * w.B * w.H * w.dk * w.dv * 4  # + state out (fp32) read/written once
+    cb = chunk_bytes(w.B, w.H, w.N, w.dk, w.dv) + w.B * w.H * w.dk * w.dv * 4  # + the fp32 final state, written once
     db = decode_bytes(d.B, d.H, d.dk, d.dv)
     chunk_tflops = cf / t_chunk / 1e12
     tokens_per_s = w.B * w.N / t_chunk
