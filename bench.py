@@ -118,12 +118,12 @@ def cpu_model():
 
 
 def measured_peaks(torch, dev, stream):
-    """This GPU's own peaks from the hand-written probes (probe/peak_probe.hip): dense bf16 MFMA rate
+    """This GPU's own peaks from the hand-written probes (peak_probe.hip): dense bf16 MFMA rate
     (every wave issuing independent 16x16x32 MFMA chains, 8 waves per SIMD) and HBM rates (a 4 GiB
     read; a 1 GiB device copy, read + write). Each is the best of 3 timed launches. The roofline
     fractions stay against the published peaks; these say how much of them the chip reaches."""
     import ctypes
-    path = os.path.join(ROOT, "linear_recurrent_sequence_chunkwise_amd", "probe", "libpeakprobe.so")
+    path = os.path.join(ROOT, "libpeakprobe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
@@ -161,7 +161,7 @@ def measured_peaks(torch, dev, stream):
     del buf, dst, out, rout
     return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_read_GBps": round(read_gbps, 1),
             "hbm_copy_GBps": round(copy_gbps, 1),
-            "how": "probe/peak_probe.hip: bf16 16x16x32 MFMA chains (2048 workgroups x 4 waves x 2048 trips x 16 MFMAs); "
+            "how": "peak_probe.hip: bf16 16x16x32 MFMA chains (2048 workgroups x 4 waves x 2048 trips x 16 MFMAs); "
                    "4 GiB non-temporal read; 1 GiB torch device copy counted as read + write; best of 3"}
 
 

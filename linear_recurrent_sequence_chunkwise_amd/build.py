@@ -1,5 +1,4 @@
-"""Compile the gfx950 HIP sources under csrc/ into libretention.so (in this package directory), and the
-peak microbenchmarks under probe/ into probe/libpeakprobe.so.
+"""Compile the gfx950 HIP sources under csrc/ into libretention.so (in this package directory).
 
 Every call recompiles. Objects go to _build/ at the repository root; the .so lands next to this
 file so that it ships with the source tree. No torch extension machinery is involved: the
@@ -63,25 +62,7 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
-    build_probe(verbose)
     return LIB
-
-
-PROBE_SRC = os.path.join(PKG, "probe", "peak_probe.hip")
-PROBE_LIB = os.path.join(PKG, "probe", "libpeakprobe.so")
-
-
-def build_probe(verbose: bool = True) -> str:
-    """The peak microbenchmarks (probe/peak_probe.hip) as their own small library, beside the source."""
-    tmp = PROBE_LIB + ".tmp"
-    cmd = [HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed for the peak probes:\n" + " ".join(cmd) + "\n" + res.stderr)
-    os.replace(tmp, PROBE_LIB)
-    if verbose:
-        print("built", PROBE_LIB)
-    return PROBE_LIB
 
 
 if __name__ == "__main__":

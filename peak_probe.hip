@@ -1,6 +1,6 @@
 // Microbenchmarks of this GPU's own peaks, for the roofline fractions the benchmark reports: the
 // dense bf16 matrix-core rate and the HBM read rate. Not part of the retention library or its ABI;
-// bench.py loads this small library on its own.
+// bench.py (beside this file) loads the small library built from it.
 //
 //   mfma_peak_kernel  every wave issues 16x16x32 bf16 MFMAs on eight independent accumulators (so
 //                     that no issue waits on a result), operands in registers, no memory traffic
