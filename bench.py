@@ -119,7 +119,7 @@ def cpu_model():
 
 def measured_peaks(torch, dev, stream):
     """This GPU's own peaks from the hand-written probes (peak_probe.hip): dense bf16 MFMA rate
-    (every wave issuing independent 16x16x32 MFMA chains, 8 waves per SIMD) and HBM rates (a 4 GiB
+    (every wave issuing independent 32x32x16 MFMA chains, 8 waves per SIMD) and HBM rates (a 4 GiB
     read; a 1 GiB device copy, read + write). Each is the best of 3 timed launches. The roofline
     fractions stay against the published peaks; these say how much of them the chip reaches."""
     import ctypes
@@ -145,10 +145,10 @@ def measured_peaks(torch, dev, stream):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return min(ts)
 
-    blocks, iters = 256 * 8, 2048
+    blocks, iters = 256 * 8, 4096
     out = torch.empty(blocks * nthr, dtype=torch.float32, device=dev)
     t = best(lambda: lib.probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp))
-    mfma_tflops = blocks * 4 * iters * 16 * 16384 / t / 1e12
+    mfma_tflops = blocks * 4 * iters * 4 * 32768 / t / 1e12
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     rblocks = 256 * 16
@@ -161,7 +161,7 @@ def measured_peaks(torch, dev, stream):
     del buf, dst, out, rout
     return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_read_GBps": round(read_gbps, 1),
             "hbm_copy_GBps": round(copy_gbps, 1),
-            "how": "peak_probe.hip: bf16 16x16x32 MFMA chains (2048 workgroups x 4 waves x 2048 trips x 16 MFMAs); "
+            "how": "peak_probe.hip: bf16 32x32x16 MFMA chains (2048 workgroups x 4 waves x 4096 trips x 4 MFMAs); "
                    "4 GiB non-temporal read; 1 GiB torch device copy counted as read + write; best of 3"}
 
 

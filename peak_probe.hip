@@ -2,9 +2,10 @@
 // dense bf16 matrix-core rate and the HBM read rate. Not part of the retention library or its ABI;
 // bench.py (beside this file) loads the small library built from it.
 //
-//   mfma_peak_kernel  every wave issues 16x16x32 bf16 MFMAs on eight independent accumulators (so
-//                     that no issue waits on a result), operands in registers, no memory traffic
-//                     inside the loop. One launch = blocks * 4 waves * iters * 16 MFMAs of 16384 flop.
+//   mfma_peak_kernel  every wave issues 32x32x16 bf16 MFMAs on four independent accumulators (so
+//                     that no issue waits on a result; distinct start values, or the compiler merges
+//                     the chains), operands in registers, no memory traffic inside the loop. One
+//                     launch = blocks * 4 waves * iters * 4 MFMAs of 32768 flop.
 //   hbm_read_kernel   a grid-stride sum over a buffer with 16-byte non-temporal loads, four loads in
 //                     flight per thread; the buffer is read once per launch.
 #include <hip/hip_runtime.h>
@@ -15,9 +16,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kChains = 8;
+constexpr int kChains = 4;
 
 __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(int iters, float* __restrict__ out) {
     bf16x8 a, b;
@@ -26,18 +28,21 @@ __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(int iters, float* _
         a[j] = (__bf16)(1e-3f * (float)(threadIdx.x + j));
         b[j] = (__bf16)(1e-3f * (float)(j + 1));
     }
-    f32x4 acc[kChains];
+    f32x16 acc[kChains];
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) acc[c] = f32x4{(float)c, 0.f, 0.f, 0.f};  // distinct chains (identical ones would merge)
-    for (int i = 0; i < iters; ++i) {  // two rounds of the chains per trip
+    for (int c = 0; c < kChains; ++c) {
+        acc[c] = f32x16{};
+        acc[c][0] = (float)c;  // distinct chains (identical ones would merge)
+    }
+    for (int i = 0; i < iters; ++i) {
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-#pragma unroll
-        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc[c], 0, 0, 0);
+        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) s += (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+    for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s += acc[c][j];
     out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;  // one float per thread: the work is used
 }
 
