@@ -130,8 +130,11 @@ typedef struct {
  * state_in: fp32 [B][H][d_k][d_v] or NULL (zero). state_out: fp32, or NULL. state_out may equal
  * state_in (in place). out may be NULL only when state_out is not NULL (state-only prefill);
  * out must not alias q, k or v.
- * Supported: (d_k, d_v) in {(64,64), (256,512)} for bf16; d_k in {64,128,256}, d_v a multiple of
- * 64 up to 512 for fp32. H <= RETENTION_MAX_HEADS.
+ * Supported: d_k in {64, 256} and d_v in {32, 64, 128, 256, 512} for bf16; d_k in {64,128,256}, d_v a
+ * multiple of 64 up to 512 for fp32. H <= RETENTION_MAX_HEADS. bf16 inputs also need one head's
+ * padded extent within 32-bit offsets: P = ceil(N / chunk) * chunk, P * max(d_k, d_v) * 4 < 2^31 and
+ * P * chunk * 2 < 2^31 (about 1M tokens at d_v = 512); longer sequences return RET_ERR_UNSUPPORTED
+ * (run them as segments through state_in / state_out).
  * Precision (bf16 inputs): products accumulate in fp32; the carried state is fp32 and enters the
  * matrix cores as a bf16 high part plus a bf16 low part, as does v scaled by its decay.
  */
@@ -159,7 +162,8 @@ ret_status retention_recurrent_step(const ret_shape* shape,
 /*
  * Parallel form (abeam.tech summary, retention as content-based reference times distance-based
  * forgetting): O = (Q K^T (.) D) V over the whole sequence, causal, no state.
- * Supported shapes as for the chunkwise form.
+ * Supported: (d_k, d_v) in {(64,64), (256,512)} for bf16; d_k <= 512 and d_v a multiple of 64 up to
+ * 512 for fp32. H <= RETENTION_MAX_HEADS.
  */
 ret_status retention_parallel_fwd(const ret_shape* shape,
                                   const void* q, const void* k, const void* v,
@@ -176,8 +180,10 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
  * q, k: [B][H][N][d_k]; v, dout: [B][H][N][d_v], in shape->in_dtype; state_in: fp32
  * [B][H][d_k][d_v] or NULL (zero). Outputs, each fp32 and each optional: dq, dk like q; dv like v;
  * dstate_in like state_in. shape->out_dtype must be RET_F32. Outputs must not alias inputs or each
- * other. chunk and (d_k, d_v) as for retention_chunkwise_fwd; a d_v with no forward kernel of
- * contraction width d_v runs as two column blocks of d_v / 2.
+ * other. Supported where the forwards it runs exist: retention_chunkwise_fwd at (d_k, d_v) and at
+ * contraction width d_v with value width d_k; a d_v with no forward kernel of contraction width d_v
+ * runs as two column blocks of d_v / 2 (bf16 (64, 32), for one, has neither and returns
+ * RET_ERR_UNSUPPORTED). The same bound on one head's extent as retention_chunkwise_fwd.
  * With a rotation, dq and dk are the gradients with respect to the unrotated q and k: the
  * gradients at the rotated inputs turned back by the inverse rotation (its transpose).
  * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): the workspace of the forward

@@ -49,6 +49,21 @@ ret_status check_shape(const ret_shape* s, bool step) {
     return RET_OK;
 }
 
+// The bf16 chunk kernels address one head's rows (q, k, v and out up to 4 bytes per element, or rows
+// of the wider operand in the backward) and its scores in 32-bit byte offsets: every such extent,
+// with the sequence padded to whole chunks, must stay below 2^31 bytes.
+bool bf16_head_fits(const ret_shape* s, int chunk) {
+    const double n_pad = std::ceil((double)s->seq_len / chunk) * chunk;
+    const double widest = (double)(s->d_k > s->d_v ? s->d_k : s->d_v);
+    return n_pad * widest * 4.0 < 2147483648.0 && n_pad * chunk * 2.0 < 2147483648.0;
+}
+
+ret_status check_bf16_head(const ret_shape* s, int chunk) {
+    if (s->in_dtype != RET_BF16 || chunk <= 0 || bf16_head_fits(s, chunk)) return RET_OK;
+    return fail(RET_ERR_UNSUPPORTED, "seq_len %d is too long for the bf16 chunk kernels at d_k %d, d_v %d, chunk %d: one head's rows "
+                "and scores must stay below 2^31 bytes (about 1M tokens at d_v 512)", s->seq_len, s->d_k, s->d_v, chunk);
+}
+
 ret_status check_gamma(const ret_shape* s, const double* gamma, ret::HeadConsts* hc) {
     if (!gamma) return fail(RET_ERR_INVALID_ARG, "gamma is NULL");
     for (int h = 0; h < s->heads; ++h) {
@@ -227,15 +242,17 @@ bool shape_supported(int32_t fn, const ret_shape* s, int chunk, bool rot) {
     if (rot && (dk % 2 || dk / 2 > ret::kMaxPairs)) return false;
     const bool step_ok = dv % 4 == 0 && dv / 4 <= 256 && 256 % (dv / 4) == 0;
     switch (fn) {
-        case RET_FN_CHUNKWISE: return bf ? ret::chunkwise_bf16_supported(dk, dv, chunk) : ret::chunkwise_f32_supported(dk, dv, chunk);
+        case RET_FN_CHUNKWISE:
+            return bf ? ret::chunkwise_bf16_supported(dk, dv, chunk) && bf16_head_fits(s, chunk) : ret::chunkwise_f32_supported(dk, dv, chunk);
         case RET_FN_RECURRENT_STEP: return step_ok && dk <= 8192;
         case RET_FN_PARALLEL: return bf ? ret::parallel_bf16_supported(dk, dv) : ret::parallel_f32_supported(dk, dv);
-        case RET_FN_CHUNKWISE_BWD: return ret::bwd_split(bf, dk, dv, chunk) != 0;
+        case RET_FN_CHUNKWISE_BWD: return ret::bwd_split(bf, dk, dv, chunk) != 0 && (!bf || bf16_head_fits(s, chunk));
         case RET_FN_RLA: {
             const size_t vrow = (size_t)dv * elem_size(s->in_dtype);
             if (rot || dk > 256 || dk % 4 || vrow % 16 != 0 || vrow > 4096) return false;
             if (s->seq_len == 1) return step_ok;
-            return bf ? ret::chunkwise_bf16_supported(dk, dv, chunk) : ret::chunkwise_f32_supported(dk, dv, chunk);
+            return bf ? ret::chunkwise_bf16_supported(dk, dv, chunk) && bf16_head_fits(s, chunk)
+                      : ret::chunkwise_f32_supported(dk, dv, chunk);
         }
         default: return false;
     }
@@ -290,6 +307,7 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
            : !ret::chunkwise_f32_supported(shape->d_k, shape->d_v, chunk))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise: no kernel for %s inputs with d_k %d, d_v %d, chunk %d", bf ? "bf16" : "fp32",
                     shape->d_k, shape->d_v, chunk);
+    RET_TRY(check_bf16_head(shape, chunk));
     const size_t rows = (size_t)shape->batch * shape->heads * shape->seq_len;
     const size_t in_sz = elem_size(shape->in_dtype);
     const size_t out_bytes = rows * shape->d_v * elem_size(shape->out_dtype);
@@ -344,6 +362,7 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const 
     if (!ret::bwd_split(bf, shape->d_k, shape->d_v, chunk))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise backward: no kernels for %s inputs with d_k %d, d_v %d, chunk %d", bf ? "bf16" : "fp32",
                     shape->d_k, shape->d_v, chunk);
+    RET_TRY(check_bf16_head(shape, chunk));
     const size_t rows = (size_t)shape->batch * shape->heads * shape->seq_len;
     const size_t in_sz = elem_size(shape->in_dtype);
     const size_t st_bytes = (size_t)shape->batch * shape->heads * shape->d_k * shape->d_v * sizeof(float);
@@ -489,6 +508,7 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, dv, chunk) : !ret::chunkwise_f32_supported(shape->d_k, dv, chunk))
             return fail(RET_ERR_UNSUPPORTED, "residual linear attention: no chunkwise kernel for %s inputs with d_k %d, d_v %d, chunk %d",
                         bf ? "bf16" : "fp32", shape->d_k, dv, chunk);
+        RET_TRY(check_bf16_head(shape, chunk));
     }
     const size_t rows = (size_t)shape->batch * shape->heads * N;
     const size_t es = elem_size(shape->in_dtype);

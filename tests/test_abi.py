@@ -312,3 +312,22 @@ def test_workspace_query_unsupported_shapes(lib):
     # each rejected shape is one the call itself rejects
     assert bwd(lib, shape(dv=32)) == R.RET_ERR_UNSUPPORTED
     assert chunk(lib, shape(dk=128)) == R.RET_ERR_UNSUPPORTED
+
+
+def test_bf16_sequence_length_limit(lib):
+    """One head's rows and scores must fit 32-bit offsets in the bf16 chunk kernels: about 1M tokens
+    at d_v = 512; longer sequences are refused (not truncated), by the calls and the query alike."""
+    bad = ctypes.c_size_t(-1).value
+    ok_n, long_n = 1 << 19, 1 << 20  # 2^19 * 512 * 4 = 1 GiB fits; 2^20 * 512 * 4 = 2 GiB does not
+    for fn in (R.RET_FN_CHUNKWISE, R.RET_FN_CHUNKWISE_BWD, R.RET_FN_RLA):
+        assert lib.retention_workspace_bytes(fn, ctypes.byref(shape(H=1, N=ok_n, dk=256, dv=512)), 128, 0) != bad, fn
+        assert lib.retention_workspace_bytes(fn, ctypes.byref(shape(H=1, N=long_n, dk=256, dv=512)), 128, 0) == bad, fn
+    # fp32 inputs address through 64-bit pointers: no such bound
+    assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(shape(H=1, N=long_n, dk=256, dv=512, i=R.RET_F32)), 128,
+                                         0) != bad
+    s = shape(H=1, N=long_n, dk=256, dv=512)
+    assert lib.retention_chunkwise_fwd(ctypes.byref(s), 128, Q, K, V, gam([0.9]), None, None, None, OUT, ST, WS, 1 << 40,
+                                       None) == R.RET_ERR_UNSUPPORTED
+    assert "2^31" in lib.retention_last_error().decode()
+    assert bwd(lib, s, C=128) == R.RET_ERR_UNSUPPORTED
+    assert rla(lib, s, C=128) == R.RET_ERR_UNSUPPORTED
