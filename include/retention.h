@@ -162,8 +162,8 @@ ret_status retention_recurrent_step(const ret_shape* shape,
 /*
  * Parallel form (abeam.tech summary, retention as content-based reference times distance-based
  * forgetting): O = (Q K^T (.) D) V over the whole sequence, causal, no state.
- * Supported: (d_k, d_v) in {(64,64), (256,512)} for bf16; d_k <= 512 and d_v a multiple of 64 up to
- * 512 for fp32. H <= RETENTION_MAX_HEADS.
+ * Supported: d_k in {64, 256} and d_v in {64, 128, 256, 512} for bf16; d_k <= 512 and d_v a multiple
+ * of 64 up to 512 for fp32. H <= RETENTION_MAX_HEADS.
  */
 ret_status retention_parallel_fwd(const ret_shape* shape,
                                   const void* q, const void* k, const void* v,

@@ -289,11 +289,21 @@ hipError_t launch_shape(const LaunchArgs& a) {
 
 }  // namespace
 
-bool parallel_bf16_supported(int DK, int DV) { return (DK == 64 && DV == 64) || (DK == 256 && DV == 512); }
-
-hipError_t launch_parallel_bf16(const LaunchArgs& a) {
-    if (a.DK == 64) return launch_shape<64, 64>(a);
-    return launch_shape<256, 512>(a);
+// d_k 64 or 256 (K rows of whole 128-byte lines); d_v 64 .. 512, four column groups of 16-column tiles
+bool parallel_bf16_supported(int DK, int DV) {
+    return (DK == 64 || DK == 256) && (DV == 64 || DV == 128 || DV == 256 || DV == 512);
 }
+
+template <int DK>
+hipError_t launch_dk(const LaunchArgs& a) {
+    switch (a.DV) {
+        case 64: return launch_shape<DK, 64>(a);
+        case 128: return launch_shape<DK, 128>(a);
+        case 256: return launch_shape<DK, 256>(a);
+        default: return launch_shape<DK, 512>(a);
+    }
+}
+
+hipError_t launch_parallel_bf16(const LaunchArgs& a) { return a.DK == 64 ? launch_dk<64>(a) : launch_dk<256>(a); }
 
 }  // namespace ret

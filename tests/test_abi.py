@@ -301,7 +301,9 @@ def test_workspace_query_unsupported_shapes(lib):
     assert q(R.RET_FN_CHUNKWISE, shape(), C=96) == bad
     assert q(R.RET_FN_CHUNKWISE_BWD, shape(dv=32)) == bad  # no column split of d_v = 32 for the swapped forwards
     assert q(R.RET_FN_CHUNKWISE_BWD, shape(dv=128)) != bad
-    assert q(R.RET_FN_PARALLEL, shape(dk=128, dv=128)) == bad
+    assert q(R.RET_FN_PARALLEL, shape(dk=128, dv=128)) == bad  # bf16 parallel: d_k 64 or 256
+    assert q(R.RET_FN_PARALLEL, shape(dk=64, dv=32)) == bad  # d_v in four groups of 16-column tiles
+    assert q(R.RET_FN_PARALLEL, shape(dk=256, dv=128)) != bad
     assert q(R.RET_FN_PARALLEL, shape(dk=128, dv=128, i=R.RET_F32)) != bad
     assert q(R.RET_FN_RECURRENT_STEP, shape(N=1, dv=12), 0) == bad
     assert q(R.RET_FN_RECURRENT_STEP, shape(N=1, dv=16), 0) == 0

@@ -774,6 +774,11 @@ def test_bf16_chunkwise_shape_sweep(orc, dk, dv):
         report(f"bf16 ({dk},{dv}) C={C} state", rel_err(s, ref_s), TOL["bf16"])
     o, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, state_in=s0d, groupnorm=R.GroupNorm(1e-5), want_state=False)
     report(f"bf16 ({dk},{dv}) GN out", rel_err(o, orc.groupnorm(ref, 1e-5)), TOL["bf16"])
+    if dv >= 64:  # the parallel kernel splits d_v into four groups of 16-column tiles
+        ref_p, _ = orc.recurrent(q, k, v, gam)
+        report(f"bf16 ({dk},{dv}) parallel", rel_err(R.parallel_fwd(qd, kd, vd, gam), ref_p), TOL["bf16"])
+        op = R.parallel_fwd(qd, kd, vd, gam, groupnorm=R.GroupNorm(1e-5), out_dtype=torch.bfloat16)
+        report(f"bf16 ({dk},{dv}) parallel GN bf16 out", rel_err(op, orc.groupnorm(ref_p, 1e-5)), TOL["bf16"])
 
 
 @pytest.mark.parametrize("dk", [64, 128, 256])
