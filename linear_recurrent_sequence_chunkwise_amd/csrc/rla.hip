@@ -6,14 +6,17 @@
 // tokens that have left the window. phi is the identity or the softmax over the d_k features of a
 // row (the page's "softmax-based" feature map).
 //
-//   rla_prepare_kernel   one wave per (b*h, n) row: phi(q[n]) (unless phi is the identity, where q
-//                        is used in place) and phi of the shifted key row, in the input dtype; the
-//                        shifted value row only for n below a split (w + 1 rounded up to a 32-token
-//                        stage, at most N), into a prefix buffer. d_k <= 256, a multiple of 4 (4
-//                        consecutive features per lane, one 8- or 16-byte access); the softmax in
-//                        double precision.
+//   rla_prepare_kernel   grid-stride, one wave per row: first the shifted value rows for n below a
+//                        split (w + 1 rounded up to a 32-token stage, at most N), into a prefix
+//                        buffer; then, row by row, phi(q[n]) (unless phi is the identity, where q is
+//                        used in place) and phi of the shifted key row, in the input dtype, with the
+//                        next row's loads in flight. d_k <= 256, a multiple of 4 (4 consecutive
+//                        features per lane, one 8- or 16-byte access); the softmax in double
+//                        precision.
 // The retention itself runs in the chunkwise kernels (N > 1), which read value rows at and past the
 // split from v itself, shifted by w + 1 rows (VShift), or the decode-step kernel (N = 1).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace ret {
@@ -67,11 +70,6 @@ __device__ __forceinline__ void wave_sum2(double& a, double& b) {
 // -inf past the end or without a row.
 template <typename T> struct Vec4;
 template <> struct Vec4<bf16> {
-    static __device__ __forceinline__ void load(const bf16* p, float* v) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = (float)x[j];
-    }
     static __device__ __forceinline__ void store(bf16* p, const float* v) {
         bf16x4 x;
 #pragma unroll
@@ -80,25 +78,10 @@ template <> struct Vec4<bf16> {
     }
 };
 template <> struct Vec4<float> {
-    static __device__ __forceinline__ void load(const float* p, float* v) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = x[j];
-    }
     static __device__ __forceinline__ void store(float* p, const float* v) {
         *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
     }
 };
-
-template <typename T>
-__device__ __forceinline__ void load_row4(const T* x, int d, int lane, float* v) {
-    if (x && 4 * lane < d) {
-        Vec4<T>::load(x + 4 * lane, v);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = -INFINITY;
-    }
-}
 
 template <typename T>
 __device__ __forceinline__ void store_row4(T* y, int d, int lane, const float* v) {
@@ -157,58 +140,127 @@ __device__ __forceinline__ void softmax2(int d, int lane, float* a, float* b, co
     }
 }
 
-constexpr int kMaxV16 = 4;  // 16-byte chunks of a value row per lane: d_v * size <= 4 KiB
+
+// The q and key features 4l .. 4l+3 of one row, as loaded (bf16x4 or f32x4).
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> { typedef bf16x4 type; };
+template <> struct Raw4<float> { typedef f32x4 type; };
+
+// Where row (bh, n) of the prepare pass reads and writes. ks is null where no key row lands (a
+// token before the caller's window rows); vs then is null too.
+template <typename T>
+struct RowAt {
+    long row;
+    int bh, n;
+    const T* ks;
+    const T* vs;
+};
 
 template <typename T>
-__global__ __launch_bounds__(256) void rla_prepare_kernel(long rows, int N, int dk, int dv, int P, int prev_len, int fmap,
-                                                          int vsplit, const T* q, const T* k, const T* v, const T* kp,
-                                                          const T* vp, T* qo, T* ko, T* vo) {
+__device__ __forceinline__ RowAt<T> locate(int bh, int n, int N, int dk, int dv, int P, int prev_len, const T* k,
+                                           const T* v, const T* kp, const T* vp) {
+    RowAt<T> r{(long)bh * N + n, bh, n, nullptr, nullptr};
+    const int p = n - P;  // position of the token whose key and value land in row n
+    if (p >= 0) {
+        r.ks = k + ((size_t)bh * N + p) * dk;
+        r.vs = v + ((size_t)bh * N + p) * dv;
+    } else if (p >= -prev_len) {
+        r.ks = kp + ((size_t)bh * P + (p + P)) * dk;
+        r.vs = vp + ((size_t)bh * P + (p + P)) * dv;
+    }
+    return r;
+}
+
+// Issues the q and key loads of a row without a condition, so that the compiler's load waits stay
+// exact while the loads are in flight across the previous row's work. Lanes past d_k read feature
+// 0; an absent key row reads the q row, and with the identity map (want_q false) the q load reads
+// the key row again. finish_row discards what these stand-ins read.
+template <typename T>
+__device__ __forceinline__ void load_row(const RowAt<T>& r, const T* q, int dk, int lane, bool want_q,
+                                         typename Raw4<T>::type& xq, typename Raw4<T>::type& xk) {
+    const int off = 4 * lane < dk ? 4 * lane : 0;
+    const T* qrow = q + (size_t)r.row * dk;
+    const T* krow = r.ks ? r.ks : qrow;
+    xq = *reinterpret_cast<const typename Raw4<T>::type*>((want_q ? qrow : krow) + off);
+    xk = *reinterpret_cast<const typename Raw4<T>::type*>(krow + off);
+}
+
+// The rest of one row: phi(q[n]) (unless phi is the identity) and phi of the key row that lands at n
+// (zero where none does).
+template <typename T>
+__device__ __forceinline__ void finish_row(const RowAt<T>& r, const typename Raw4<T>::type& xq,
+                                           const typename Raw4<T>::type& xk, int dk, int fmap, int lane,
+                                           const double* tab, T* qo, T* ko) {
+    const bool live = 4 * lane < dk;
+    float fq[4], fk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        fq[j] = live ? (float)xq[j] : -INFINITY;
+        fk[j] = live && r.ks ? (float)xk[j] : -INFINITY;
+    }
+    if (fmap == 1) softmax2(dk, lane, fq, fk, tab);
+    if (qo) store_row4(qo + (size_t)r.row * dk, dk, lane, fq);
+    if (!r.ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fk[j] = 0.f;
+    }
+    store_row4(ko + (size_t)r.row * dk, dk, lane, fk);
+}
+
+// The next row of a wave's stride after r, or r itself past the end (more false).
+template <typename T>
+__device__ __forceinline__ RowAt<T> advance(const RowAt<T>& r, int BH, int N, int dk, int dv, int P, int prev_len,
+                                            int step_bh, int step_n, const T* k, const T* v, const T* kp, const T* vp,
+                                            bool& more) {
+    int bh = r.bh + step_bh, n = r.n + step_n;  // step_n < N, so one carry at most
+    if (n >= N) {
+        n -= N;
+        ++bh;
+    }
+    more = bh < BH;
+    return more ? locate<T>(bh, n, N, dk, dv, P, prev_len, k, v, kp, vp) : r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rla_prepare_kernel(int BH, int N, int dk, int dv, int P, int prev_len, int fmap,
+                                                          int vsplit, int step_bh, int step_n, const T* q, const T* k,
+                                                          const T* v, const T* kp, const T* vp, T* qo, T* ko, T* vo) {
     __shared__ double tab[32];
     if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Frac[threadIdx.x];
     __syncthreads();
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // the whole wave leaves together
     const int lane = threadIdx.x & 63;
-    const long bh = row / N;
-    const int n = (int)(row % N);
-    const int p = n - P;  // position of the token whose key and value land in row n
-    const T* ks = nullptr;
-    const T* vs = nullptr;
-    if (p >= 0) {
-        ks = k + ((size_t)bh * N + p) * dk;
-        vs = v + ((size_t)bh * N + p) * dv;
-    } else if (p >= -prev_len) {
-        ks = kp + ((size_t)bh * P + (p + P)) * dk;
-        vs = vp + ((size_t)bh * P + (p + P)) * dv;
+    // Rows are wave-uniform, so their index and address arithmetic runs on the scalar unit.
+    const int wave = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves = (int)gridDim.x * 4;
+    // The shifted value rows below vsplit, [B*H][vsplit][d_v] (the chunk kernels read the later rows
+    // from v itself): one wave per row, d_v * size / 16 whole 16-byte chunks.
+    const int n16 = dv * (int)sizeof(T) / 16;
+    for (long vr = wave; vr < (long)BH * vsplit; vr += waves) {
+        const int bh = (int)(vr / vsplit), n = (int)(vr % vsplit);
+        const RowAt<T> r = locate<T>(bh, n, N, dk, dv, P, prev_len, k, v, kp, vp);
+        u32x4* dst = reinterpret_cast<u32x4*>(vo + (size_t)vr * dv);
+        for (int c = lane; c < n16; c += 64)
+            dst[c] = r.vs ? reinterpret_cast<const u32x4*>(r.vs)[c] : u32x4{0u, 0u, 0u, 0u};
     }
-    // every load first
-    float fq[4], fk[4];
-    load_row4(qo ? q + (size_t)row * dk : nullptr, dk, lane, fq);
-    load_row4(ks, dk, lane, fk);
-    // the shifted value row only below vsplit (the chunk kernels read the later rows from v itself)
-    const bool vrow = n < vsplit;
-    const int n16 = dv * (int)sizeof(T) / 16;  // whole 16-byte chunks (d_v * size is a multiple of 16)
-    u32x4 vv[kMaxV16];
-#pragma unroll
-    for (int j = 0; j < kMaxV16; ++j) {
-        const int c = lane + 64 * j;
-        vv[j] = (vrow && vs && c < n16) ? reinterpret_cast<const u32x4*>(vs)[c] : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (fmap == 1) softmax2(dk, lane, fq, fk, tab);
-    if (qo) store_row4(qo + (size_t)row * dk, dk, lane, fq);
-    if (ks) {
-        store_row4(ko + (size_t)row * dk, dk, lane, fk);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fk[j] = 0.f;
-        store_row4(ko + (size_t)row * dk, dk, lane, fk);
-    }
-    if (vrow) {
-#pragma unroll
-        for (int j = 0; j < kMaxV16; ++j) {
-            const int c = lane + 64 * j;
-            if (c < n16) reinterpret_cast<u32x4*>(vo + ((size_t)bh * vsplit + n) * dv)[c] = vv[j];
-        }
+    // phi(q) and the shifted phi(k). A wave takes every waves-th row, (step_bh, step_n) in (b*h, n)
+    // form: one division per wave, then an add and a carry per row. The next row's loads are issued
+    // before this row's softmax, into the other of two register sets (a copy between them would be
+    // a use that waits for the load).
+    if (wave >= (long)BH * N) return;  // the whole wave leaves together
+    RowAt<T> ra = locate<T>(wave / N, wave % N, N, dk, dv, P, prev_len, k, v, kp, vp), rb;
+    typename Raw4<T>::type aq, ak, bq, bk;
+    const bool want_q = qo != nullptr;
+    load_row(ra, q, dk, lane, want_q, aq, ak);
+    bool more;
+    for (;;) {
+        rb = advance(ra, BH, N, dk, dv, P, prev_len, step_bh, step_n, k, v, kp, vp, more);
+        load_row(rb, q, dk, lane, want_q, bq, bk);
+        finish_row(ra, aq, ak, dk, fmap, lane, tab, qo, ko);
+        if (!more) break;
+        ra = advance(rb, BH, N, dk, dv, P, prev_len, step_bh, step_n, k, v, kp, vp, more);
+        load_row(ra, q, dk, lane, want_q, aq, ak);
+        finish_row(rb, bq, bk, dk, fmap, lane, tab, qo, ko);
+        if (!more) break;
     }
 }
 
@@ -223,16 +275,19 @@ __global__ __launch_bounds__(256) void copy_state_kernel(size_t n4, const float*
 hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream) {
     const long rows = r.rows;
     if (rows <= 0) return hipSuccess;
-    const unsigned grid = (unsigned)((rows + 3) / 4);
+    // 8 four-wave blocks per CU fill the 8 wave slots of each SIMD on 256 CUs; larger inputs loop
+    const long grid = std::min<long>((rows + 3) / 4, 256 * 8);
+    const long step = 4 * grid;
+    const int BH = (int)(rows / r.N), step_bh = (int)(step / r.N), step_n = (int)(step % r.N);
     if (r.bf16)
-        hipLaunchKernelGGL(rla_prepare_kernel<bf16>, dim3(grid), dim3(256), 0, stream, rows, r.N, r.dk, r.dv, r.P, r.prev_len, r.fmap,
-                           r.vsplit,
+        hipLaunchKernelGGL(rla_prepare_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
+                           r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const bf16*>(r.q), static_cast<const bf16*>(r.k), static_cast<const bf16*>(r.v),
                            static_cast<const bf16*>(r.kp), static_cast<const bf16*>(r.vp), static_cast<bf16*>(r.qo),
                            static_cast<bf16*>(r.ko), static_cast<bf16*>(r.vo));
     else
-        hipLaunchKernelGGL(rla_prepare_kernel<float>, dim3(grid), dim3(256), 0, stream, rows, r.N, r.dk, r.dv, r.P, r.prev_len, r.fmap,
-                           r.vsplit,
+        hipLaunchKernelGGL(rla_prepare_kernel<float>, dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
+                           r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const float*>(r.q), static_cast<const float*>(r.k), static_cast<const float*>(r.v),
                            static_cast<const float*>(r.kp), static_cast<const float*>(r.vp), static_cast<float*>(r.qo),
                            static_cast<float*>(r.ko), static_cast<float*>(r.vo));
