@@ -275,8 +275,10 @@ __global__ __launch_bounds__(256) void copy_state_kernel(size_t n4, const float*
 hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream) {
     const long rows = r.rows;
     if (rows <= 0) return hipSuccess;
-    // 8 four-wave blocks per CU fill the 8 wave slots of each SIMD on 256 CUs; larger inputs loop
-    const long grid = std::min<long>((rows + 3) / 4, 256 * 8);
+    // 16 four-wave blocks per CU on 256 CUs: 8 of them fill the 8 wave slots of each SIMD and the
+    // rest start as those finish, which evens out the tail (measured faster than 4 or 8 per CU);
+    // larger inputs loop
+    const long grid = std::min<long>((rows + 3) / 4, 256 * 16);
     const long step = 4 * grid;
     const int BH = (int)(rows / r.N), step_bh = (int)(step / r.N), step_n = (int)(step % r.N);
     if (r.bf16)
