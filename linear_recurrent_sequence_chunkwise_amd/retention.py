@@ -101,13 +101,10 @@ class GroupNorm:
     gate: Optional[torch.Tensor] = None  # shaped like the output, in the input dtype, or None
 
     def as_struct(self, in_dtype, out_shape):
-        for t in (self.weight, self.bias):
-            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
-                raise ValueError("groupnorm weight/bias must be contiguous fp32 device tensors")
-        g = self.gate
-        if g is not None and (g.dtype != in_dtype or tuple(g.shape) != tuple(out_shape) or not g.is_contiguous() or not g.is_cuda):
-            raise ValueError(f"gate must be a contiguous {in_dtype} device tensor of shape {tuple(out_shape)}")
-        return RetGroupNorm(1, float(self.eps), _ptr(self.weight), _ptr(self.bias), _ptr(g))
+        c = _Checks()
+        c.groupnorm(self, in_dtype, out_shape)
+        c.done()
+        return RetGroupNorm(1, float(self.eps), _ptr(self.weight), _ptr(self.bias), _ptr(self.gate))
 
 
 @dataclass
@@ -158,16 +155,64 @@ def _shape(B, H, N, dk, dv, in_code, out_code):
     return RetShape(B, H, N, dk, dv, in_code, out_code)
 
 
-def _check_inputs(q, k, v, ndim):
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.dim() != ndim:
-            raise ValueError(f"{name} must have {ndim} dimensions")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k and v must share a dtype")
+_IN_DTYPES = (torch.float32, torch.bfloat16)
+
+
+class _Checks:
+    """The caller-supplied tensors of one call. The C ABI takes bare pointers and cannot see buffer
+    sizes, so every tensor is checked here before any pointer crosses it: first the exact shape and
+    dtype of every tensor, then that each is contiguous and on the GPU (so the size checks also
+    run, and can be tested, on CPU tensors)."""
+
+    def __init__(self):
+        self.seen = []
+
+    def tensor(self, name, t, shape, dtypes):
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+        self.seen.append((name, t))
+
+    def inputs(self, q, k, v, ndim):
+        """q, k, v: q and k [B,H,N,d_k] (decode: [B,H,d_k]), v [B,H,N,d_v] ([B,H,d_v]), one dtype
+        (fp32 or bf16). Returns the leading dims, d_k and d_v."""
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+                raise ValueError(f"{name} must be a tensor with {ndim} dimensions")
+        lead, dk, dv = tuple(q.shape[:-1]), q.shape[-1], v.shape[-1]
+        self.tensor("q", q, q.shape, _IN_DTYPES)
+        self.tensor("k", k, lead + (dk,), (q.dtype,))
+        self.tensor("v", v, lead + (dv,), (q.dtype,))
+        if min(q.shape) <= 0 or dv <= 0:
+            raise ValueError(f"q and v need positive dimensions (q {tuple(q.shape)}, v {tuple(v.shape)})")
+        return lead, dk, dv
+
+    def state(self, name, t, B, H, dk, dv):
+        self.tensor(name, t, (B, H, dk, dv), (torch.float32,))
+
+    def out(self, t, shape):
+        self.tensor("out", t, shape, _IN_DTYPES)
+
+    def groupnorm(self, gn, in_dtype, out_shape):
+        if gn is None:
+            return
+        H, dv = out_shape[1], out_shape[-1]
+        self.tensor("groupnorm weight", gn.weight, (H, dv), (torch.float32,))
+        self.tensor("groupnorm bias", gn.bias, (H, dv), (torch.float32,))
+        self.tensor("gate", gn.gate, out_shape, (in_dtype,))
+
+    def done(self):
+        for name, t in self.seen:
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor")
 
 
 def _flags(groupnorm, rotation):
@@ -187,6 +232,8 @@ def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() or not workspace.is_cuda:
+            raise ValueError("workspace must be a contiguous device tensor")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return workspace, workspace.numel() * workspace.element_size()
@@ -200,10 +247,14 @@ def chunkwise_fwd(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None,
     """Chunkwise retention forward. q, k: [B,H,N,dk]; v: [B,H,N,dv] (fp32 or bf16, device).
     Returns (out [B,H,N,dv] of out_dtype or None, state_out fp32 [B,H,dk,dv] or None).
     state_out may be passed as the same tensor as state_in (in place)."""
+    c = _Checks()
+    (B, H, N), dk, dv = c.inputs(q, k, v, 4)
+    c.out(out, (B, H, N, dv))
+    c.state("state_in", state_in, B, H, dk, dv)
+    c.state("state_out", state_out, B, H, dk, dv)
+    c.groupnorm(groupnorm, q.dtype, (B, H, N, dv))
+    c.done()
     lib = load_library()
-    _check_inputs(q, k, v, 4)
-    B, H, N, dk = q.shape
-    dv = v.shape[-1]
     in_code = _dtype_code(q.dtype)
     if out is not None:
         out_dtype = out.dtype
@@ -236,12 +287,15 @@ def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optiona
     """One recurrent step: state <- g*state + k^T v (in place), o = q state.
     q, k: [B,H,dk]; v: [B,H,dv]; state: fp32 [B,H,dk,dv]. Returns o [B,H,dv] (or None).
     With a rotation, rotation.offset is the position of this token."""
+    c = _Checks()
+    (B, H), dk, dv = c.inputs(q, k, v, 3)
+    if state is None:
+        raise ValueError("state is required")
+    c.state("state", state, B, H, dk, dv)
+    c.out(out, (B, H, dv))
+    c.groupnorm(groupnorm, q.dtype, (B, H, dv))
+    c.done()
     lib = load_library()
-    _check_inputs(q, k, v, 3)
-    B, H, dk = q.shape
-    dv = v.shape[-1]
-    if not (state.is_cuda and state.is_contiguous() and state.dtype == torch.float32):
-        raise ValueError("state must be a contiguous fp32 device tensor")
     if out is not None:
         out_dtype = out.dtype
     if want_out and out is None:
@@ -264,10 +318,12 @@ def recurrent_step(q, k, v, gamma: Sequence[float], state, *, groupnorm: Optiona
 def parallel_fwd(q, k, v, gamma: Sequence[float], *, groupnorm: Optional[GroupNorm] = None,
                  rotation: Optional[Rotation] = None, out=None, out_dtype=torch.float32, workspace=None, stream=None):
     """Parallel form O = (Q K^T (.) D) V. Returns out [B,H,N,dv]."""
+    c = _Checks()
+    (B, H, N), dk, dv = c.inputs(q, k, v, 4)
+    c.out(out, (B, H, N, dv))
+    c.groupnorm(groupnorm, q.dtype, (B, H, N, dv))
+    c.done()
     lib = load_library()
-    _check_inputs(q, k, v, 4)
-    B, H, N, dk = q.shape
-    dv = v.shape[-1]
     if out is not None:
         out_dtype = out.dtype
     else:
@@ -291,12 +347,14 @@ def chunkwise_bwd(q, k, v, gamma: Sequence[float], dout, chunk: int, *, state_in
     (shaped like q, k, v) and dstate_in ([B,H,dk,dv]); the names not in `want` come back None.
     dout is laid out like v, in the input dtype. With a rotation, dq and dk are the gradients with
     respect to the unrotated q and k."""
+    c = _Checks()
+    (B, H, N), dk, dv = c.inputs(q, k, v, 4)
+    if dout is None:
+        raise ValueError("dout is required")
+    c.tensor("dout", dout, (B, H, N, dv), (q.dtype,))
+    c.state("state_in", state_in, B, H, dk, dv)
+    c.done()
     lib = load_library()
-    _check_inputs(q, k, v, 4)
-    B, H, N, dk = q.shape
-    dv = v.shape[-1]
-    if not (dout.is_cuda and dout.is_contiguous() and dout.dtype == q.dtype and tuple(dout.shape) == tuple(v.shape)):
-        raise ValueError("dout must be a contiguous device tensor shaped and typed like v")
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty((B, H, N, dk), **f32) if "dq" in want else None
     dk_ = torch.empty((B, H, N, dk), **f32) if "dk" in want else None
@@ -325,15 +383,25 @@ def rla_fwd(q, k, v, window: int, chunk: int = 128, *, fmap: str = "softmax", k_
     before the segment, of which the last prev_len (default: all, or none without them) hold tokens.
     state_in / state_out: fp32 [B,H,dk,dv], the sum over the tokens that have left the window
     (state_out may be state_in; a one-token segment needs a state_out). Returns (out, state_out)."""
-    lib = load_library()
-    _check_inputs(q, k, v, 4)
-    B, H, N, dk = q.shape
-    dv = v.shape[-1]
+    c = _Checks()
+    (B, H, N), dk, dv = c.inputs(q, k, v, 4)
+    if window < 0:
+        raise ValueError(f"window must be >= 0 (got {window})")
     if prev_len is None:
         prev_len = 0 if k_prev is None else window + 1
-    for name, t, d in (("k_prev", k_prev, dk), ("v_prev", v_prev, dv)):
-        if t is not None and (tuple(t.shape) != (B, H, window + 1, d) or t.dtype != q.dtype or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous {q.dtype} tensor of shape {(B, H, window + 1, d)}")
+    c.tensor("k_prev", k_prev, (B, H, window + 1, dk), (q.dtype,))
+    c.tensor("v_prev", v_prev, (B, H, window + 1, dv), (q.dtype,))
+    if not 0 <= prev_len <= window + 1:
+        raise ValueError(f"prev_len must be in [0, window + 1] (got {prev_len})")
+    if prev_len > 0 and (k_prev is None or v_prev is None):
+        raise ValueError("prev_len > 0 needs k_prev and v_prev")
+    c.out(out, (B, H, N, dv))
+    c.state("state_in", state_in, B, H, dk, dv)
+    c.state("state_out", state_out, B, H, dk, dv)
+    if fmap not in _FMAPS:
+        raise ValueError(f"fmap must be one of {sorted(_FMAPS)} (got {fmap!r})")
+    c.done()
+    lib = load_library()
     if out is not None:
         out_dtype = out.dtype
     if want_out and out is None:
