@@ -66,6 +66,19 @@ def backward_flops(B, H, N, dk, dv, C):
 
 RLA_WINDOW = 512  # the window the RAttention page reports matching full attention with
 
+# The only figures the pages print for this method are whole-model ones (abeam.tech RetNet summary,
+# "Experiments": "Training cost" and "Inference cost"). Reported beside the kernel numbers as
+# context only: another machine, a whole 6.7B model (every layer, projections, FFN, backward) in
+# plain PyTorch, so neither a same-node nor a same-workload comparison, and no vs_baseline.
+PAGES_CONTEXT = {
+    "not_comparable": "whole 6.7B RetNet model on 8x A100 80GB in plain PyTorch without kernel fusion (training) and an "
+                      "unstated setup (decoding); not this kernel, not this node",
+    "training_words_per_s": 17458.6, "training_seq_len": 8192, "training_hardware": "8x A100 80GB",
+    "training_memory_GB": 48.0,
+    "decode_speedup_vs_kv_cache_transformer": 8.4, "decode_memory_saving_frac": 0.70, "decode_input_len": 8192,
+    "source": "abeam.tech RetNet paper summary, Experiments: Training cost, Inference cost",
+}
+
 
 def time_calls(fn, n, stream, torch):
     """Average time of fn() over n calls, with HIP events on the library's stream."""
@@ -446,6 +459,7 @@ def main():
         "long_context": long_ctx,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
+        "pages_context": PAGES_CONTEXT,
     }
     print(json.dumps(line), flush=True)
 

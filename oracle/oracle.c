@@ -259,7 +259,7 @@ void oracle_chunkwise(int B, int H, int N, int dk, int dv, int C,
 /*
  * Per-head GroupNorm (mlnews bullet summary: retention outputs are
  * normalised per head with GroupNorm before the heads are concatenated;
- * abeam.tech summary, "Multi-scale decay, gate and normalisation").
+ * abeam.tech summary, "Multi-timescale decay, gate and normalisation").
  * One group = the d_v channels of one head at one position, so each
  * row x of x[B][H][N][dv] is normalised on its own:
  *     mu = mean(x), var = mean((x - mu)^2)   (biased)
