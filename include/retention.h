@@ -24,7 +24,9 @@
  * by the caller. `gamma` is a HOST pointer to H doubles, and `rotation` and `groupnorm` HOST
  * pointers to structs; all three are read during the call only. The library
  * never allocates device memory and keeps no state between calls except a thread-local error
- * string. All device pointers must be 16-byte aligned.
+ * string and, for retention_chunkwise_fwd_noalloc only, its fixed per-GPU scratch array (part of
+ * the loaded code object) and the address of it on each device. All device pointers must be
+ * 16-byte aligned.
  * Streams: all work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
  * call returns without synchronising. Errors found during execution surface at the caller's
  * next synchronisation.
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 3
+#define RETENTION_ABI_VERSION 4
 #define RETENTION_MAX_HEADS 128
 
 typedef enum {
@@ -232,6 +234,26 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
                              const void* k_prev, const void* v_prev, int32_t prev_len,
                              const float* state_in, void* out, float* state_out,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The chunkwise forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results as retention_chunkwise_fwd, with its scratch taken
+ * from a fixed array inside the library instead of a caller workspace. The call allocates nothing.
+ * The array holds RETENTION_NOALLOC_SCRATCH_BYTES; a call whose workspace
+ * (retention_workspace_bytes(RET_FN_CHUNKWISE, ...)) exceeds it returns RET_ERR_WORKSPACE before any
+ * HIP call. Each GPU holds one copy of the array from the library's first use on it until the
+ * process ends; its address is looked up once per device, on the first call with that device
+ * current. The stream must belong to the current device. Every call on one GPU shares that GPU's
+ * array and it keeps the last call's contents: calls that overlap in time on one GPU (different
+ * streams, or host threads) race on it and must be ordered by the caller.
+ */
+#define RETENTION_NOALLOC_SCRATCH_BYTES (64ull << 20)
+ret_status retention_chunkwise_fwd_noalloc(const ret_shape* shape, int32_t chunk,
+                                           const void* q, const void* k, const void* v,
+                                           const double* gamma, const ret_rotation* rotation, const float* state_in,
+                                           const ret_groupnorm* groupnorm, void* out, float* state_out,
+                                           void* hip_stream);
 
 /* Bytes of device workspace the call `fn` needs for this shape, chunk and flags (a bitwise OR of
  * RET_WS_GROUPNORM when a GroupNorm epilogue is enabled and RET_WS_ROTATION when a rotation is).

@@ -10,6 +10,7 @@
 
 #include "../../include/retention.h"
 #include "common.hpp"
+#include "entry.hpp"
 
 namespace {
 
@@ -217,6 +218,10 @@ ret_status check_ws(size_t need, const void* ws, size_t wsb) {
 
 }  // namespace
 
+// Sets the thread-local message that retention_last_error() returns (for entry points defined in
+// other files of the library).
+void ret::set_last_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+
 extern "C" {
 
 int32_t retention_abi_version(void) { return RETENTION_ABI_VERSION; }
@@ -285,6 +290,19 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
                                    const double* gamma, const ret_rotation* rotation, const float* state_in,
                                    const ret_groupnorm* groupnorm, void* out, float* state_out, void* workspace,
                                    size_t workspace_bytes, void* hip_stream) {
+    return (ret_status)ret::chunkwise_fwd_entry(shape, chunk, q, k, v, gamma, rotation, state_in, groupnorm, out, state_out, workspace,
+                                                workspace_bytes, nullptr, hip_stream);
+}
+
+}  // extern "C"
+
+// The chunkwise forward behind both entry points. provide (may be null) is asked for the
+// workspace after every argument has been validated, with the bytes the call needs, only when it
+// needs some; it returns RET_OK with the buffer, or a status (its message already set).
+int ret::chunkwise_fwd_entry(const ret_shape* shape, int32_t chunk, const void* q, const void* k, const void* v,
+                             const double* gamma, const ret_rotation* rotation, const float* state_in,
+                             const ret_groupnorm* groupnorm, void* out, float* state_out, void* workspace,
+                             size_t workspace_bytes, int (*provide)(size_t need, void** ws, size_t* bytes), void* hip_stream) {
     g_err[0] = '\0';
     RET_TRY(check_shape(shape, false));
     RET_TRY(check_ptr(q, "q", true));
@@ -324,6 +342,7 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
         gn.gate = nullptr;
     }
     const size_t need = (rot ? rotation_ws(shape) : 0) + chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
+    if (provide && need > 0) RET_TRY((ret_status)provide(need, &workspace, &workspace_bytes));
     RET_TRY(check_ws(need, workspace, workspace_bytes));
     if (rot) {
         const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
@@ -334,6 +353,8 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk, const 
     hipError_t e = bf ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a);
     return device_status(e, "retention_chunkwise_fwd launch");
 }
+
+extern "C" {
 
 ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const void* q, const void* k, const void* v,
                                    const double* gamma, const ret_rotation* rotation, const float* state_in, const void* dout,

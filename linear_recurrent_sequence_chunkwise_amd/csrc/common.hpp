@@ -233,6 +233,7 @@ struct BwdArgs {
 
 // Launchers (one per kernel family), called by the C-ABI layer after validation.
 namespace ret {
+void set_last_error(const char* msg);  // the message retention_last_error() returns
 hipError_t launch_recurrent_step(const LaunchArgs& a);
 hipError_t launch_chunkwise_bf16(const LaunchArgs& a);
 hipError_t launch_parallel_bf16(const LaunchArgs& a);

@@ -22,7 +22,7 @@ RET_WS_GROUPNORM, RET_WS_ROTATION = 1, 2
 
 EXPORTED = [
     "retention_chunkwise_fwd", "retention_recurrent_step", "retention_parallel_fwd", "retention_chunkwise_bwd",
-    "retention_rla_fwd",
+    "retention_rla_fwd", "retention_chunkwise_fwd_noalloc",
     "retention_workspace_bytes",
     "retention_status_string", "retention_last_error", "retention_abi_version",
 ]
@@ -68,8 +68,9 @@ def load_library(path: str = LIB_PATH):
     lib.retention_parallel_fwd.argtypes = [sp, vp, vp, vp, dp, rp, gp, vp, vp, sz, vp]
     lib.retention_chunkwise_bwd.argtypes = [sp, i32, vp, vp, vp, dp, rp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.retention_rla_fwd.argtypes = [sp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.retention_chunkwise_fwd_noalloc.argtypes = [sp, i32, vp, vp, vp, dp, rp, vp, gp, vp, vp, vp]
     for f in (lib.retention_chunkwise_fwd, lib.retention_recurrent_step, lib.retention_parallel_fwd, lib.retention_chunkwise_bwd,
-              lib.retention_rla_fwd):
+              lib.retention_rla_fwd, lib.retention_chunkwise_fwd_noalloc):
         f.restype = ctypes.c_int
     lib.retention_workspace_bytes.argtypes = [i32, sp, i32, i32]
     lib.retention_workspace_bytes.restype = sz
@@ -277,6 +278,33 @@ def chunkwise_fwd(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None,
     st = lib.retention_chunkwise_fwd(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H),
                                      _rot(rotation), _ptr(state_in), ctypes.byref(gn) if gn is not None else None, _ptr(out),
                                      _ptr(state_out), _ptr(ws), wsb, _stream(q.device, stream))
+    _check(st)
+    return out, state_out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # RETENTION_NOALLOC_SCRATCH_BYTES
+
+
+def chunkwise_fwd_noalloc(q, k, v, gamma: Sequence[float], chunk: int, *, state_in=None,
+                          groupnorm: Optional[GroupNorm] = None, rotation: Optional[Rotation] = None, out, state_out=None,
+                          stream=None):
+    """The chunkwise forward through retention_chunkwise_fwd_noalloc: no workspace, the library's own
+    fixed scratch array instead. The caller passes every output (out and/or state_out), so this
+    call allocates nothing either. Returns (out, state_out)."""
+    c = _Checks()
+    (B, H, N), dk, dv = c.inputs(q, k, v, 4)
+    c.out(out, (B, H, N, dv))
+    c.state("state_in", state_in, B, H, dk, dv)
+    c.state("state_out", state_out, B, H, dk, dv)
+    c.groupnorm(groupnorm, q.dtype, (B, H, N, dv))
+    c.done()
+    lib = load_library()
+    out_code = _dtype_code(out.dtype) if out is not None else RET_F32
+    gn = groupnorm.as_struct(q.dtype, (B, H, N, dv)) if groupnorm is not None else None
+    shp = _shape(B, H, N, dk, dv, _dtype_code(q.dtype), out_code)
+    st = lib.retention_chunkwise_fwd_noalloc(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _gamma(gamma, H),
+                                             _rot(rotation), _ptr(state_in), ctypes.byref(gn) if gn is not None else None,
+                                             _ptr(out), _ptr(state_out), _stream(q.device, stream))
     _check(st)
     return out, state_out
 

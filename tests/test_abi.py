@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.retention_abi_version() == 3
+    assert lib.retention_abi_version() == 4
     for s in range(5):
         assert lib.retention_status_string(s).decode().startswith("RET_")
     assert lib.retention_status_string(99).decode() == "unknown status"
@@ -333,3 +333,36 @@ def test_bf16_sequence_length_limit(lib):
     assert "2^31" in lib.retention_last_error().decode()
     assert bwd(lib, s, C=128) == R.RET_ERR_UNSUPPORTED
     assert rla(lib, s, C=128) == R.RET_ERR_UNSUPPORTED
+
+
+def noalloc(lib, shp=None, C=64, q=Q, k=K, v=V, g=None, sin=None, gn=None, out=OUT, sout=ST, rot=None):
+    shp = shp if shp is not None else shape()
+    g = g if g is not None else gam([0.9] * shp.heads)
+    return lib.retention_chunkwise_fwd_noalloc(ctypes.byref(shp), C, q, k, v, g, rot, sin, gn, out, sout, None)
+
+
+def test_noalloc_validates_like_the_plain_call(lib):
+    # the same host validation as retention_chunkwise_fwd, before the scratch array is touched
+    assert noalloc(lib, q=None) == R.RET_ERR_INVALID_ARG
+    assert "q is NULL" in lib.retention_last_error().decode()
+    assert noalloc(lib, out=None, sout=None) == R.RET_ERR_INVALID_ARG
+    assert noalloc(lib, g=gam([0.9, 1.5])) == R.RET_ERR_INVALID_ARG
+    assert noalloc(lib, C=96) == R.RET_ERR_UNSUPPORTED
+
+
+def test_noalloc_refuses_beyond_its_array(lib):
+    # the N=8192 layer with GroupNorm needs more scratch than the fixed array holds: refused on the
+    # host with a message that names both sizes
+    s = shape(B=1, H=16, N=8192, dk=256, dv=512, o=R.RET_BF16)
+    gn = R.RetGroupNorm(1, 1e-5, None, None, None)
+    need = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(s), 128, R.RET_WS_GROUPNORM)
+    assert need > R.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, s, C=128, g=gam([0.9] * 16), gn=ctypes.byref(gn)) == R.RET_ERR_WORKSPACE
+    msg = lib.retention_last_error().decode()
+    assert str(need) in msg and str(R.NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_noalloc_scratch_size_matches_header():
+    txt = open(HEADER).read()
+    m = re.search(r"#define RETENTION_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == R.NOALLOC_SCRATCH_BYTES
