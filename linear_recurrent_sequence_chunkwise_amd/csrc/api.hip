@@ -195,12 +195,23 @@ size_t chunkwise_ws(const ret_shape* s, int chunk, int gn, int want_out) {
     return want_out ? ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16) : 0;
 }
 
-// Residual linear attention: phi(q), the shifted phi(k) and v (input dtype, each 256-byte
-// aligned), then the chunkwise workspace for N > 1 (no GroupNorm).
-size_t rla_ws(const ret_shape* s, int chunk) {
-    const size_t rows = (size_t)s->batch * s->heads * s->seq_len, es = elem_size(s->in_dtype);
+// Residual linear attention with bf16 inputs and the softmax map keeps its features in fp32: the
+// softmax concentrates a row's weight on a few features, and their bf16 rounding alone moves the
+// output by 2e-2 to 5e-2 of its RMS. Those calls run the fp32 kernels, whose chunks are at most 128
+// tokens (the chunk length changes the blocking of the sum, not its value).
+bool rla_f32_features(const ret_shape* s, int fmap) { return s->in_dtype == RET_BF16 && fmap == RET_FMAP_SOFTMAX; }
+int rla_chunk(const ret_shape* s, int fmap, int chunk) { return rla_f32_features(s, fmap) ? std::min(chunk, 128) : chunk; }
+
+// Residual linear attention: phi(q), the shifted phi(k) and v (input dtype, or fp32 with
+// rla_f32_features; each 256-byte aligned), then the chunkwise workspace for N > 1 (no GroupNorm).
+size_t rla_ws(const ret_shape* s, int chunk, int fmap) {
+    const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
+    const bool f32 = rla_f32_features(s, fmap);
+    const size_t es = f32 ? sizeof(float) : elem_size(s->in_dtype);
     const size_t ops = 2 * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
-    return ops + (s->seq_len > 1 ? chunkwise_ws(s, chunk, 0, 1) : 0);
+    if (s->seq_len == 1) return ops;
+    if (f32) return ops + ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, 0, s->out_dtype == RET_BF16);
+    return ops + chunkwise_ws(s, chunk, 0, 1);
 }
 
 size_t parallel_ws(const ret_shape* s, int gn) {
@@ -281,7 +292,7 @@ size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chu
                                                       shape->d_k, shape->d_v, chunk);
         case RET_FN_RLA:
             if (shape->seq_len > 1 && chunk <= 0) return (size_t)-1;
-            return rla_ws(shape, chunk);
+            return std::max(rla_ws(shape, chunk, RET_FMAP_IDENTITY), rla_ws(shape, chunk, RET_FMAP_SOFTMAX));
         default: return (size_t)-1;
     }
 }
@@ -529,6 +540,9 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, dv, chunk) : !ret::chunkwise_f32_supported(shape->d_k, dv, chunk))
             return fail(RET_ERR_UNSUPPORTED, "residual linear attention: no chunkwise kernel for %s inputs with d_k %d, d_v %d, chunk %d",
                         bf ? "bf16" : "fp32", shape->d_k, dv, chunk);
+        if (rla_f32_features(shape, feature_map) && !ret::chunkwise_f32_supported(shape->d_k, dv, rla_chunk(shape, feature_map, chunk)))
+            return fail(RET_ERR_UNSUPPORTED, "residual linear attention with fp32 features: no chunkwise kernel for d_k %d, d_v %d",
+                        shape->d_k, dv);
         RET_TRY(check_bf16_head(shape, chunk));
     }
     const size_t rows = (size_t)shape->batch * shape->heads * N;
@@ -543,21 +557,25 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     if (state_out && out && overlaps(out, out_bytes, state_out, st_bytes)) return fail(RET_ERR_INVALID_ARG, "out must not alias state_out");
     if (state_out && state_in && state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes))
         return fail(RET_ERR_INVALID_ARG, "state_out may equal state_in but must not partly overlap it");
-    RET_TRY(check_ws(rla_ws(shape, chunk), workspace, workspace_bytes));
+    RET_TRY(check_ws(rla_ws(shape, chunk, feature_map), workspace, workspace_bytes));
 
     // operands: phi(q), shifted phi(k) and v, in the front of the workspace
     const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     char* w = static_cast<char*>(workspace);
-    const size_t Aq = align256(rows * shape->d_k * es), Av = align256(rows * dv * es);
+    const bool f32feat = rla_f32_features(shape, feature_map);
+    const size_t eo = f32feat ? sizeof(float) : es;  // bytes per prepared element
+    const size_t Aq = align256(rows * shape->d_k * eo), Av = align256(rows * dv * eo);
     ret::RlaPrep r{};
     r.rows = (long)rows; r.N = N; r.dk = shape->d_k; r.dv = dv; r.P = P; r.prev_len = prev_len; r.fmap = feature_map; r.bf16 = bf;
+    r.feat_f32 = f32feat;
     r.q = q; r.k = k; r.v = v; r.kp = k_prev; r.vp = v_prev;
     r.qo = feature_map == RET_FMAP_IDENTITY ? nullptr : w;
     r.ko = w + Aq;
     r.vo = w + 2 * Aq;
     // shifted value rows in the workspace only up to vsplit (w + 1 rounded up to a 32-token stage,
-    // at most N); the chunkwise kernels read the later rows from v, w + 1 rows back
-    r.vsplit = (int)std::min<long long>(((long long)P + 31) / 32 * 32, N);
+    // at most N); the chunkwise kernels read the later rows from v, w + 1 rows back. With fp32
+    // features every value row is written there in fp32.
+    r.vsplit = f32feat ? N : (int)std::min<long long>(((long long)P + 31) / 32 * 32, N);
     hipError_t e = ret::launch_rla_prepare(r, st);
     if (e != hipSuccess) return device_status(e, "retention_rla_fwd prepare launch");
     ret::HeadConsts hc;
@@ -565,8 +583,9 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         hc.gamma[h] = 1.f;
         hc.log2g[h] = 0.f;
     }
-    ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, w + 2 * Aq + Av, workspace_bytes - (2 * Aq + Av),
-                                  hip_stream);
+    ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : rla_chunk(shape, feature_map, chunk), hc, ret::GnArgs{}, w + 2 * Aq + Av,
+                                  workspace_bytes - (2 * Aq + Av), hip_stream);
+    if (f32feat) a.in_bf16 = 0;  // the fp32 kernels, on the fp32 features and value rows
     a.q = r.qo ? r.qo : q; a.k = r.ko; a.out = out;
     if (r.vsplit == N) {
         a.v = r.vo;  // every value row is in the prefix buffer (laid out like v)
@@ -583,7 +602,7 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         return device_status(ret::launch_recurrent_step(a), "retention_rla_fwd step launch");
     }
     a.state_in = state_in; a.state_out = state_out;
-    return device_status(bf ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
+    return device_status(a.in_bf16 ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
 }
 
 }  // extern "C"

@@ -7,21 +7,23 @@
 //     R  <- g^L R + K^T (V (.) zeta),                    zeta_t = g^(L-1-t)
 //
 // Kernels:
-//   chunk_scores_kernel   parallel over (64-row band, chunk, b*h): P = (Q K^T) (.) D on MFMA with the
-//                         decay and causal mask applied in registers, stored as bf16 in the workspace
-//                         (32-key blocks on and below the diagonal). Q and K go through LDS with all
-//                         loads of a block issued together; the next key block is prefetched.
-//   chunk_ws_kernel       (chunks up to 256, output wanted) one workgroup per (b, h, 32-column slice
-//                         of d_v), walking the sequence in 32-token stages, with a loader wave,
-//                         state waves and output waves (see the kernel):
-//                           out  = g^(j+1) Q R + P V      (R of the previous chunk as bf16 hi + lo)
+//   chunk_scores_kernel   parallel over (chunk, b*h): P = (Q K^T) (.) D on MFMA with the decay and
+//                         causal mask applied in registers, stored in the workspace as bf16 hi and,
+//                         in a second plane, lo = P - hi rounded (32-key blocks on and below the
+//                         diagonal). A single bf16 P moves the output by about 1e-2 of its RMS.
+//   chunk_ws_kernel       (chunks up to 256 whose stage buffers fit, output wanted) one workgroup
+//                         per (b, h, 32-column slice of d_v), walking the sequence in 32-token
+//                         stages, with loader waves, state waves and output waves (see the kernel):
+//                           out  = g^(j+1) Q R + P V      (R of the previous chunk and P as bf16
+//                                                         hi + lo)
 //                           R   += K^T (V (.) zeta)       (V (.) zeta as bf16 hi + lo; R fp32 in
 //                                                         accumulators, scaled by g^L at chunk start)
-//   chunk_main_kernel     the same per stage with every wave doing both parts (512-token chunks, and
-//                         state-only prefills, which have no output part).
+//   chunk_main_kernel     the same per stage with every wave doing both parts (d_k 256 at chunks of
+//                         256 and 512, and state-only prefills, which have no output part).
 //   gn_rows_kernel        the optional per-head GroupNorm over d_v, on fp32 pre-norm rows that the
 //                         chunk kernel writes to the workspace.
-// The d_v slices of one head sit on one XCD to share its L2.
+// The d_v slices of one head sit on one XCD to share its L2. Plain calls whose (b, h, slice)
+// workgroups would leave compute units idle run on the segmented kernels of chunk_seg.hip instead.
 #include "common.hpp"
 
 namespace ret {
@@ -32,7 +34,8 @@ constexpr int kW = 32;     // d_v columns per workgroup
 constexpr int kST = 32;    // tokens per pipeline stage
 
 // ---------------------------------------------------------------------------------------------
-// P = (Q K^T) (.) D for every chunk, into the workspace as [B*H][nchunks][C][C] bf16. Grid
+// P = (Q K^T) (.) D for every chunk, into the workspace as [B*H][nchunks][C][C] bf16, its high
+// part in P and, when Plo is given, the low part (P - hi, rounded) in Plo, same layout. Grid
 // (nchunks, B*H), 256 threads. The MFMAs compute P^T = K Q^T per 16 x 16 tile so that each lane
 // ends with 4 consecutive keys of one row (one 8-byte store). K rows go through LDS in 128-key
 // blocks (buffer-to-LDS loads, swizzled rows); each wave reads the Q fragments of its row tile
@@ -41,8 +44,8 @@ constexpr int kST = 32;    // tokens per pipeline stage
 // Waves take row tiles in mirrored pairs (t, T-1-t) so that the causal work is balanced.
 template <int DK>
 __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
-                                                           const bf16* __restrict__ k, bf16* __restrict__ P, HeadConsts hc,
-                                                           int rev, int ldqk, int qcol_blk, int srcBH) {
+                                                           const bf16* __restrict__ k, bf16* __restrict__ P, bf16* __restrict__ Plo,
+                                                           HeadConsts hc, int rev, int ldqk, int qcol_blk, int srcBH) {
     constexpr int KB = 128;       // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row
     constexpr int NKB = KB * QRB / 1024;  // kilobytes of a K block
@@ -59,6 +62,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + qbase), 0, q_bytes, 0x00020000);
     auto row_of = [&](int t) __attribute__((always_inline)) { return rev ? N - 1 - t : t; };
     bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
+    bf16* Plc = Plo ? Plo + ((size_t)bh * nchunks + chunk) * (size_t)C * C : nullptr;
     const int T = C / 16;  // row tiles of the chunk
 
     for (int kb0 = 0; kb0 < C; kb0 += KB) {
@@ -89,13 +93,17 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
                     acc = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qf[ks], acc);
                 // lane: row 16t + c16, keys 16kt + 4g4 + i
                 const int row = 16 * t + c16;
-                bf16x4 o;
+                bf16x4 o, ol;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 16 * kt + 4 * g4 + i;
-                    o[i] = (bf16)(row >= key ? acc[i] * decay_pow(l2g, (float)(row - key)) : 0.f);
+                    bf16 hi, lo;
+                    split_hi_lo(row >= key ? acc[i] * decay_pow(l2g, (float)(row - key)) : 0.f, hi, lo);
+                    o[i] = hi;
+                    ol[i] = lo;
                 }
                 *reinterpret_cast<bf16x4*>(Pc + (size_t)row * C + 16 * kt + 4 * g4) = o;
+                if (Plc) *reinterpret_cast<bf16x4*>(Plc + (size_t)row * C + 16 * kt + 4 * g4) = ol;
             }
         }
     }
@@ -120,12 +128,13 @@ struct MainParams {
     const bf16* v;
     const bf16* vpre;
     const bf16* P;
+    const bf16* Plo;  // low part of P (same layout), when the kernel uses it
     const float* state_in;
     float* state_out;
     void* out;
 };
 
-template <int DK, int C>
+template <int DK, int C, bool PLO = false>
 struct MainGeom {
     static constexpr int LQ = DK + 8;    // Q rows (16-byte reads)
     static constexpr int LK = DK + 16;   // K rows (transposing reads)
@@ -138,19 +147,29 @@ struct MainGeom {
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t OFF_K = OFF_Q + (size_t)kST * LQ * 2;
     static constexpr size_t OFF_P = OFF_K + (size_t)kST * LK * 2;
-    static constexpr size_t OFF_V = OFF_P + (size_t)kST * LP * 2;
-    static constexpr size_t OFF_RH = OFF_V + (size_t)C * LV * 2;
-    static constexpr size_t OFF_RL = OFF_RH + (size_t)kW * LR * 2;
-    static constexpr size_t OFF_ZH = OFF_RL + (size_t)kW * LR * 2;   // V (.) zeta, bf16 high part, this stage
+    static constexpr size_t OFF_PL = OFF_P + (size_t)kST * LP * 2;                // P low part (PLO)
+    static constexpr size_t OFF_V = OFF_PL + (PLO ? (size_t)kST * LP * 2 : 0);
+    static constexpr size_t V_END = OFF_V + (size_t)C * LV * 2;
+    static constexpr size_t R_BYTES = (size_t)kW * LR * 2;  // R^T, one part
+    static constexpr size_t Z_BYTES = (size_t)kST * LV * 2;
+    // R^T (hi, lo) is written at a chunk end and read at the next chunk's first stage, before the
+    // second stage stores V rows 32.. of the chunk: where the separate layout does not fit in LDS it
+    // lives in those rows
+    static constexpr bool R_IN_V =
+        V_END + 2 * R_BYTES + 2 * Z_BYTES > 160 * 1024 && (size_t)(C - kST) * LV * 2 >= 2 * R_BYTES;
+    static constexpr size_t OFF_RH = R_IN_V ? OFF_V + (size_t)kST * LV * 2 : V_END;
+    static constexpr size_t OFF_RL = OFF_RH + R_BYTES;
+    static constexpr size_t OFF_ZH = R_IN_V ? V_END : OFF_RL + R_BYTES;  // V (.) zeta, bf16 high part, this stage
     static constexpr size_t OFF_ZL = OFF_ZH + (size_t)kST * LV * 2;  // ... low part
     static constexpr size_t BYTES = OFF_ZL + (size_t)kST * LV * 2;
 };
 
-template <int DK, int C>
+template <int DK, int C, bool PLO>
 struct StageRegs {
     bf16x8 q[MainGeom<DK, C>::QN];
     bf16x8 k[MainGeom<DK, C>::QN];
     bf16x8 p[MainGeom<DK, C>::PN > 0 ? MainGeom<DK, C>::PN : 1];
+    bf16x8 pl[PLO && MainGeom<DK, C>::PN > 0 ? MainGeom<DK, C>::PN : 1];
     bf16x8 v;
 };
 
@@ -174,15 +193,17 @@ __device__ __forceinline__ void team_slice(int teams, int NS, int& team, int& sl
 // One (b, h, d_v slice) per workgroup. Wave w owns R rows [w*DK/4, (w+1)*DK/4) (state update) and,
 // in every 32-token stage, the 16 x 16 output tile (rows 16*(w>>1), columns 16*(w&1)).
 // VSH: value rows through VShift (residual linear attention); the plain instantiation has none of it.
-template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH>
+// PLO: P arrives as bf16 hi + lo (P V runs on both parts).
+template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH, bool PLO>
 __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, HeadConsts hc) {
-    using G = MainGeom<DK, C>;
+    using G = MainGeom<DK, C, PLO>;
     constexpr int RTR = DK / 64;  // 16-row R tiles per wave
     constexpr int SPC = C / kST;  // stages per full chunk
     extern __shared__ __attribute__((aligned(16))) char smem[];
     bf16* Qs = reinterpret_cast<bf16*>(smem + G::OFF_Q);
     bf16* Ks = reinterpret_cast<bf16*>(smem + G::OFF_K);
     bf16* Ps = reinterpret_cast<bf16*>(smem + G::OFF_P);
+    bf16* Pls = reinterpret_cast<bf16*>(smem + G::OFF_PL);
     bf16* Vs = reinterpret_cast<bf16*>(smem + G::OFF_V);
     bf16* Rhi = reinterpret_cast<bf16*>(smem + G::OFF_RH);
     bf16* Rlo = reinterpret_cast<bf16*>(smem + G::OFF_RL);
@@ -217,9 +238,11 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     const unsigned p_bytes = WANT_OUT ? (unsigned)((size_t)nchunks * C * C * 2) : 0u;
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(WANT_OUT ? p.P + (size_t)bh * nchunks * C * C : p.q), 0, p_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rpl = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(WANT_OUT && PLO ? p.Plo + (size_t)bh * nchunks * C * C : p.q), 0, PLO ? p_bytes : 0u, 0x00020000);
 
     // ---- stage loads: global -> registers (unconditional instructions), registers -> LDS
-    auto load_stage = [&](StageRegs<DK, C>& r, int g) __attribute__((always_inline)) {
+    auto load_stage = [&](StageRegs<DK, C, PLO>& r, int g) __attribute__((always_inline)) {
         const int gg = g < total ? g : total - 1;  // past the end: reload the last stage (unused)
         const int ci = gg / SPC, s = gg % SPC;
         const int tok0 = ci * C + kST * s;
@@ -252,10 +275,11 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
                 const int row = j / (C / 8), sg = j % (C / 8);
                 const unsigned off = sg < per_row ? (base + (unsigned)(row * C + 8 * sg)) * 2u : p_bytes;
                 r.p[u] = buf_load16(rp, off);
+                if constexpr (PLO) r.pl[u] = buf_load16(rpl, off);
             }
         }
     };
-    auto store_stage = [&](const StageRegs<DK, C>& r, int s, int L) __attribute__((always_inline)) {
+    auto store_stage = [&](const StageRegs<DK, C, PLO>& r, int s, int L) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < G::QN; ++u) {
             const int j = threadIdx.x + kThreads * u;
@@ -288,7 +312,10 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
             for (int u = 0; u < G::PN; ++u) {
                 const int j = threadIdx.x + kThreads * u;
                 const int row = j / (C / 8), sg = j % (C / 8);
-                if (sg < per_row) *reinterpret_cast<bf16x8*>(Ps + row * G::LP + 8 * sg) = r.p[u];
+                if (sg < per_row) {
+                    *reinterpret_cast<bf16x8*>(Ps + row * G::LP + 8 * sg) = r.p[u];
+                    if constexpr (PLO) *reinterpret_cast<bf16x8*>(Pls + row * G::LP + 8 * sg) = r.pl[u];
+                }
             }
         }
     };
@@ -343,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     };
 
     // ---- one pipeline stage
-    auto stage = [&](StageRegs<DK, C>& r, int g) __attribute__((always_inline)) {
+    auto stage = [&](StageRegs<DK, C, PLO>& r, int g) __attribute__((always_inline)) {
         const int ci = g / SPC, s = g % SPC;
         const int L = min(C, N - ci * C);
         const bool chunk_end = (s == SPC - 1) || (g == total - 1);
@@ -379,6 +406,7 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
                 const bf16x8 a = frag_rowmajor(Ps, G::LP, 16 * rt_o, 32 * ks, lane);
                 const bf16x8 b = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
                 pv = mfma16(a, b, pv);
+                if constexpr (PLO) pv = mfma16(frag_rowmajor(Pls, G::LP, 16 * rt_o, 32 * ks, lane), b, pv);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = qr[i] * decay_pow(l2g, (float)(kST * s + 16 * rt_o + 4 * g4 + i + 1)) + pv[i];
@@ -409,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     };
 
     write_R();
-    StageRegs<DK, C> r0, r1;
+    StageRegs<DK, C, PLO> r0, r1;
     load_stage(r0, 0);
     load_stage(r1, 1);
     for (int g = 0; g < total; g += 2) {
@@ -448,8 +476,9 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 //                g^(j+1) Q R + P V, with R^T (hi + lo) held in registers for the chunk, and its store.
 // Q, K, P and R^T tiles are swizzled (SwzTile). At each chunk end the state waves write R^T as bf16
 // hi + lo into the Q/K region of the buffer that the finished stage used; the output waves read
-// their fragments from it at the next stage, before the loaders refill that buffer.
-template <int DK, int C>
+// their fragments from it at the next stage, before the loaders refill that buffer. PLO: P comes
+// as bf16 hi + lo, both parts loaded, P V on both.
+template <int DK, int C, bool PLO = false>
 struct WsGeom {
     static constexpr int QRB = DK * 2;            // bytes per Q / K tile row
     static constexpr int PRB = C * 2;             // bytes per P tile row
@@ -457,7 +486,8 @@ struct WsGeom {
     static constexpr size_t Q_BYTES = (size_t)kST * QRB;
     static constexpr size_t P_BYTES = (size_t)kST * PRB;
     static constexpr size_t Z_BYTES = (size_t)kST * LV * 2;
-    static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_ZH = OFF_P + P_BYTES, OFF_ZL = OFF_ZH + Z_BYTES;
+    static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_PL = OFF_P + P_BYTES;
+    static constexpr size_t OFF_ZH = OFF_PL + (PLO ? P_BYTES : 0), OFF_ZL = OFF_ZH + Z_BYTES;
     static constexpr size_t BUF = OFF_ZL + Z_BYTES;  // one stage buffer
     // V rows of the chunk, double-buffered by chunk parity: during a chunk's last stage the state
     // waves already store the next chunk's first V rows while the output waves still read these
@@ -472,7 +502,7 @@ struct WsGeom {
     static_assert((size_t)kW * QRB == Q_BYTES, "R^T hi / lo fill the Q / K regions");
     static_assert(Q_BYTES % 4096 == 0 && P_BYTES % 4096 == 0, "tiles are split over four loader waves in kilobytes");
     static constexpr int Q_KB = (int)(Q_BYTES / 1024), P_KB = (int)(P_BYTES / 1024);
-    static constexpr int NDMA = (2 * Q_KB + P_KB) / 4;  // buffer-to-LDS loads per stage and loader wave
+    static constexpr int NDMA = (2 * Q_KB + (PLO ? 2 : 1) * P_KB) / 4;  // buffer-to-LDS loads per stage and loader wave
     static_assert(NDMA + 2 <= 63, "the loads of one stage must fit the vmcnt counter");
 };
 
@@ -491,9 +521,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int C, typename TOUT, bool VSH>
+template <int DK, int C, typename TOUT, bool VSH, bool PLO>
 __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
-    using G = WsGeom<DK, C>;
+    using G = WsGeom<DK, C, PLO>;
     constexpr int NB = G::NB;
     constexpr int RTR = DK / 64;  // 16-row R tiles per state wave
     constexpr int SPC = C / kST;
@@ -535,6 +565,8 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rp =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rpl = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((PLO ? p.Plo : p.P) + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
         // This wave's share (kilobytes j = lw mod 4) of the Q, K and P rows of stage g, into its
         // buffer; lane l fills bytes [16l, 16l+16) of each kilobyte. P: only the 32-key steps up to
         // this stage; the rest read as zero, no traffic.
@@ -560,6 +592,8 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 const int c = ((byte % G::PRB) >> 4) ^ (r & SwzTile<G::PRB>::M);
                 const unsigned off = c < per_row ? (base + (unsigned)(r * C + 8 * c)) * 2u : p_bytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void*)(bq + G::OFF_P + 1024 * j), 16, off, 0, 0, 0);
+                if constexpr (PLO)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rpl, (__attribute__((address_space(3))) void*)(bq + G::OFF_PL + 1024 * j), 16, off, 0, 0, 0);
             }
         };
         // L2 warm-up of stage g: one 16-byte load per 128-byte line, this slice's share (lines
@@ -778,6 +812,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             }
             const char* Qs = buf(g);
             const char* Ps = buf(g) + G::OFF_P;
+            const char* Pls = buf(g) + G::OFF_PL;
             const bf16* Vs = Vc(g / SPC);
             // the Q fragments and the first two P V steps' fragments first (their read latencies
             // overlap), then the QR chains; the other P and V reads go out while those run
@@ -802,10 +837,16 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             // keys (its rows are loaded as zero there), and the V rows there are finite (zeroed at
             // the start, or rows of an earlier chunk), so the unrolled sum needs no branch
             f32x4 pa[2] = {mfma16(pf[0], vf[0], f32x4{0.f, 0.f, 0.f, 0.f}), mfma16(pf[1], vf[1], f32x4{0.f, 0.f, 0.f, 0.f})};
+            if constexpr (PLO) {
 #pragma unroll
-            for (int ks = 2; ks < SPC; ++ks)
-                pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane),
-                                    pa[ks & 1]);
+                for (int ks = 0; ks < 2; ++ks) pa[ks] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vf[ks], pa[ks]);
+            }
+#pragma unroll
+            for (int ks = 2; ks < SPC; ++ks) {
+                const bf16x8 vk = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
+                pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
+                if constexpr (PLO) pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
+            }
             const f32x4 qr = (qa[0] + qa[2]) + (qa[1] + qa[3]);
             const f32x4 pv = pa[0] + pa[1];
             // g^(j+1) for row j = 32 s + r of the chunk: g^(32 s) (one per stage) times g^(r+1)
@@ -888,7 +929,8 @@ __global__ __launch_bounds__(256) void gn_rows_kernel(long rows, int H, int N, i
 
 // ---------------------------------------------------------------------------------------------
 // Workspace layout (bytes, each part 256-aligned):
-//   P     B*H*nchunks*C*C bf16      scores of every chunk (only when the output is wanted)
+//   P     B*H*nchunks*C*C bf16      scores of every chunk (only when the output is wanted), followed
+//                                   by their low parts in the same layout when the kernel uses them
 //   pre   B*H*N*DV fp32             pre-norm output rows (only with GroupNorm)
 struct WsLayout {
     size_t p_off, p_bytes, pre_off, pre_bytes, total;
@@ -896,31 +938,74 @@ struct WsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(int B, int H, int N, int DV, int C, int gn, int want_out) {
+WsLayout ws_layout(int B, int H, int N, int DV, int C, int gn, int want_out, bool plo) {
     WsLayout l{};
     const size_t nchunks = (size_t)(N + C - 1) / C;
     l.p_off = 0;
-    l.p_bytes = want_out ? align256((size_t)B * H * nchunks * C * C * sizeof(bf16)) : 0;
+    l.p_bytes = want_out ? align256((plo ? 2 : 1) * (size_t)B * H * nchunks * C * C * sizeof(bf16)) : 0;
     l.pre_off = l.p_off + l.p_bytes;
     l.pre_bytes = gn && want_out ? align256((size_t)B * H * N * DV * sizeof(float)) : 0;
     l.total = l.pre_off + l.pre_bytes;
     return l;
 }
 
-// Chunks up to 256 with an output use the warp-specialised kernel; 512-token chunks (whose stage
-// buffers do not fit twice in LDS) and state-only prefills use the single-group kernel.
-template <int C, bool WANT_OUT>
-constexpr bool use_ws() { return WANT_OUT && C <= 256; }
+// Workspace of the segmented kernels (chunk_seg.hip), when they serve the call:
+//   sin   B*H*DK*DV fp32   a copy of state_in when the call updates the state in place
+//   U     the segments' own final states
+//   pre   B*H*N*DV fp32    pre-norm output rows (only with GroupNorm)
+struct SegWsLayout {
+    size_t sin_off, u_off, pre_off, total;
+};
+
+SegWsLayout seg_ws_layout(int B, int H, int N, int DK, int DV, int C, int gn) {
+    SegWsLayout l{};
+    l.sin_off = 0;
+    l.u_off = align256((size_t)B * H * DK * DV * sizeof(float));
+    l.pre_off = l.u_off + align256(chunkwise_seg_state_bytes(B, H, N, DK, DV, C));
+    l.total = l.pre_off + (gn ? align256((size_t)B * H * N * DV * sizeof(float)) : 0);
+    return l;
+}
+
+// Whether a plain call (operands contiguous, in time order) at this shape runs on the segmented kernels
+bool seg_shape(int DK, int DV, int C, int want_out) {
+    LaunchArgs a{};
+    a.B = a.H = 1; a.DK = DK; a.DV = DV; a.chunk = C; a.in_bf16 = 1;
+    a.out = want_out ? reinterpret_cast<void*>(16) : nullptr;
+    return chunkwise_seg_supported(a);
+}
+
+// Chunks up to 256 with an output use the warp-specialised kernel, with P as bf16 hi + lo, where
+// its stage buffers fit in LDS; the other calls with an output use the single-group kernel, with P
+// as hi + lo where that fits (every supported shape), and state-only prefills use the single-group
+// kernel without P.
+constexpr size_t kLdsBytes = 160 * 1024;
+template <int DK, int C, bool WANT_OUT>
+constexpr bool use_ws() { return WANT_OUT && C <= 256 && WsGeom<DK, C, true>::BYTES <= kLdsBytes; }
+template <int DK, int C>
+constexpr bool p_lo() { return use_ws<DK, C, true>() || MainGeom<DK, C, true>::BYTES <= kLdsBytes; }
+
+template <int DK>
+bool p_lo_dk(int C) {
+    switch (C) {
+        case 64: return p_lo<DK, 64>();
+        case 128: return p_lo<DK, 128>();
+        case 256: return p_lo<DK, 256>();
+        default: return p_lo<DK, 512>();
+    }
+}
+// whether a call with an output at (DK, C) keeps the low part of P
+bool p_lo_used(int DK, int C) { return DK == 64 ? p_lo_dk<64>(C) : p_lo_dk<256>(C); }
 
 template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH>
 hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
-    constexpr bool ws = use_ws<C, WANT_OUT>();
+    constexpr bool ws = use_ws<DK, C, WANT_OUT>();
+    constexpr bool plo = WANT_OUT && p_lo<DK, C>();
     const void* kern;
-    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH>);
-    else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT, VSH>);
+    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true>);
+    else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT, VSH, plo>);
     size_t dyn;
-    if constexpr (ws) dyn = WsGeom<DK, C>::BYTES;
-    else dyn = MainGeom<DK, C>::BYTES;
+    if constexpr (ws) dyn = WsGeom<DK, C, true>::BYTES;
+    else dyn = MainGeom<DK, C, plo>::BYTES;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
     MainParams lp = mp;
@@ -935,11 +1020,48 @@ hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
     return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true>(a, mp) : launch_main_v<DK, C, TOUT, WANT_OUT, false>(a, mp);
 }
 
+// The segmented kernels, then the GroupNorm row pass when there is one.
+template <typename TOUT>
+hipError_t launch_seg(const LaunchArgs& a) {
+    const SegWsLayout l = seg_ws_layout(a.B, a.H, a.N, a.DK, a.DV, a.chunk, a.gn.enabled);
+    char* ws = reinterpret_cast<char*>(a.ws);
+    LaunchArgs b = a;
+    hipError_t e;
+    if (a.state_in && a.state_in == a.state_out) {
+        // the last segment writes state_out while workgroups of other segments may still be about to
+        // read state_in: they read a copy
+        float* cp = reinterpret_cast<float*>(ws + l.sin_off);
+        e = launch_copy_state((size_t)a.B * a.H * a.DK * a.DV, a.state_in, cp, a.stream);
+        if (e != hipSuccess) return e;
+        b.state_in = cp;
+    }
+    float* U = reinterpret_cast<float*>(ws + l.u_off);
+    if (!a.gn.enabled) return launch_chunkwise_seg(b, U, a.out, false);
+    float* pre = reinterpret_cast<float*>(ws + l.pre_off);
+    e = launch_chunkwise_seg(b, U, pre, true);
+    if (e != hipSuccess) return e;
+    const long rows = (long)a.B * a.H * a.N;
+    hipLaunchKernelGGL(gn_rows_kernel<TOUT>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.stream, rows, a.H, a.N, a.DV, pre,
+                       reinterpret_cast<TOUT*>(a.out), a.gn);
+    return hipGetLastError();
+}
+
+// The segmented kernels take a plain call when one workgroup per (head, 32-column slice of d_v)
+// would leave compute units idle: they spread the same work over segments of the sequence too.
+bool seg_preferred(const LaunchArgs& a) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return chunkwise_seg_supported(a) && (long)a.B * a.H * (a.DV / kW) < cus;
+}
+
 template <int DK, int C, typename TOUT>
 hipError_t launch_dk_c(const LaunchArgs& a) {
+    if (seg_preferred(a)) return launch_seg<TOUT>(a);
     const int nchunks = (a.N + C - 1) / C;
     const bool want_out = a.out != nullptr;
-    const WsLayout l = ws_layout(a.B, a.H, a.N, a.DV, C, a.gn.enabled, want_out);
+    const bool plo = want_out && p_lo<DK, C>();
+    const WsLayout l = ws_layout(a.B, a.H, a.N, a.DV, C, a.gn.enabled, want_out, plo);
     char* ws = reinterpret_cast<char*>(a.ws);
     MainParams mp{};
     mp.H = a.H; mp.N = a.N; mp.C = C; mp.NS = a.DV / kW; mp.nchunks = nchunks; mp.teams = a.B * a.H;
@@ -950,11 +1072,13 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;
     mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;
+    mp.Plo = plo ? mp.P + (size_t)a.B * a.H * nchunks * C * C : nullptr;
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
 
     hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C,
-                       nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), a.hc, mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH);
+                       nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), a.hc, mp.rev, mp.ldqk,
+                       mp.qcol_blk, mp.srcBH);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!a.gn.enabled) return launch_main<DK, C, TOUT, true>(a, mp);
@@ -989,8 +1113,12 @@ bool chunkwise_bf16_supported(int DK, int DV, int chunk) {
 }
 
 size_t chunkwise_bf16_workspace(int B, int H, int N, int DK, int DV, int chunk, int gn, int want_out) {
-    (void)DK;
-    return ws_layout(B, H, N, DV, chunk, gn && want_out, want_out).total;
+    // enough for either kernel family: callers that read operands in place (the backward, residual
+    // linear attention) run the warp-specialised kernels at shapes the segmented ones also serve
+    const size_t t = ws_layout(B, H, N, DV, chunk, gn && want_out, want_out, want_out && p_lo_used(DK, chunk)).total;
+    if (!seg_shape(DK, DV, chunk, want_out)) return t;
+    const size_t u = seg_ws_layout(B, H, N, DK, DV, chunk, gn && want_out).total;
+    return t > u ? t : u;
 }
 
 hipError_t launch_chunkwise_bf16(const LaunchArgs& a) {

@@ -243,6 +243,12 @@ size_t chunkwise_bf16_workspace(int B, int H, int N, int DK, int DV, int chunk, 
 size_t chunkwise_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16);
 size_t parallel_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16);
 bool chunkwise_bf16_supported(int DK, int DV, int chunk);
+// The segmented bf16 chunkwise kernels (chunk_seg.hip): plain operands, an output, d_k 64 or 256,
+// chunk 64 or 128, d_v a multiple of 64. U: the segment states in the workspace; out: the call's
+// output, or fp32 pre-norm rows when out_f32 (a GroupNorm pass follows).
+bool chunkwise_seg_supported(const LaunchArgs& a);
+size_t chunkwise_seg_state_bytes(int B, int H, int N, int DK, int DV, int chunk);
+hipError_t launch_chunkwise_seg(const LaunchArgs& a, float* U, void* out, bool out_f32);
 bool chunkwise_f32_supported(int DK, int DV, int chunk);
 bool parallel_bf16_supported(int DK, int DV);
 bool parallel_f32_supported(int DK, int DV);
@@ -264,7 +270,8 @@ hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, con
 struct RlaPrep {
     long rows;  // B * H * N
     int N, dk, dv, P, prev_len, fmap, bf16;
-    int vsplit;  // shifted value rows written per head ([B*H][vsplit][dv] at vo)
+    int feat_f32;  // bf16 inputs: features and value rows written in fp32 (else in the input dtype)
+    int vsplit;    // shifted value rows written per head ([B*H][vsplit][dv] at vo)
     const void *q, *k, *v, *kp, *vp;
     void *qo, *ko, *vo;
 };

@@ -187,10 +187,10 @@ __device__ __forceinline__ void load_row(const RowAt<T>& r, const T* q, int dk, 
 
 // The rest of one row: phi(q[n]) (unless phi is the identity) and phi of the key row that lands at n
 // (zero where none does).
-template <typename T>
+template <typename T, typename TO>
 __device__ __forceinline__ void finish_row(const RowAt<T>& r, const typename Raw4<T>::type& xq,
                                            const typename Raw4<T>::type& xk, int dk, int fmap, int lane,
-                                           const double* tab, T* qo, T* ko) {
+                                           const double* tab, TO* qo, TO* ko) {
     const bool live = 4 * lane < dk;
     float fq[4], fk[4];
 #pragma unroll
@@ -221,10 +221,12 @@ __device__ __forceinline__ RowAt<T> advance(const RowAt<T>& r, int BH, int N, in
     return more ? locate<T>(bh, n, N, dk, dv, P, prev_len, k, v, kp, vp) : r;
 }
 
-template <typename T>
+// T: the input dtype; TO: the dtype of the features and value rows written (T, or fp32 for bf16
+// inputs whose features the fp32 kernels consume).
+template <typename T, typename TO>
 __global__ __launch_bounds__(256) void rla_prepare_kernel(int BH, int N, int dk, int dv, int P, int prev_len, int fmap,
                                                           int vsplit, int step_bh, int step_n, const T* q, const T* k,
-                                                          const T* v, const T* kp, const T* vp, T* qo, T* ko, T* vo) {
+                                                          const T* v, const T* kp, const T* vp, TO* qo, TO* ko, TO* vo) {
     __shared__ double tab[32];
     if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Frac[threadIdx.x];
     __syncthreads();
@@ -233,14 +235,25 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(int BH, int N, int dk,
     const int wave = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = (int)gridDim.x * 4;
     // The shifted value rows below vsplit, [B*H][vsplit][d_v] (the chunk kernels read the later rows
-    // from v itself): one wave per row, d_v * size / 16 whole 16-byte chunks.
-    const int n16 = dv * (int)sizeof(T) / 16;
+    // from v itself): one wave per row, d_v * size / 16 whole 16-byte chunks (bf16 to fp32: 4 values
+    // per chunk written).
+    const int n16 = dv * (int)sizeof(TO) / 16;
     for (long vr = wave; vr < (long)BH * vsplit; vr += waves) {
         const int bh = (int)(vr / vsplit), n = (int)(vr % vsplit);
         const RowAt<T> r = locate<T>(bh, n, N, dk, dv, P, prev_len, k, v, kp, vp);
         u32x4* dst = reinterpret_cast<u32x4*>(vo + (size_t)vr * dv);
-        for (int c = lane; c < n16; c += 64)
-            dst[c] = r.vs ? reinterpret_cast<const u32x4*>(r.vs)[c] : u32x4{0u, 0u, 0u, 0u};
+        for (int c = lane; c < n16; c += 64) {
+            if constexpr (sizeof(T) == sizeof(TO)) {
+                dst[c] = r.vs ? reinterpret_cast<const u32x4*>(r.vs)[c] : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                if (r.vs) {
+                    const bf16x4 b = reinterpret_cast<const bf16x4*>(r.vs)[c];
+                    x = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+                }
+                reinterpret_cast<f32x4*>(dst)[c] = x;
+            }
+        }
     }
     // phi(q) and the shifted phi(k). A wave takes every waves-th row, (step_bh, step_n) in (b*h, n)
     // form: one division per wave, then an add and a carry per row. The next row's loads are issued
@@ -281,14 +294,20 @@ hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream) {
     const long grid = std::min<long>((rows + 3) / 4, 256 * 16);
     const long step = 4 * grid;
     const int BH = (int)(rows / r.N), step_bh = (int)(step / r.N), step_n = (int)(step % r.N);
-    if (r.bf16)
-        hipLaunchKernelGGL(rla_prepare_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
+    if (r.bf16 && r.feat_f32)
+        hipLaunchKernelGGL((rla_prepare_kernel<bf16, float>), dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
+                           r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
+                           static_cast<const bf16*>(r.q), static_cast<const bf16*>(r.k), static_cast<const bf16*>(r.v),
+                           static_cast<const bf16*>(r.kp), static_cast<const bf16*>(r.vp), static_cast<float*>(r.qo),
+                           static_cast<float*>(r.ko), static_cast<float*>(r.vo));
+    else if (r.bf16)
+        hipLaunchKernelGGL((rla_prepare_kernel<bf16, bf16>), dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
                            r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const bf16*>(r.q), static_cast<const bf16*>(r.k), static_cast<const bf16*>(r.v),
                            static_cast<const bf16*>(r.kp), static_cast<const bf16*>(r.vp), static_cast<bf16*>(r.qo),
                            static_cast<bf16*>(r.ko), static_cast<bf16*>(r.vo));
     else
-        hipLaunchKernelGGL(rla_prepare_kernel<float>, dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
+        hipLaunchKernelGGL((rla_prepare_kernel<float, float>), dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
                            r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const float*>(r.q), static_cast<const float*>(r.k), static_cast<const float*>(r.v),
                            static_cast<const float*>(r.kp), static_cast<const float*>(r.vp), static_cast<float*>(r.qo),

@@ -287,9 +287,11 @@ def test_rla_validation(lib):
     assert need >= rows * (2 * s.d_k + s.d_v) * 2
     assert rla(lib, wsb=need - 1) == R.RET_ERR_WORKSPACE
     assert rla(lib, ws=None, wsb=0) == R.RET_ERR_WORKSPACE
-    # a decode step needs only the operands
+    # a decode step needs only the operands: 2 rows x 64 features or values each, in fp32 for bf16
+    # inputs with the softmax map (the larger need), so three 512-byte planes
     s1 = shape(N=1)
-    assert lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(s1), 0, 0) == 3 * 256
+    assert lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(s1), 0, 0) == 3 * 512
+    assert lib.retention_workspace_bytes(R.RET_FN_RLA, ctypes.byref(shape(N=1, i=R.RET_F32)), 0, 0) == 3 * 512
 
 
 def test_workspace_query_unsupported_shapes(lib):
