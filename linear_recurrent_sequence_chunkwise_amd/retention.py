@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libretention.so")
+# the library (RETENTION_LIB names another build of it, e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("RETENTION_LIB", os.path.join(_PKG, "libretention.so"))
 
 RET_OK, RET_ERR_INVALID_ARG, RET_ERR_UNSUPPORTED, RET_ERR_WORKSPACE, RET_ERR_DEVICE = range(5)
 RET_F32, RET_BF16 = 0, 1

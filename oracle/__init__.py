@@ -43,9 +43,11 @@ def load(path: str = LIB):
 
 
 def _get():
+    """The process's oracle library: liboracle.so, or the library that RETENTION_ORACLE_LIB names
+    (the sanitized build, under the sanitizer test)."""
     global _lib
     if _lib is None:
-        _lib = load()
+        _lib = load(os.environ.get("RETENTION_ORACLE_LIB", LIB))
     return _lib
 
 
