@@ -263,9 +263,13 @@ ret_status retention_chunkwise_fwd_noalloc(const ret_shape* shape, int32_t chunk
  * Returns 0 when none is needed, and (size_t)-1 when the arguments are invalid or no kernel
  * supports the shape, chunk and flags (the call itself would return RET_ERR_UNSUPPORTED; residual
  * linear attention takes no rotation).
- * Chunkwise with bf16 inputs: the bf16 intra-chunk scores (B*H*ceil(N/chunk)*chunk^2*2 bytes)
- * when an output is wanted, plus fp32 pre-norm rows (B*H*N*d_v*4 bytes) with GroupNorm. Other
- * calls: fp32 staging rows when GroupNorm or a bf16 output needs them. A rotation adds the
+ * Chunkwise with bf16 inputs: the larger of what a call with an output and a state-only call
+ * need. With an output: the intra-chunk scores as bf16 high and low parts
+ * (2*B*H*ceil(N/chunk)*chunk^2*2 bytes), plus fp32 pre-norm rows (B*H*N*d_v*4 bytes) with
+ * GroupNorm; or, where one workgroup per (b, h, 32 columns of d_v) would leave compute units idle,
+ * the fp32 states of the sequence segments the call is split into (up to B*H*S*d_k*d_v*4 bytes for
+ * S segments) plus the pre-norm rows. State-only: the segments' states when there are several.
+ * Other calls: fp32 staging rows when GroupNorm or a bf16 output needs them. A rotation adds the
  * rotated q and k (2*B*H*N*d_k elements of the input dtype, each copy 256-byte aligned) in front.
  * The caller owns it; its contents are scratch and need no initialisation. */
 size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chunk, int32_t flags);

@@ -189,9 +189,14 @@ ret::LaunchArgs base_args(const ret_shape* s, int chunk, const ret::HeadConsts& 
     return a;
 }
 
+// The chunkwise call's workspace: with want_out, enough for a call with an output or without one
+// (a state-only bf16 call on the segment-state kernel can need more than the call with an output).
 size_t chunkwise_ws(const ret_shape* s, int chunk, int gn, int want_out) {
-    if (s->in_dtype == RET_BF16)
-        return ret::chunkwise_bf16_workspace(s->batch, s->heads, s->seq_len, s->d_k, s->d_v, chunk, gn, want_out);
+    if (s->in_dtype == RET_BF16) {
+        const size_t st = ret::chunkwise_bf16_workspace(s->batch, s->heads, s->seq_len, s->d_k, s->d_v, chunk, gn, 0);
+        if (!want_out) return st;
+        return std::max(st, ret::chunkwise_bf16_workspace(s->batch, s->heads, s->seq_len, s->d_k, s->d_v, chunk, gn, 1));
+    }
     return want_out ? ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16) : 0;
 }
 

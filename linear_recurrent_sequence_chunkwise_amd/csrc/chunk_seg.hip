@@ -34,6 +34,8 @@
 // in LDS rings for the scores and P V.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace ret {
@@ -205,8 +207,10 @@ struct SegParams {
     const bf16* v;
     const float* state_in;
     float* state_out;
-    float* U;    // [teams][segs - 1][DK][DV] fp32: the segments' own final states
+    float* U;    // [teams][segs - 1][DK][DV] fp32: the segments' own final states ([teams][segs][DK][DV] for
+                 // a state-only call with more than one segment)
     void* out;   // [teams][N][DV] in TOUT (pre-norm fp32 rows when GroupNorm follows)
+    int state_only;  // seg_states_kernel covers every segment, the last one ending at N
 };
 
 // V (.) zeta of one B fragment (8 consecutive tokens of one column), split into bf16 hi + lo
@@ -246,6 +250,9 @@ __device__ __forceinline__ void state_update(f32x4 (&accR)[DTH_][CT_], const cha
 // g^(b - t) k_t^T v_t, b its last token. Grid: teams * (segs - 1) * NS workgroups of 8 waves, laid
 // out as in the main kernel (wave (c, r): column group c, d_k half r). Three K and V tile buffers:
 // each step's tiles are stored two steps ahead of use.
+// A state-only call (state_only) takes every segment, the last one ending at token N - 1 (its
+// last step reads rows past N as zero); with one segment the workgroup writes the final state
+// g^N state_in + U itself, else the segments' U for seg_final_kernel.
 template <int DK, int C, int W>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_per_eu(2, 2))) void seg_states_kernel(SegParams p,
                                                                                                                    HeadConsts hc) {
@@ -254,14 +261,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_pe
     // w is the same in every lane of a wave: readfirstlane keeps it in scalar registers
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g4 = lane >> 4, c16 = lane & 15;
     const int c = w & 3, r = w >> 2;
-    const int S1 = p.segs - 1;
+    const int S1 = p.state_only ? p.segs : p.segs - 1;
     const int i = blockIdx.x;
     const int team = i / (S1 * p.NS), seg = (i / p.NS) % S1, slice = i % p.NS;
     const int N = p.N, DV = p.DV, h = team % p.H;
     const float l2g = hc.log2g[h];
     const int col0 = slice * W, cc0 = c * 16 * G::CT;
-    const int t0 = seg_chunk(seg, p.nchunks, p.segs) * C, t1 = seg_chunk(seg + 1, p.nchunks, p.segs) * C;  // [t0, t1), t1 <= N
-    const int steps = (t1 - t0) / kST;
+    const int t0 = seg_chunk(seg, p.nchunks, p.segs) * C, t1 = min(seg_chunk(seg + 1, p.nchunks, p.segs) * C, N);  // [t0, t1)
+    const int steps = (t1 - t0 + kST - 1) / kST;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)team * N * DK), 0,
                                                                         (unsigned)((size_t)N * DK * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)team * N * DV), 0,
@@ -297,6 +304,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_pe
         for (int e = 0; e < 8; ++e) z[e] = __builtin_amdgcn_exp2f(zs + zl[e]);
         state_update<DK, C, W>(acc, Kb(g % 3), Vb(g % 3), z, r, cc0, lane);
     }
+    if (p.state_only && p.segs == 1) {
+        // the final state: g^N state_in + U (each lane reads the state_in elements it writes, so
+        // state_out may be state_in)
+        const float gN = decay_pow(l2g, (float)N);
+        const size_t base = (size_t)team * DK * DV;
+#pragma unroll
+        for (int dt = 0; dt < G::DTH; ++dt)
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const size_t o = base + (size_t)(r * G::DKH + 16 * dt + 4 * g4 + e) * DV + col0 + cc0 + 16 * ct + c16;
+                    p.state_out[o] = (p.state_in ? gN * p.state_in[o] : 0.f) + acc[dt][ct][e];
+                }
+        return;
+    }
     float* U = p.U + ((size_t)team * S1 + seg) * DK * DV;
 #pragma unroll
     for (int dt = 0; dt < G::DTH; ++dt)
@@ -305,6 +328,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_pe
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 U[(size_t)(r * G::DKH + 16 * dt + 4 * g4 + e) * DV + col0 + cc0 + 16 * ct + c16] = acc[dt][ct][e];
+}
+
+// The final state of a state-only call over several segments: g^N state_in + sum over segments s
+// of g^(N - 1 - b_s) U_s, b_s the segment's last token. Grid-stride over groups of four elements
+// (DK * DV a multiple of 4); each thread reads the state_in elements it writes.
+__global__ __launch_bounds__(256) void seg_final_kernel(SegParams p, HeadConsts hc, int DK, int C) {
+    const size_t per = (size_t)DK * p.DV / 4, n4 = (size_t)p.teams * per;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        const int team = (int)(i / per);
+        const float l2g = hc.log2g[team % p.H];
+        f32x4 acc = p.state_in ? reinterpret_cast<const f32x4*>(p.state_in)[i] * decay_pow(l2g, (float)p.N) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < p.segs; ++s) {
+            const int b = min(seg_chunk(s + 1, p.nchunks, p.segs) * C, p.N) - 1;
+            acc += reinterpret_cast<const f32x4*>(p.U + ((size_t)team * p.segs + s) * DK * p.DV)[i % per] *
+                   decay_pow(l2g, (float)(p.N - 1 - b));
+        }
+        reinterpret_cast<f32x4*>(p.state_out)[i] = acc;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -618,6 +659,33 @@ hipError_t seg_launch_t(const LaunchArgs& a, float* U, void* out) {
     return hipLaunchKernel(kern, dim3(p.teams * p.segs * p.NS), dim3(kNT), args, G::BYTES, a.stream);
 }
 
+// A state-only call: every segment's U in one launch (128-token chunk geometry: the chunk length
+// only sets where segments may split), then their decayed sum when there are several.
+template <int DK, int W>
+hipError_t seg_state_launch_t(const LaunchArgs& a, float* U) {
+    constexpr int C = 128;
+    using G = SegGeom<DK, C, W>;
+    SegParams p{};
+    p.H = a.H; p.N = a.N; p.C = C; p.DV = a.DV; p.NS = a.DV / W; p.teams = a.B * a.H;
+    p.nchunks = (a.N + C - 1) / C;
+    p.segs = seg_count(p.teams, p.NS, p.nchunks);
+    p.k = (const bf16*)a.k; p.v = (const bf16*)a.v;
+    p.state_in = a.state_in; p.state_out = a.state_out; p.U = U;
+    p.state_only = 1;
+    HeadConsts hc = a.hc;
+    const void* kern = reinterpret_cast<const void*>(seg_states_kernel<DK, C, W>);
+    const size_t dyn = 3 * (G::Q_BYTES + G::V_BYTES);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    void* args[] = {&p, &hc};
+    e = hipLaunchKernel(kern, dim3(p.teams * p.segs * p.NS), dim3(kNT), args, dyn, a.stream);
+    if (e != hipSuccess || p.segs == 1) return e;
+    const size_t n4 = (size_t)p.teams * DK * p.DV / 4;
+    const unsigned grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(seg_final_kernel, dim3(grid), dim3(256), 0, a.stream, p, hc, DK, C);
+    return hipGetLastError();
+}
+
 template <int DK, int C, typename TOUT>
 hipError_t seg_launch_c(const LaunchArgs& a, float* U, void* out) {
     return seg_width(a.DV) == 128 ? seg_launch_t<DK, C, 128, TOUT>(a, U, out) : seg_launch_t<DK, C, 64, TOUT>(a, U, out);
@@ -635,6 +703,26 @@ bool chunkwise_seg_supported(const LaunchArgs& a) {
                        (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.vs.split == 0;
     return plain && a.in_bf16 && a.out != nullptr && (a.DK == 64 || a.DK == 256) && (a.chunk == 64 || a.chunk == 128) &&
            seg_width(a.DV) != 0;
+}
+
+// A state-only call (no output) with plain operands that the segment-state kernel serves.
+bool chunkwise_seg_state_supported(const LaunchArgs& a) {
+    const bool plain = a.addr.rev == 0 && (a.addr.ldqk == 0 || a.addr.ldqk == a.DK) && a.addr.qcol_blk == 0 &&
+                       (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.vs.split == 0;
+    return plain && a.in_bf16 && a.out == nullptr && a.state_out != nullptr && (a.DK == 64 || a.DK == 256) && seg_width(a.DV) != 0;
+}
+
+// Bytes of the segment states of a state-only call (none with a single segment).
+size_t chunkwise_seg_state_only_bytes(int B, int H, int N, int DK, int DV) {
+    const int W = seg_width(DV);
+    if (!W) return 0;
+    const int segs = seg_count(B * H, DV / W, (N + 127) / 128);
+    return segs > 1 ? (size_t)B * H * segs * DK * DV * sizeof(float) : 0;
+}
+
+hipError_t launch_chunkwise_seg_state(const LaunchArgs& a, float* U) {
+    if (a.DK == 64) return seg_width(a.DV) == 128 ? seg_state_launch_t<64, 128>(a, U) : seg_state_launch_t<64, 64>(a, U);
+    return seg_width(a.DV) == 128 ? seg_state_launch_t<256, 128>(a, U) : seg_state_launch_t<256, 64>(a, U);
 }
 
 // Bytes of the segment states U (the call's pre-norm rows, if any, are laid out by the caller).

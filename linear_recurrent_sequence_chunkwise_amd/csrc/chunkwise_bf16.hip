@@ -24,6 +24,8 @@
 //                         chunk kernel writes to the workspace.
 // The d_v slices of one head sit on one XCD to share its L2. Plain calls whose (b, h, slice)
 // workgroups would leave compute units idle run on the segmented kernels of chunk_seg.hip instead.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace ret {
@@ -1058,6 +1060,7 @@ bool seg_preferred(const LaunchArgs& a) {
 template <int DK, int C, typename TOUT>
 hipError_t launch_dk_c(const LaunchArgs& a) {
     if (seg_preferred(a)) return launch_seg<TOUT>(a);
+    if (chunkwise_seg_state_supported(a)) return launch_chunkwise_seg_state(a, reinterpret_cast<float*>(a.ws));
     const int nchunks = (a.N + C - 1) / C;
     const bool want_out = a.out != nullptr;
     const bool plo = want_out && p_lo<DK, C>();
@@ -1116,6 +1119,14 @@ size_t chunkwise_bf16_workspace(int B, int H, int N, int DK, int DV, int chunk, 
     // enough for either kernel family: callers that read operands in place (the backward, residual
     // linear attention) run the warp-specialised kernels at shapes the segmented ones also serve
     const size_t t = ws_layout(B, H, N, DV, chunk, gn && want_out, want_out, want_out && p_lo_used(DK, chunk)).total;
+    if (!want_out) {
+        // state-only calls with plain operands run on the segment-state kernel (callers that read
+        // operands in place run the single-group kernel, which needs no workspace)
+        LaunchArgs a{};
+        a.B = B; a.H = H; a.N = N; a.DK = DK; a.DV = DV; a.chunk = chunk; a.in_bf16 = 1;
+        a.state_out = reinterpret_cast<float*>(16);
+        return chunkwise_seg_state_supported(a) ? std::max(t, chunkwise_seg_state_only_bytes(B, H, N, DK, DV)) : t;
+    }
     if (!seg_shape(DK, DV, chunk, want_out)) return t;
     const size_t u = seg_ws_layout(B, H, N, DK, DV, chunk, gn && want_out).total;
     return t > u ? t : u;

@@ -249,6 +249,11 @@ bool chunkwise_bf16_supported(int DK, int DV, int chunk);
 bool chunkwise_seg_supported(const LaunchArgs& a);
 size_t chunkwise_seg_state_bytes(int B, int H, int N, int DK, int DV, int chunk);
 hipError_t launch_chunkwise_seg(const LaunchArgs& a, float* U, void* out, bool out_f32);
+// State-only calls (no output, state_out given) on the segment-state kernel: plain operands, bf16,
+// d_k 64 or 256, d_v a multiple of 64, any chunk length. U: the segment states in the workspace.
+bool chunkwise_seg_state_supported(const LaunchArgs& a);
+size_t chunkwise_seg_state_only_bytes(int B, int H, int N, int DK, int DV);
+hipError_t launch_chunkwise_seg_state(const LaunchArgs& a, float* U);
 bool chunkwise_f32_supported(int DK, int DV, int chunk);
 bool parallel_bf16_supported(int DK, int DV);
 bool parallel_f32_supported(int DK, int DV);

@@ -127,6 +127,9 @@ def test_bf16_ragged_state_in(orc, dk, dv, N, C):
     # state-only prefill (out = NULL) gives the same state
     _, s_only = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, want_out=False)
     report(f"bf16 dk={dk} N={N} C={C} state-only", rel_err(s_only, ref_s), TOL["bf16"])
+    s_ip = s0d.clone()
+    R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s_ip, state_out=s_ip, want_out=False)
+    report(f"bf16 dk={dk} N={N} C={C} state-only in place", rel_err(s_ip, ref_s), TOL["bf16"])
     # in-place state: state_out is state_in
     s_inplace = s0d.clone()
     R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s_inplace, state_out=s_inplace)
