@@ -18,8 +18,9 @@
 //                                                         hi + lo)
 //                           R   += K^T (V (.) zeta)       (V (.) zeta as bf16 hi + lo; R fp32 in
 //                                                         accumulators, scaled by g^L at chunk start)
-//   chunk_main_kernel     the same per stage with every wave doing both parts (d_k 256 at chunks of
-//                         256 and 512, and state-only prefills, which have no output part).
+//   chunk_main_kernel     the same per stage with every wave doing both parts (512-token chunks,
+//                         and state-only calls that read their operands in place, which have no
+//                         output part).
 //   gn_rows_kernel        the optional per-head GroupNorm over d_v, on fp32 pre-norm rows that the
 //                         chunk kernel writes to the workspace.
 // The d_v slices of one head sit on one XCD to share its L2. Plain calls whose (b, h, slice)
@@ -491,14 +492,17 @@ struct WsGeom {
     static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_PL = OFF_P + P_BYTES;
     static constexpr size_t OFF_ZH = OFF_PL + (PLO ? P_BYTES : 0), OFF_ZL = OFF_ZH + Z_BYTES;
     static constexpr size_t BUF = OFF_ZL + Z_BYTES;  // one stage buffer
-    // V rows of the chunk, double-buffered by chunk parity: during a chunk's last stage the state
-    // waves already store the next chunk's first V rows while the output waves still read these
-    static constexpr size_t V_BYTES = (size_t)C * LV * 2;
+    // V rows in a ring of C / 32 + 1 blocks of 32 rows: block s of chunk ci sits in slot
+    // (ci * C / 32 + s) mod (C / 32 + 1), so during a chunk's last stage the state waves store the
+    // next chunk's first rows into the one slot that the chunk's own blocks leave free
+    static constexpr int V_SLOTS = C / kST + 1;
+    static constexpr size_t V_BLK = (size_t)kST * LV * 2;
+    static constexpr size_t V_RING = V_SLOTS * V_BLK;
     static constexpr size_t SCRATCH = 1024;  // target of the L2 warm-up loads
     // three stage buffers when they fit in the 160 KiB of LDS, else two
-    static constexpr int NB = 3 * BUF + 2 * V_BYTES + SCRATCH <= 160 * 1024 ? 3 : 2;
+    static constexpr int NB = 3 * BUF + V_RING + SCRATCH <= 160 * 1024 ? 3 : 2;
     static constexpr size_t OFF_V = NB * BUF;
-    static constexpr size_t OFF_SCRATCH = OFF_V + 2 * V_BYTES;
+    static constexpr size_t OFF_SCRATCH = OFF_V + V_RING;
     static constexpr size_t BYTES = OFF_SCRATCH + SCRATCH;
     // R^T (kW rows of DK bf16, swizzled like Q) hi part in the Q region, lo part in the K region
     static_assert((size_t)kW * QRB == Q_BYTES, "R^T hi / lo fill the Q / K regions");
@@ -531,7 +535,12 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     constexpr int SPC = C / kST;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     auto buf = [&](int g) __attribute__((always_inline)) { return smem + (g % NB) * G::BUF; };  // buffer of stage g
-    auto Vc = [&](int ci) __attribute__((always_inline)) { return reinterpret_cast<bf16*>(smem + G::OFF_V + (ci & 1) * G::V_BYTES); };
+    // V ring slot of chunk ci's first block, and the block s slots after a first slot f
+    auto vfirst = [&](int ci) __attribute__((always_inline)) { return (ci * SPC) % G::V_SLOTS; };
+    auto Vblk = [&](int f, int s) __attribute__((always_inline)) {
+        const int i = f + s;
+        return reinterpret_cast<bf16*>(smem + G::OFF_V + (i >= G::V_SLOTS ? i - G::V_SLOTS : i) * G::V_BLK);
+    };
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
     const int wl = w & 3;  // wave index within the output or state group
@@ -680,7 +689,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             const int L = min(C, N - ci * C);
             if (st < kST * 4) {
                 const int row = st >> 2, sg = st & 3;
-                *reinterpret_cast<bf16x8*>(Vc(ci) + (kST * s + row) * G::LV + 8 * sg) = v;
+                *reinterpret_cast<bf16x8*>(Vblk(vfirst(ci), s) + row * G::LV + 8 * sg) = v;
                 const int t = kST * s + row;
                 const float z = t < L ? decay_pow(l2g, (float)(L - 1 - t)) : 0.f;
                 bf16x8 hi, lo;
@@ -794,10 +803,10 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
         float row_decay[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) row_decay[i] = decay_pow(l2g, (float)(16 * rt_o + 4 * g4 + i + 1));
-        // zero the V rows that the state waves do not write before the first stage: all of the
-        // second chunk buffer and the first buffer past stage 0
-        for (int i = threadIdx.x; i < (int)((2 * G::V_BYTES - kST * G::LV * 2) / 16); i += 256)
-            *reinterpret_cast<f32x4*>(smem + G::OFF_V + kST * G::LV * 2 + 16 * i) = f32x4{0.f, 0.f, 0.f, 0.f};
+        // zero the V ring slots that the state waves do not write before the first stage (all but
+        // slot 0): P V reads every block of a chunk, zero P times these rows
+        for (int i = threadIdx.x; i < (int)((G::V_RING - G::V_BLK) / 16); i += 256)
+            *reinterpret_cast<f32x4*>(smem + G::OFF_V + G::V_BLK + 16 * i) = f32x4{0.f, 0.f, 0.f, 0.f};
         lds_barrier();
         for (int g = 0; g < total; ++g) {
             const int s = g % SPC;
@@ -815,7 +824,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             const char* Qs = buf(g);
             const char* Ps = buf(g) + G::OFF_P;
             const char* Pls = buf(g) + G::OFF_PL;
-            const bf16* Vs = Vc(g / SPC);
+            const int vf0 = vfirst(g / SPC);
             // the Q fragments and the first two P V steps' fragments first (their read latencies
             // overlap), then the QR chains; the other P and V reads go out while those run
             bf16x8 qf[DK / 32], pf[2], vf[2];
@@ -824,7 +833,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 pf[ks] = frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane);
-                vf[ks] = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
+                vf[ks] = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 qa[4];
@@ -845,7 +854,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             }
 #pragma unroll
             for (int ks = 2; ks < SPC; ++ks) {
-                const bf16x8 vk = lds_frag_kmajor(Vs, G::LV, 32 * ks, 16 * ct_o, lane);
+                const bf16x8 vk = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
                 pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
                 if constexpr (PLO) pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
             }
@@ -976,10 +985,10 @@ bool seg_shape(int DK, int DV, int C, int want_out) {
     return chunkwise_seg_supported(a);
 }
 
-// Chunks up to 256 with an output use the warp-specialised kernel, with P as bf16 hi + lo, where
-// its stage buffers fit in LDS; the other calls with an output use the single-group kernel, with P
-// as hi + lo where that fits (every supported shape), and state-only prefills use the single-group
-// kernel without P.
+// Chunks up to 256 with an output use the warp-specialised kernel, with P as bf16 hi + lo (its
+// stage buffers fit in LDS for every supported d_k); 512-token chunks use the single-group kernel,
+// with P as hi + lo as well, and state-only calls that reach this point (operands read in place)
+// use the single-group kernel without P.
 constexpr size_t kLdsBytes = 160 * 1024;
 template <int DK, int C, bool WANT_OUT>
 constexpr bool use_ws() { return WANT_OUT && C <= 256 && WsGeom<DK, C, true>::BYTES <= kLdsBytes; }
