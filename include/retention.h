@@ -228,9 +228,11 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
  * map (or fp32 inputs) they are in the input dtype and only the first
  * min(ceil((window + 1) / 32) * 32, N) shifted value rows of each head are written there (the
  * kernels read the later ones from v itself). With bf16 inputs and the softmax map the features
- * and every shifted value row are kept in fp32 and the call runs the fp32 kernels, in chunks of
- * min(chunk, 128) tokens: the softmax puts most of a row's weight on a few features, whose bf16
- * rounding alone would move the output by 2e-2 to 5e-2 of its RMS.
+ * keep more than bf16 (the softmax puts most of a row's weight on a few features, whose bf16
+ * rounding alone would move the output by 2e-2 to 5e-2 of its RMS): a segment (N > 1) writes their
+ * bf16 high and low parts and runs the bf16 chunkwise kernels on (q_hi, k_hi), (q_hi, k_lo) and
+ * (q_lo, k_hi), whose fp32 partial outputs and states are then added (the workspace holds the
+ * partial results too); a decode step (N = 1) takes the features and the value row in fp32.
  */
 ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t window, int32_t feature_map,
                              const void* q, const void* k, const void* v,

@@ -200,23 +200,35 @@ size_t chunkwise_ws(const ret_shape* s, int chunk, int gn, int want_out) {
     return want_out ? ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16) : 0;
 }
 
-// Residual linear attention with bf16 inputs and the softmax map keeps its features in fp32: the
-// softmax concentrates a row's weight on a few features, and their bf16 rounding alone moves the
-// output by 2e-2 to 5e-2 of its RMS. Those calls run the fp32 kernels, whose chunks are at most 128
-// tokens (the chunk length changes the blocking of the sum, not its value).
-bool rla_f32_features(const ret_shape* s, int fmap) { return s->in_dtype == RET_BF16 && fmap == RET_FMAP_SOFTMAX; }
-int rla_chunk(const ret_shape* s, int fmap, int chunk) { return rla_f32_features(s, fmap) ? std::min(chunk, 128) : chunk; }
+// Residual linear attention with bf16 inputs and the softmax map keeps more than bf16 of its
+// features: the softmax concentrates a row's weight on a few features, and their bf16 rounding alone
+// moves the output by 2e-2 to 5e-2 of its RMS. A decode step (N = 1) takes them in fp32 on the fp32
+// decode kernel. A segment (N > 1) runs the bf16 chunkwise kernels three times on the features'
+// bf16 high and low parts: the output is bilinear in (phi(q), phi(k)), so
+//   o = A(q_hi, k_hi) + A(q_hi, k_lo) + A(q_lo, k_hi) + (the lo x lo term, about 2^-16 relative),
+// with state_in entering the calls on q_hi and q_lo once each and the state from the k_hi and k_lo
+// calls added (rla_split_features).
+bool rla_f32_features(const ret_shape* s, int fmap) { return s->in_dtype == RET_BF16 && fmap == RET_FMAP_SOFTMAX && s->seq_len == 1; }
+bool rla_split_features(const ret_shape* s, int fmap) { return s->in_dtype == RET_BF16 && fmap == RET_FMAP_SOFTMAX && s->seq_len > 1; }
 
-// Residual linear attention: phi(q), the shifted phi(k) and v (input dtype, or fp32 with
-// rla_f32_features; each 256-byte aligned), then the chunkwise workspace for N > 1 (no GroupNorm).
+// The workspace of a split call after its operands: the fp32 partial outputs (two, three when the
+// output is bf16) and the second partial state, each 256-byte aligned.
+size_t rla_split_extra(const ret_shape* s) {
+    const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
+    const size_t o = align256(rows * s->d_v * sizeof(float));
+    return (s->out_dtype == RET_BF16 ? 3 : 2) * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float));
+}
+
+// Residual linear attention: phi(q), the shifted phi(k) and v (input dtype, fp32 for
+// rla_f32_features, bf16 high and low feature parts for rla_split_features; each 256-byte aligned),
+// the split call's partial results, then the chunkwise workspace for N > 1 (no GroupNorm).
 size_t rla_ws(const ret_shape* s, int chunk, int fmap) {
     const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
-    const bool f32 = rla_f32_features(s, fmap);
+    const bool f32 = rla_f32_features(s, fmap), split = rla_split_features(s, fmap);
     const size_t es = f32 ? sizeof(float) : elem_size(s->in_dtype);
-    const size_t ops = 2 * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
+    const size_t ops = (split ? 4 : 2) * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
     if (s->seq_len == 1) return ops;
-    if (f32) return ops + ret::chunkwise_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, 0, s->out_dtype == RET_BF16);
-    return ops + chunkwise_ws(s, chunk, 0, 1);
+    return ops + (split ? rla_split_extra(s) : 0) + chunkwise_ws(s, chunk, 0, 1);
 }
 
 size_t parallel_ws(const ret_shape* s, int gn) {
@@ -545,9 +557,6 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         if (bf ? !ret::chunkwise_bf16_supported(shape->d_k, dv, chunk) : !ret::chunkwise_f32_supported(shape->d_k, dv, chunk))
             return fail(RET_ERR_UNSUPPORTED, "residual linear attention: no chunkwise kernel for %s inputs with d_k %d, d_v %d, chunk %d",
                         bf ? "bf16" : "fp32", shape->d_k, dv, chunk);
-        if (rla_f32_features(shape, feature_map) && !ret::chunkwise_f32_supported(shape->d_k, dv, rla_chunk(shape, feature_map, chunk)))
-            return fail(RET_ERR_UNSUPPORTED, "residual linear attention with fp32 features: no chunkwise kernel for d_k %d, d_v %d",
-                        shape->d_k, dv);
         RET_TRY(check_bf16_head(shape, chunk));
     }
     const size_t rows = (size_t)shape->batch * shape->heads * N;
@@ -567,19 +576,24 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     // operands: phi(q), shifted phi(k) and v, in the front of the workspace
     const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     char* w = static_cast<char*>(workspace);
-    const bool f32feat = rla_f32_features(shape, feature_map);
+    const bool f32feat = rla_f32_features(shape, feature_map), split = rla_split_features(shape, feature_map);
     const size_t eo = f32feat ? sizeof(float) : es;  // bytes per prepared element
     const size_t Aq = align256(rows * shape->d_k * eo), Av = align256(rows * dv * eo);
+    const size_t nq = split ? 4 : 2;  // feature planes: q and k, or their high and low parts
     ret::RlaPrep r{};
     r.rows = (long)rows; r.N = N; r.dk = shape->d_k; r.dv = dv; r.P = P; r.prev_len = prev_len; r.fmap = feature_map; r.bf16 = bf;
     r.feat_f32 = f32feat;
     r.q = q; r.k = k; r.v = v; r.kp = k_prev; r.vp = v_prev;
     r.qo = feature_map == RET_FMAP_IDENTITY ? nullptr : w;
     r.ko = w + Aq;
-    r.vo = w + 2 * Aq;
+    if (split) {
+        r.qlo = w + 2 * Aq;
+        r.klo = w + 3 * Aq;
+    }
+    r.vo = w + nq * Aq;
     // shifted value rows in the workspace only up to vsplit (w + 1 rounded up to a 32-token stage,
     // at most N); the chunkwise kernels read the later rows from v, w + 1 rows back. With fp32
-    // features every value row is written there in fp32.
+    // features (a decode step) the one value row is written there in fp32.
     r.vsplit = f32feat ? N : (int)std::min<long long>(((long long)P + 31) / 32 * 32, N);
     hipError_t e = ret::launch_rla_prepare(r, st);
     if (e != hipSuccess) return device_status(e, "retention_rla_fwd prepare launch");
@@ -588,9 +602,12 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         hc.gamma[h] = 1.f;
         hc.log2g[h] = 0.f;
     }
-    ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : rla_chunk(shape, feature_map, chunk), hc, ret::GnArgs{}, w + 2 * Aq + Av,
-                                  workspace_bytes - (2 * Aq + Av), hip_stream);
-    if (f32feat) a.in_bf16 = 0;  // the fp32 kernels, on the fp32 features and value rows
+    char* rest = w + nq * Aq + Av;  // after the operands
+    char* parts = rest;             // split calls: partial outputs and state
+    if (split) rest += rla_split_extra(shape);
+    ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, rest,
+                                  workspace_bytes - (size_t)(rest - w), hip_stream);
+    if (f32feat) a.in_bf16 = 0;  // the fp32 decode kernel, on the fp32 features and value row
     a.q = r.qo ? r.qo : q; a.k = r.ko; a.out = out;
     if (r.vsplit == N) {
         a.v = r.vo;  // every value row is in the prefix buffer (laid out like v)
@@ -606,8 +623,46 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         a.state_out = state_out;
         return device_status(ret::launch_recurrent_step(a), "retention_rla_fwd step launch");
     }
-    a.state_in = state_in; a.state_out = state_out;
-    return device_status(a.in_bf16 ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
+    if (!split) {
+        a.state_in = state_in; a.state_out = state_out;
+        return device_status(a.in_bf16 ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
+    }
+    // split features: (q_lo, k_hi, state_in) and (q_hi, k_lo) into partial results, then (q_hi,
+    // k_hi, state_in) into out and state_out (last, so that an in-place state_in is read first by the
+    // calls that need it), then the sums
+    const size_t ob = align256(rows * dv * sizeof(float));
+    float* o2 = reinterpret_cast<float*>(parts);
+    float* o3 = reinterpret_cast<float*>(parts + ob);
+    float* o1 = shape->out_dtype == RET_BF16 ? reinterpret_cast<float*>(parts + 2 * ob) : static_cast<float*>(out);
+    float* s2 = reinterpret_cast<float*>(parts + (shape->out_dtype == RET_BF16 ? 3 : 2) * ob);
+    a.out_bf16 = 0;  // the partial outputs are fp32
+    if (out) {
+        ret::LaunchArgs c = a;
+        c.q = r.qlo; c.k = r.ko; c.out = o3; c.state_in = state_in; c.state_out = nullptr;
+        e = ret::launch_chunkwise_bf16(c);
+        if (e != hipSuccess) return device_status(e, "retention_rla_fwd launch (q low part)");
+    }
+    {
+        ret::LaunchArgs c = a;
+        c.q = r.qo; c.k = r.klo; c.out = out ? o2 : nullptr; c.state_in = nullptr; c.state_out = state_out ? s2 : nullptr;
+        e = ret::launch_chunkwise_bf16(c);
+        if (e != hipSuccess) return device_status(e, "retention_rla_fwd launch (k low part)");
+    }
+    {
+        ret::LaunchArgs c = a;
+        c.q = r.qo; c.k = r.ko; c.out = out ? o1 : nullptr; c.state_in = state_in; c.state_out = state_out;
+        e = ret::launch_chunkwise_bf16(c);
+        if (e != hipSuccess) return device_status(e, "retention_rla_fwd launch");
+    }
+    if (out) {
+        e = ret::launch_add_rows(rows * dv, o1, o2, o3, out, shape->out_dtype == RET_BF16, st);
+        if (e != hipSuccess) return device_status(e, "retention_rla_fwd sum launch");
+    }
+    if (state_out) {
+        e = ret::launch_add_rows(st_bytes / sizeof(float), state_out, s2, nullptr, state_out, false, st);
+        if (e != hipSuccess) return device_status(e, "retention_rla_fwd state sum launch");
+    }
+    return RET_OK;
 }
 
 }  // extern "C"

@@ -279,8 +279,12 @@ struct RlaPrep {
     int vsplit;    // shifted value rows written per head ([B*H][vsplit][dv] at vo)
     const void *q, *k, *v, *kp, *vp;
     void *qo, *ko, *vo;
+    void *qlo, *klo;  // bf16 features: the low parts (feature - its bf16 rounding, rounded), or null
 };
 hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream);
+// out = a + b + c over n values (c may be null; out may be a), fp32 sums, stored in fp32 or bf16;
+// n a multiple of 4, every pointer 16-byte aligned.
+hipError_t launch_add_rows(size_t n, const float* a, const float* b, const float* c, void* out, bool out_bf16, hipStream_t stream);
 // dst = src, or zero when src is null (n floats, a multiple of 4, 16-byte aligned).
 hipError_t launch_copy_state(size_t n, const float* src, float* dst, hipStream_t stream);
 }  // namespace ret

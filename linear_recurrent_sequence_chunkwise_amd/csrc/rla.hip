@@ -187,10 +187,20 @@ __device__ __forceinline__ void load_row(const RowAt<T>& r, const T* q, int dk, 
 
 // The rest of one row: phi(q[n]) (unless phi is the identity) and phi of the key row that lands at n
 // (zero where none does).
+// Stores the bf16 low parts of 4 features (x - bf16(x), rounded) when y is given.
+__device__ __forceinline__ void store_lo4(bf16* y, int d, int lane, const float* v) {
+    if (!y || 4 * lane >= d) return;
+    float lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo[j] = v[j] - (float)(bf16)v[j];
+    Vec4<bf16>::store(y + 4 * lane, lo);
+}
+__device__ __forceinline__ void store_lo4(float*, int, int, const float*) {}
+
 template <typename T, typename TO>
 __device__ __forceinline__ void finish_row(const RowAt<T>& r, const typename Raw4<T>::type& xq,
                                            const typename Raw4<T>::type& xk, int dk, int fmap, int lane,
-                                           const double* tab, TO* qo, TO* ko) {
+                                           const double* tab, TO* qo, TO* ko, TO* qlo, TO* klo) {
     const bool live = 4 * lane < dk;
     float fq[4], fk[4];
 #pragma unroll
@@ -200,11 +210,13 @@ __device__ __forceinline__ void finish_row(const RowAt<T>& r, const typename Raw
     }
     if (fmap == 1) softmax2(dk, lane, fq, fk, tab);
     if (qo) store_row4(qo + (size_t)r.row * dk, dk, lane, fq);
+    if (qlo) store_lo4(qlo + (size_t)r.row * dk, dk, lane, fq);
     if (!r.ks) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) fk[j] = 0.f;
     }
     store_row4(ko + (size_t)r.row * dk, dk, lane, fk);
+    if (klo) store_lo4(klo + (size_t)r.row * dk, dk, lane, fk);
 }
 
 // The next row of a wave's stride after r, or r itself past the end (more false).
@@ -226,7 +238,8 @@ __device__ __forceinline__ RowAt<T> advance(const RowAt<T>& r, int BH, int N, in
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void rla_prepare_kernel(int BH, int N, int dk, int dv, int P, int prev_len, int fmap,
                                                           int vsplit, int step_bh, int step_n, const T* q, const T* k,
-                                                          const T* v, const T* kp, const T* vp, TO* qo, TO* ko, TO* vo) {
+                                                          const T* v, const T* kp, const T* vp, TO* qo, TO* ko, TO* vo,
+                                                          TO* qlo, TO* klo) {
     __shared__ double tab[32];
     if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Frac[threadIdx.x];
     __syncthreads();
@@ -268,12 +281,26 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(int BH, int N, int dk,
     for (;;) {
         rb = advance(ra, BH, N, dk, dv, P, prev_len, step_bh, step_n, k, v, kp, vp, more);
         load_row(rb, q, dk, lane, want_q, bq, bk);
-        finish_row(ra, aq, ak, dk, fmap, lane, tab, qo, ko);
+        finish_row(ra, aq, ak, dk, fmap, lane, tab, qo, ko, qlo, klo);
         if (!more) break;
         ra = advance(rb, BH, N, dk, dv, P, prev_len, step_bh, step_n, k, v, kp, vp, more);
         load_row(ra, q, dk, lane, want_q, aq, ak);
-        finish_row(rb, bq, bk, dk, fmap, lane, tab, qo, ko);
+        finish_row(rb, bq, bk, dk, fmap, lane, tab, qo, ko, qlo, klo);
         if (!more) break;
+    }
+}
+
+// out = a + b + c, four values per thread and step (c may be null; out may alias a).
+template <typename TOUT>
+__global__ __launch_bounds__(256) void add_rows_kernel(size_t n4, const float* a, const float* b, const float* c, TOUT* out) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        f32x4 x = reinterpret_cast<const f32x4*>(a)[i] + reinterpret_cast<const f32x4*>(b)[i];
+        if (c) x += reinterpret_cast<const f32x4*>(c)[i];
+        if constexpr (sizeof(TOUT) == 4) {
+            reinterpret_cast<f32x4*>(out)[i] = x;
+        } else {
+            reinterpret_cast<bf16x4*>(out)[i] = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        }
     }
 }
 
@@ -299,19 +326,31 @@ hipError_t launch_rla_prepare(const RlaPrep& r, hipStream_t stream) {
                            r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const bf16*>(r.q), static_cast<const bf16*>(r.k), static_cast<const bf16*>(r.v),
                            static_cast<const bf16*>(r.kp), static_cast<const bf16*>(r.vp), static_cast<float*>(r.qo),
-                           static_cast<float*>(r.ko), static_cast<float*>(r.vo));
+                           static_cast<float*>(r.ko), static_cast<float*>(r.vo), nullptr, nullptr);
     else if (r.bf16)
         hipLaunchKernelGGL((rla_prepare_kernel<bf16, bf16>), dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
                            r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const bf16*>(r.q), static_cast<const bf16*>(r.k), static_cast<const bf16*>(r.v),
                            static_cast<const bf16*>(r.kp), static_cast<const bf16*>(r.vp), static_cast<bf16*>(r.qo),
-                           static_cast<bf16*>(r.ko), static_cast<bf16*>(r.vo));
+                           static_cast<bf16*>(r.ko), static_cast<bf16*>(r.vo), static_cast<bf16*>(r.qlo),
+                           static_cast<bf16*>(r.klo));
     else
         hipLaunchKernelGGL((rla_prepare_kernel<float, float>), dim3((unsigned)grid), dim3(256), 0, stream, BH, r.N, r.dk, r.dv, r.P,
                            r.prev_len, r.fmap, r.vsplit, step_bh, step_n,
                            static_cast<const float*>(r.q), static_cast<const float*>(r.k), static_cast<const float*>(r.v),
                            static_cast<const float*>(r.kp), static_cast<const float*>(r.vp), static_cast<float*>(r.qo),
-                           static_cast<float*>(r.ko), static_cast<float*>(r.vo));
+                           static_cast<float*>(r.ko), static_cast<float*>(r.vo), nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_rows(size_t n, const float* a, const float* b, const float* c, void* out, bool out_bf16, hipStream_t stream) {
+    const size_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 256 * 8);
+    if (out_bf16)
+        hipLaunchKernelGGL(add_rows_kernel<bf16>, dim3(grid), dim3(256), 0, stream, n4, a, b, c, static_cast<bf16*>(out));
+    else
+        hipLaunchKernelGGL(add_rows_kernel<float>, dim3(grid), dim3(256), 0, stream, n4, a, b, c, static_cast<float*>(out));
     return hipGetLastError();
 }
 
