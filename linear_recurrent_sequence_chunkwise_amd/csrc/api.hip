@@ -157,6 +157,84 @@ hipError_t stage_rotation(const ret_shape* s, const ret::RotConsts& rc, const vo
     return hipSuccess;
 }
 
+// ---- q and k carried as bf16 high + low parts (rotated operands of the bf16 forward forms, and
+// RLA's softmax features). A retention call is bilinear in (q, k) and linear in state_in, so three
+// bf16 calls on the parts give
+//     out = A(q_hi, k_hi) + A(q_hi, k_lo) + A(q_lo, k_hi)     (lo x lo, about 2^-16 relative, dropped)
+// with state_in entering the calls on q_hi and q_lo once each, and the final state the sum of the
+// states of the calls on k_hi and k_lo. The partial outputs are fp32; a GroupNorm (and gate)
+// follows their sum.
+
+// Bytes of the partial results: the fp32 partial outputs (two; three when the sum cannot go to out
+// directly, i.e. a bf16 output or a GroupNorm after it) and the second partial state.
+size_t split_parts_bytes(const ret_shape* s, bool gn) {
+    const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
+    const size_t o = align256(rows * s->d_v * sizeof(float));
+    return ((s->out_dtype == RET_BF16 || gn) ? 3 : 2) * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float));
+}
+
+// Rotated q and k of a bf16 forward call as high and low parts: four planes.
+size_t rotation_split_ws(const ret_shape* s) { return 2 * rotation_ws(s); }
+
+// Writes the four planes (q_hi, q_lo, k_hi, k_lo) at the front of *ws and advances it past them.
+hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, const void* q, const void* k, const void* parts[4],
+                                void** ws, size_t* wsb, hipStream_t st) {
+    const size_t A = rotation_ws(s) / 2;
+    char* base = static_cast<char*>(*ws);
+    const long rows = (long)s->batch * s->heads * s->seq_len;
+    const hipError_t e = ret::launch_rotate2(rows, s->seq_len, s->d_k, q, base, k, base + 2 * A, 1, 1, rc, 0, st, base + A, base + 3 * A);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < 4; ++i) parts[i] = base + i * A;
+    *ws = base + 4 * A;
+    *wsb -= 4 * A;
+    return hipSuccess;
+}
+
+// The three partial calls and the sums. a: the call (q and k unset; out, state_in, state_out, gn
+// and out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn) of workspace; launch: the
+// bf16 kernel family (chunkwise or parallel). An in-place state_in is read by the calls that need
+// it before the last call writes state_out.
+hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, const void* kh, const void* kl, char* parts,
+                     hipError_t (*launch)(const ret::LaunchArgs&)) {
+    const size_t rows = (size_t)a.B * a.H * a.N;
+    const size_t ob = align256(rows * a.DV * sizeof(float));
+    const bool staged = a.out_bf16 || a.gn.enabled;  // the sum goes through o1 in the workspace
+    float* o2 = reinterpret_cast<float*>(parts);
+    float* o3 = reinterpret_cast<float*>(parts + ob);
+    float* o1 = staged ? reinterpret_cast<float*>(parts + 2 * ob) : static_cast<float*>(a.out);
+    float* s2 = reinterpret_cast<float*>(parts + (staged ? 3 : 2) * ob);
+    ret::LaunchArgs c = a;
+    c.out_bf16 = 0;
+    c.gn = ret::GnArgs{};
+    hipError_t e;
+    if (a.out) {
+        c.q = ql; c.k = kh; c.out = o3; c.state_in = a.state_in; c.state_out = nullptr;
+        if ((e = launch(c)) != hipSuccess) return e;
+    }
+    if (a.out || a.state_out) {
+        c.q = qh; c.k = kl; c.out = a.out ? o2 : nullptr; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
+        if ((e = launch(c)) != hipSuccess) return e;
+    }
+    c.q = qh; c.k = kh; c.out = a.out ? o1 : nullptr; c.state_in = a.state_in; c.state_out = a.state_out;
+    if ((e = launch(c)) != hipSuccess) return e;
+    if (a.out) {
+        if (a.gn.enabled) {
+            if ((e = ret::launch_add_rows(rows * a.DV, o1, o2, o3, o1, false, a.stream)) != hipSuccess) return e;
+            if ((e = ret::launch_gn_rows((long)rows, a.H, a.N, a.DV, o1, a.out, a.out_bf16, a.gn, a.stream)) != hipSuccess) return e;
+        } else if ((e = ret::launch_add_rows(rows * a.DV, o1, o2, o3, a.out, a.out_bf16, a.stream)) != hipSuccess) {
+            return e;
+        }
+    }
+    if (a.state_out)
+        return ret::launch_add_rows((size_t)a.B * a.H * a.DK * a.DV, a.state_out, s2, nullptr, a.state_out, false, a.stream);
+    return hipSuccess;
+}
+
+// Workspace of the forward forms with a rotation: bf16 inputs carry the rotated q and k as high and
+// low parts (three calls, partial results), fp32 inputs one rotated copy.
+size_t chunkwise_rot_ws(const ret_shape* s, int chunk, bool gn, int want_out);
+size_t parallel_rot_ws(const ret_shape* s, bool gn);
+
 ret_status check_ptr(const void* p, const char* name, bool required) {
     if (!p) return required ? fail(RET_ERR_INVALID_ARG, "%s is NULL", name) : RET_OK;
     if (!aligned16(p)) return fail(RET_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
@@ -211,14 +289,6 @@ size_t chunkwise_ws(const ret_shape* s, int chunk, int gn, int want_out) {
 bool rla_f32_features(const ret_shape* s, int fmap) { return s->in_dtype == RET_BF16 && fmap == RET_FMAP_SOFTMAX && s->seq_len == 1; }
 bool rla_split_features(const ret_shape* s, int fmap) { return s->in_dtype == RET_BF16 && fmap == RET_FMAP_SOFTMAX && s->seq_len > 1; }
 
-// The workspace of a split call after its operands: the fp32 partial outputs (two, three when the
-// output is bf16) and the second partial state, each 256-byte aligned.
-size_t rla_split_extra(const ret_shape* s) {
-    const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
-    const size_t o = align256(rows * s->d_v * sizeof(float));
-    return (s->out_dtype == RET_BF16 ? 3 : 2) * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float));
-}
-
 // Residual linear attention: phi(q), the shifted phi(k) and v (input dtype, fp32 for
 // rla_f32_features, bf16 high and low feature parts for rla_split_features; each 256-byte aligned),
 // the split call's partial results, then the chunkwise workspace for N > 1 (no GroupNorm).
@@ -228,12 +298,22 @@ size_t rla_ws(const ret_shape* s, int chunk, int fmap) {
     const size_t es = f32 ? sizeof(float) : elem_size(s->in_dtype);
     const size_t ops = (split ? 4 : 2) * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
     if (s->seq_len == 1) return ops;
-    return ops + (split ? rla_split_extra(s) : 0) + chunkwise_ws(s, chunk, 0, 1);
+    return ops + (split ? split_parts_bytes(s, false) : 0) + chunkwise_ws(s, chunk, 0, 1);
 }
 
 size_t parallel_ws(const ret_shape* s, int gn) {
     if (s->in_dtype == RET_BF16) return 0;
     return ret::parallel_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16);
+}
+
+size_t chunkwise_rot_ws(const ret_shape* s, int chunk, bool gn, int want_out) {
+    if (s->in_dtype != RET_BF16) return rotation_ws(s) + chunkwise_ws(s, chunk, gn, want_out);
+    return rotation_split_ws(s) + split_parts_bytes(s, gn) + chunkwise_ws(s, chunk, 0, want_out);
+}
+
+size_t parallel_rot_ws(const ret_shape* s, bool gn) {
+    if (s->in_dtype != RET_BF16) return rotation_ws(s) + parallel_ws(s, gn);
+    return rotation_split_ws(s) + split_parts_bytes(s, gn) + parallel_ws(s, 0);
 }
 
 ret_status check_ws(size_t need, const void* ws, size_t wsb) {
@@ -300,9 +380,9 @@ size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chu
     switch (fn) {
         case RET_FN_CHUNKWISE:
             if (chunk <= 0) return (size_t)-1;
-            return rot + chunkwise_ws(shape, chunk, gn, 1);
+            return rot ? chunkwise_rot_ws(shape, chunk, gn, 1) : chunkwise_ws(shape, chunk, gn, 1);
         case RET_FN_RECURRENT_STEP: return rot;
-        case RET_FN_PARALLEL: return rot + parallel_ws(shape, gn);
+        case RET_FN_PARALLEL: return rot ? parallel_rot_ws(shape, gn) : parallel_ws(shape, gn);
         case RET_FN_CHUNKWISE_BWD:
             if (chunk <= 0) return (size_t)-1;
             return rot + ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len,
@@ -369,11 +449,26 @@ int ret::chunkwise_fwd_entry(const ret_shape* shape, int32_t chunk, const void* 
         gn.enabled = 0;
         gn.gate = nullptr;
     }
-    const size_t need = (rot ? rotation_ws(shape) : 0) + chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
+    const size_t need = rot ? chunkwise_rot_ws(shape, chunk, gn.enabled, out != nullptr)
+                            : chunkwise_ws(shape, chunk, gn.enabled, out != nullptr);
     if (provide && need > 0) RET_TRY((ret_status)provide(need, &workspace, &workspace_bytes));
     RET_TRY(check_ws(need, workspace, workspace_bytes));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    if (rot && bf) {
+        // rotated bf16 operands as high and low parts, three calls (the rotated values rounded once
+        // to bf16 would move the output by up to 2.4e-2 of its RMS)
+        const void* pq[4];
+        hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, st);
+        if (e != hipSuccess) return device_status(e, "retention_chunkwise_fwd rotation launch");
+        char* parts = static_cast<char*>(workspace);
+        const size_t pb = split_parts_bytes(shape, gn.enabled);
+        ret::LaunchArgs a = base_args(shape, chunk, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
+        a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
+        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_chunkwise_bf16);
+        return device_status(e, "retention_chunkwise_fwd launch");
+    }
     if (rot) {
-        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
+        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, st);
         if (e != hipSuccess) return device_status(e, "retention_chunkwise_fwd rotation launch");
     }
     ret::LaunchArgs a = base_args(shape, chunk, hc, gn, workspace, workspace_bytes, hip_stream);
@@ -508,8 +603,20 @@ ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const v
     ret::RotConsts rc;
     bool rot = false;
     RET_TRY(check_rotation(rotation, shape, &rc, &rot));
-    const size_t need = (rot ? rotation_ws(shape) : 0) + parallel_ws(shape, gn.enabled);
+    const size_t need = rot ? parallel_rot_ws(shape, gn.enabled) : parallel_ws(shape, gn.enabled);
     RET_TRY(check_ws(need, workspace, workspace_bytes));
+    if (rot && bf) {
+        // rotated bf16 operands as high and low parts, three calls
+        const void* pq[4];
+        hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return device_status(e, "retention_parallel_fwd rotation launch");
+        char* parts = static_cast<char*>(workspace);
+        const size_t pb = split_parts_bytes(shape, gn.enabled);
+        ret::LaunchArgs a = base_args(shape, 0, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
+        a.v = v; a.out = out;
+        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_parallel_bf16);
+        return device_status(e, "retention_parallel_fwd launch");
+    }
     if (rot) {
         const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
         if (e != hipSuccess) return device_status(e, "retention_parallel_fwd rotation launch");
@@ -604,7 +711,7 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     }
     char* rest = w + nq * Aq + Av;  // after the operands
     char* parts = rest;             // split calls: partial outputs and state
-    if (split) rest += rla_split_extra(shape);
+    if (split) rest += split_parts_bytes(shape, false);
     ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, rest,
                                   workspace_bytes - (size_t)(rest - w), hip_stream);
     if (f32feat) a.in_bf16 = 0;  // the fp32 decode kernel, on the fp32 features and value row
@@ -627,42 +734,8 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         a.state_in = state_in; a.state_out = state_out;
         return device_status(a.in_bf16 ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
     }
-    // split features: (q_lo, k_hi, state_in) and (q_hi, k_lo) into partial results, then (q_hi,
-    // k_hi, state_in) into out and state_out (last, so that an in-place state_in is read first by the
-    // calls that need it), then the sums
-    const size_t ob = align256(rows * dv * sizeof(float));
-    float* o2 = reinterpret_cast<float*>(parts);
-    float* o3 = reinterpret_cast<float*>(parts + ob);
-    float* o1 = shape->out_dtype == RET_BF16 ? reinterpret_cast<float*>(parts + 2 * ob) : static_cast<float*>(out);
-    float* s2 = reinterpret_cast<float*>(parts + (shape->out_dtype == RET_BF16 ? 3 : 2) * ob);
-    a.out_bf16 = 0;  // the partial outputs are fp32
-    if (out) {
-        ret::LaunchArgs c = a;
-        c.q = r.qlo; c.k = r.ko; c.out = o3; c.state_in = state_in; c.state_out = nullptr;
-        e = ret::launch_chunkwise_bf16(c);
-        if (e != hipSuccess) return device_status(e, "retention_rla_fwd launch (q low part)");
-    }
-    {
-        ret::LaunchArgs c = a;
-        c.q = r.qo; c.k = r.klo; c.out = out ? o2 : nullptr; c.state_in = nullptr; c.state_out = state_out ? s2 : nullptr;
-        e = ret::launch_chunkwise_bf16(c);
-        if (e != hipSuccess) return device_status(e, "retention_rla_fwd launch (k low part)");
-    }
-    {
-        ret::LaunchArgs c = a;
-        c.q = r.qo; c.k = r.ko; c.out = out ? o1 : nullptr; c.state_in = state_in; c.state_out = state_out;
-        e = ret::launch_chunkwise_bf16(c);
-        if (e != hipSuccess) return device_status(e, "retention_rla_fwd launch");
-    }
-    if (out) {
-        e = ret::launch_add_rows(rows * dv, o1, o2, o3, out, shape->out_dtype == RET_BF16, st);
-        if (e != hipSuccess) return device_status(e, "retention_rla_fwd sum launch");
-    }
-    if (state_out) {
-        e = ret::launch_add_rows(st_bytes / sizeof(float), state_out, s2, nullptr, state_out, false, st);
-        if (e != hipSuccess) return device_status(e, "retention_rla_fwd state sum launch");
-    }
-    return RET_OK;
+    a.state_in = state_in; a.state_out = state_out;
+    return device_status(run_split(a, r.qo, r.qlo, r.ko, r.klo, parts, ret::launch_chunkwise_bf16), "retention_rla_fwd launch");
 }
 
 }  // extern "C"

@@ -1141,6 +1141,17 @@ size_t chunkwise_bf16_workspace(int B, int H, int N, int DK, int DV, int chunk, 
     return t > u ? t : u;
 }
 
+hipError_t launch_gn_rows(long rows, int H, int N, int DV, const float* pre, void* y, bool y_bf16, const GnArgs& gn,
+                          hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (y_bf16)
+        hipLaunchKernelGGL(gn_rows_kernel<bf16>, grid, dim3(256), 0, stream, rows, H, N, DV, pre, static_cast<bf16*>(y), gn);
+    else
+        hipLaunchKernelGGL(gn_rows_kernel<float>, grid, dim3(256), 0, stream, rows, H, N, DV, pre, static_cast<float*>(y), gn);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunkwise_bf16(const LaunchArgs& a) {
     if (a.DK == 64) return a.out_bf16 ? launch_dk<64, bf16>(a) : launch_dk<64, float>(a);
     return a.out_bf16 ? launch_dk<256, bf16>(a) : launch_dk<256, float>(a);

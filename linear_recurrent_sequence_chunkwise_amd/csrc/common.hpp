@@ -264,9 +264,14 @@ hipError_t launch_chunkwise_bwd(const BwdArgs& b);
 // buffer. inverse != 0 turns by the opposite angles.
 hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc,
                          int inverse, hipStream_t stream);
-// Two tensors of the same shape in one launch (x0 -> y0, x1 -> y1; x1 may be null).
+// Two tensors of the same shape in one launch (x0 -> y0, x1 -> y1; x1 may be null). With bf16
+// outputs, lo0 / lo1 (when not null) also receive the low parts of the turned values (value minus
+// its bf16 rounding, rounded to bf16).
 hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, int x_bf16, int y_bf16,
-                          const RotConsts& rc, int inverse, hipStream_t stream);
+                          const RotConsts& rc, int inverse, hipStream_t stream, void* lo0 = nullptr, void* lo1 = nullptr);
+// The per-head GroupNorm (and gate) over fp32 pre-norm rows [rows][DV], into y (fp32 or bf16).
+hipError_t launch_gn_rows(long rows, int H, int N, int DV, const float* pre, void* y, bool y_bf16, const GnArgs& gn,
+                          hipStream_t stream);
 // Residual linear attention operands: qo = phi(q) (qo null: phi is the identity and q is used as
 // is), ko = phi(k) shifted by P = window + 1 rows, and vo = the first vsplit rows of v shifted the
 // same way ([rows / N][vsplit][dv]; the chunk kernels read the later rows from v, see VShift); the

@@ -57,10 +57,11 @@ template <> struct Vec8<float> {
 constexpr int RB = 8;
 
 // Two tensors in one launch: units [0, units) turn x0 into y0, units [units, 2 units) x1 into y1
-// (x1 null: one tensor).
+// (x1 null: one tensor). With bf16 outputs, lo0 / lo1 (when given) receive the low parts of the
+// turned values, value - bf16(value) rounded to bf16, laid out like y0 / y1.
 template <typename TI, typename TO, int PAIRS>
 __global__ __launch_bounds__(256) void rotate_kernel(long units, int N, int d, const TI* x0, TO* y0, const TI* x1, TO* y1,
-                                                     RotConsts rc, float sgn) {
+                                                     TO* lo0, TO* lo1, RotConsts rc, float sgn) {
     const int per_row = d / (2 * PAIRS);
     const int nblk = (N + RB - 1) / RB;
     const long all = x1 ? 2 * units : units;
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(long units, int N, int d, c
         const long u = second ? uu - units : uu;
         const TI* x = second ? x1 : x0;
         TO* y = second ? y1 : y0;
+        TO* lo = second ? lo1 : lo0;
         const int i0 = (int)(u % per_row) * PAIRS;  // first pair
         const long blk = u / per_row;
         const long bh = blk / nblk;
@@ -114,37 +116,50 @@ __global__ __launch_bounds__(256) void rotate_kernel(long units, int N, int d, c
                     y[base + (size_t)r * d] = from_float<TO>(v[r][0]);
                     y[base + (size_t)r * d + 1] = from_float<TO>(v[r][1]);
                 }
+                if (sizeof(TO) == 2 && lo) {
+                    float l[2 * PAIRS];
+#pragma unroll
+                    for (int j = 0; j < 2 * PAIRS; ++j) l[j] = v[r][j] - (float)from_float<TO>(v[r][j]);
+                    if constexpr (PAIRS == 4) {
+                        Vec8<TO>::store(lo + base + (size_t)r * d, l);
+                    } else {
+                        lo[base + (size_t)r * d] = from_float<TO>(l[0]);
+                        lo[base + (size_t)r * d + 1] = from_float<TO>(l[1]);
+                    }
+                }
             }
         }
     }
 }
 
 template <typename TI, typename TO>
-hipError_t launch_t(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, const RotConsts& rc, float sgn,
-                    hipStream_t st) {
+hipError_t launch_t(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, void* lo0, void* lo1,
+                    const RotConsts& rc, float sgn, hipStream_t st) {
     const bool vec = d % 8 == 0;
     const long units = rows / N * ((N + RB - 1) / RB) * (long)(d / (vec ? 8 : 2));
     const long blocks = ((x1 ? 2 : 1) * units + 255) / 256;
     const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
     if (vec)
         hipLaunchKernelGGL((rotate_kernel<TI, TO, 4>), dim3(grid), dim3(256), 0, st, units, N, d, static_cast<const TI*>(x0),
-                           static_cast<TO*>(y0), static_cast<const TI*>(x1), static_cast<TO*>(y1), rc, sgn);
+                           static_cast<TO*>(y0), static_cast<const TI*>(x1), static_cast<TO*>(y1), static_cast<TO*>(lo0),
+                           static_cast<TO*>(lo1), rc, sgn);
     else
         hipLaunchKernelGGL((rotate_kernel<TI, TO, 1>), dim3(grid), dim3(256), 0, st, units, N, d, static_cast<const TI*>(x0),
-                           static_cast<TO*>(y0), static_cast<const TI*>(x1), static_cast<TO*>(y1), rc, sgn);
+                           static_cast<TO*>(y0), static_cast<const TI*>(x1), static_cast<TO*>(y1), static_cast<TO*>(lo0),
+                           static_cast<TO*>(lo1), rc, sgn);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_rotate2(long rows, int N, int d, const void* x0, void* y0, const void* x1, void* y1, int x_bf16, int y_bf16,
-                          const RotConsts& rc, int inverse, hipStream_t stream) {
+                          const RotConsts& rc, int inverse, hipStream_t stream, void* lo0, void* lo1) {
     if (rows <= 0) return hipSuccess;
     const float sgn = inverse ? -1.f : 1.f;
-    if (x_bf16 && y_bf16) return launch_t<bf16, bf16>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
-    if (x_bf16) return launch_t<bf16, float>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
-    if (y_bf16) return launch_t<float, bf16>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
-    return launch_t<float, float>(rows, N, d, x0, y0, x1, y1, rc, sgn, stream);
+    if (x_bf16 && y_bf16) return launch_t<bf16, bf16>(rows, N, d, x0, y0, x1, y1, lo0, lo1, rc, sgn, stream);
+    if (x_bf16) return launch_t<bf16, float>(rows, N, d, x0, y0, x1, y1, nullptr, nullptr, rc, sgn, stream);
+    if (y_bf16) return launch_t<float, bf16>(rows, N, d, x0, y0, x1, y1, lo0, lo1, rc, sgn, stream);
+    return launch_t<float, float>(rows, N, d, x0, y0, x1, y1, nullptr, nullptr, rc, sgn, stream);
 }
 
 hipError_t launch_rotate(long rows, int N, int d, const void* x, int x_bf16, void* y, int y_bf16, const RotConsts& rc, int inverse,

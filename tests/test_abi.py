@@ -240,13 +240,27 @@ def test_rotation_shapes(lib):
 
 
 def test_rotation_workspace(lib):
-    # a rotation stages the rotated q and k (input dtype, each copy 256-byte aligned) in front
-    for fn, C in ((R.RET_FN_CHUNKWISE, 64), (R.RET_FN_PARALLEL, 0), (R.RET_FN_CHUNKWISE_BWD, 64)):
-        s = shape()
+    al = lambda n: (n + 255) // 256 * 256
+    # a rotation stages the rotated q and k (input dtype, each copy 256-byte aligned) in front: one
+    # copy each for the backward and for fp32 inputs
+    for fn, C, i in ((R.RET_FN_CHUNKWISE_BWD, 64, R.RET_BF16), (R.RET_FN_CHUNKWISE, 64, R.RET_F32), (R.RET_FN_PARALLEL, 0, R.RET_F32)):
+        s = shape(i=i)
         base = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, 0)
         with_rot = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION)
-        copy = s.batch * s.heads * s.seq_len * s.d_k * 2
-        assert with_rot == base + 2 * ((copy + 255) // 256 * 256), fn
+        copy = s.batch * s.heads * s.seq_len * s.d_k * (2 if i == R.RET_BF16 else 4)
+        assert with_rot == base + 2 * al(copy), fn
+    # the bf16 forward forms keep high and low parts (four planes), then the three calls' fp32
+    # partial outputs (two, three with a GroupNorm after their sum or a bf16 output) and second
+    # partial state, then the calls' own workspace without a GroupNorm
+    s = shape()
+    rows = s.batch * s.heads * s.seq_len
+    planes = 4 * al(rows * s.d_k * 2)
+    o, st = al(rows * s.d_v * 4), al(s.batch * s.heads * s.d_k * s.d_v * 4)
+    for fn, C in ((R.RET_FN_CHUNKWISE, 64), (R.RET_FN_PARALLEL, 0)):
+        base = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, 0)
+        assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION) == planes + 2 * o + st + base, fn
+        assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION | R.RET_WS_GROUPNORM) == \
+            planes + 3 * o + st + base, fn
     s = shape(N=1)
     assert lib.retention_workspace_bytes(R.RET_FN_RECURRENT_STEP, ctypes.byref(s), 0, R.RET_WS_ROTATION) == 2 * 256
     assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(shape()), 64, 4) == ctypes.c_size_t(-1).value

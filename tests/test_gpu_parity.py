@@ -463,14 +463,12 @@ def _rot_bf16(orc, x, base, off):
     return torch.from_numpy(orc.rotate(x, base, off)).to(torch.float32).to(torch.bfloat16)
 
 
-# Checks that fail the stated metric: the bf16 path rounds the rotated q and k to bf16, and for
-# these the oracle run on the rounded operands is already 1.8e-2 to 2.4e-2 from the exact oracle
-# (oracle against oracle, no GPU arithmetic in it), so no kernel arithmetic can bring them under
-# 2e-2. They are computed and printed, and the test reports xfail when one exceeds the bound.
+# Checks that fail the stated metric: the bf16 backward rounds the rotated q and k to bf16 once
+# (the forward forms keep them as high and low parts), and for this check the oracle run on the
+# rounded operands is already 2.3e-2 from the exact oracle (oracle against oracle, no GPU
+# arithmetic in it), so no kernel arithmetic can bring it under 2e-2. It is computed and printed,
+# and the test reports xfail when it exceeds the bound.
 ROT_BF16_FLOOR = {
-    "rotated layer GN bf16 out",
-    "rotated split/resume out",
-    "rotated layer fp32 out at offset 5000 (exact: the offset-0 oracle)",
     "rotated backward bf16 (64,64) N=2048 C=128 offset 0 dv",
 }
 
@@ -535,10 +533,11 @@ def test_rotation_layer_6p7b(orc):
     ex, ex_s = orc.recurrent_rot(q, k, v, gam, 10000.0, 0)
     ref_gn = orc.groupnorm(ref, w.eps)
     over = []
-    rot_report("rotated layer GN bf16 out", o, ref_gn, orc.groupnorm(ex, w.eps), TOL["bf16"], over)
+    ex_gn = orc.groupnorm(ex, w.eps)
+    rot_report("rotated layer GN bf16 out", o, ref_gn, ex_gn, TOL["bf16"], over)
     # most of that is the bf16 storage of the normalised output; the kernels' own share is small
-    floor = rel_err(torch.from_numpy(ref_gn).to(torch.bfloat16), ref_gn)
-    report("rotated layer GN bf16 out above the bf16 storage floor", rel_err(o, ref_gn) - floor, 5e-3)
+    floor = rel_err(torch.from_numpy(ex_gn).to(torch.bfloat16), ex_gn)
+    report("rotated layer GN bf16 out above the bf16 storage floor", rel_err(o, ex_gn) - floor, 5e-3)
     rot_report("rotated layer state", s, ref_s, ex_s, TOL["bf16"])
     ref2, _ = orc.recurrent(_rot_bf16(orc, q, 10000.0, 5000), _rot_bf16(orc, k, 10000.0, 5000), v, gam, want_state=False)
     rot_report("rotated layer fp32 out at offset 5000 (exact: the offset-0 oracle)", o2, ref2, ex, TOL["bf16"], over)
