@@ -55,11 +55,12 @@ def eager_noise(x):
     return y
 
 
-def test_graph_chunkwise_groupnorm(orc):
-    B, H, N, dk, dv = 1, 4, 1000, 256, 512
+@pytest.mark.parametrize("H", [4, 16])  # 4 heads: the segmented kernels; 16: the (b, h, slice) chunk kernels
+def test_graph_chunkwise_groupnorm(orc, H):
+    B, N, dk, dv = 1, 1000, 256, 512
     q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=950)
     s0 = I.make_state(B, H, dk, dv, seed=951, scale=0.02)
-    gam = I.multiscale_gammas(16)[::4]
+    gam = I.multiscale_gammas(16)[::16 // H]
     qd, kd, vd, s0d = (t.to(DEV) for t in (q, k, v, s0))
     gn = R.GroupNorm(1e-5)
     call = lambda: R.chunkwise_fwd(qd, kd, vd, gam, 128, state_in=s0d, groupnorm=gn, out_dtype=torch.bfloat16)

@@ -155,8 +155,10 @@ def test_bf16_parallel_layer_shape_groupnorm(orc):
 
 # GroupNorm after the bf16 chunk kernels: every chunk size, fp32 and bf16 out, per-channel affine,
 # ragged N, B > 1, head counts that are not a multiple of 8 (the d_v slices of a head then sit on
-# different XCDs), and a grid of 512 workgroups (more than the GPU holds at once).
-@pytest.mark.parametrize("dk,dv,B,H,N", [(64, 64, 3, 5, 777), (256, 512, 1, 3, 1100), (256, 512, 2, 16, 600)])
+# different XCDs), and a grid of 512 workgroups (more than the GPU holds at once). The first two
+# shapes run on the segmented kernels, the last two on the (b, h, slice) chunk kernels.
+@pytest.mark.parametrize("dk,dv,B,H,N", [(64, 64, 3, 5, 777), (256, 512, 1, 3, 1100), (256, 512, 2, 16, 600),
+                                         (256, 512, 1, 17, 300)])
 def test_bf16_chunkwise_groupnorm_shapes(orc, dk, dv, B, H, N):
     q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=300 + N)
     gam = I.multiscale_gammas(H)
@@ -170,6 +172,27 @@ def test_bf16_chunkwise_groupnorm_shapes(orc, dk, dv, B, H, N):
         for odt in (torch.float32, torch.bfloat16):
             o, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, groupnorm=gn, out_dtype=odt, want_state=False)
             report(f"GN B={B} H={H} N={N} dk={dk} C={C} {str(odt)[6:]} out", rel_err(o, ref_gn), TOL["bf16"])
+
+
+# The gated GroupNorm after the (b, h, slice) chunk kernels (17 heads x 16 slices: 272 workgroups,
+# the slices of a head on different XCDs), fp32 and bf16 out, against the oracle.
+def test_groupnorm_gate_chunk_kernels(orc):
+    B, H, N, dk, dv = 1, 17, 300, 256, 512
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=431)
+    gam = I.multiscale_gammas(16) + [0.95]
+    g = _gate((B, H, N, dv), torch.bfloat16, 432)
+    gw = (1.0 + 0.1 * torch.randn(H, dv, generator=torch.Generator().manual_seed(433))).float()
+    ref, _ = orc.recurrent(q, k, v, gam)
+    ref_g = orc.groupnorm(ref, 1e-5, gw, None, g)
+    qd, kd, vd, gd = dev(q, k, v, g)
+    gn = R.GroupNorm(1e-5, gw.to(DEV), None, gd)
+    for C in (64, 128, 256):
+        o, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, groupnorm=gn, want_state=False)
+        report(f"gated GN (1, 17) C={C} fp32 out", rel_err(o, ref_g), TOL["bf16"])
+    ob, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=gn, out_dtype=torch.bfloat16, want_state=False)
+    o32, _ = R.chunkwise_fwd(qd, kd, vd, gam, 128, groupnorm=gn, want_state=False)
+    ob, o32 = ob.double().cpu(), o32.double().cpu()
+    report("gated GN (1, 17) bf16 out vs fp32 out rounded", float(((ob - o32).abs() / o32.abs().clamp_min(1e-30)).max()), 2.0 ** -8)
 
 
 # The swish gate after GroupNorm, out = swish(g) * GN(o), through every kernel that applies
