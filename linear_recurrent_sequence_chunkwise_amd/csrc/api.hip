@@ -306,6 +306,21 @@ size_t parallel_ws(const ret_shape* s, int gn) {
     return ret::parallel_f32_workspace(s->batch, s->heads, s->seq_len, s->d_v, gn, s->out_dtype == RET_BF16);
 }
 
+// The backward's partial gradients of the split: dq (k_lo) and dk (q_lo), dv twice, dstate_in.
+size_t bwd_split_parts_bytes(const ret_shape* s) {
+    const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
+    return 2 * align256(rows * s->d_k * 4) + 2 * align256(rows * s->d_v * 4) +
+           align256((size_t)s->batch * s->heads * s->d_k * s->d_v * 4);
+}
+
+// The backward with a rotation: bf16 inputs carry the rotated q and k as high and low parts (three
+// backward calls, partial gradients), fp32 inputs one rotated copy.
+size_t bwd_rot_ws(const ret_shape* s, int chunk) {
+    const size_t b = ret::chunkwise_bwd_workspace(s->in_dtype == RET_BF16, s->batch, s->heads, s->seq_len, s->d_k, s->d_v, chunk);
+    if (s->in_dtype != RET_BF16) return rotation_ws(s) + b;
+    return rotation_split_ws(s) + bwd_split_parts_bytes(s) + b;
+}
+
 size_t chunkwise_rot_ws(const ret_shape* s, int chunk, bool gn, int want_out) {
     if (s->in_dtype != RET_BF16) return rotation_ws(s) + chunkwise_ws(s, chunk, gn, want_out);
     return rotation_split_ws(s) + split_parts_bytes(s, gn) + chunkwise_ws(s, chunk, 0, want_out);
@@ -385,8 +400,9 @@ size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chu
         case RET_FN_PARALLEL: return rot ? parallel_rot_ws(shape, gn) : parallel_ws(shape, gn);
         case RET_FN_CHUNKWISE_BWD:
             if (chunk <= 0) return (size_t)-1;
-            return rot + ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len,
-                                                      shape->d_k, shape->d_v, chunk);
+            if (rot) return bwd_rot_ws(shape, chunk);
+            return ret::chunkwise_bwd_workspace(shape->in_dtype == RET_BF16, shape->batch, shape->heads, shape->seq_len,
+                                                shape->d_k, shape->d_v, chunk);
         case RET_FN_RLA:
             if (shape->seq_len > 1 && chunk <= 0) return (size_t)-1;
             return std::max(rla_ws(shape, chunk, RET_FMAP_IDENTITY), rla_ws(shape, chunk, RET_FMAP_SOFTMAX));
@@ -521,19 +537,58 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk, const 
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(outs[i], out_b[i], outs[j], out_b[j])) return fail(RET_ERR_INVALID_ARG, "gradient outputs must not alias each other");
     }
-    const size_t need = (rot ? rotation_ws(shape) : 0) +
-                        ret::chunkwise_bwd_workspace(bf, shape->batch, shape->heads, shape->seq_len, shape->d_k, shape->d_v, chunk);
+    const size_t need = rot ? bwd_rot_ws(shape, chunk)
+                            : ret::chunkwise_bwd_workspace(bf, shape->batch, shape->heads, shape->seq_len, shape->d_k, shape->d_v, chunk);
     RET_TRY(check_ws(need, workspace, workspace_bytes));
     const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    if (rot) {
-        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, st);
+    hipError_t e;
+    if (rot && bf) {
+        // rotated bf16 q and k as high and low parts: dq is linear in k, dk and dstate_in in q, dv
+        // bilinear in both, so (q_hi, k_hi) gives every gradient, (q_hi, k_lo) adds to dq (without the
+        // state_in term, which does not involve k) and dv, and (q_lo, k_hi) adds to dk, dv and dstate_in
+        const void* pq[4];
+        e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, st);
         if (e != hipSuccess) return device_status(e, "retention_chunkwise_bwd rotation launch");
+        char* parts = static_cast<char*>(workspace);
+        const size_t gk = align256(rows * shape->d_k * 4), gv = align256(rows * shape->d_v * 4);
+        float* dq2 = reinterpret_cast<float*>(parts);
+        float* dk3 = reinterpret_cast<float*>(parts + gk);
+        float* dv2 = reinterpret_cast<float*>(parts + 2 * gk);
+        float* dv3 = reinterpret_cast<float*>(parts + 2 * gk + gv);
+        float* ds3 = reinterpret_cast<float*>(parts + 2 * gk + 2 * gv);
+        const size_t pb = bwd_split_parts_bytes(shape);
+        ret::BwdArgs b{};
+        b.base = base_args(shape, chunk, hc, ret::GnArgs{}, parts + pb, workspace_bytes - pb, hip_stream);
+        b.v = v; b.dout = dout;
+        ret::BwdArgs c = b;
+        c.q = pq[0]; c.k = pq[3]; c.dq = dq ? dq2 : nullptr; c.dv = dv ? dv2 : nullptr;
+        if ((c.dq || c.dv) && (e = ret::launch_chunkwise_bwd(c)) != hipSuccess) return device_status(e, "retention_chunkwise_bwd launch");
+        c = b;
+        c.q = pq[1]; c.k = pq[2]; c.dk = dk ? dk3 : nullptr; c.dv = dv ? dv3 : nullptr; c.dstate_in = dstate_in ? ds3 : nullptr;
+        if ((c.dk || c.dv || c.dstate_in) && (e = ret::launch_chunkwise_bwd(c)) != hipSuccess)
+            return device_status(e, "retention_chunkwise_bwd launch");
+        c = b;
+        c.q = pq[0]; c.k = pq[2]; c.state_in = state_in; c.dq = dq; c.dk = dk; c.dv = dv; c.dstate_in = dstate_in;
+        if ((e = ret::launch_chunkwise_bwd(c)) != hipSuccess) return device_status(e, "retention_chunkwise_bwd launch");
+        if (dq && (e = ret::launch_add_rows(rows * shape->d_k, dq, dq2, nullptr, dq, false, st)) != hipSuccess)
+            return device_status(e, "retention_chunkwise_bwd sum launch");
+        if (dk && (e = ret::launch_add_rows(rows * shape->d_k, dk, dk3, nullptr, dk, false, st)) != hipSuccess)
+            return device_status(e, "retention_chunkwise_bwd sum launch");
+        if (dv && (e = ret::launch_add_rows(rows * shape->d_v, dv, dv2, dv3, dv, false, st)) != hipSuccess)
+            return device_status(e, "retention_chunkwise_bwd sum launch");
+        if (dstate_in && (e = ret::launch_add_rows(st_bytes / 4, dstate_in, ds3, nullptr, dstate_in, false, st)) != hipSuccess)
+            return device_status(e, "retention_chunkwise_bwd sum launch");
+    } else {
+        if (rot) {
+            e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, st);
+            if (e != hipSuccess) return device_status(e, "retention_chunkwise_bwd rotation launch");
+        }
+        ret::BwdArgs b{};
+        b.base = base_args(shape, chunk, hc, ret::GnArgs{}, workspace, workspace_bytes, hip_stream);
+        b.q = q; b.k = k; b.v = v; b.dout = dout; b.state_in = state_in;
+        b.dq = dq; b.dk = dk; b.dv = dv; b.dstate_in = dstate_in;
+        e = ret::launch_chunkwise_bwd(b);
     }
-    ret::BwdArgs b{};
-    b.base = base_args(shape, chunk, hc, ret::GnArgs{}, workspace, workspace_bytes, hip_stream);
-    b.q = q; b.k = k; b.v = v; b.dout = dout; b.state_in = state_in;
-    b.dq = dq; b.dk = dk; b.dv = dv; b.dstate_in = dstate_in;
-    hipError_t e = ret::launch_chunkwise_bwd(b);
     // gradients at the rotated q and k, turned back by the inverse rotation (in place)
     const long rrows = (long)shape->batch * shape->heads * shape->seq_len;
     if (e == hipSuccess && rot && (dq || dk))

@@ -242,8 +242,8 @@ def test_rotation_shapes(lib):
 def test_rotation_workspace(lib):
     al = lambda n: (n + 255) // 256 * 256
     # a rotation stages the rotated q and k (input dtype, each copy 256-byte aligned) in front: one
-    # copy each for the backward and for fp32 inputs
-    for fn, C, i in ((R.RET_FN_CHUNKWISE_BWD, 64, R.RET_BF16), (R.RET_FN_CHUNKWISE, 64, R.RET_F32), (R.RET_FN_PARALLEL, 0, R.RET_F32)):
+    # copy each for fp32 inputs
+    for fn, C, i in ((R.RET_FN_CHUNKWISE_BWD, 64, R.RET_F32), (R.RET_FN_CHUNKWISE, 64, R.RET_F32), (R.RET_FN_PARALLEL, 0, R.RET_F32)):
         s = shape(i=i)
         base = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, 0)
         with_rot = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION)
@@ -261,6 +261,10 @@ def test_rotation_workspace(lib):
         assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION) == planes + 2 * o + st + base, fn
         assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION | R.RET_WS_GROUPNORM) == \
             planes + 3 * o + st + base, fn
+    # the bf16 backward likewise, with the partial gradients (dq, dk, two dv, dstate_in)
+    base = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s), 64, 0)
+    g = 2 * al(rows * s.d_k * 4) + 2 * al(rows * s.d_v * 4) + st
+    assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s), 64, R.RET_WS_ROTATION) == planes + g + base
     s = shape(N=1)
     assert lib.retention_workspace_bytes(R.RET_FN_RECURRENT_STEP, ctypes.byref(s), 0, R.RET_WS_ROTATION) == 2 * 256
     assert lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE, ctypes.byref(shape()), 64, 4) == ctypes.c_size_t(-1).value

@@ -486,36 +486,14 @@ def _rot_bf16(orc, x, base, off):
     return torch.from_numpy(orc.rotate(x, base, off)).to(torch.float32).to(torch.bfloat16)
 
 
-# Checks that fail the stated metric: the bf16 backward rounds the rotated q and k to bf16 once
-# (the forward forms keep them as high and low parts), and for this check the oracle run on the
-# rounded operands is already 2.3e-2 from the exact oracle (oracle against oracle, no GPU
-# arithmetic in it), so no kernel arithmetic can bring it under 2e-2. It is computed and printed,
-# and the test reports xfail when it exceeds the bound.
-ROT_BF16_FLOOR = {
-    "rotated backward bf16 (64,64) N=2048 C=128 offset 0 dv",
-}
-
-
-def rot_report(name, gpu, ref_rounded, ref_exact, tol, over=None):
-    """Asserted: the stated metric against the exact-rotation oracle (for the checks listed in
-    ROT_BF16_FLOOR: appended to `over` instead when above the bound). Printed: the error against the
+def rot_report(name, gpu, ref_rounded, ref_exact, tol):
+    """Asserted: the stated metric against the exact-rotation oracle. Printed: the error against the
     oracle run on the rotated operands rounded to bf16, and that reference's own distance from the
-    exact one (the part of the error that rounding the rotated operands accounts for)."""
+    exact one (what rounding the rotated operands once would cost)."""
     floor = rel_err(torch.from_numpy(np.asarray(ref_rounded)), ref_exact)
     print(f"  {name}: vs oracle on bf16-rounded rotated operands {rel_err(gpu, ref_rounded):.3e}; that oracle vs exact "
           f"{floor:.3e}", flush=True)
-    e = rel_err(gpu, ref_exact)
-    if over is not None and name in ROT_BF16_FLOOR:
-        print(f"  {name} (exact rotation): err {e:.3e} (bound {tol}){'  FAILS' if e > tol else ''}", flush=True)
-        if e > tol:
-            over.append(f"{name}: {e:.3e} > {tol} (rounded-operand oracle alone {floor:.3e})")
-        return
-    report(f"{name} (exact rotation)", e, tol)
-
-
-def xfail_if(over):
-    if over:
-        pytest.xfail("bf16 rotated operands: " + "; ".join(over))
+    report(f"{name} (exact rotation)", rel_err(gpu, ref_exact), tol)
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
@@ -555,16 +533,14 @@ def test_rotation_layer_6p7b(orc):
     ref, ref_s = orc.recurrent(_rot_bf16(orc, q, 10000.0, 0), _rot_bf16(orc, k, 10000.0, 0), v, gam)
     ex, ex_s = orc.recurrent_rot(q, k, v, gam, 10000.0, 0)
     ref_gn = orc.groupnorm(ref, w.eps)
-    over = []
     ex_gn = orc.groupnorm(ex, w.eps)
-    rot_report("rotated layer GN bf16 out", o, ref_gn, ex_gn, TOL["bf16"], over)
+    rot_report("rotated layer GN bf16 out", o, ref_gn, ex_gn, TOL["bf16"])
     # most of that is the bf16 storage of the normalised output; the kernels' own share is small
     floor = rel_err(torch.from_numpy(ex_gn).to(torch.bfloat16), ex_gn)
     report("rotated layer GN bf16 out above the bf16 storage floor", rel_err(o, ex_gn) - floor, 5e-3)
     rot_report("rotated layer state", s, ref_s, ex_s, TOL["bf16"])
     ref2, _ = orc.recurrent(_rot_bf16(orc, q, 10000.0, 5000), _rot_bf16(orc, k, 10000.0, 5000), v, gam, want_state=False)
-    rot_report("rotated layer fp32 out at offset 5000 (exact: the offset-0 oracle)", o2, ref2, ex, TOL["bf16"], over)
-    xfail_if(over)
+    rot_report("rotated layer fp32 out at offset 5000 (exact: the offset-0 oracle)", o2, ref2, ex, TOL["bf16"])
 
 
 def test_rotation_split_resume_and_decode(orc):
@@ -579,13 +555,11 @@ def test_rotation_split_resume_and_decode(orc):
                             rotation=R.Rotation(10000.0, 0))
     b, sb = R.chunkwise_fwd(qd[:, :, n1:N].contiguous(), kd[:, :, n1:N].contiguous(), vd[:, :, n1:N].contiguous(), gam, 256,
                             state_in=sa, rotation=R.Rotation(10000.0, n1))
-    over = []
-    rot_report("rotated split/resume out", torch.cat([a, b], dim=2), ref[:, :, :N], ex[:, :, :N], TOL["bf16"], over)
+    rot_report("rotated split/resume out", torch.cat([a, b], dim=2), ref[:, :, :N], ex[:, :, :N], TOL["bf16"])
     o = R.recurrent_step(qd[:, :, N].contiguous(), kd[:, :, N].contiguous(), vd[:, :, N].contiguous(), gam, sb,
                          rotation=R.Rotation(10000.0, N))
     rot_report("rotated decode after prefill out", o, ref[:, :, N], ex[:, :, N], TOL["bf16"])
     rot_report("rotated decode after prefill state", sb, ref_s, ex_s, TOL["bf16"])
-    xfail_if(over)
 
 
 # The decode workload (128 sequences x 16 heads, 256 x 512 fp32 states) at position 8192.
@@ -619,14 +593,12 @@ def test_rotation_backward(orc, dt, B, H, N, dk, dv, C, off):
         ref = (orc.rotate(gq, 10000.0, off, inverse=True), orc.rotate(gk, 10000.0, off, inverse=True), gv, gs)
     qd, kd, vd, dod, s0d = dev(q, k, v, dout, s0)
     got = R.chunkwise_bwd(qd, kd, vd, gam, dod, C, state_in=s0d, rotation=R.Rotation(10000.0, off))
-    over = []
     for i, name in enumerate(("dq", "dk", "dv", "dstate_in")):
         tag = f"rotated backward {dt} ({dk},{dv}) N={N} C={C} offset {off} {name}"
         if dt == "bf16":
-            rot_report(tag, got[i], ref[i], ex[i], TOL[dt], over)
+            rot_report(tag, got[i], ref[i], ex[i], TOL[dt])
         else:
             report(tag, rel_err(got[i], ex[i]), TOL[dt])
-    xfail_if(over)
 
 
 # ---------------------------------------------------------------------------------------------
