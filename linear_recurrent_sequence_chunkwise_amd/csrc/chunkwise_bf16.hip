@@ -844,9 +844,11 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 qa[2 * (ks & 1)] = mfma16(qf[ks], rfh[ks], qa[2 * (ks & 1)]);
                 qa[2 * (ks & 1) + 1] = mfma16(qf[ks], rfl[ks], qa[2 * (ks & 1) + 1]);
             }
-            // P V over every 32-key step of the chunk, in two chains: P is zero past this stage's
-            // keys (its rows are loaded as zero there), and the V rows there are finite (zeroed at
-            // the start, or rows of an earlier chunk), so the unrolled sum needs no branch
+            // P V over the 32-key steps up to this stage's own, in two chains. The first two steps
+            // run at every stage (their fragments are read with Q above): P is zero past the
+            // stage's keys (its rows are loaded as zero there) and the V rows there are finite
+            // (zeroed at the start, or rows of an earlier chunk); the later steps stop at the
+            // stage (measured 10-20 us faster at the N=8192 layer than running every step)
             f32x4 pa[2] = {mfma16(pf[0], vf[0], f32x4{0.f, 0.f, 0.f, 0.f}), mfma16(pf[1], vf[1], f32x4{0.f, 0.f, 0.f, 0.f})};
             if constexpr (PLO) {
 #pragma unroll
@@ -854,6 +856,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             }
 #pragma unroll
             for (int ks = 2; ks < SPC; ++ks) {
+                if (ks > s) break;  // P is zero past this stage's keys
                 const bf16x8 vk = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
                 pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
                 if constexpr (PLO) pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
