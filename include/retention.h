@@ -189,9 +189,12 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
  * With a rotation, dq and dk are the gradients with respect to the unrotated q and k: the
  * gradients at the rotated inputs turned back by the inverse rotation (its transpose).
  * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): the workspace of the forward
- * calls, the fp32 outputs of the column blocks and the blocks of state_in^T (bf16 inputs, whose
- * forwards read every operand in place); for fp32 inputs also time-reversed and block copies of
- * q, k, v and dout (plus the rotated q and k with RET_WS_ROTATION).
+ * calls and the blocks of state_in^T (bf16 inputs, whose forwards read every operand in place and
+ * add the two column blocks' rows of dq and dk into those outputs); for fp32 inputs also the fp32
+ * outputs of the column blocks and time-reversed and block copies of q, k, v and dout (plus the
+ * rotated q and k with RET_WS_ROTATION). With bf16 inputs and two column blocks, dq and dk are
+ * zeroed and then written by atomic fp32 adds: each element receives exactly two, so the result
+ * does not depend on their order.
  */
 ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
                                    const void* q, const void* k, const void* v,

@@ -12,12 +12,12 @@
 //   dstate_in = g U_0, U_0 = sum_n g^n q_n^T dout_n   = g * state_out of the dv forward
 // A forward whose contraction width (d_v here) has no kernel runs over s column blocks of width
 // d_v / s, whose outputs add (the scores are sums over the contraction index). The blocks are
-// stacked along the batch (B' = s B), so one launch covers them with s times the workgroups, and a
-// last pass sums the s outputs.
+// stacked along the batch (B' = s B), so one launch covers them with s times the workgroups.
 // bf16 inputs: the forwards read every operand in place (OpAddr: the time reversal, the row stride
-// and column block of a 512-wide operand, the source head of a stacked block) and write dv in
-// place; only the column-block sums pass through the workspace. fp32 inputs: the reversed and
-// stacked operands are copied into the workspace first.
+// and column block of a 512-wide operand, the source head of a stacked block) and write every
+// gradient in place; the s = 2 column blocks add their rows atomically into the zeroed gradient.
+// fp32 inputs: the reversed and stacked operands are copied into the workspace first, and a last
+// pass sums the s outputs.
 // The gradients come out in fp32; the forwards accumulate in fp32 with the operand precision of
 // the forward path (bf16 scores and bf16 hi + lo state and scaled values for bf16 inputs).
 #include "common.hpp"
@@ -114,6 +114,12 @@ __global__ __launch_bounds__(kCopyThreads) void sum_blocks_kernel(long BH, int N
     }
 }
 
+// x[0 .. n4*4) = 0, 16 bytes per thread (a kernel, so that a captured call records no memset node)
+__global__ __launch_bounds__(kCopyThreads) void zero_kernel(size_t n4, float* __restrict__ x) {
+    for (size_t i = blockIdx.x * (size_t)kCopyThreads + threadIdx.x; i < n4; i += (size_t)gridDim.x * kCopyThreads)
+        reinterpret_cast<float4*>(x)[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
 // x[bh][...] *= gamma_h for each of the per-head blocks of `per` elements
 __global__ __launch_bounds__(kCopyThreads) void scale_heads_kernel(long BH, int H, size_t per, HeadConsts hc, float* __restrict__ x) {
     const size_t total = (size_t)BH * per;
@@ -137,7 +143,7 @@ size_t fwd_workspace(int in_bf16, int B, int H, int N, int dk, int dv, int chunk
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace regions, each 256-aligned. With s column blocks, "stacked" buffers hold s copies one
-// after another (the batch of the stacked forward). bf16 inputs need only fwd, tmp and st.
+// after another (the batch of the stacked forward). bf16 inputs need only fwd and st.
 struct BwdLayout {
     int split;  // column blocks of d_v in the dq and dk forwards
     size_t fwd, rq, rk, rdo, sa, sb, sc, ta, tb, tc, tmp, st, total;
@@ -153,10 +159,8 @@ BwdLayout bwd_layout(int in_bf16, int B, int H, int N, int DK, int DV, int chunk
     if (f2 > fw) fw = f2;
     size_t o = 0;
     l.fwd = o; o += al(fw);
-    if (in_bf16) {                                      // operands read in place
-        const size_t t2 = s > 1 ? s * rows * (size_t)DK * 4 : 0;
-        l.rq = l.rk = l.rdo = l.sa = l.sb = l.sc = l.ta = l.tb = l.tc = o;
-        l.tmp = o; o += al(t2);                         // stacked fp32 outputs of the dq / dk forwards
+    if (in_bf16) {                                      // operands read in place, column blocks added in place
+        l.rq = l.rk = l.rdo = l.sa = l.sb = l.sc = l.ta = l.tb = l.tc = l.tmp = o;
         l.st = o; o += al((size_t)s * B * H * w * DK * 4);
         l.total = o;
         return l;
@@ -224,7 +228,8 @@ size_t chunkwise_bwd_workspace(int in_bf16, int B, int H, int N, int DK, int DV,
     return bwd_layout(in_bf16, B, H, N, DK, DV, chunk).total;
 }
 
-// bf16: every forward reads its operands in place.
+// bf16: every forward reads its operands in place. With two column blocks the stacked forward adds
+// both blocks' rows into the gradient (zeroed first): a + b in either order is the same fp32 value.
 hipError_t bwd_in_place(const BwdArgs& b) {
     const LaunchArgs& a = b.base;
     const BwdLayout l = bwd_layout(1, a.B, a.H, a.N, a.DK, a.DV, a.chunk);
@@ -232,13 +237,13 @@ hipError_t bwd_in_place(const BwdArgs& b) {
     const size_t rows = (size_t)BH * a.N;
     char* ws = reinterpret_cast<char*>(a.ws);
     void* fws = ws + l.fwd;
-    const size_t fwb = l.tmp - l.fwd;
-    float* tmp = reinterpret_cast<float*>(ws + l.tmp);
+    const size_t fwb = l.st - l.fwd;
     LaunchArgs stacked = a;  // the column blocks stacked along the batch
     stacked.B = s * a.B;
-    auto sum_blocks = [&](float* dst) {
-        const size_t work = rows * DK / 4;
-        hipLaunchKernelGGL(sum_blocks_kernel, dim3(grid_for(work)), dim3(kCopyThreads), 0, a.stream, (long)BH, a.N, DK, s, 0, tmp, dst);
+    const int acc = s > 1;
+    auto zero = [&](float* dst) {
+        const size_t n4 = rows * DK / 4;
+        hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(kCopyThreads), 0, a.stream, n4, dst);
     };
     hipError_t e;
     // dq = sum over column blocks j of forward(dout_j, v_j, k, (S_in^T)_j): dout and v rows DV apart,
@@ -253,13 +258,13 @@ hipError_t bwd_in_place(const BwdArgs& b) {
             }
             st = reinterpret_cast<const float*>(ws + l.st);
         }
-        e = forward(stacked, w, DK, b.dout, b.v, b.k, st, s > 1 ? tmp : b.dq, nullptr, fws, fwb, OpAddr{0, DV, w, BH});
+        if (acc) zero(b.dq);
+        e = forward(stacked, w, DK, b.dout, b.v, b.k, st, b.dq, nullptr, fws, fwb, OpAddr{0, DV, w, BH, acc});
         if (e != hipSuccess) return e;
-        if (s > 1) sum_blocks(b.dq);
     }
     // dv = rev(forward(rev k, rev q, rev dout)), written in place; its final state is U_0
     if (b.dv || b.dstate_in) {
-        e = forward(a, DK, DV, b.k, b.q, b.dout, nullptr, b.dv, b.dstate_in, fws, fwb, OpAddr{1, DK, 0, BH});
+        e = forward(a, DK, DV, b.k, b.q, b.dout, nullptr, b.dv, b.dstate_in, fws, fwb, OpAddr{1, DK, 0, BH, 0});
         if (e != hipSuccess) return e;
         if (b.dstate_in) {
             const size_t per = (size_t)DK * DV;
@@ -270,9 +275,9 @@ hipError_t bwd_in_place(const BwdArgs& b) {
     // dk = rev(sum over column blocks j of forward(rev v_j, rev dout_j, rev q)); the reversed
     // forward writes its rows back in time order
     if (b.dk) {
-        e = forward(stacked, w, DK, b.v, b.dout, b.q, nullptr, s > 1 ? tmp : b.dk, nullptr, fws, fwb, OpAddr{1, DV, w, BH});
+        if (acc) zero(b.dk);
+        e = forward(stacked, w, DK, b.v, b.dout, b.q, nullptr, b.dk, nullptr, fws, fwb, OpAddr{1, DV, w, BH, acc});
         if (e != hipSuccess) return e;
-        if (s > 1) sum_blocks(b.dk);
     }
     return hipGetLastError();
 }

@@ -125,6 +125,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_rsrc(bool pre, const bf1
 struct MainParams {
     int H, N, C, NS, nchunks, teams;
     int rev, ldqk, qcol_blk, srcBH;  // operand addressing (OpAddr, defaults resolved)
+    int out_acc;                     // fp32 out added atomically to the rows of head bh % srcBH
     int vsplit, vshift;              // value rows through VShift (vsplit = 0: plain)
     const bf16* q;
     const bf16* k;
@@ -363,12 +364,22 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
     };
 
     TOUT* out = reinterpret_cast<TOUT*>(p.out);
+    const int obh = p.out_acc ? bh % p.srcBH : bh;  // output head
     auto store_tile = [&](const f32x4& a, int g) __attribute__((always_inline)) {
         const int ci = g / SPC, s = g % SPC, c0 = ci * C;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = c0 + kST * s + 16 * rt_o + 4 * g4 + i;
-            if (r < N) out[((size_t)bh * N + row_of(r)) * DV + col0 + 16 * ct_o + c16] = from_float<TOUT>(a[i]);
+            if (r >= N) continue;
+            TOUT* o = out + ((size_t)obh * N + row_of(r)) * DV + col0 + 16 * ct_o + c16;
+            if constexpr (sizeof(TOUT) == 4) {
+                if (p.out_acc)
+                    __builtin_amdgcn_global_atomic_fadd_f32(o, a[i]);
+                else
+                    *o = a[i];
+            } else {
+                *o = from_float<TOUT>(a[i]);
+            }
         }
     };
 
@@ -796,8 +807,9 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     } else {
         // ---------------- output waves: 16 x 16 tile of each stage
         // output rows of this head through a buffer resource: stores past row N are dropped
+        const int obh = p.out_acc ? bh % p.srcBH : bh;  // output head
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(reinterpret_cast<TOUT*>(p.out) + (size_t)bh * N * DV), 0, (unsigned)((size_t)N * DV * sizeof(TOUT)), 0x00020000);
+            (void*)(reinterpret_cast<TOUT*>(p.out) + (size_t)obh * N * DV), 0, (unsigned)((size_t)N * DV * sizeof(TOUT)), 0x00020000);
         bf16x8 rfh[DK / 32], rfl[DK / 32];
         // g^(r+1) for this lane's rows r = 16 rt_o + 4 g4 + i of a stage
         float row_decay[4];
@@ -871,9 +883,12 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 const int j = kST * s + 16 * rt_o + 4 * g4 + i;  // row within the chunk
                 const float acc = qr[i] * (gs * row_decay[i]) + pv[i];
                 const unsigned off = (unsigned)((row_of(c0 + j) * DV + col0 + 16 * ct_o + c16) * (int)sizeof(TOUT));
-                if constexpr (sizeof(TOUT) == 4)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 0);
-                else
+                if constexpr (sizeof(TOUT) == 4) {
+                    if (p.out_acc)
+                        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc, ro, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 0);
+                } else
                     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_float<TOUT>(acc)), ro, off, 0, 0);
             }
             lds_barrier();  // stage g consumed; stage g+1 in LDS
@@ -1084,6 +1099,8 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.ldqk = a.addr.ldqk ? a.addr.ldqk : DK;
     mp.qcol_blk = a.addr.qcol_blk;
     mp.srcBH = a.addr.srcBH ? a.addr.srcBH : a.B * a.H;
+    mp.out_acc = a.addr.out_acc;
+    if (mp.out_acc && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
     mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;
     mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;

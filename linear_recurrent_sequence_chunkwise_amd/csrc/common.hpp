@@ -40,9 +40,12 @@ struct GnArgs {
 //   ldqk      elements between consecutive q rows (and k rows); 0: d_k
 //   qcol_blk  the workgroups of stacked head index bh read q and k from column (bh / srcBH) * qcol_blk
 //   srcBH     q, k and v of stacked head index bh are those of head bh % srcBH; 0: B * H
-// P, out and the states are laid out by the stacked head index.
+//   out_acc   fp32 out only: out rows of stacked head index bh are those of head bh % srcBH, and
+//             the forward adds its values to them atomically instead of storing them. out must
+//             start at zero; with two stacked blocks the result is order independent (a + b).
+// P, the states and (without out_acc) out are laid out by the stacked head index.
 struct OpAddr {
-    int rev, ldqk, qcol_blk, srcBH;
+    int rev, ldqk, qcol_blk, srcBH, out_acc;
 };
 
 // Value rows read with a shift (chunkwise kernels; residual linear attention): row t of the value
