@@ -163,14 +163,20 @@ hipError_t stage_rotation(const ret_shape* s, const ret::RotConsts& rc, const vo
 //     out = A(q_hi, k_hi) + A(q_hi, k_lo) + A(q_lo, k_hi)     (lo x lo, about 2^-16 relative, dropped)
 // with state_in entering the calls on q_hi and q_lo once each, and the final state the sum of the
 // states of the calls on k_hi and k_lo. The partial outputs are fp32; a GroupNorm (and gate)
-// follows their sum.
+// follows their sum. The chunkwise kernels add the second and third calls' rows into the first's
+// (OpAddr::out_acc: one atomic add per element and call, the calls in stream order, so the sum is
+// the same every time); the parallel kernel writes three partial outputs that a last pass adds.
 
-// Bytes of the partial results: the fp32 partial outputs (two; three when the sum cannot go to out
-// directly, i.e. a bf16 output or a GroupNorm after it) and the second partial state.
-size_t split_parts_bytes(const ret_shape* s, bool gn) {
+// Bytes of the partial results. Summed by a last pass (acc false): the fp32 partial outputs (two;
+// three when the sum cannot go to out directly, i.e. a bf16 output or a GroupNorm after it). Added
+// in place (acc true): one fp32 output when the sum cannot go to out directly, else none. Then the
+// second partial state.
+size_t split_parts_bytes(const ret_shape* s, bool gn, bool acc) {
     const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
     const size_t o = align256(rows * s->d_v * sizeof(float));
-    return ((s->out_dtype == RET_BF16 || gn) ? 3 : 2) * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float));
+    const bool staged = s->out_dtype == RET_BF16 || gn;
+    const size_t outs = acc ? (staged ? 1 : 0) : (staged ? 3 : 2);
+    return outs * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float));
 }
 
 // Rotated q and k of a bf16 forward call as high and low parts: four planes.
@@ -191,22 +197,47 @@ hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, co
 }
 
 // The three partial calls and the sums. a: the call (q and k unset; out, state_in, state_out, gn
-// and out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn) of workspace; launch: the
-// bf16 kernel family (chunkwise or parallel). An in-place state_in is read by the calls that need
-// it before the last call writes state_out.
+// and out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn, acc) of workspace;
+// launch: the bf16 kernel family (chunkwise, which adds the partial outputs in place (acc), or
+// parallel). An in-place state_in is read by the calls that need it before the last call writes
+// state_out.
 hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, const void* kh, const void* kl, char* parts,
-                     hipError_t (*launch)(const ret::LaunchArgs&)) {
+                     hipError_t (*launch)(const ret::LaunchArgs&), bool acc) {
     const size_t rows = (size_t)a.B * a.H * a.N;
     const size_t ob = align256(rows * a.DV * sizeof(float));
-    const bool staged = a.out_bf16 || a.gn.enabled;  // the sum goes through o1 in the workspace
-    float* o2 = reinterpret_cast<float*>(parts);
-    float* o3 = reinterpret_cast<float*>(parts + ob);
-    float* o1 = staged ? reinterpret_cast<float*>(parts + 2 * ob) : static_cast<float*>(a.out);
-    float* s2 = reinterpret_cast<float*>(parts + (staged ? 3 : 2) * ob);
+    const bool staged = a.out_bf16 || a.gn.enabled;  // the sum goes through the workspace
     ret::LaunchArgs c = a;
     c.out_bf16 = 0;
     c.gn = ret::GnArgs{};
     hipError_t e;
+    if (acc) {
+        // the first call stores its rows, the next two add theirs: ((lo,hi) + (hi,lo)) + (hi,hi)
+        float* o = staged ? reinterpret_cast<float*>(parts) : static_cast<float*>(a.out);
+        float* s2 = reinterpret_cast<float*>(parts + (staged ? ob : 0));
+        if (a.out) {
+            c.q = ql; c.k = kh; c.out = o; c.state_in = a.state_in; c.state_out = nullptr;
+            if ((e = launch(c)) != hipSuccess) return e;
+        }
+        c.addr.out_acc = a.out != nullptr;
+        if (a.out || a.state_out) {
+            c.q = qh; c.k = kl; c.out = a.out ? o : nullptr; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
+            if ((e = launch(c)) != hipSuccess) return e;
+        }
+        c.q = qh; c.k = kh; c.out = a.out ? o : nullptr; c.state_in = a.state_in; c.state_out = a.state_out;
+        if ((e = launch(c)) != hipSuccess) return e;
+        if (a.out && a.gn.enabled) {
+            if ((e = ret::launch_gn_rows((long)rows, a.H, a.N, a.DV, o, a.out, a.out_bf16, a.gn, a.stream)) != hipSuccess) return e;
+        } else if (a.out && staged) {
+            if ((e = ret::launch_add_rows(rows * a.DV, o, nullptr, nullptr, a.out, true, a.stream)) != hipSuccess) return e;
+        }
+        if (a.state_out)
+            return ret::launch_add_rows((size_t)a.B * a.H * a.DK * a.DV, a.state_out, s2, nullptr, a.state_out, false, a.stream);
+        return hipSuccess;
+    }
+    float* o2 = reinterpret_cast<float*>(parts);
+    float* o3 = reinterpret_cast<float*>(parts + ob);
+    float* o1 = staged ? reinterpret_cast<float*>(parts + 2 * ob) : static_cast<float*>(a.out);
+    float* s2 = reinterpret_cast<float*>(parts + (staged ? 3 : 2) * ob);
     if (a.out) {
         c.q = ql; c.k = kh; c.out = o3; c.state_in = a.state_in; c.state_out = nullptr;
         if ((e = launch(c)) != hipSuccess) return e;
@@ -298,7 +329,7 @@ size_t rla_ws(const ret_shape* s, int chunk, int fmap) {
     const size_t es = f32 ? sizeof(float) : elem_size(s->in_dtype);
     const size_t ops = (split ? 4 : 2) * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
     if (s->seq_len == 1) return ops;
-    return ops + (split ? split_parts_bytes(s, false) : 0) + chunkwise_ws(s, chunk, 0, 1);
+    return ops + (split ? split_parts_bytes(s, false, true) : 0) + chunkwise_ws(s, chunk, 0, 1);
 }
 
 size_t parallel_ws(const ret_shape* s, int gn) {
@@ -323,12 +354,12 @@ size_t bwd_rot_ws(const ret_shape* s, int chunk) {
 
 size_t chunkwise_rot_ws(const ret_shape* s, int chunk, bool gn, int want_out) {
     if (s->in_dtype != RET_BF16) return rotation_ws(s) + chunkwise_ws(s, chunk, gn, want_out);
-    return rotation_split_ws(s) + split_parts_bytes(s, gn) + chunkwise_ws(s, chunk, 0, want_out);
+    return rotation_split_ws(s) + split_parts_bytes(s, gn, true) + chunkwise_ws(s, chunk, 0, want_out);
 }
 
 size_t parallel_rot_ws(const ret_shape* s, bool gn) {
     if (s->in_dtype != RET_BF16) return rotation_ws(s) + parallel_ws(s, gn);
-    return rotation_split_ws(s) + split_parts_bytes(s, gn) + parallel_ws(s, 0);
+    return rotation_split_ws(s) + split_parts_bytes(s, gn, false) + parallel_ws(s, 0);
 }
 
 ret_status check_ws(size_t need, const void* ws, size_t wsb) {
@@ -477,10 +508,10 @@ int ret::chunkwise_fwd_entry(const ret_shape* shape, int32_t chunk, const void* 
         hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, st);
         if (e != hipSuccess) return device_status(e, "retention_chunkwise_fwd rotation launch");
         char* parts = static_cast<char*>(workspace);
-        const size_t pb = split_parts_bytes(shape, gn.enabled);
+        const size_t pb = split_parts_bytes(shape, gn.enabled, true);
         ret::LaunchArgs a = base_args(shape, chunk, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
         a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
-        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_chunkwise_bf16);
+        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_chunkwise_bf16, true);
         return device_status(e, "retention_chunkwise_fwd launch");
     }
     if (rot) {
@@ -666,10 +697,10 @@ ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const v
         hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
         if (e != hipSuccess) return device_status(e, "retention_parallel_fwd rotation launch");
         char* parts = static_cast<char*>(workspace);
-        const size_t pb = split_parts_bytes(shape, gn.enabled);
+        const size_t pb = split_parts_bytes(shape, gn.enabled, false);
         ret::LaunchArgs a = base_args(shape, 0, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
         a.v = v; a.out = out;
-        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_parallel_bf16);
+        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_parallel_bf16, false);
         return device_status(e, "retention_parallel_fwd launch");
     }
     if (rot) {
@@ -766,7 +797,7 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     }
     char* rest = w + nq * Aq + Av;  // after the operands
     char* parts = rest;             // split calls: partial outputs and state
-    if (split) rest += split_parts_bytes(shape, false);
+    if (split) rest += split_parts_bytes(shape, false, true);
     ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, rest,
                                   workspace_bytes - (size_t)(rest - w), hip_stream);
     if (f32feat) a.in_bf16 = 0;  // the fp32 decode kernel, on the fp32 features and value row
@@ -790,7 +821,7 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
         return device_status(a.in_bf16 ? ret::launch_chunkwise_bf16(a) : ret::launch_chunkwise_f32(a), "retention_rla_fwd launch");
     }
     a.state_in = state_in; a.state_out = state_out;
-    return device_status(run_split(a, r.qo, r.qlo, r.ko, r.klo, parts, ret::launch_chunkwise_bf16), "retention_rla_fwd launch");
+    return device_status(run_split(a, r.qo, r.qlo, r.ko, r.klo, parts, ret::launch_chunkwise_bf16, true), "retention_rla_fwd launch");
 }
 
 }  // extern "C"

@@ -290,11 +290,12 @@ __global__ __launch_bounds__(256) void rla_prepare_kernel(int BH, int N, int dk,
     }
 }
 
-// out = a + b + c, four values per thread and step (c may be null; out may alias a).
+// out = a + b + c, four values per thread and step (b and c may be null; out may alias a).
 template <typename TOUT>
 __global__ __launch_bounds__(256) void add_rows_kernel(size_t n4, const float* a, const float* b, const float* c, TOUT* out) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
-        f32x4 x = reinterpret_cast<const f32x4*>(a)[i] + reinterpret_cast<const f32x4*>(b)[i];
+        f32x4 x = reinterpret_cast<const f32x4*>(a)[i];
+        if (b) x += reinterpret_cast<const f32x4*>(b)[i];
         if (c) x += reinterpret_cast<const f32x4*>(c)[i];
         if constexpr (sizeof(TOUT) == 4) {
             reinterpret_cast<f32x4*>(out)[i] = x;
