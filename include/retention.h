@@ -114,7 +114,9 @@ typedef struct {
  * output by up to 2.4e-2 of its RMS, so the chunkwise and parallel forms and the backward stage
  * them as bf16 high and low parts and run on (q_hi, k_hi), (q_hi, k_lo) and (q_lo, k_hi) (the
  * lo x lo term, about 2^-16 relative, is dropped); the chunkwise calls add their fp32 rows in
- * place, the parallel and backward calls keep fp32 partial results in the workspace and add them.
+ * place (where the chunk kernel takes q as two parts, at chunk 64 and 128 and at chunk 256 with
+ * d_k = 64, (q_hi, k_hi) and (q_lo, k_hi) are one call on q_hi + q_lo), the parallel and backward
+ * calls keep fp32 partial results in the workspace and add them.
  * The decode step rounds the turned q and k to bf16 once.
  * Angles: the per-pair frequency theta_i / pi and the offset's phase are formed on the host in
  * double precision; the device adds n times the frequency with an exact two-product and
@@ -239,9 +241,10 @@ ret_status retention_chunkwise_bwd(const ret_shape* shape, int32_t chunk,
  * keep more than bf16 (the softmax puts most of a row's weight on a few features, whose bf16
  * rounding alone would move the output by 2e-2 to 5e-2 of its RMS): a segment (N > 1) writes their
  * bf16 high and low parts and runs the bf16 chunkwise kernels on (q_hi, k_hi), (q_hi, k_lo) and
- * (q_lo, k_hi): the second and third add their fp32 rows into the first's (into out for an fp32
- * output, else through one fp32 buffer in the workspace) and the second partial state is added
- * after them; a decode step (N = 1) takes the features and the value row in fp32.
+ * (q_lo, k_hi) (the first and last as one call on q_hi + q_lo where the chunk kernel takes q as
+ * two parts): the later calls add their fp32 rows into the first's (into out for an fp32 output,
+ * else through one fp32 buffer in the workspace) and the second partial state is added after
+ * them; a decode step (N = 1) takes the features and the value row in fp32.
  */
 ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t window, int32_t feature_map,
                              const void* q, const void* k, const void* v,

@@ -196,11 +196,12 @@ hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, co
     return hipSuccess;
 }
 
-// The three partial calls and the sums. a: the call (q and k unset; out, state_in, state_out, gn
-// and out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn, acc) of workspace;
-// launch: the bf16 kernel family (chunkwise, which adds the partial outputs in place (acc), or
-// parallel). An in-place state_in is read by the calls that need it before the last call writes
-// state_out.
+// The partial calls and the sums. a: the call (q and k unset; out, state_in, state_out, gn and
+// out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn, acc) of workspace; launch: the
+// bf16 kernel family (chunkwise, which adds the partial outputs in place (acc), or parallel). Where
+// the chunkwise kernel takes q as two parts, A(q_hi, k_hi) + A(q_lo, k_hi) is one call on
+// (q_hi + q_lo, k_hi). An in-place state_in is read by the calls that need it before the last call
+// writes state_out.
 hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, const void* kh, const void* kl, char* parts,
                      hipError_t (*launch)(const ret::LaunchArgs&), bool acc) {
     const size_t rows = (size_t)a.B * a.H * a.N;
@@ -211,20 +212,31 @@ hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, c
     c.gn = ret::GnArgs{};
     hipError_t e;
     if (acc) {
-        // the first call stores its rows, the next two add theirs: ((lo,hi) + (hi,lo)) + (hi,hi)
         float* o = staged ? reinterpret_cast<float*>(parts) : static_cast<float*>(a.out);
         float* s2 = reinterpret_cast<float*>(parts + (staged ? ob : 0));
-        if (a.out) {
-            c.q = ql; c.k = kh; c.out = o; c.state_in = a.state_in; c.state_out = nullptr;
+        if (a.out && ret::chunkwise_bf16_qlo_supported(a.DK, a.chunk)) {
+            // two calls: (q_hi, k_lo) stores its rows and its state; (q_hi + q_lo, k_hi), on the
+            // kernel that takes q as two parts, adds its rows and writes the state from state_in
+            c.q = qh; c.k = kl; c.out = o; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
+            if ((e = launch(c)) != hipSuccess) return e;
+            c.addr.out_acc = 1;
+            c.q = qh; c.qlo = ql; c.k = kh; c.state_in = a.state_in; c.state_out = a.state_out;
+            if ((e = launch(c)) != hipSuccess) return e;
+        } else {
+            // three calls: the first stores its rows, the next two add theirs:
+            // ((q_lo, k_hi) + (q_hi, k_lo)) + (q_hi, k_hi)
+            if (a.out) {
+                c.q = ql; c.k = kh; c.out = o; c.state_in = a.state_in; c.state_out = nullptr;
+                if ((e = launch(c)) != hipSuccess) return e;
+            }
+            c.addr.out_acc = a.out != nullptr;
+            if (a.out || a.state_out) {
+                c.q = qh; c.k = kl; c.out = a.out ? o : nullptr; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
+                if ((e = launch(c)) != hipSuccess) return e;
+            }
+            c.q = qh; c.k = kh; c.out = a.out ? o : nullptr; c.state_in = a.state_in; c.state_out = a.state_out;
             if ((e = launch(c)) != hipSuccess) return e;
         }
-        c.addr.out_acc = a.out != nullptr;
-        if (a.out || a.state_out) {
-            c.q = qh; c.k = kl; c.out = a.out ? o : nullptr; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
-            if ((e = launch(c)) != hipSuccess) return e;
-        }
-        c.q = qh; c.k = kh; c.out = a.out ? o : nullptr; c.state_in = a.state_in; c.state_out = a.state_out;
-        if ((e = launch(c)) != hipSuccess) return e;
         if (a.out && a.gn.enabled) {
             if ((e = ret::launch_gn_rows((long)rows, a.H, a.N, a.DV, o, a.out, a.out_bf16, a.gn, a.stream)) != hipSuccess) return e;
         } else if (a.out && staged) {

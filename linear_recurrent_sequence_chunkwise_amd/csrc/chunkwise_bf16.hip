@@ -38,7 +38,8 @@ constexpr int kST = 32;    // tokens per pipeline stage
 
 // ---------------------------------------------------------------------------------------------
 // P = (Q K^T) (.) D for every chunk, into the workspace as [B*H][nchunks][C][C] bf16, its high
-// part in P and, when Plo is given, the low part (P - hi, rounded) in Plo, same layout. Grid
+// part in P and, when Plo is given, the low part (P - hi, rounded) in Plo, same layout. With qlo
+// (the low part of a q that bf16 does not hold) Q K^T is q K^T + qlo K^T, each in fp32. Grid
 // (nchunks, B*H), 256 threads. The MFMAs compute P^T = K Q^T per 16 x 16 tile so that each lane
 // ends with 4 consecutive keys of one row (one 8-byte store). K rows go through LDS in 128-key
 // blocks (buffer-to-LDS loads, swizzled rows); each wave reads the Q fragments of its row tile
@@ -47,7 +48,8 @@ constexpr int kST = 32;    // tokens per pipeline stage
 // Waves take row tiles in mirrored pairs (t, T-1-t) so that the causal work is balanced.
 template <int DK>
 __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
-                                                           const bf16* __restrict__ k, bf16* __restrict__ P, bf16* __restrict__ Plo,
+                                                           const bf16* __restrict__ qlo, const bf16* __restrict__ k,
+                                                           bf16* __restrict__ P, bf16* __restrict__ Plo,
                                                            HeadConsts hc, int rev, int ldqk, int qcol_blk, int srcBH) {
     constexpr int KB = 128;       // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     const size_t qbase = (size_t)(bh % srcBH) * N * ldqk + (size_t)(bh / srcBH) * qcol_blk;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + qbase), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rql = __builtin_amdgcn_make_buffer_rsrc((void*)((qlo ? qlo : q) + qbase), 0, q_bytes, 0x00020000);
     auto row_of = [&](int t) __attribute__((always_inline)) { return rev ? N - 1 - t : t; };
     bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
     bf16* Plc = Plo ? Plo + ((size_t)bh * nchunks + chunk) * (size_t)C * C : nullptr;
@@ -89,11 +92,26 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
                 const unsigned off = (unsigned)((row_of(c0 + 16 * t + c16) * ldqk + 32 * ks + 8 * g4) * 2);
                 qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
             }
+            bf16x8 qlf[DK / 32];
+            if (qlo) {
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const unsigned off = (unsigned)((row_of(c0 + 16 * t + c16) * ldqk + 32 * ks + 8 * g4) * 2);
+                    qlf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rql, off, 0, 0));
+                }
+            }
             for (int kt = kb0 / 16; kt <= last; ++kt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks)
                     acc = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qf[ks], acc);
+                if (qlo) {
+                    f32x4 al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < DK / 32; ++ks)
+                        al = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qlf[ks], al);
+                    acc += al;
+                }
                 // lane: row 16t + c16, keys 16kt + 4g4 + i
                 const int row = 16 * t + c16;
                 bf16x4 o, ol;
@@ -128,6 +146,7 @@ struct MainParams {
     int out_acc;                     // fp32 out added atomically to the rows of head bh % srcBH
     int vsplit, vshift;              // value rows through VShift (vsplit = 0: plain)
     const bf16* q;
+    const bf16* qlo;  // low part of q (same addressing), added to Q R and to the scores; or null
     const bf16* k;
     const bf16* v;
     const bf16* vpre;
@@ -491,8 +510,10 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 // Q, K, P and R^T tiles are swizzled (SwzTile). At each chunk end the state waves write R^T as bf16
 // hi + lo into the Q/K region of the buffer that the finished stage used; the output waves read
 // their fragments from it at the next stage, before the loaders refill that buffer. PLO: P comes
-// as bf16 hi + lo, both parts loaded, P V on both.
-template <int DK, int C, bool PLO = false>
+// as bf16 hi + lo, both parts loaded, P V on both. QLO: q comes as two bf16 parts (q + qlo, the
+// high and low parts of an operand that bf16 does not hold), both loaded, Q R on both (qlo times
+// the high part of R; the scores kernel forms P from both parts).
+template <int DK, int C, bool PLO = false, bool QLO = false>
 struct WsGeom {
     static constexpr int QRB = DK * 2;            // bytes per Q / K tile row
     static constexpr int PRB = C * 2;             // bytes per P tile row
@@ -501,7 +522,8 @@ struct WsGeom {
     static constexpr size_t P_BYTES = (size_t)kST * PRB;
     static constexpr size_t Z_BYTES = (size_t)kST * LV * 2;
     static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_PL = OFF_P + P_BYTES;
-    static constexpr size_t OFF_ZH = OFF_PL + (PLO ? P_BYTES : 0), OFF_ZL = OFF_ZH + Z_BYTES;
+    static constexpr size_t OFF_QL = OFF_PL + (PLO ? P_BYTES : 0);
+    static constexpr size_t OFF_ZH = OFF_QL + (QLO ? Q_BYTES : 0), OFF_ZL = OFF_ZH + Z_BYTES;
     static constexpr size_t BUF = OFF_ZL + Z_BYTES;  // one stage buffer
     // V rows in a ring of C / 32 + 1 blocks of 32 rows: block s of chunk ci sits in slot
     // (ci * C / 32 + s) mod (C / 32 + 1), so during a chunk's last stage the state waves store the
@@ -519,7 +541,7 @@ struct WsGeom {
     static_assert((size_t)kW * QRB == Q_BYTES, "R^T hi / lo fill the Q / K regions");
     static_assert(Q_BYTES % 4096 == 0 && P_BYTES % 4096 == 0, "tiles are split over four loader waves in kilobytes");
     static constexpr int Q_KB = (int)(Q_BYTES / 1024), P_KB = (int)(P_BYTES / 1024);
-    static constexpr int NDMA = (2 * Q_KB + (PLO ? 2 : 1) * P_KB) / 4;  // buffer-to-LDS loads per stage and loader wave
+    static constexpr int NDMA = ((QLO ? 3 : 2) * Q_KB + (PLO ? 2 : 1) * P_KB) / 4;  // buffer-to-LDS loads per stage and loader wave
     static_assert(NDMA + 2 <= 63, "the loads of one stage must fit the vmcnt counter");
 };
 
@@ -538,9 +560,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int C, typename TOUT, bool VSH, bool PLO>
+template <int DK, int C, typename TOUT, bool VSH, bool PLO, bool QLO = false>
 __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
-    using G = WsGeom<DK, C, PLO>;
+    using G = WsGeom<DK, C, PLO, QLO>;
     constexpr int NB = G::NB;
     constexpr int RTR = DK / 64;  // 16-row R tiles per state wave
     constexpr int SPC = C / kST;
@@ -584,6 +606,8 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
         const int lw = __builtin_amdgcn_readfirstlane(w - 8);  // wave-uniform: one buffer resource per wave
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qbase), 0, q_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qbase), 0, q_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rql =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((QLO ? p.qlo : p.q) + qbase), 0, q_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rp =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
@@ -604,6 +628,8 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 const unsigned off = (unsigned)((row_of(tok0 + r) * ldqk + 8 * c) * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(bq + 1024 * j), 16, off, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(bq + G::OFF_K + 1024 * j), 16, off, 0, 0, 0);
+                if constexpr (QLO)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rql, (__attribute__((address_space(3))) void*)(bq + G::OFF_QL + 1024 * j), 16, off, 0, 0, 0);
             }
             const int per_row = 4 * (s + 1);
             const unsigned base = (unsigned)((ci * C + kST * s) * C);
@@ -856,6 +882,12 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 qa[2 * (ks & 1)] = mfma16(qf[ks], rfh[ks], qa[2 * (ks & 1)]);
                 qa[2 * (ks & 1) + 1] = mfma16(qf[ks], rfl[ks], qa[2 * (ks & 1) + 1]);
             }
+            if constexpr (QLO) {
+                const char* Qls = buf(g) + G::OFF_QL;
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks)
+                    qa[2 * (ks & 1) + 1] = mfma16(frag_rowmajor_swz<G::QRB>(Qls, 16 * rt_o, 32 * ks, lane), rfh[ks], qa[2 * (ks & 1) + 1]);
+            }
             // P V over the 32-key steps up to this stage's own, in two chains. The first two steps
             // run at every stage (their fragments are read with Q above): P is zero past the
             // stage's keys (its rows are loaded as zero there) and the V rows there are finite
@@ -1012,6 +1044,9 @@ template <int DK, int C, bool WANT_OUT>
 constexpr bool use_ws() { return WANT_OUT && C <= 256 && WsGeom<DK, C, true>::BYTES <= kLdsBytes; }
 template <int DK, int C>
 constexpr bool p_lo() { return use_ws<DK, C, true>() || MainGeom<DK, C, true>::BYTES <= kLdsBytes; }
+// whether the warp-specialised kernel takes q as two parts (q + qlo) at (DK, C)
+template <int DK, int C>
+constexpr bool q_lo_fits() { return C <= 256 && WsGeom<DK, C, true, true>::BYTES <= kLdsBytes; }
 
 template <int DK>
 bool p_lo_dk(int C) {
@@ -1025,15 +1060,16 @@ bool p_lo_dk(int C) {
 // whether a call with an output at (DK, C) keeps the low part of P
 bool p_lo_used(int DK, int C) { return DK == 64 ? p_lo_dk<64>(C) : p_lo_dk<256>(C); }
 
-template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH>
+template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH, bool QLO = false>
 hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
     constexpr bool ws = use_ws<DK, C, WANT_OUT>();
     constexpr bool plo = WANT_OUT && p_lo<DK, C>();
+    static_assert(!QLO || (ws && q_lo_fits<DK, C>()), "q as two parts on the warp-specialised kernel only");
     const void* kern;
-    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true>);
+    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true, QLO>);
     else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT, VSH, plo>);
     size_t dyn;
-    if constexpr (ws) dyn = WsGeom<DK, C, true>::BYTES;
+    if constexpr (ws) dyn = WsGeom<DK, C, true, QLO>::BYTES;
     else dyn = MainGeom<DK, C, plo>::BYTES;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
@@ -1043,9 +1079,16 @@ hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
     return hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(ws ? 768 : kThreads), args, dyn, a.stream);
 }
 
-// value rows through VShift only in the instantiations that need it
+// value rows through VShift, and q as two parts (fp32 output only), only in the instantiations
+// that need them
 template <int DK, int C, typename TOUT, bool WANT_OUT>
 hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
+    if constexpr (WANT_OUT && sizeof(TOUT) == 4 && use_ws<DK, C, WANT_OUT>() && q_lo_fits<DK, C>()) {
+        if (mp.qlo)
+            return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true, true>(a, mp)
+                             : launch_main_v<DK, C, TOUT, WANT_OUT, false, true>(a, mp);
+    }
+    if (mp.qlo) return hipErrorInvalidValue;
     return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true>(a, mp) : launch_main_v<DK, C, TOUT, WANT_OUT, false>(a, mp);
 }
 
@@ -1101,7 +1144,9 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.srcBH = a.addr.srcBH ? a.addr.srcBH : a.B * a.H;
     mp.out_acc = a.addr.out_acc;
     if (mp.out_acc && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
-    mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
+    if (a.qlo && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
+    mp.q = (const bf16*)a.q;
+    mp.qlo = (const bf16*)a.qlo; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;
     mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;
     mp.Plo = plo ? mp.P + (size_t)a.B * a.H * nchunks * C * C : nullptr;
@@ -1109,7 +1154,7 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
 
     hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C,
-                       nchunks, mp.q, mp.k, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), a.hc, mp.rev, mp.ldqk,
+                       nchunks, mp.q, mp.qlo, mp.k, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), a.hc, mp.rev, mp.ldqk,
                        mp.qcol_blk, mp.srcBH);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1171,6 +1216,17 @@ hipError_t launch_gn_rows(long rows, int H, int N, int DV, const float* pre, voi
         hipLaunchKernelGGL(gn_rows_kernel<float>, grid, dim3(256), 0, stream, rows, H, N, DV, pre, static_cast<float*>(y), gn);
     return hipGetLastError();
 }
+
+template <int DK>
+bool q_lo_dk(int C) {
+    switch (C) {
+        case 64: return q_lo_fits<DK, 64>();
+        case 128: return q_lo_fits<DK, 128>();
+        case 256: return q_lo_fits<DK, 256>();
+        default: return false;
+    }
+}
+bool chunkwise_bf16_qlo_supported(int DK, int C) { return DK == 64 ? q_lo_dk<64>(C) : DK == 256 && q_lo_dk<256>(C); }
 
 hipError_t launch_chunkwise_bf16(const LaunchArgs& a) {
     if (a.DK == 64) return a.out_bf16 ? launch_dk<64, bf16>(a) : launch_dk<64, float>(a);

@@ -63,6 +63,7 @@ struct LaunchArgs {
     OpAddr addr;  // bf16 chunkwise only
     VShift vs;    // chunkwise only
     const void* q;
+    const void* qlo;  // bf16 chunkwise with an fp32 output only: low part of q, or null
     const void* k;
     const void* v;
     void* out;              // may be null (chunkwise state-only)
@@ -246,6 +247,10 @@ size_t chunkwise_bf16_workspace(int B, int H, int N, int DK, int DV, int chunk, 
 size_t chunkwise_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16);
 size_t parallel_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16);
 bool chunkwise_bf16_supported(int DK, int DV, int chunk);
+// Whether a bf16 chunkwise call with an fp32 output and no GroupNorm takes q as two parts
+// (LaunchArgs::qlo) at this d_k and chunk: the warp-specialised kernel, when its stage buffers with
+// the second q plane fit in LDS.
+bool chunkwise_bf16_qlo_supported(int DK, int chunk);
 // The segmented bf16 chunkwise kernels (chunk_seg.hip): plain operands, an output, d_k 64 or 256,
 // chunk 64 or 128, d_v a multiple of 64. U: the segment states in the workspace; out: the call's
 // output, or fp32 pre-norm rows when out_f32 (a GroupNorm pass follows).

@@ -497,7 +497,7 @@ def rot_report(name, gpu, ref_rounded, ref_exact, tol):
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
-@pytest.mark.parametrize("N,C,off", [(37, 64, 0), (700, 256, 1000), (1100, 512, 123457)])
+@pytest.mark.parametrize("N,C,off", [(37, 64, 0), (900, 128, 77), (700, 256, 1000), (1100, 512, 123457)])
 def test_rotation_bf16_chunkwise(orc, dk, dv, N, C, off):
     B, H = 1, 4
     q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=610 + N + dk)
@@ -629,7 +629,7 @@ def test_rla_fp32(orc, fmap, w, C, plen):
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
-@pytest.mark.parametrize("N,C,w", [(37, 64, 0), (700, 256, 63), (1100, 512, 512)])
+@pytest.mark.parametrize("N,C,w", [(37, 64, 0), (900, 128, 100), (700, 256, 63), (1100, 512, 512)])
 def test_rla_bf16(orc, dk, dv, N, C, w):
     B, H = 1, 4
     q, k, v, kp, vp = _rla_inputs(B, H, N, dk, dv, "bf16", 710 + N + dk, P=w + 1)
