@@ -422,6 +422,30 @@ def test_chunkwise_backward(orc, dt, B, H, N, dk, dv, C):
     assert got0[1] is None and got0[2] is None
 
 
+# Outputs built by atomic fp32 adds are the same on every call: the backward's two column blocks
+# add exactly twice onto a zeroed gradient (a + b = b + a), and the split passes of rotated and
+# softmax-feature calls add once each, in stream order. Each call runs three times on the same
+# inputs and must match bit for bit (and the oracle, as elsewhere).
+def test_atomic_accumulation_is_deterministic(orc):
+    B, H, N, dk, dv, C = 1, 4, 1000, 256, 512, 128
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=590)
+    dout = _dout((B, H, N, dv), q.dtype, 591)
+    s0 = I.make_state(B, H, dk, dv, seed=592, scale=0.02)
+    gam = I.multiscale_gammas(H)
+    qd, kd, vd, dod, s0d = dev(q, k, v, dout, s0)
+    runs = [R.chunkwise_bwd(qd, kd, vd, gam, dod, C, state_in=s0d, want=("dq", "dk")) for _ in range(3)]
+    for name, i in (("dq", 0), ("dk", 1)):
+        assert all(torch.equal(r[i], runs[0][i]) for r in runs[1:]), f"backward {name} differs between calls"
+    rot = R.Rotation(10000.0, 321)
+    fw = [R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, rotation=rot) for _ in range(3)]
+    assert all(torch.equal(o, fw[0][0]) and torch.equal(st, fw[0][1]) for o, st in fw[1:]), "rotated forward differs"
+    rl = [R.rla_fwd(qd, kd, vd, 100, C) for _ in range(3)]
+    assert all(torch.equal(o, rl[0][0]) and torch.equal(st, rl[0][1]) for o, st in rl[1:]), "rla forward differs"
+    ref = orc.recurrent_bwd(q, k, v, gam, dout, state_in=s0)
+    report("repeated backward dq", rel_err(runs[0][0], ref[0]), TOL["bf16"])
+    report("repeated backward dk", rel_err(runs[0][1], ref[1]), TOL["bf16"])
+
+
 # The N=8192 layer (B=1, H=16, d_k=256, d_v=512, chunk 128): the oracle on heads 0 and 15, and on
 # every head the adjoint identities <dout, forward(dq-direction)> = <dq, direction> (the output is
 # linear in q, in k and in v), through the GPU forward.
