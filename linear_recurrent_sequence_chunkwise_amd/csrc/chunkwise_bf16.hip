@@ -603,6 +603,9 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
     // end of the stage, and one more after a chunk end that is not the last stage.
     if (w >= 8) {
         // ---------------- loader waves
+        // first claim on instruction issue in their SIMD, so that each stage's loads go out as soon
+        // as the buffer is free (measured 5-7 us faster at the N=8192 layer than equal priorities)
+        __builtin_amdgcn_s_setprio(3);
         const int lw = __builtin_amdgcn_readfirstlane(w - 8);  // wave-uniform: one buffer resource per wave
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qbase), 0, q_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + qbase), 0, q_bytes, 0x00020000);
