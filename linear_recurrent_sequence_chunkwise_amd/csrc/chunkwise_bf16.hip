@@ -503,8 +503,10 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 //                so without it every slice would wait for the same lines to come from memory. The
 //                loader waves never read LDS, so the compiler adds no waits for these loads.
 //   state waves  (w = 4..7): per 32-token stage g, accumulate R += K^T (V (.) zeta) for their d_k
-//                quarter of R (fp32, scaled by g^L at each chunk start), and write stage g+1's V rows
-//                and V (.) zeta as bf16 hi + lo (V loaded into registers two stages ahead).
+//                quarter of R (fp32, scaled by g^L at each chunk start), V (.) zeta formed as bf16
+//                hi + lo in registers from the stage's V block, and write stage g+1's V rows into
+//                the V ring (V loaded into registers two stages ahead). No V (.) zeta planes in the
+//                stage buffers leaves room for three buffers at d_k = 256, chunk 128.
 //   output waves (w = 0..3): per stage, the 16 x 16 tile (rows 16*(w>>1), columns 16*(w&1)) of
 //                g^(j+1) Q R + P V, with R^T (hi + lo) held in registers for the chunk, and its store.
 // Q, K, P and R^T tiles are swizzled (SwzTile). At each chunk end the state waves write R^T as bf16
@@ -520,11 +522,9 @@ struct WsGeom {
     static constexpr int LV = kW;                 // V and V (.) zeta rows: 32 bf16, dense
     static constexpr size_t Q_BYTES = (size_t)kST * QRB;
     static constexpr size_t P_BYTES = (size_t)kST * PRB;
-    static constexpr size_t Z_BYTES = (size_t)kST * LV * 2;
     static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_PL = OFF_P + P_BYTES;
     static constexpr size_t OFF_QL = OFF_PL + (PLO ? P_BYTES : 0);
-    static constexpr size_t OFF_ZH = OFF_QL + (QLO ? Q_BYTES : 0), OFF_ZL = OFF_ZH + Z_BYTES;
-    static constexpr size_t BUF = OFF_ZL + Z_BYTES;  // one stage buffer
+    static constexpr size_t BUF = OFF_QL + (QLO ? Q_BYTES : 0);  // one stage buffer
     // V rows in a ring of C / 32 + 1 blocks of 32 rows: block s of chunk ci sits in slot
     // (ci * C / 32 + s) mod (C / 32 + 1), so during a chunk's last stage the state waves store the
     // next chunk's first rows into the one slot that the chunk's own blocks leave free
@@ -725,23 +725,9 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             }
         };
         auto store_v = [&](const bf16x8& v, int g) __attribute__((always_inline)) {
-            const int ci = g / SPC, s = g % SPC;
-            const int L = min(C, N - ci * C);
             if (st < kST * 4) {
                 const int row = st >> 2, sg = st & 3;
-                *reinterpret_cast<bf16x8*>(Vblk(vfirst(ci), s) + row * G::LV + 8 * sg) = v;
-                const int t = kST * s + row;
-                const float z = t < L ? decay_pow(l2g, (float)(L - 1 - t)) : 0.f;
-                bf16x8 hi, lo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bf16 a, c;
-                    split_hi_lo((float)v[e] * z, a, c);
-                    hi[e] = a;
-                    lo[e] = c;
-                }
-                *reinterpret_cast<bf16x8*>(buf(g) + G::OFF_ZH + (row * G::LV + 8 * sg) * 2) = hi;
-                *reinterpret_cast<bf16x8*>(buf(g) + G::OFF_ZL + (row * G::LV + 8 * sg) * 2) = lo;
+                *reinterpret_cast<bf16x8*>(Vblk(vfirst(g / SPC), g % SPC) + row * G::LV + 8 * sg) = v;
             }
         };
         f32x4 accR[RTR][2];
@@ -793,15 +779,33 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             if (s == 0) lds_barrier();
             const char* Ks = buf(g) + G::OFF_K;
             bf16x8 bhi[2], blo[2], ak[RTR];
+            {
+                // V (.) zeta of this stage as bf16 hi + lo, formed in registers from the stage's V
+                // block: this lane's tokens t = 32 s + 8 g4 + j, zeta = g^(L-1-t) (0 past the chunk)
+                const int L = min(C, N - (g / SPC) * C);
+                float z[8];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                bhi[ct] = lds_frag_kmajor(reinterpret_cast<const bf16*>(buf(g) + G::OFF_ZH), G::LV, 0, 16 * ct, lane);
-                blo[ct] = lds_frag_kmajor(reinterpret_cast<const bf16*>(buf(g) + G::OFF_ZL), G::LV, 0, 16 * ct, lane);
+                for (int j = 0; j < 8; ++j) {
+                    const int t = kST * s + 8 * g4 + j;
+                    z[j] = t < L ? decay_pow(l2g, (float)(L - 1 - t)) : 0.f;
+                }
+                const bf16* Vb = Vblk(vfirst(g / SPC), s);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const bf16x8 vv = lds_frag_kmajor(Vb, G::LV, 0, 16 * ct, lane);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        bf16 a, c;
+                        split_hi_lo((float)vv[j] * z[j], a, c);
+                        bhi[ct][j] = a;
+                        blo[ct][j] = c;
+                    }
+                }
             }
 #pragma unroll
             for (int rt = 0; rt < RTR; ++rt) ak[rt] = lds_frag_kmajor_swz<G::QRB>(Ks, 0, wl * (DK / 4) + 16 * rt, lane);
             if (g + 1 < total) {
-                store_v(vn, g + 1);  // into Vc and stage g+1's buffer (its Q/K/P come from the loader)
+                store_v(vn, g + 1);  // into the V ring (stage g+1's Q/K/P come from the loader)
                 vn = load_v(g + 3);
             }
 #pragma unroll
