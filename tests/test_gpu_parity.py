@@ -198,12 +198,12 @@ def test_groupnorm_gate_chunk_kernels(orc):
 # The swish gate after GroupNorm, out = swish(g) * GN(o), through every kernel that applies
 # GroupNorm: the bf16 chunkwise pass (chunks 128 and 512), the bf16 parallel kernel, the fp32
 # chunkwise and parallel passes, and the decode step in both input dtypes. Gate inputs g ~ N(0, 1).
-# Bound: the gate multiplies each element, and so its error, by swish(g) (plus about 1e-6 relative
-# from the fp32 gate), so max|out - ref| <= max|swish(g)| * max|ungated out - ungated ref|. The
-# gated error is therefore measured against RMS(ungated ref) * max|swish(g)| and held to the inputs'
-# bound; max|gpu - ref| / RMS(ref) itself is not invariant under an elementwise gate. Each gated
-# output is also compared with the same kernel's ungated output times swish(g) in fp64, which
-# isolates the gate stage. fp32 out throughout; one bf16-out case is checked against the fp32 one.
+# Asserted: the stated metric, max|gpu - oracle| / RMS(oracle), on the gated output. Printed beside
+# it: the error relative to RMS(ungated ref) * max|swish(g)| (the gate multiplies each element, and
+# so its error, by swish(g), so max|out - ref| <= max|swish(g)| * max|ungated out - ungated ref|).
+# Each gated output is also compared with the same kernel's ungated output times swish(g) in fp64,
+# which isolates the gate stage. fp32 out throughout; one bf16-out case is checked against the fp32
+# one.
 def _gate(shape, dtype, seed):
     return torch.randn(*shape, generator=torch.Generator().manual_seed(seed)).to(dtype)
 
