@@ -197,7 +197,9 @@ ret_status retention_parallel_fwd(const ret_shape* shape,
  * gradients at the rotated inputs turned back by the inverse rotation (its transpose).
  * Workspace: retention_workspace_bytes(RET_FN_CHUNKWISE_BWD, ...): the workspace of the forward
  * calls and the blocks of state_in^T (bf16 inputs, whose forwards read every operand in place and
- * add the two column blocks' rows of dq and dk into those outputs); for fp32 inputs also the fp32
+ * add the two column blocks' rows of dq and dk into those outputs; with seq_len a multiple of the
+ * chunk also the dq forward's scores, anti-transposed, which the dk forward reads in place of its
+ * own); for fp32 inputs also the fp32
  * outputs of the column blocks and time-reversed and block copies of q, k, v and dout (plus the
  * rotated q and k with RET_WS_ROTATION). With bf16 inputs and two column blocks, dq and dk are
  * zeroed and then written by atomic fp32 adds: each element receives exactly two, so the result

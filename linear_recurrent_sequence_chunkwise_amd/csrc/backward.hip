@@ -146,7 +146,8 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 // after another (the batch of the stacked forward). bf16 inputs need only fwd and st.
 struct BwdLayout {
     int split;  // column blocks of d_v in the dq and dk forwards
-    size_t fwd, rq, rk, rdo, sa, sb, sc, ta, tb, tc, tmp, st, total;
+    size_t fwd, rq, rk, rdo, sa, sb, sc, ta, tb, tc, tmp, st, pa, total;
+    bool share;  // the dk forward takes the dq forward's scores, anti-transposed (at pa)
 };
 
 BwdLayout bwd_layout(int in_bf16, int B, int H, int N, int DK, int DV, int chunk) {
@@ -162,6 +163,8 @@ BwdLayout bwd_layout(int in_bf16, int B, int H, int N, int DK, int DV, int chunk
     if (in_bf16) {                                      // operands read in place, column blocks added in place
         l.rq = l.rk = l.rdo = l.sa = l.sb = l.sc = l.ta = l.tb = l.tc = l.tmp = o;
         l.st = o; o += al((size_t)s * B * H * w * DK * 4);
+        l.share = chunk > 0 && N % chunk == 0 && chunkwise_bf16_supported(w, DK, chunk) && chunkwise_bf16_scores_split(w, chunk);
+        l.pa = o; o += l.share ? al(chunkwise_bf16_scores_bytes(s * B, H, N, w, chunk)) : 0;
         l.total = o;
         return l;
     }
@@ -259,7 +262,9 @@ hipError_t bwd_in_place(const BwdArgs& b) {
             st = reinterpret_cast<const float*>(ws + l.st);
         }
         if (acc) zero(b.dq);
-        e = forward(stacked, w, DK, b.dout, b.v, b.k, st, b.dq, nullptr, fws, fwb, OpAddr{0, DV, w, BH, acc});
+        LaunchArgs sq = stacked;
+        if (l.share && b.dk) sq.p_anti = ws + l.pa;  // the dk forward's scores, written on the way
+        e = forward(sq, w, DK, b.dout, b.v, b.k, st, b.dq, nullptr, fws, fwb, OpAddr{0, DV, w, BH, acc});
         if (e != hipSuccess) return e;
     }
     // dv = rev(forward(rev k, rev q, rev dout)), written in place; its final state is U_0
@@ -276,7 +281,9 @@ hipError_t bwd_in_place(const BwdArgs& b) {
     // forward writes its rows back in time order
     if (b.dk) {
         if (acc) zero(b.dk);
-        e = forward(stacked, w, DK, b.v, b.dout, b.q, nullptr, b.dk, nullptr, fws, fwb, OpAddr{1, DV, w, BH, acc});
+        LaunchArgs sk = stacked;
+        if (l.share && b.dq) sk.p_given = ws + l.pa;
+        e = forward(sk, w, DK, b.v, b.dout, b.q, nullptr, b.dk, nullptr, fws, fwb, OpAddr{1, DV, w, BH, acc});
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();

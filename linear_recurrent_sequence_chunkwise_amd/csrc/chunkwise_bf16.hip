@@ -39,7 +39,10 @@ constexpr int kST = 32;    // tokens per pipeline stage
 // ---------------------------------------------------------------------------------------------
 // P = (Q K^T) (.) D for every chunk, into the workspace as [B*H][nchunks][C][C] bf16, its high
 // part in P and, when Plo is given, the low part (P - hi, rounded) in Plo, same layout. With qlo
-// (the low part of a q that bf16 does not hold) Q K^T is q K^T + qlo K^T, each in fp32. Grid
+// (the low part of a q that bf16 does not hold) Q K^T is q K^T + qlo K^T, each in fp32. With Pa
+// (no qlo) the kernel also writes the scores anti-transposed, P'[C-1-m][C-1-r] = P[r][m], for chunk
+// nchunks-1-c at Pa (high parts, then the low parts one plane of P further): these are the scores
+// of the time-reversed walk with the roles of q and k exchanged, when N is a multiple of C. Grid
 // (nchunks, B*H), 256 threads. The MFMAs compute P^T = K Q^T per 16 x 16 tile so that each lane
 // ends with 4 consecutive keys of one row (one 8-byte store). K rows go through LDS in 128-key
 // blocks (buffer-to-LDS loads, swizzled rows); each wave reads the Q fragments of its row tile
@@ -49,7 +52,7 @@ constexpr int kST = 32;    // tokens per pipeline stage
 template <int DK>
 __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
                                                            const bf16* __restrict__ qlo, const bf16* __restrict__ k,
-                                                           bf16* __restrict__ P, bf16* __restrict__ Plo,
+                                                           bf16* __restrict__ P, bf16* __restrict__ Plo, bf16* __restrict__ Pa,
                                                            HeadConsts hc, int rev, int ldqk, int qcol_blk, int srcBH) {
     constexpr int KB = 128;       // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row
@@ -69,6 +72,9 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     auto row_of = [&](int t) __attribute__((always_inline)) { return rev ? N - 1 - t : t; };
     bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
     bf16* Plc = Plo ? Plo + ((size_t)bh * nchunks + chunk) * (size_t)C * C : nullptr;
+    // the anti-transposed scores (both parts), chunk nchunks-1-chunk of the time-reversed walk
+    bf16* Pac = Pa ? Pa + ((size_t)bh * nchunks + (nchunks - 1 - chunk)) * (size_t)C * C : nullptr;
+    bf16* Palc = Pa ? Pac + (size_t)gridDim.y * nchunks * C * C : nullptr;
     const int T = C / 16;  // row tiles of the chunk
 
     for (int kb0 = 0; kb0 < C; kb0 += KB) {
@@ -101,10 +107,31 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
                 }
             }
             for (int kt = kb0 / 16; kt <= last; ++kt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc_t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qf[ks], acc);
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const bf16x8 kf = frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane);
+                    acc = mfma16(kf, qf[ks], acc);
+                    // the same tile untransposed (the two operands' lane layouts coincide): lane
+                    // holds rows 16t + 4g4 + i of key 16kt + c16
+                    if (Pa) acc_t = mfma16(qf[ks], kf, acc_t);
+                }
+                if (Pa) {
+                    // anti-transposed: element (row r, key m) at (C-1-m, C-1-r), so this lane's four
+                    // rows are four consecutive columns, in reverse order
+                    const int m = 16 * kt + c16, r0 = 16 * t + 4 * g4;
+                    bf16x4 o, ol;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bf16 hi, lo;
+                        split_hi_lo(r0 + i >= m ? acc_t[i] * decay_pow(l2g, (float)(r0 + i - m)) : 0.f, hi, lo);
+                        o[3 - i] = hi;
+                        ol[3 - i] = lo;
+                    }
+                    const size_t at = (size_t)(C - 1 - m) * C + (C - 4 - r0);
+                    *reinterpret_cast<bf16x4*>(Pac + at) = o;
+                    *reinterpret_cast<bf16x4*>(Palc + at) = ol;
+                }
                 if (qlo) {
                     f32x4 al = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1152,17 +1179,20 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.out_acc = a.addr.out_acc;
     if (mp.out_acc && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
     if (a.qlo && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
+    if ((a.p_anti || a.p_given) && (!want_out || !plo || a.qlo || a.N % C != 0)) return hipErrorInvalidValue;
     mp.q = (const bf16*)a.q;
     mp.qlo = (const bf16*)a.qlo; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;
-    mp.P = want_out ? reinterpret_cast<const bf16*>(ws + l.p_off) : nullptr;
+    mp.P = want_out ? reinterpret_cast<const bf16*>(a.p_given ? a.p_given : ws + l.p_off) : nullptr;
     mp.Plo = plo ? mp.P + (size_t)a.B * a.H * nchunks * C * C : nullptr;
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
 
-    hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C,
-                       nchunks, mp.q, mp.qlo, mp.k, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), a.hc, mp.rev, mp.ldqk,
-                       mp.qcol_blk, mp.srcBH);
+    if (!a.p_given) {
+        hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C, nchunks, mp.q,
+                           mp.qlo, mp.k, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), static_cast<bf16*>(a.p_anti), a.hc,
+                           mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!a.gn.enabled) return launch_main<DK, C, TOUT, true>(a, mp);
@@ -1233,6 +1263,13 @@ bool q_lo_dk(int C) {
         default: return false;
     }
 }
+size_t chunkwise_bf16_scores_bytes(int B, int H, int N, int DK, int chunk) {
+    const size_t nchunks = (size_t)(N + chunk - 1) / chunk;
+    return (p_lo_used(DK, chunk) ? 2 : 1) * (size_t)B * H * nchunks * chunk * chunk * sizeof(bf16);
+}
+
+bool chunkwise_bf16_scores_split(int DK, int chunk) { return p_lo_used(DK, chunk); }
+
 bool chunkwise_bf16_qlo_supported(int DK, int C) { return DK == 64 ? q_lo_dk<64>(C) : DK == 256 && q_lo_dk<256>(C); }
 
 hipError_t launch_chunkwise_bf16(const LaunchArgs& a) {

@@ -64,6 +64,12 @@ struct LaunchArgs {
     VShift vs;    // chunkwise only
     const void* q;
     const void* qlo;  // bf16 chunkwise with an fp32 output only: low part of q, or null
+    // bf16 chunkwise with an output, N a multiple of the chunk: p_anti receives the scores of this
+    // call anti-transposed (the scores of the time-reversed call with q and k exchanged), laid out
+    // as the workspace's scores (chunkwise_bf16_scores_bytes); p_given supplies such scores instead
+    // of computing them. Both null: the call computes its own.
+    void* p_anti;
+    const void* p_given;
     const void* k;
     const void* v;
     void* out;              // may be null (chunkwise state-only)
@@ -251,6 +257,10 @@ bool chunkwise_bf16_supported(int DK, int DV, int chunk);
 // (LaunchArgs::qlo) at this d_k and chunk: the warp-specialised kernel, when its stage buffers with
 // the second q plane fit in LDS.
 bool chunkwise_bf16_qlo_supported(int DK, int chunk);
+// Bytes of the scores (both parts) a bf16 chunkwise call with an output keeps, for p_anti / p_given,
+// and whether it keeps them as high and low parts (p_anti and p_given need that).
+size_t chunkwise_bf16_scores_bytes(int B, int H, int N, int DK, int chunk);
+bool chunkwise_bf16_scores_split(int DK, int chunk);
 // The segmented bf16 chunkwise kernels (chunk_seg.hip): plain operands, an output, d_k 64 or 256,
 // chunk 64 or 128, d_v a multiple of 64. U: the segment states in the workspace; out: the call's
 // output, or fp32 pre-norm rows when out_f32 (a GroupNorm pass follows).

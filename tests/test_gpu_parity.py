@@ -404,7 +404,9 @@ def _dout(shape, dtype, seed):
 @pytest.mark.parametrize("dt,B,H,N,dk,dv,C", [
     ("f32", 1, 2, 256, 64, 64, 64), ("f32", 2, 3, 250, 64, 128, 128), ("bf16", 4, 8, 2048, 64, 64, 128),
     ("bf16", 1, 4, 1000, 256, 512, 128), ("bf16", 1, 3, 700, 256, 512, 256), ("bf16", 1, 2, 1100, 256, 512, 512),
-    ("bf16", 1, 2, 37, 256, 512, 64)])
+    ("bf16", 1, 2, 37, 256, 512, 64),
+    # N a multiple of the chunk: the dk forward takes the dq forward's scores, anti-transposed
+    ("bf16", 1, 3, 1024, 256, 512, 256), ("bf16", 1, 2, 1024, 256, 512, 512), ("bf16", 2, 2, 512, 64, 128, 64)])
 def test_chunkwise_backward(orc, dt, B, H, N, dk, dv, C):
     q, k, v = I.make_qkv(B, H, N, dk, dv, dt, seed=500 + N)
     dout = _dout((B, H, N, dv), q.dtype, 501 + N)

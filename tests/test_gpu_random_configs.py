@@ -137,7 +137,9 @@ def _bwd_configs(n=16, seed=20261204):
             dk, C = int(rng.choice([64, 128, 256])), int(rng.choice([64, 128]))
         dv = int(rng.choice([64, 128, 256, 512]))
         B, H = [(1, 1), (1, 3), (2, 2), (1, 4), (1, 6)][int(rng.integers(0, 5))]
-        out.append(dict(i=i, dt=dt, dk=dk, dv=dv, C=C, B=B, H=H, N=int(rng.integers(1, 500)), state=bool(rng.random() < 0.5),
+        # N a multiple of the chunk in some cases (bf16: the dk forward then reuses the dq forward's scores)
+        N = C * int(rng.integers(1, 4)) if rng.random() < 0.4 else int(rng.integers(1, 500))
+        out.append(dict(i=i, dt=dt, dk=dk, dv=dv, C=C, B=B, H=H, N=N, state=bool(rng.random() < 0.5),
                         rot=bool(rng.random() < 0.3), off=int(rng.integers(0, 100000)), gseed=int(rng.integers(0, 2 ** 31))))
     return out
 
