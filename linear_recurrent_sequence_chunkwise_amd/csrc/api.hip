@@ -170,13 +170,16 @@ hipError_t stage_rotation(const ret_shape* s, const ret::RotConsts& rc, const vo
 // Bytes of the partial results. Summed by a last pass (acc false): the fp32 partial outputs (two;
 // three when the sum cannot go to out directly, i.e. a bf16 output or a GroupNorm after it). Added
 // in place (acc true): one fp32 output when the sum cannot go to out directly, else none. Then the
-// second partial state.
-size_t split_parts_bytes(const ret_shape* s, bool gn, bool acc) {
+// second partial state, then (acc, two calls at this chunk) the scores of the three products.
+size_t split_parts_bytes(const ret_shape* s, bool gn, bool acc, int chunk) {
     const size_t rows = (size_t)s->batch * s->heads * s->seq_len;
     const size_t o = align256(rows * s->d_v * sizeof(float));
     const bool staged = s->out_dtype == RET_BF16 || gn;
     const size_t outs = acc ? (staged ? 1 : 0) : (staged ? 3 : 2);
-    return outs * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float));
+    const size_t p = acc && ret::chunkwise_bf16_split2_supported(s->d_k, chunk)
+                         ? align256(ret::chunkwise_bf16_scores_bytes(s->batch, s->heads, s->seq_len, s->d_k, chunk))
+                         : 0;
+    return outs * o + align256((size_t)s->batch * s->heads * s->d_k * s->d_v * sizeof(float)) + p;
 }
 
 // Rotated q and k of a bf16 forward call as high and low parts: four planes.
@@ -197,7 +200,7 @@ hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, co
 }
 
 // The partial calls and the sums. a: the call (q and k unset; out, state_in, state_out, gn and
-// out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn, acc) of workspace; launch: the
+// out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn, acc, chunk) of workspace; launch: the
 // bf16 kernel family (chunkwise, which adds the partial outputs in place (acc), or parallel). Where
 // the chunkwise kernel takes q as two parts, A(q_hi, k_hi) + A(q_lo, k_hi) is one call on
 // (q_hi + q_lo, k_hi). An in-place state_in is read by the calls that need it before the last call
@@ -214,7 +217,20 @@ hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, c
     if (acc) {
         float* o = staged ? reinterpret_cast<float*>(parts) : static_cast<float*>(a.out);
         float* s2 = reinterpret_cast<float*>(parts + (staged ? ob : 0));
-        if (a.out && ret::chunkwise_bf16_qlo_supported(a.DK, a.chunk)) {
+        char* sc = parts + (staged ? ob : 0) + align256((size_t)a.B * a.H * a.DK * a.DV * sizeof(float));
+        if (a.out && ret::chunkwise_bf16_split2_supported(a.DK, a.chunk)) {
+            // two calls sharing one scores pass over all three products: (q_hi, k_lo) with those
+            // scores stores its rows and its state; (q_hi + q_lo, k_hi) without an intra-chunk term
+            // adds its rows and writes the state from state_in
+            if ((e = ret::launch_chunkwise_bf16_scores(a, qh, ql, kh, kl, sc)) != hipSuccess) return e;
+            c.q = qh; c.k = kl; c.p_given = sc; c.out = o; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
+            if ((e = launch(c)) != hipSuccess) return e;
+            c.p_given = nullptr;
+            c.addr.out_acc = 1;
+            c.no_pv = 1;
+            c.q = qh; c.qlo = ql; c.k = kh; c.state_in = a.state_in; c.state_out = a.state_out;
+            if ((e = launch(c)) != hipSuccess) return e;
+        } else if (a.out && ret::chunkwise_bf16_qlo_supported(a.DK, a.chunk)) {
             // two calls: (q_hi, k_lo) stores its rows and its state; (q_hi + q_lo, k_hi), on the
             // kernel that takes q as two parts, adds its rows and writes the state from state_in
             c.q = qh; c.k = kl; c.out = o; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
@@ -341,7 +357,7 @@ size_t rla_ws(const ret_shape* s, int chunk, int fmap) {
     const size_t es = f32 ? sizeof(float) : elem_size(s->in_dtype);
     const size_t ops = (split ? 4 : 2) * align256(rows * s->d_k * es) + align256(rows * s->d_v * es);
     if (s->seq_len == 1) return ops;
-    return ops + (split ? split_parts_bytes(s, false, true) : 0) + chunkwise_ws(s, chunk, 0, 1);
+    return ops + (split ? split_parts_bytes(s, false, true, chunk) : 0) + chunkwise_ws(s, chunk, 0, 1);
 }
 
 size_t parallel_ws(const ret_shape* s, int gn) {
@@ -366,12 +382,12 @@ size_t bwd_rot_ws(const ret_shape* s, int chunk) {
 
 size_t chunkwise_rot_ws(const ret_shape* s, int chunk, bool gn, int want_out) {
     if (s->in_dtype != RET_BF16) return rotation_ws(s) + chunkwise_ws(s, chunk, gn, want_out);
-    return rotation_split_ws(s) + split_parts_bytes(s, gn, true) + chunkwise_ws(s, chunk, 0, want_out);
+    return rotation_split_ws(s) + split_parts_bytes(s, gn, true, chunk) + chunkwise_ws(s, chunk, 0, want_out);
 }
 
 size_t parallel_rot_ws(const ret_shape* s, bool gn) {
     if (s->in_dtype != RET_BF16) return rotation_ws(s) + parallel_ws(s, gn);
-    return rotation_split_ws(s) + split_parts_bytes(s, gn, false) + parallel_ws(s, 0);
+    return rotation_split_ws(s) + split_parts_bytes(s, gn, false, 0) + parallel_ws(s, 0);
 }
 
 ret_status check_ws(size_t need, const void* ws, size_t wsb) {
@@ -520,7 +536,7 @@ int ret::chunkwise_fwd_entry(const ret_shape* shape, int32_t chunk, const void* 
         hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, st);
         if (e != hipSuccess) return device_status(e, "retention_chunkwise_fwd rotation launch");
         char* parts = static_cast<char*>(workspace);
-        const size_t pb = split_parts_bytes(shape, gn.enabled, true);
+        const size_t pb = split_parts_bytes(shape, gn.enabled, true, chunk);
         ret::LaunchArgs a = base_args(shape, chunk, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
         a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
         e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_chunkwise_bf16, true);
@@ -709,7 +725,7 @@ ret_status retention_parallel_fwd(const ret_shape* shape, const void* q, const v
         hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
         if (e != hipSuccess) return device_status(e, "retention_parallel_fwd rotation launch");
         char* parts = static_cast<char*>(workspace);
-        const size_t pb = split_parts_bytes(shape, gn.enabled, false);
+        const size_t pb = split_parts_bytes(shape, gn.enabled, false, 0);
         ret::LaunchArgs a = base_args(shape, 0, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
         a.v = v; a.out = out;
         e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_parallel_bf16, false);
@@ -809,7 +825,7 @@ ret_status retention_rla_fwd(const ret_shape* shape, int32_t chunk, int32_t wind
     }
     char* rest = w + nq * Aq + Av;  // after the operands
     char* parts = rest;             // split calls: partial outputs and state
-    if (split) rest += split_parts_bytes(shape, false, true);
+    if (split) rest += split_parts_bytes(shape, false, true, chunk);
     ret::LaunchArgs a = base_args(shape, N == 1 ? 1 : chunk, hc, ret::GnArgs{}, rest,
                                   workspace_bytes - (size_t)(rest - w), hip_stream);
     if (f32feat) a.in_bf16 = 0;  // the fp32 decode kernel, on the fp32 features and value row

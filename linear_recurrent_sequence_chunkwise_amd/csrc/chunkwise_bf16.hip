@@ -49,15 +49,18 @@ constexpr int kST = 32;    // tokens per pipeline stage
 // straight from global memory into registers. Row tile t (16 rows) gets key tiles 0 .. (t|1): the
 // consumer reads whole 32-key steps up to the diagonal one, whose upper part is written as zero.
 // Waves take row tiles in mirrored pairs (t, T-1-t) so that the causal work is balanced.
-template <int DK>
+// KLO: k comes as two parts too (k + klo), and Q K^T = q K^T + qlo K^T + q Klo^T (the qlo Klo^T
+// term, about 2^-16 relative, dropped): the K and Klo blocks of 64 keys sit side by side in LDS.
+template <int DK, bool KLO = false>
 __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
                                                            const bf16* __restrict__ qlo, const bf16* __restrict__ k,
-                                                           bf16* __restrict__ P, bf16* __restrict__ Plo, bf16* __restrict__ Pa,
-                                                           HeadConsts hc, int rev, int ldqk, int qcol_blk, int srcBH) {
-    constexpr int KB = 128;       // keys per LDS block
+                                                           const bf16* __restrict__ klo, bf16* __restrict__ P,
+                                                           bf16* __restrict__ Plo, bf16* __restrict__ Pa, HeadConsts hc, int rev,
+                                                           int ldqk, int qcol_blk, int srcBH) {
+    constexpr int KB = KLO ? 64 : 128;  // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row
     constexpr int NKB = KB * QRB / 1024;  // kilobytes of a K block
-    __shared__ __attribute__((aligned(1024))) char Ks[KB * QRB];
+    __shared__ __attribute__((aligned(1024))) char Ks[(KLO ? 2 : 1) * KB * QRB];
     const int chunk = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, c16 = lane & 15;
     const int c0 = chunk * C;
@@ -69,6 +72,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rql = __builtin_amdgcn_make_buffer_rsrc((void*)((qlo ? qlo : q) + qbase), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc((void*)((KLO ? klo : k) + qbase), 0, q_bytes, 0x00020000);
     auto row_of = [&](int t) __attribute__((always_inline)) { return rev ? N - 1 - t : t; };
     bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
     bf16* Plc = Plo ? Plo + ((size_t)bh * nchunks + chunk) * (size_t)C * C : nullptr;
@@ -85,6 +89,9 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
             const int c = ((byte % QRB) >> 4) ^ (r & SwzTile<QRB>::M);
             const unsigned off = (unsigned)((row_of(c0 + kb0 + r) * ldqk + 8 * c) * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + 1024 * j), 16, off, 0, 0, 0);
+            if constexpr (KLO)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rkl, (__attribute__((address_space(3))) void*)(Ks + KB * QRB + 1024 * j), 16, off,
+                                                         0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
@@ -132,11 +139,13 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
                     *reinterpret_cast<bf16x4*>(Pac + at) = o;
                     *reinterpret_cast<bf16x4*>(Palc + at) = ol;
                 }
-                if (qlo) {
+                if (qlo || KLO) {
                     f32x4 al = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < DK / 32; ++ks)
-                        al = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qlf[ks], al);
+                    for (int ks = 0; ks < DK / 32; ++ks) {
+                        if (qlo) al = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qlf[ks], al);
+                        if constexpr (KLO) al = mfma16(frag_rowmajor_swz<QRB>(Ks + KB * QRB, 16 * kt - kb0, 32 * ks, lane), qf[ks], al);
+                    }
                     acc += al;
                 }
                 // lane: row 16t + c16, keys 16kt + 4g4 + i
@@ -541,14 +550,15 @@ __global__ __launch_bounds__(kThreads) void chunk_main_kernel(MainParams p, Head
 // their fragments from it at the next stage, before the loaders refill that buffer. PLO: P comes
 // as bf16 hi + lo, both parts loaded, P V on both. QLO: q comes as two bf16 parts (q + qlo, the
 // high and low parts of an operand that bf16 does not hold), both loaded, Q R on both (qlo times
-// the high part of R; the scores kernel forms P from both parts).
-template <int DK, int C, bool PLO = false, bool QLO = false>
+// the high part of R; the scores kernel forms P from both parts). NOP: no intra-chunk term (no P,
+// no P V): the output is g^(j+1) Q R alone, for split calls whose P V another call carries.
+template <int DK, int C, bool PLO = false, bool QLO = false, bool NOP = false>
 struct WsGeom {
     static constexpr int QRB = DK * 2;            // bytes per Q / K tile row
     static constexpr int PRB = C * 2;             // bytes per P tile row
     static constexpr int LV = kW;                 // V and V (.) zeta rows: 32 bf16, dense
     static constexpr size_t Q_BYTES = (size_t)kST * QRB;
-    static constexpr size_t P_BYTES = (size_t)kST * PRB;
+    static constexpr size_t P_BYTES = NOP ? 0 : (size_t)kST * PRB;
     static constexpr size_t OFF_K = Q_BYTES, OFF_P = 2 * Q_BYTES, OFF_PL = OFF_P + P_BYTES;
     static constexpr size_t OFF_QL = OFF_PL + (PLO ? P_BYTES : 0);
     static constexpr size_t BUF = OFF_QL + (QLO ? Q_BYTES : 0);  // one stage buffer
@@ -587,9 +597,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int C, typename TOUT, bool VSH, bool PLO, bool QLO = false>
+template <int DK, int C, typename TOUT, bool VSH, bool PLO, bool QLO = false, bool NOP = false>
 __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
-    using G = WsGeom<DK, C, PLO, QLO>;
+    using G = WsGeom<DK, C, PLO, QLO, NOP>;
     constexpr int NB = G::NB;
     constexpr int RTR = DK / 64;  // 16-row R tiles per state wave
     constexpr int SPC = C / kST;
@@ -639,10 +649,11 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
         const __amdgpu_buffer_rsrc_t rql =
             __builtin_amdgcn_make_buffer_rsrc((void*)((QLO ? p.qlo : p.q) + qbase), 0, q_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (size_t)src * N * DV), 0, v_bytes, 0x00020000);
+        // (no scores without P V: empty resources that no load uses)
         const __amdgpu_buffer_rsrc_t rp =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.P + (size_t)bh * nchunks * C * C), 0, NOP ? 0u : p_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rpl = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((PLO ? p.Plo : p.P) + (size_t)bh * nchunks * C * C), 0, p_bytes, 0x00020000);
+            (void*)((PLO ? p.Plo : p.P) + (size_t)bh * nchunks * C * C), 0, NOP ? 0u : p_bytes, 0x00020000);
         // This wave's share (kilobytes j = lw mod 4) of the Q, K and P rows of stage g, into its
         // buffer; lane l fills bytes [16l, 16l+16) of each kilobyte. P: only the 32-key steps up to
         // this stage; the rest read as zero, no traffic.
@@ -687,6 +698,10 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             if (lw < 2) {
                 off = g < total && i < kST * LPR ? (unsigned)(row_of(tok0 + i / LPR) * ldqk * 2 + 128 * (i % LPR)) : q_bytes;
                 if (lw == 1) r = rk;
+            } else if (NOP && lw == 2) {
+                // no P: the lines of q's low part (with QLO), else a load past the end
+                off = QLO && g < total && i < kST * LPR ? (unsigned)(row_of(tok0 + i / LPR) * ldqk * 2 + 128 * (i % LPR)) : q_bytes;
+                r = rql;
             } else if (lw == 2) {
                 const int plr = (kST * (s + 1) * 2 + 127) / 128;  // P lines per row up to this stage
                 off = g < total && i < kST * plr ? (unsigned)(((ci * C + kST * s + i / plr) * C) * 2 + 128 * (i % plr)) : p_bytes;
@@ -902,10 +917,12 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             bf16x8 qf[DK / 32], pf[2], vf[2];
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = frag_rowmajor_swz<G::QRB>(Qs, 16 * rt_o, 32 * ks, lane);
+            if constexpr (!NOP) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                pf[ks] = frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane);
-                vf[ks] = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
+                for (int ks = 0; ks < 2; ++ks) {
+                    pf[ks] = frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane);
+                    vf[ks] = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 qa[4];
@@ -927,17 +944,21 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
             // stage's keys (its rows are loaded as zero there) and the V rows there are finite
             // (zeroed at the start, or rows of an earlier chunk); the later steps stop at the
             // stage (measured 10-20 us faster at the N=8192 layer than running every step)
-            f32x4 pa[2] = {mfma16(pf[0], vf[0], f32x4{0.f, 0.f, 0.f, 0.f}), mfma16(pf[1], vf[1], f32x4{0.f, 0.f, 0.f, 0.f})};
-            if constexpr (PLO) {
+            f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            if constexpr (!NOP) {
+                pa[0] = mfma16(pf[0], vf[0], pa[0]);
+                pa[1] = mfma16(pf[1], vf[1], pa[1]);
+                if constexpr (PLO) {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) pa[ks] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vf[ks], pa[ks]);
-            }
+                    for (int ks = 0; ks < 2; ++ks) pa[ks] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vf[ks], pa[ks]);
+                }
 #pragma unroll
-            for (int ks = 2; ks < SPC; ++ks) {
-                if (ks > s) break;  // P is zero past this stage's keys
-                const bf16x8 vk = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
-                pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
-                if constexpr (PLO) pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
+                for (int ks = 2; ks < SPC; ++ks) {
+                    if (ks > s) break;  // P is zero past this stage's keys
+                    const bf16x8 vk = lds_frag_kmajor(Vblk(vf0, ks), G::LV, 0, 16 * ct_o, lane);
+                    pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Ps, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
+                    if constexpr (PLO) pa[ks & 1] = mfma16(frag_rowmajor_swz<G::PRB>(Pls, 16 * rt_o, 32 * ks, lane), vk, pa[ks & 1]);
+                }
             }
             const f32x4 qr = (qa[0] + qa[2]) + (qa[1] + qa[3]);
             const f32x4 pv = pa[0] + pa[1];
@@ -1081,6 +1102,9 @@ constexpr bool p_lo() { return use_ws<DK, C, true>() || MainGeom<DK, C, true>::B
 // whether the warp-specialised kernel takes q as two parts (q + qlo) at (DK, C)
 template <int DK, int C>
 constexpr bool q_lo_fits() { return C <= 256 && WsGeom<DK, C, true, true>::BYTES <= kLdsBytes; }
+// ... and with no intra-chunk term (no P)
+template <int DK, int C>
+constexpr bool q_lo_nop_fits() { return C <= 256 && WsGeom<DK, C, true, true, true>::BYTES <= kLdsBytes; }
 
 template <int DK>
 bool p_lo_dk(int C) {
@@ -1094,16 +1118,18 @@ bool p_lo_dk(int C) {
 // whether a call with an output at (DK, C) keeps the low part of P
 bool p_lo_used(int DK, int C) { return DK == 64 ? p_lo_dk<64>(C) : p_lo_dk<256>(C); }
 
-template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH, bool QLO = false>
+template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH, bool QLO = false, bool NOP = false>
 hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
     constexpr bool ws = use_ws<DK, C, WANT_OUT>();
     constexpr bool plo = WANT_OUT && p_lo<DK, C>();
-    static_assert(!QLO || (ws && q_lo_fits<DK, C>()), "q as two parts on the warp-specialised kernel only");
+    static_assert(!QLO || (ws && (NOP ? q_lo_nop_fits<DK, C>() : q_lo_fits<DK, C>())),
+                  "q as two parts on the warp-specialised kernel only");
+    static_assert(!NOP || QLO, "no intra-chunk term only with q as two parts");
     const void* kern;
-    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true, QLO>);
+    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true, QLO, NOP>);
     else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT, VSH, plo>);
     size_t dyn;
-    if constexpr (ws) dyn = WsGeom<DK, C, true, QLO>::BYTES;
+    if constexpr (ws) dyn = WsGeom<DK, C, true, QLO, NOP>::BYTES;
     else dyn = MainGeom<DK, C, plo>::BYTES;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
@@ -1117,12 +1143,17 @@ hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
 // that need them
 template <int DK, int C, typename TOUT, bool WANT_OUT>
 hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
+    if constexpr (WANT_OUT && sizeof(TOUT) == 4 && use_ws<DK, C, WANT_OUT>() && q_lo_nop_fits<DK, C>()) {
+        if (mp.qlo && a.no_pv)
+            return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true, true, true>(a, mp)
+                             : launch_main_v<DK, C, TOUT, WANT_OUT, false, true, true>(a, mp);
+    }
     if constexpr (WANT_OUT && sizeof(TOUT) == 4 && use_ws<DK, C, WANT_OUT>() && q_lo_fits<DK, C>()) {
-        if (mp.qlo)
+        if (mp.qlo && !a.no_pv)
             return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true, true>(a, mp)
                              : launch_main_v<DK, C, TOUT, WANT_OUT, false, true>(a, mp);
     }
-    if (mp.qlo) return hipErrorInvalidValue;
+    if (mp.qlo || a.no_pv) return hipErrorInvalidValue;
     return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true>(a, mp) : launch_main_v<DK, C, TOUT, WANT_OUT, false>(a, mp);
 }
 
@@ -1179,7 +1210,9 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.out_acc = a.addr.out_acc;
     if (mp.out_acc && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
     if (a.qlo && (!want_out || a.gn.enabled || sizeof(TOUT) != 4)) return hipErrorInvalidValue;
-    if ((a.p_anti || a.p_given) && (!want_out || !plo || a.qlo || a.N % C != 0)) return hipErrorInvalidValue;
+    if (a.p_anti && (!want_out || !plo || a.qlo || a.N % C != 0)) return hipErrorInvalidValue;
+    if (a.p_given && (!want_out || !plo || a.qlo)) return hipErrorInvalidValue;
+    if (a.no_pv && (!a.qlo || a.p_anti || a.p_given)) return hipErrorInvalidValue;
     mp.q = (const bf16*)a.q;
     mp.qlo = (const bf16*)a.qlo; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;
@@ -1188,10 +1221,10 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = a.out;
     if (!want_out) return launch_main<DK, C, TOUT, false>(a, mp);
 
-    if (!a.p_given) {
+    if (!a.p_given && !a.no_pv) {
         hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C, nchunks, mp.q,
-                           mp.qlo, mp.k, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), static_cast<bf16*>(a.p_anti), a.hc,
-                           mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH);
+                           mp.qlo, mp.k, nullptr, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), static_cast<bf16*>(a.p_anti),
+                           a.hc, mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1263,6 +1296,37 @@ bool q_lo_dk(int C) {
         default: return false;
     }
 }
+template <int DK>
+bool split2_dk(int C) {
+    switch (C) {
+        case 64: return q_lo_nop_fits<DK, 64>() && p_lo<DK, 64>();
+        case 128: return q_lo_nop_fits<DK, 128>() && p_lo<DK, 128>();
+        case 256: return q_lo_nop_fits<DK, 256>() && p_lo<DK, 256>();
+        default: return false;
+    }
+}
+bool chunkwise_bf16_split2_supported(int DK, int chunk) { return DK == 64 ? split2_dk<64>(chunk) : DK == 256 && split2_dk<256>(chunk); }
+
+hipError_t launch_chunkwise_bf16_scores(const LaunchArgs& a, const void* q, const void* qlo, const void* k, const void* klo, void* P) {
+    const int C = a.chunk, nchunks = (a.N + C - 1) / C;
+    if (a.N <= 0 || a.B * a.H <= 0) return hipSuccess;
+    if (!(a.DK == 64 || a.DK == 256) || !p_lo_used(a.DK, C)) return hipErrorInvalidValue;
+    bf16* ph = static_cast<bf16*>(P);
+    bf16* pl = ph + (size_t)a.B * a.H * nchunks * C * C;
+    const bf16 *q_ = static_cast<const bf16*>(q), *ql = static_cast<const bf16*>(qlo), *k_ = static_cast<const bf16*>(k),
+               *kl = static_cast<const bf16*>(klo);
+    const dim3 grid(nchunks, a.B * a.H);
+    const int BH = a.B * a.H;
+    if (a.DK == 64) {
+        if (kl) hipLaunchKernelGGL((chunk_scores_kernel<64, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, kl, ph, pl, nullptr, a.hc, 0, 64, 0, BH);
+        else hipLaunchKernelGGL((chunk_scores_kernel<64, false>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, nullptr, ph, pl, nullptr, a.hc, 0, 64, 0, BH);
+    } else {
+        if (kl) hipLaunchKernelGGL((chunk_scores_kernel<256, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, kl, ph, pl, nullptr, a.hc, 0, 256, 0, BH);
+        else hipLaunchKernelGGL((chunk_scores_kernel<256, false>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, nullptr, ph, pl, nullptr, a.hc, 0, 256, 0, BH);
+    }
+    return hipGetLastError();
+}
+
 size_t chunkwise_bf16_scores_bytes(int B, int H, int N, int DK, int chunk) {
     const size_t nchunks = (size_t)(N + chunk - 1) / chunk;
     return (p_lo_used(DK, chunk) ? 2 : 1) * (size_t)B * H * nchunks * chunk * chunk * sizeof(bf16);

@@ -70,6 +70,9 @@ struct LaunchArgs {
     // of computing them. Both null: the call computes its own.
     void* p_anti;
     const void* p_given;
+    // bf16 chunkwise, q as two parts (qlo), fp32 out: no intra-chunk term (no scores, no P V): the
+    // output is g^(j+1) Q R alone, for a split call whose intra-chunk term another call carries
+    int no_pv;
     const void* k;
     const void* v;
     void* out;              // may be null (chunkwise state-only)
@@ -261,6 +264,13 @@ bool chunkwise_bf16_qlo_supported(int DK, int chunk);
 // and whether it keeps them as high and low parts (p_anti and p_given need that).
 size_t chunkwise_bf16_scores_bytes(int B, int H, int N, int DK, int chunk);
 bool chunkwise_bf16_scores_split(int DK, int chunk);
+// The two-call split of a bf16 chunkwise call on (q_hi + q_lo, k_hi + k_lo) at this d_k and chunk:
+// the scores of all three products from one kernel (launch_chunkwise_bf16_scores with qlo and klo)
+// go to the (q_hi, k_lo) call (p_given), and the (q_hi + q_lo, k_hi) call runs without P (no_pv).
+bool chunkwise_bf16_split2_supported(int DK, int chunk);
+// The scores kernel alone (plain operands, a.B, a.H, a.N, a.DK, a.chunk, a.hc): P = q k^T (+ qlo k^T
+// with qlo, + q klo^T with klo) as bf16 high and low planes at P (chunkwise_bf16_scores_bytes).
+hipError_t launch_chunkwise_bf16_scores(const LaunchArgs& a, const void* q, const void* qlo, const void* k, const void* klo, void* P);
 // The segmented bf16 chunkwise kernels (chunk_seg.hip): plain operands, an output, d_k 64 or 256,
 // chunk 64 or 128, d_v a multiple of 64. U: the segment states in the workspace; out: the call's
 // output, or fp32 pre-norm rows when out_f32 (a GroupNorm pass follows).

@@ -252,16 +252,18 @@ def test_rotation_workspace(lib):
     # the bf16 forward forms keep high and low parts (four planes), then the three calls' fp32
     # partial outputs and second partial state, then the calls' own workspace without a GroupNorm.
     # The parallel form keeps two partial outputs (three with a GroupNorm after their sum or a bf16
-    # output); the chunkwise calls add theirs in place, into out or (GroupNorm, bf16 out) one.
+    # output); the chunkwise calls add theirs in place, into out or (GroupNorm, bf16 out) one, and
+    # keep the scores of the three products (both bf16 parts) that their two calls share.
     s = shape()
     rows = s.batch * s.heads * s.seq_len
     planes = 4 * al(rows * s.d_k * 2)
     o, st = al(rows * s.d_v * 4), al(s.batch * s.heads * s.d_k * s.d_v * 4)
-    for fn, C, n0, n1 in ((R.RET_FN_CHUNKWISE, 64, 0, 1), (R.RET_FN_PARALLEL, 0, 2, 3)):
+    sc = al(2 * s.batch * s.heads * (s.seq_len // 64) * 64 * 64 * 2)
+    for fn, C, n0, n1, extra in ((R.RET_FN_CHUNKWISE, 64, 0, 1, sc), (R.RET_FN_PARALLEL, 0, 2, 3, 0)):
         base = lib.retention_workspace_bytes(fn, ctypes.byref(s), C, 0)
-        assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION) == planes + n0 * o + st + base, fn
+        assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION) == planes + n0 * o + st + extra + base, fn
         assert lib.retention_workspace_bytes(fn, ctypes.byref(s), C, R.RET_WS_ROTATION | R.RET_WS_GROUPNORM) == \
-            planes + n1 * o + st + base, fn
+            planes + n1 * o + st + extra + base, fn
     # the bf16 backward likewise, with the partial gradients (dq, dk, two dv, dstate_in)
     base = lib.retention_workspace_bytes(R.RET_FN_CHUNKWISE_BWD, ctypes.byref(s), 64, 0)
     g = 2 * al(rows * s.d_k * 4) + 2 * al(rows * s.d_v * 4) + st
