@@ -1192,9 +1192,60 @@ bool seg_preferred(const LaunchArgs& a) {
     return chunkwise_seg_supported(a) && (long)a.B * a.H * (a.DV / kW) < cus;
 }
 
+// Chunks of 512 with an output and plain operands: the two terms of the chunkwise form in two
+// kernels. The intra-chunk term (Q K^T (.) D) V runs on the parallel-form kernel restricted to each
+// query's own chunk (fp32 rows; P as hi + lo there too); then the warp-specialised kernel without
+// an intra-chunk term adds g^(j+1) Q R to them (atomic fp32 adds, one per element) and carries the
+// state. Its stage buffers hold Q and K only (32 KiB at d_k = 256), so three fit beside the
+// 34 KiB V ring, where the stage buffers with the 512-key scores would not fit twice. With a
+// GroupNorm or a bf16 output the rows go through the fp32 staging in the workspace (the scores'
+// region, unused here, which holds N x 512 fp32 values per head).
+bool c512_split_ok(const LaunchArgs& a, int DK) {
+    const bool plain = a.addr.rev == 0 && (a.addr.ldqk == 0 || a.addr.ldqk == DK) && a.addr.qcol_blk == 0 &&
+                       (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0;
+    return plain && a.in_bf16 && a.out != nullptr && !a.qlo && !a.p_anti && !a.p_given && !a.no_pv && a.vs.split == 0 &&
+           parallel_bf16_supported(DK, a.DV);
+}
+
+template <int DK, typename TOUT>
+hipError_t launch_c512(const LaunchArgs& a) {
+    constexpr int C = 512;
+    using G = WsGeom<DK, C, true, false, true>;
+    static_assert(G::BYTES <= kLdsBytes && p_lo<DK, C>(), "chunk-512 split: stage buffers and staging fit");
+    const int nchunks = (a.N + C - 1) / C;
+    const WsLayout l = ws_layout(a.B, a.H, a.N, a.DV, C, a.gn.enabled, true, true);
+    const bool direct = !a.gn.enabled && sizeof(TOUT) == 4;
+    float* o32 = direct ? static_cast<float*>(a.out) : reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + l.p_off);
+    LaunchArgs pa = a;  // the intra-chunk term: parallel form within each chunk, fp32 rows
+    pa.out = o32;
+    pa.out_bf16 = 0;
+    pa.gn = GnArgs{};
+    pa.intra_chunk = C;
+    hipError_t e = launch_parallel_bf16(pa);
+    if (e != hipSuccess) return e;
+    MainParams mp{};
+    mp.H = a.H; mp.N = a.N; mp.C = C; mp.NS = a.DV / kW; mp.nchunks = nchunks; mp.teams = a.B * a.H;
+    mp.rev = 0; mp.ldqk = DK; mp.qcol_blk = 0; mp.srcBH = a.B * a.H;
+    mp.out_acc = 1;
+    mp.q = (const bf16*)a.q; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
+    mp.state_in = a.state_in; mp.state_out = a.state_out; mp.out = o32;
+    const void* kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, float, false, true, false, true>);
+    if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::BYTES)) != hipSuccess) return e;
+    HeadConsts hc = a.hc;
+    void* args[] = {&mp, &hc};
+    if ((e = hipLaunchKernel(kern, dim3(mp.teams * mp.NS), dim3(768), args, G::BYTES, a.stream)) != hipSuccess) return e;
+    const long rows = (long)a.B * a.H * a.N;
+    if (a.gn.enabled) return launch_gn_rows(rows, a.H, a.N, a.DV, o32, a.out, sizeof(TOUT) == 2, a.gn, a.stream);
+    if (!direct) return launch_add_rows((size_t)rows * a.DV, o32, nullptr, nullptr, a.out, true, a.stream);
+    return hipSuccess;
+}
+
 template <int DK, int C, typename TOUT>
 hipError_t launch_dk_c(const LaunchArgs& a) {
     if (seg_preferred(a)) return launch_seg<TOUT>(a);
+    if constexpr (C == 512) {
+        if (c512_split_ok(a, DK)) return launch_c512<DK, TOUT>(a);
+    }
     if (chunkwise_seg_state_supported(a)) return launch_chunkwise_seg_state(a, reinterpret_cast<float*>(a.ws));
     const int nchunks = (a.N + C - 1) / C;
     const bool want_out = a.out != nullptr;

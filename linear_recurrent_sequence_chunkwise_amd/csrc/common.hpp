@@ -73,6 +73,9 @@ struct LaunchArgs {
     // bf16 chunkwise, q as two parts (qlo), fp32 out: no intra-chunk term (no scores, no P V): the
     // output is g^(j+1) Q R alone, for a split call whose intra-chunk term another call carries
     int no_pv;
+    // bf16 parallel form: > 0 keeps only the keys of each query's own chunk of this many tokens (a
+    // multiple of 64): the intra-chunk term of the chunkwise form
+    int intra_chunk;
     const void* k;
     const void* v;
     void* out;              // may be null (chunkwise state-only)

@@ -40,10 +40,12 @@ struct ParLds {
 // Eight waves, two per SIMD. Scores: wave w computes the 16 x 16 tile S^T of query tile w & 3 and
 // key tile w >> 2 of the block. P V: wave w owns rows 32 (w >> 2) .. +32 and the column quarter
 // (w & 3) * DV / 4 .. +DV/4.
+// chunk > 0: only the keys of the query's own chunk of that many tokens (a multiple of 64), the
+// intra-chunk term of the chunkwise form.
 template <int DK, int DV, typename TOUT, bool GN>
 __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const bf16* __restrict__ q,
                                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
-                                                            TOUT* __restrict__ out, HeadConsts hc, GnArgs gn) {
+                                                            TOUT* __restrict__ out, HeadConsts hc, GnArgs gn, int chunk) {
     using Lds = ParLds<DK, DV>;
     using KT = SwzTile<DK * 2>;
     using VT = SwzTile<DV * 2>;
@@ -81,6 +83,7 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
         for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nkb = min((n0 + 64 + kKB - 1) / kKB, (N + kKB - 1) / kKB);  // key blocks up to the diagonal
+    const int kbs = chunk > 0 ? (n0 / chunk) * chunk / kKB : 0;             // first key block
     // K and V rows of a block go through registers (16-byte pieces, idx = threadIdx.x + kThreads * j
     // < pieces; rows past the sequence read as zero): loaded one iteration before they are written
     // to LDS, so that a whole iteration hides the load latency.
@@ -179,17 +182,17 @@ __global__ __launch_bounds__(kThreads) void parallel_kernel(int H, int N, const 
     // P(kb), and the registers hold K(kb+2) and V(kb+1). Iteration kb writes those registers to the
     // buffers that iteration kb-1 finished reading, loads K(kb+3) and V(kb+2), and computes the
     // scores of block kb+1 together with P V of block kb.
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-    if (nkb > 1) load_k(1);
-    if (nkb > 1) load_v(1);
+    load_k(kbs);
+    load_v(kbs);
+    store_k(kbs & 1);
+    store_v(kbs & 1);
+    if (nkb > kbs + 1) load_k(kbs + 1);
+    if (nkb > kbs + 1) load_v(kbs + 1);
     __syncthreads();
-    scores(0);
-    if (nkb > 1) store_k(1);
-    if (nkb > 2) load_k(2);
-    for (int kb = 0; kb < nkb; ++kb) {
+    scores(kbs);
+    if (nkb > kbs + 1) store_k((kbs + 1) & 1);
+    if (nkb > kbs + 2) load_k(kbs + 2);
+    for (int kb = kbs; kb < nkb; ++kb) {
         __syncthreads();  // iteration kb-1's reads and writes are done and visible
         if (kb + 2 < nkb) store_k(kb & 1);
         if (kb + 1 < nkb) store_v((kb + 1) & 1);
@@ -277,7 +280,7 @@ hipError_t launch_typed(const LaunchArgs& a) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((parallel_kernel<DK, DV, TOUT, GN>), dim3((a.N + 63) / 64 * a.B * a.H), dim3(kThreads), lds, a.stream,
-                       a.H, a.N, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOUT*)a.out, a.hc, a.gn);
+                       a.H, a.N, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOUT*)a.out, a.hc, a.gn, a.intra_chunk);
     return hipGetLastError();
 }
 
