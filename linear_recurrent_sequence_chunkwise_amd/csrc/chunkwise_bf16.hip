@@ -1060,7 +1060,9 @@ WsLayout ws_layout(int B, int H, int N, int DV, int C, int gn, int want_out, boo
     l.p_off = 0;
     l.p_bytes = want_out ? align256((plo ? 2 : 1) * (size_t)B * H * nchunks * C * C * sizeof(bf16)) : 0;
     l.pre_off = l.p_off + l.p_bytes;
-    l.pre_bytes = gn && want_out ? align256((size_t)B * H * N * DV * sizeof(float)) : 0;
+    // fp32 rows: the GroupNorm's pre-norm staging, and at chunks of 256 and 512 (two kernels, see
+    // launch_intra_split) the staging of any output that is not fp32 out itself
+    l.pre_bytes = want_out && (gn || C >= 256) ? align256((size_t)B * H * N * DV * sizeof(float)) : 0;
     l.total = l.pre_off + l.pre_bytes;
     return l;
 }
@@ -1192,30 +1194,29 @@ bool seg_preferred(const LaunchArgs& a) {
     return chunkwise_seg_supported(a) && (long)a.B * a.H * (a.DV / kW) < cus;
 }
 
-// Chunks of 512 with an output and plain operands: the two terms of the chunkwise form in two
-// kernels. The intra-chunk term (Q K^T (.) D) V runs on the parallel-form kernel restricted to each
+// Chunks of 512 (and 256) with an output and plain operands: the two terms of the chunkwise form in
+// two kernels. The intra-chunk term (Q K^T (.) D) V runs on the parallel-form kernel restricted to each
 // query's own chunk (fp32 rows; P as hi + lo there too); then the warp-specialised kernel without
 // an intra-chunk term adds g^(j+1) Q R to them (atomic fp32 adds, one per element) and carries the
 // state. Its stage buffers hold Q and K only (32 KiB at d_k = 256), so three fit beside the
 // 34 KiB V ring, where the stage buffers with the 512-key scores would not fit twice. With a
-// GroupNorm or a bf16 output the rows go through the fp32 staging in the workspace (the scores'
-// region, unused here, which holds N x 512 fp32 values per head).
-bool c512_split_ok(const LaunchArgs& a, int DK) {
+// GroupNorm or a bf16 output the rows go through the fp32 pre-norm staging in the workspace.
+bool intra_split_ok(const LaunchArgs& a, int DK) {
     const bool plain = a.addr.rev == 0 && (a.addr.ldqk == 0 || a.addr.ldqk == DK) && a.addr.qcol_blk == 0 &&
                        (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0;
     return plain && a.in_bf16 && a.out != nullptr && !a.qlo && !a.p_anti && !a.p_given && !a.no_pv && a.vs.split == 0 &&
            parallel_bf16_supported(DK, a.DV);
 }
 
-template <int DK, typename TOUT>
-hipError_t launch_c512(const LaunchArgs& a) {
-    constexpr int C = 512;
+template <int DK, int C, typename TOUT>
+hipError_t launch_intra_split(const LaunchArgs& a) {
     using G = WsGeom<DK, C, true, false, true>;
-    static_assert(G::BYTES <= kLdsBytes && p_lo<DK, C>(), "chunk-512 split: stage buffers and staging fit");
+    static_assert(G::BYTES <= kLdsBytes && p_lo<DK, C>(), "intra-chunk split: stage buffers and staging fit");
     const int nchunks = (a.N + C - 1) / C;
     const WsLayout l = ws_layout(a.B, a.H, a.N, a.DV, C, a.gn.enabled, true, true);
     const bool direct = !a.gn.enabled && sizeof(TOUT) == 4;
-    float* o32 = direct ? static_cast<float*>(a.out) : reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + l.p_off);
+    // fp32 staging of a GroupNorm or bf16 output: the pre-norm rows
+    float* o32 = direct ? static_cast<float*>(a.out) : reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + l.pre_off);
     LaunchArgs pa = a;  // the intra-chunk term: parallel form within each chunk, fp32 rows
     pa.out = o32;
     pa.out_bf16 = 0;
@@ -1243,8 +1244,10 @@ hipError_t launch_c512(const LaunchArgs& a) {
 template <int DK, int C, typename TOUT>
 hipError_t launch_dk_c(const LaunchArgs& a) {
     if (seg_preferred(a)) return launch_seg<TOUT>(a);
-    if constexpr (C == 512) {
-        if (c512_split_ok(a, DK)) return launch_c512<DK, TOUT>(a);
+    // chunks of 512 and 256 (measured 3.08 against 3.22 ms at N = 65536, chunk 256; at chunk 128 the
+    // split is slower, 480 against 427 us at the N = 8192 layer, and the fused kernel stays)
+    if constexpr (C == 512 || C == 256) {
+        if (intra_split_ok(a, DK)) return launch_intra_split<DK, C, TOUT>(a);
     }
     if (chunkwise_seg_state_supported(a)) return launch_chunkwise_seg_state(a, reinterpret_cast<float*>(a.ws));
     const int nchunks = (a.N + C - 1) / C;
