@@ -92,7 +92,8 @@ __device__ __forceinline__ void store_row4(T* y, int d, int lane, const float* v
 __constant__ double kExp2Frac[32] = {1.0, 1.0218971486541166, 1.0442737824274138, 1.0671404006768237, 1.0905077326652577, 1.1143867425958924, 1.1387886347566916, 1.1637248587775775, 1.189207115002721, 1.215247359980469, 1.241857812073484, 1.2690509571917332, 1.2968395546510096, 1.3252366431597413, 1.3542555469368927, 1.383909881963832, 1.4142135623730951, 1.4451808069770467, 1.4768261459394993, 1.5091644275934228, 1.5422108254079407, 1.5759808451078865, 1.6104903319492543, 1.645755478153965, 1.681792830507429, 1.718619298122478, 1.7562521603732995, 1.7947090750031072, 1.8340080864093424, 1.8741676341103, 1.9152065613971474, 1.9571441241754002};
 
 // exp(z) for z <= 0 in double precision: z = (32 m + j) ln2/32 + r with ln2/32 split in two (Cody
-// and Waite; n = 32 m + j times the high part is exact for |n| < 2^21), |r| <= ln2/64, exp(r) by its
+// and Waite; the two parts of ln 2 are the high/low split published with Sun's fdlibm, whose high
+// part has its low bits zero, so n = 32 m + j times it is exact for |n| < 2^21), |r| <= ln2/64, exp(r) by its
 // Taylor series to degree 6 (truncation below 4e-18 relative), times 2^(j/32) from the table in
 // LDS, scaled by 2^m (ldexp, which flushes to zero below the double range). z is clamped at -746,
 // below which exp is zero in double precision. Measured against libm's exp on [-700, 0]: relative
