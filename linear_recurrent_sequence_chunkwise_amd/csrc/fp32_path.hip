@@ -1,7 +1,7 @@
 // fp32-input retention on the vector ALU: the chunkwise form, the parallel form, and a row-wise
 // per-head GroupNorm pass. On gfx950 the fp32 matrix cores and the fp32 vector units have the
-// same peak rate, so this path uses plain fused multiply-adds with LDS-staged operands. It serves
-// fp32 workloads (small, tolerance 1e-4), where accuracy rather than throughput is the point.
+// same peak rate, so this path uses plain fused multiply-adds with LDS-staged operands and register
+// blocking. It serves fp32 inputs (tolerance 1e-4): every product and sum in fp32.
 //
 // Chunkwise form (abeam.tech RetNet summary, "Chunk recursion for long-sequence training"), for a
 // chunk of length L with carried state R and local row j:
@@ -15,68 +15,200 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCols = 64;  // d_v columns per workgroup
 
-// Grid: B*H*(DV/64) workgroups. Dynamic LDS: R [DK][64] fp32 then S [C][C] fp32.
-// Thread t: column t % 64, row group t / 64 (rows strided by 4).
-__global__ __launch_bounds__(kThreads) void chunk_f32_kernel(int H, int N, int DK, int DV, int C,
-                                                             const float* __restrict__ q, const float* __restrict__ k,
-                                                             const float* __restrict__ v, const float* __restrict__ state_in,
-                                                             float* __restrict__ state_out, float* __restrict__ out,
-                                                             HeadConsts hc, const float* __restrict__ vpre, int vsplit, int vshift) {
+// Grid: B*H*(DV/64) workgroups of 256 threads, one (b, h, 64-column slice) each, walking the
+// chunks in order. Thread (ty, tx) = (t / 16, t % 16) owns rows j = ty + 16 r of a chunk (r < C/16)
+// and columns 4 tx .. 4 tx + 3 of the slice; for the scores also keys tx + 16 c; for the state
+// rows d = ty + 16 r of R. Per chunk, with register blocking and operands staged in LDS:
+//   A  S = Q K^T and Q R together, over d_k in 16-wide tiles of Q and K (rows padded to 17 floats,
+//      so the 16 key rows a wave reads sit in distinct banks); then S (.) D into LDS and
+//      g^(j+1) Q R kept in registers;
+//   B  + S V over 16-token tiles of V; the rows go out as 16-byte stores;
+//   C  R <- g^L R + K^T (V (.) zeta) over 16-token tiles of K and zeta-scaled V.
+// LDS: R [DK][64], S [C][C+1], and one tile region shared by the phases.
+template <int DK, int C>
+__global__ __launch_bounds__(kThreads) void chunk_f32_kernel(int H, int N, int DV, const float* __restrict__ q,
+                                                             const float* __restrict__ k, const float* __restrict__ v,
+                                                             const float* __restrict__ state_in, float* __restrict__ state_out,
+                                                             float* __restrict__ out, HeadConsts hc, const float* __restrict__ vpre,
+                                                             int vsplit, int vshift) {
+    constexpr int RB = C / 16;    // chunk rows per thread (and key columns of S per thread)
+    constexpr int RD = DK / 16;   // state rows per thread
+    constexpr int TK = 16;        // d_k tile of phase A, token tile of phases B and C
+    constexpr int LQ = TK + 1;    // padded row of the Q and K tiles
     extern __shared__ float smem[];
+    float* R = smem;                                  // [DK][64]
+    float* S = R + DK * kCols;                        // [C][C + 1]
+    float* U = S + C * (C + 1);                       // tiles
+    float* Qs = U;                                    // A: [C][LQ]
+    float* Ks = U + C * LQ;                           // A: [C][LQ]
+    float* Vs = U;                                    // B: [TK][64]
+    float* Kt = U;                                    // C: [TK][DK]
+    float* Vt = U + TK * DK;                          // C: [TK][64]
     const int nsl = DV / kCols;
     const int bh = blockIdx.x / nsl, slice = blockIdx.x % nsl, h = bh % H;
-    const int col = threadIdx.x % kCols, rgp = threadIdx.x / kCols;
-    const int c = slice * kCols + col;
-    float* R = smem;             // [DK][64]
-    float* S = smem + DK * kCols;  // [C][C]
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const int col0 = slice * kCols;
     const float l2g = hc.log2g[h];
     const float* qh = q + (size_t)bh * N * DK;
     const float* kh = k + (size_t)bh * N * DK;
     const float* vh = v + (size_t)bh * N * DV;
-    // value row t: row t of the prefix buffer below vsplit, else row t - vshift of v (VShift)
-    auto vat = [&](int t) __attribute__((always_inline)) {
-        return t < vsplit ? vpre[((size_t)bh * vsplit + t) * DV + c] : vh[(size_t)(t - vshift) * DV + c];
+    // value row t, columns col0 + c .. + 3: row t of the prefix buffer below vsplit, else row t - vshift of v
+    auto vrow4 = [&](int t, int c) __attribute__((always_inline)) {
+        const float* p = t < vsplit ? vpre + ((size_t)bh * vsplit + t) * DV : vh + (size_t)(t - vshift) * DV;
+        return *reinterpret_cast<const float4*>(p + col0 + c);
     };
 
-    for (int i = rgp; i < DK; i += 4) R[i * kCols + col] = state_in ? state_in[((size_t)bh * DK + i) * DV + c] : 0.f;
+    for (int i = tid; i < DK * kCols; i += kThreads) {
+        const int d = i / kCols, c = i % kCols;
+        R[i] = state_in ? state_in[((size_t)bh * DK + d) * DV + col0 + c] : 0.f;
+    }
     __syncthreads();
 
     for (int c0 = 0; c0 < N; c0 += C) {
         const int L = min(C, N - c0);
         if (out) {
-            for (int idx = threadIdx.x; idx < L * L; idx += kThreads) {
-                const int j = idx / L, t = idx % L;
-                float s = 0.f;
-                if (t <= j) {
-                    const float* qj = qh + (size_t)(c0 + j) * DK;
-                    const float* kt = kh + (size_t)(c0 + t) * DK;
-                    for (int i = 0; i < DK; ++i) s += qj[i] * kt[i];
-                    s *= decay_pow(l2g, (float)(j - t));
+            // ---- A: S = Q K^T and Q R
+            float acc[RB][RB], aq[RB][4];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+#pragma unroll
+                for (int c = 0; c < RB; ++c) acc[r][c] = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) aq[r][c] = 0.f;
+            }
+            for (int d0 = 0; d0 < DK; d0 += TK) {
+                for (int f = tid; f < C * TK / 4; f += kThreads) {
+                    const int j = f / (TK / 4), kq = f % (TK / 4);
+                    float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+                    if (j < L) {
+                        a = *reinterpret_cast<const float4*>(qh + (size_t)(c0 + j) * DK + d0 + 4 * kq);
+                        b = *reinterpret_cast<const float4*>(kh + (size_t)(c0 + j) * DK + d0 + 4 * kq);
+                    }
+                    float* qd = Qs + j * LQ + 4 * kq;
+                    float* kd = Ks + j * LQ + 4 * kq;
+                    qd[0] = a.x; qd[1] = a.y; qd[2] = a.z; qd[3] = a.w;
+                    kd[0] = b.x; kd[1] = b.y; kd[2] = b.z; kd[3] = b.w;
                 }
-                S[j * C + t] = s;
+                __syncthreads();
+#pragma unroll 4
+                for (int kk = 0; kk < TK; ++kk) {
+                    float a[RB], b[RB];
+#pragma unroll
+                    for (int r = 0; r < RB; ++r) a[r] = Qs[(ty + 16 * r) * LQ + kk];
+#pragma unroll
+                    for (int c = 0; c < RB; ++c) b[c] = Ks[(tx + 16 * c) * LQ + kk];
+                    const float4 rr = *reinterpret_cast<const float4*>(R + (d0 + kk) * kCols + 4 * tx);
+#pragma unroll
+                    for (int r = 0; r < RB; ++r) {
+#pragma unroll
+                        for (int c = 0; c < RB; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
+                        aq[r][0] = fmaf(a[r], rr.x, aq[r][0]);
+                        aq[r][1] = fmaf(a[r], rr.y, aq[r][1]);
+                        aq[r][2] = fmaf(a[r], rr.z, aq[r][2]);
+                        aq[r][3] = fmaf(a[r], rr.w, aq[r][3]);
+                    }
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int j = ty + 16 * r;
+#pragma unroll
+                for (int c = 0; c < RB; ++c) {
+                    const int t = tx + 16 * c;
+                    S[j * (C + 1) + t] = t <= j && j < L ? acc[r][c] * decay_pow(l2g, (float)(j - t)) : 0.f;
+                }
+                const float dj = decay_pow(l2g, (float)(j + 1));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) aq[r][c] *= dj;
             }
             __syncthreads();
-            for (int j = rgp; j < L; j += 4) {
-                const float* qj = qh + (size_t)(c0 + j) * DK;
-                float inter = 0.f;
-                for (int i = 0; i < DK; ++i) inter += qj[i] * R[i * kCols + col];
-                float intra = 0.f;
-                for (int t = 0; t <= j; ++t) intra += S[j * C + t] * vat(c0 + t);
-                out[((size_t)bh * N + c0 + j) * DV + c] = intra + decay_pow(l2g, (float)(j + 1)) * inter;
+            // ---- B: + S V
+            for (int t0 = 0; t0 < L; t0 += TK) {
+                {
+                    const int tt = tid / 16, cq = tid % 16;
+                    const float4 x = t0 + tt < L ? vrow4(c0 + t0 + tt, 4 * cq) : float4{0.f, 0.f, 0.f, 0.f};
+                    *reinterpret_cast<float4*>(Vs + tt * kCols + 4 * cq) = x;
+                }
+                __syncthreads();
+#pragma unroll 4
+                for (int tt = 0; tt < TK; ++tt) {
+                    const float4 vv = *reinterpret_cast<const float4*>(Vs + tt * kCols + 4 * tx);
+#pragma unroll
+                    for (int r = 0; r < RB; ++r) {
+                        const float sv = S[(ty + 16 * r) * (C + 1) + t0 + tt];
+                        aq[r][0] = fmaf(sv, vv.x, aq[r][0]);
+                        aq[r][1] = fmaf(sv, vv.y, aq[r][1]);
+                        aq[r][2] = fmaf(sv, vv.z, aq[r][2]);
+                        aq[r][3] = fmaf(sv, vv.w, aq[r][3]);
+                    }
+                }
+                __syncthreads();
             }
-            __syncthreads();  // R is read above and rewritten below
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int j = ty + 16 * r;
+                if (j < L)
+                    *reinterpret_cast<float4*>(out + ((size_t)bh * N + c0 + j) * DV + col0 + 4 * tx) =
+                        float4{aq[r][0], aq[r][1], aq[r][2], aq[r][3]};
+            }
         }
+        // ---- C: R <- g^L R + K^T (V (.) zeta), zeta_t = g^(L-1-t)
+        float ar[RD][4];
         const float gL = decay_pow(l2g, (float)L);
-        for (int i = rgp; i < DK; i += 4) {
-            float acc = 0.f;
-            for (int t = 0; t < L; ++t)
-                acc += decay_pow(l2g, (float)(L - 1 - t)) * kh[(size_t)(c0 + t) * DK + i] * vat(c0 + t);
-            R[i * kCols + col] = gL * R[i * kCols + col] + acc;
+#pragma unroll
+        for (int r = 0; r < RD; ++r) {
+            const float4 x = *reinterpret_cast<const float4*>(R + (ty + 16 * r) * kCols + 4 * tx);
+            ar[r][0] = gL * x.x; ar[r][1] = gL * x.y; ar[r][2] = gL * x.z; ar[r][3] = gL * x.w;
         }
+        for (int t0 = 0; t0 < L; t0 += TK) {
+            for (int f = tid; f < TK * DK / 4; f += kThreads) {
+                const int tt = f / (DK / 4), dq = f % (DK / 4);
+                const float4 x = t0 + tt < L ? *reinterpret_cast<const float4*>(kh + (size_t)(c0 + t0 + tt) * DK + 4 * dq)
+                                             : float4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<float4*>(Kt + tt * DK + 4 * dq) = x;
+            }
+            {
+                const int tt = tid / 16, cq = tid % 16, t = t0 + tt;
+                float4 x = {0.f, 0.f, 0.f, 0.f};
+                if (t < L) {
+                    x = vrow4(c0 + t, 4 * cq);
+                    const float z = decay_pow(l2g, (float)(L - 1 - t));
+                    x.x *= z; x.y *= z; x.z *= z; x.w *= z;
+                }
+                *reinterpret_cast<float4*>(Vt + tt * kCols + 4 * cq) = x;
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int tt = 0; tt < TK; ++tt) {
+                const float4 vv = *reinterpret_cast<const float4*>(Vt + tt * kCols + 4 * tx);
+#pragma unroll
+                for (int r = 0; r < RD; ++r) {
+                    const float kv = Kt[tt * DK + ty + 16 * r];
+                    ar[r][0] = fmaf(kv, vv.x, ar[r][0]);
+                    ar[r][1] = fmaf(kv, vv.y, ar[r][1]);
+                    ar[r][2] = fmaf(kv, vv.z, ar[r][2]);
+                    ar[r][3] = fmaf(kv, vv.w, ar[r][3]);
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < RD; ++r)
+            *reinterpret_cast<float4*>(R + (ty + 16 * r) * kCols + 4 * tx) = float4{ar[r][0], ar[r][1], ar[r][2], ar[r][3]};
         __syncthreads();
     }
     if (state_out)
-        for (int i = rgp; i < DK; i += 4) state_out[((size_t)bh * DK + i) * DV + c] = R[i * kCols + col];
+        for (int i = tid; i < DK * kCols; i += kThreads) {
+            const int d = i / kCols, c = i % kCols;
+            state_out[((size_t)bh * DK + d) * DV + col0 + c] = R[i];
+        }
+}
+
+template <int DK, int C>
+size_t chunk_f32_lds() {
+    constexpr size_t tiles = (2 * C * 17 > 16 * DK + 16 * kCols) ? 2 * C * 17 : 16 * DK + 16 * kCols;
+    return ((size_t)DK * kCols + (size_t)C * (C + 1) + tiles) * sizeof(float);
 }
 
 // Grid: (ceil(N/64), B*H*(DV/64)). Thread t: column t % 64, query rows rgp, rgp+4, ... (16 rows).
@@ -191,17 +323,28 @@ size_t parallel_f32_workspace(int B, int H, int N, int DV, int gn, int out_bf16)
     return chunkwise_f32_workspace(B, H, N, DV, gn, out_bf16);
 }
 
+template <int DK, int C>
+hipError_t launch_chunk_f32_t(const LaunchArgs& a, float* pre) {
+    const size_t lds = chunk_f32_lds<DK, C>();
+    const void* kern = reinterpret_cast<const void*>(chunk_f32_kernel<DK, C>);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_f32_kernel<DK, C>), dim3(a.B * a.H * (a.DV / kCols)), dim3(kThreads), lds, a.stream, a.H, a.N, a.DV,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, a.state_in, a.state_out, pre, a.hc,
+                       (const float*)a.vs.pre, a.vs.split, a.vs.shift);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_chunk_f32_dk(const LaunchArgs& a, float* pre) {
+    return a.chunk == 64 ? launch_chunk_f32_t<DK, 64>(a, pre) : launch_chunk_f32_t<DK, 128>(a, pre);
+}
+
 hipError_t launch_chunkwise_f32(const LaunchArgs& a) {
     const bool stage = a.out && needs_staging(a.gn.enabled, a.out_bf16);
     float* pre = a.out ? (stage ? (float*)a.ws : (float*)a.out) : nullptr;
-    const size_t lds = ((size_t)a.DK * kCols + (size_t)a.chunk * a.chunk) * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_f32_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_f32_kernel, dim3(a.B * a.H * (a.DV / kCols)), dim3(kThreads), lds, a.stream, a.H, a.N, a.DK, a.DV,
-                       a.chunk, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.state_in, a.state_out, pre, a.hc,
-                       (const float*)a.vs.pre, a.vs.split, a.vs.shift);
-    e = hipGetLastError();
+    hipError_t e = a.DK == 64 ? launch_chunk_f32_dk<64>(a, pre) : a.DK == 128 ? launch_chunk_f32_dk<128>(a, pre)
+                                                                             : launch_chunk_f32_dk<256>(a, pre);
     if (e != hipSuccess || !stage) return e;
     return finish(a, pre);
 }
