@@ -185,19 +185,35 @@ size_t split_parts_bytes(const ret_shape* s, bool gn, bool acc, int chunk) {
 // Rotated q and k of a bf16 forward call as high and low parts: four planes.
 size_t rotation_split_ws(const ret_shape* s) { return 2 * rotation_ws(s); }
 
-// Writes the four planes (q_hi, q_lo, k_hi, k_lo) at the front of *ws and advances it past them.
-hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, const void* q, const void* k, const void* parts[4],
-                                void** ws, size_t* wsb, hipStream_t st) {
+// Places the four planes (q_hi, q_lo, k_hi, k_lo) at the front of *ws and advances it past them.
+void place_rotation_split(const ret_shape* s, void* parts[4], void** ws, size_t* wsb) {
     const size_t A = rotation_ws(s) / 2;
     char* base = static_cast<char*>(*ws);
-    const long rows = (long)s->batch * s->heads * s->seq_len;
-    const hipError_t e = ret::launch_rotate2(rows, s->seq_len, s->d_k, q, base, k, base + 2 * A, 1, 1, rc, 0, st, base + A, base + 3 * A);
-    if (e != hipSuccess) return e;
     for (int i = 0; i < 4; ++i) parts[i] = base + i * A;
     *ws = base + 4 * A;
     *wsb -= 4 * A;
+}
+
+// Writes the four planes (q_hi, q_lo, k_hi, k_lo) at the front of *ws and advances it past them.
+hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, const void* q, const void* k, const void* parts[4],
+                                void** ws, size_t* wsb, hipStream_t st) {
+    void* pl[4];
+    place_rotation_split(s, pl, ws, wsb);
+    const long rows = (long)s->batch * s->heads * s->seq_len;
+    const hipError_t e = ret::launch_rotate2(rows, s->seq_len, s->d_k, q, pl[0], k, pl[2], 1, 1, rc, 0, st, pl[1], pl[3]);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < 4; ++i) parts[i] = pl[i];
     return hipSuccess;
 }
+
+// The rotation of a split call done by its scores kernel: the unrotated q and k, the constants,
+// and the planes that kernel writes (then read by the chunk passes as qh, ql, kh, kl).
+struct FusedRot {
+    const void* q;
+    const void* k;
+    const ret::RotConsts* rc;
+    void* planes[4];
+};
 
 // The partial calls and the sums. a: the call (q and k unset; out, state_in, state_out, gn and
 // out_bf16 as the caller asked), parts: split_parts_bytes(shape, gn, acc, chunk) of workspace; launch: the
@@ -206,7 +222,7 @@ hipError_t stage_rotation_split(const ret_shape* s, const ret::RotConsts& rc, co
 // (q_hi + q_lo, k_hi). An in-place state_in is read by the calls that need it before the last call
 // writes state_out.
 hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, const void* kh, const void* kl, char* parts,
-                     hipError_t (*launch)(const ret::LaunchArgs&), bool acc) {
+                     hipError_t (*launch)(const ret::LaunchArgs&), bool acc, const FusedRot* fr = nullptr) {
     const size_t rows = (size_t)a.B * a.H * a.N;
     const size_t ob = align256(rows * a.DV * sizeof(float));
     const bool staged = a.out_bf16 || a.gn.enabled;  // the sum goes through the workspace
@@ -222,7 +238,9 @@ hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, c
             // two calls sharing one scores pass over all three products: (q_hi, k_lo) with those
             // scores stores its rows and its state; (q_hi + q_lo, k_hi) without an intra-chunk term
             // adds its rows and writes the state from state_in
-            if ((e = ret::launch_chunkwise_bf16_scores(a, qh, ql, kh, kl, sc)) != hipSuccess) return e;
+            e = fr ? ret::launch_chunkwise_bf16_scores_rot(a, fr->q, fr->k, *fr->rc, fr->planes, sc)
+                   : ret::launch_chunkwise_bf16_scores(a, qh, ql, kh, kl, sc);
+            if (e != hipSuccess) return e;
             c.q = qh; c.k = kl; c.p_given = sc; c.out = o; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
             if ((e = launch(c)) != hipSuccess) return e;
             c.p_given = nullptr;
@@ -230,6 +248,8 @@ hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, c
             c.no_pv = 1;
             c.q = qh; c.qlo = ql; c.k = kh; c.state_in = a.state_in; c.state_out = a.state_out;
             if ((e = launch(c)) != hipSuccess) return e;
+        } else if (fr) {
+            return hipErrorInvalidValue;  // the planes are written only by the two-call split's scores
         } else if (a.out && ret::chunkwise_bf16_qlo_supported(a.DK, a.chunk)) {
             // two calls: (q_hi, k_lo) stores its rows and its state; (q_hi + q_lo, k_hi), on the
             // kernel that takes q as two parts, adds its rows and writes the state from state_in
@@ -530,16 +550,26 @@ int ret::chunkwise_fwd_entry(const ret_shape* shape, int32_t chunk, const void* 
     RET_TRY(check_ws(need, workspace, workspace_bytes));
     const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (rot && bf) {
-        // rotated bf16 operands as high and low parts, three calls (the rotated values rounded once
-        // to bf16 would move the output by up to 2.4e-2 of its RMS)
+        // rotated bf16 operands as high and low parts, three products (the rotated values rounded
+        // once to bf16 would move the output by up to 2.4e-2 of its RMS). With an output at the
+        // chunks of the two-call split, its scores kernel turns q and k itself and writes the
+        // planes; else a rotation pass writes them first.
         const void* pq[4];
-        hipError_t e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, st);
-        if (e != hipSuccess) return device_status(e, "retention_chunkwise_fwd rotation launch");
+        FusedRot fr;
+        const bool fuse = out && ret::chunkwise_bf16_split2_supported(shape->d_k, chunk);
+        hipError_t e = hipSuccess;
+        if (fuse) {
+            place_rotation_split(shape, fr.planes, &workspace, &workspace_bytes);
+            fr.q = q; fr.k = k; fr.rc = &rc;
+            for (int i = 0; i < 4; ++i) pq[i] = fr.planes[i];
+        } else if ((e = stage_rotation_split(shape, rc, q, k, pq, &workspace, &workspace_bytes, st)) != hipSuccess) {
+            return device_status(e, "retention_chunkwise_fwd rotation launch");
+        }
         char* parts = static_cast<char*>(workspace);
         const size_t pb = split_parts_bytes(shape, gn.enabled, true, chunk);
         ret::LaunchArgs a = base_args(shape, chunk, hc, gn, parts + pb, workspace_bytes - pb, hip_stream);
         a.v = v; a.out = out; a.state_in = state_in; a.state_out = state_out;
-        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_chunkwise_bf16, true);
+        e = run_split(a, pq[0], pq[1], pq[2], pq[3], parts, ret::launch_chunkwise_bf16, true, fuse ? &fr : nullptr);
         return device_status(e, "retention_chunkwise_fwd launch");
     }
     if (rot) {

@@ -51,12 +51,73 @@ constexpr int kST = 32;    // tokens per pipeline stage
 // Waves take row tiles in mirrored pairs (t, T-1-t) so that the causal work is balanced.
 // KLO: k comes as two parts too (k + klo), and Q K^T = q K^T + qlo K^T + q Klo^T (the qlo Klo^T
 // term, about 2^-16 relative, dropped): the K and Klo blocks of 64 keys sit side by side in LDS.
-template <int DK, bool KLO = false>
+// ROT (with KLO, plain operand addressing): q and k come unrotated, and the kernel applies the
+// positional rotation itself (abeam.tech RetNet summary, "Technical mechanism": Q and K are turned
+// after the projections), split into bf16 high and low parts, which the scores use as above and
+// which are also written out (rf.qh, rf.ql, rf.kh, rf.kl, [B*H][N][DK]) for the chunk passes that
+// follow. First the chunk's q rows pass through the K blocks' LDS, 128 rows at a time, are turned
+// and written out; the Q fragments are then read back from there. Each K block is turned in LDS
+// after its load. Each thread turns one 16-byte piece (4 pairs) of consecutive rows: sin and cos
+// at the first row and of the one-position step, then angle addition (as the rotation pass does;
+// about one rounding per step).
+struct RotFuse {
+    bf16 *qh, *ql, *kh, *kl;
+    RotConsts rc;
+};
+struct NoRot {};
+template <bool ROT> struct RotSel { typedef NoRot type; };
+template <> struct RotSel<true> { typedef RotFuse type; };
+
+// Turns piece c (features 8c .. 8c+7, pairs 4c .. 4c+3) of rows r0 .. r0+nr-1 of a block in LDS
+// (rows of QRB bytes, swizzled as SwzTile<QRB>) holding sequence positions pos0 + r: high and low
+// parts to hi_at / lo_at (LDS; lo_at null: not kept) and, for positions below N, to the planes
+// gh / gl (row pos of [N][DK] at this head).
+template <int QRB>
+__device__ __forceinline__ void turn_rows(char* blk, char* hi_at, char* lo_at, int c, int r0, int nr, int pos0, int N,
+                                          const RotConsts& rc, bf16* gh, bf16* gl) {
+    constexpr int DK = QRB / 2;
+    float sn[4], cn[4], ss[4], cs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = 4 * c + j;
+        rot_sincos(pos0 + r0, rc.fhi[i], rc.flo[i], rc.ph[i], sn[j], cn[j]);
+        sincospif(rc.fhi[i] + rc.flo[i], &ss[j], &cs[j]);
+    }
+    for (int rr = 0; rr < nr; ++rr) {
+        const int r = r0 + rr, pos = pos0 + r;
+        const int byte = r * QRB + 16 * (c ^ (r & SwzTile<QRB>::M));
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(blk + byte);
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = (float)x[2 * j], b = (float)x[2 * j + 1];
+            bf16 h, l;
+            split_hi_lo(a * cn[j] - b * sn[j], h, l);
+            hi[2 * j] = h;
+            lo[2 * j] = l;
+            split_hi_lo(a * sn[j] + b * cn[j], h, l);
+            hi[2 * j + 1] = h;
+            lo[2 * j + 1] = l;
+            const float c2 = cn[j] * cs[j] - sn[j] * ss[j];
+            sn[j] = sn[j] * cs[j] + cn[j] * ss[j];
+            cn[j] = c2;
+        }
+        if (hi_at) *reinterpret_cast<bf16x8*>(hi_at + byte) = hi;
+        if (lo_at) *reinterpret_cast<bf16x8*>(lo_at + byte) = lo;
+        if (pos < N) {
+            *reinterpret_cast<bf16x8*>(gh + (size_t)pos * DK + 8 * c) = hi;
+            *reinterpret_cast<bf16x8*>(gl + (size_t)pos * DK + 8 * c) = lo;
+        }
+    }
+}
+
+template <int DK, bool KLO = false, bool ROT = false>
 __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, int nchunks, const bf16* __restrict__ q,
                                                            const bf16* __restrict__ qlo, const bf16* __restrict__ k,
                                                            const bf16* __restrict__ klo, bf16* __restrict__ P,
                                                            bf16* __restrict__ Plo, bf16* __restrict__ Pa, HeadConsts hc, int rev,
-                                                           int ldqk, int qcol_blk, int srcBH) {
+                                                           int ldqk, int qcol_blk, int srcBH, typename RotSel<ROT>::type rf) {
+    static_assert(!ROT || KLO, "the rotated scores use both parts of k");
     constexpr int KB = KLO ? 64 : 128;  // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row
     constexpr int NKB = KB * QRB / 1024;  // kilobytes of a K block
@@ -72,7 +133,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + qbase), 0, q_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rql = __builtin_amdgcn_make_buffer_rsrc((void*)((qlo ? qlo : q) + qbase), 0, q_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc((void*)((KLO ? klo : k) + qbase), 0, q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc((void*)((KLO && !ROT ? klo : k) + qbase), 0, q_bytes, 0x00020000);
     auto row_of = [&](int t) __attribute__((always_inline)) { return rev ? N - 1 - t : t; };
     bf16* Pc = P + ((size_t)bh * nchunks + chunk) * (size_t)C * C;
     bf16* Plc = Plo ? Plo + ((size_t)bh * nchunks + chunk) * (size_t)C * C : nullptr;
@@ -80,6 +141,34 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
     bf16* Pac = Pa ? Pa + ((size_t)bh * nchunks + (nchunks - 1 - chunk)) * (size_t)C * C : nullptr;
     bf16* Palc = Pa ? Pac + (size_t)gridDim.y * nchunks * C * C : nullptr;
     const int T = C / 16;  // row tiles of the chunk
+    constexpr int UPR = QRB / 16;  // 16-byte pieces per row
+    if constexpr (ROT) {
+        // the chunk's q rows, 2 KB at a time through the K blocks' LDS, turned and written out
+        for (int rb = 0; rb < C; rb += 2 * KB) {
+            const int rows = min(2 * KB, C - rb);
+            if (rb > 0) __syncthreads();
+            for (int j = w; j < rows * QRB / 1024; j += 4) {
+                const int byte = 1024 * j + 16 * lane, r = byte / QRB;
+                const int c = ((byte % QRB) >> 4) ^ (r & SwzTile<QRB>::M);
+                const unsigned off = (unsigned)(((c0 + rb + r) * DK + 8 * c) * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(Ks + 1024 * j), 16, off, 0, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            const int rpt = rows * UPR / 256;
+            turn_rows<QRB>(Ks, nullptr, nullptr, threadIdx.x % UPR, (threadIdx.x / UPR) * rpt, rpt, c0 + rb, N, rf.rc,
+                           rf.qh + (size_t)bh * N * DK, rf.ql + (size_t)bh * N * DK);
+        }
+        __syncthreads();  // the q rows are read and written out
+    }
+    // ROT: the turned q rows, as written out (rows past the sequence read as zero)
+    const bf16 *qp = q, *qlp = q;
+    if constexpr (ROT) {
+        qp = rf.qh + (size_t)bh * N * DK;
+        qlp = rf.ql + (size_t)bh * N * DK;
+    }
+    const __amdgpu_buffer_rsrc_t rqh = __builtin_amdgcn_make_buffer_rsrc((void*)qp, 0, (unsigned)((size_t)N * DK * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rqhl = __builtin_amdgcn_make_buffer_rsrc((void*)qlp, 0, (unsigned)((size_t)N * DK * 2), 0x00020000);
 
     for (int kb0 = 0; kb0 < C; kb0 += KB) {
         // K rows kb0 .. kb0+KB-1 of the chunk (rows past the sequence read as zero)
@@ -89,24 +178,40 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
             const int c = ((byte % QRB) >> 4) ^ (r & SwzTile<QRB>::M);
             const unsigned off = (unsigned)((row_of(c0 + kb0 + r) * ldqk + 8 * c) * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + 1024 * j), 16, off, 0, 0, 0);
-            if constexpr (KLO)
+            if constexpr (KLO && !ROT)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rkl, (__attribute__((address_space(3))) void*)(Ks + KB * QRB + 1024 * j), 16, off,
                                                          0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+        if constexpr (ROT) {
+            // the K block turned in place (high part), its low part into the Klo block
+            constexpr int RPT = KB * UPR / 256;
+            turn_rows<QRB>(Ks, Ks, Ks + KB * QRB, threadIdx.x % UPR, (threadIdx.x / UPR) * RPT, RPT, c0 + kb0, N, rf.rc,
+                           rf.kh + (size_t)bh * N * DK, rf.kl + (size_t)bh * N * DK);
+            __syncthreads();
+        }
         for (int m = 0; m < T / 4; ++m) {
             const int t = (m & 1) ? 4 * m + 3 - w : 4 * m + w;  // mirrored within each group of 8
             const int last = min((t | 1), (kb0 + KB) / 16 - 1);  // last key tile of this block
             if (last * 16 < kb0) continue;
             bf16x8 qf[DK / 32];
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                const unsigned off = (unsigned)((row_of(c0 + 16 * t + c16) * ldqk + 32 * ks + 8 * g4) * 2);
-                qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-            }
             bf16x8 qlf[DK / 32];
-            if (qlo) {
+            if constexpr (ROT) {
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const unsigned off = (unsigned)(((c0 + 16 * t + c16) * DK + 32 * ks + 8 * g4) * 2);
+                    qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rqh, off, 0, 0));
+                    qlf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rqhl, off, 0, 0));
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const unsigned off = (unsigned)((row_of(c0 + 16 * t + c16) * ldqk + 32 * ks + 8 * g4) * 2);
+                    qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+                }
+            }
+            if (!ROT && qlo) {
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks) {
                     const unsigned off = (unsigned)((row_of(c0 + 16 * t + c16) * ldqk + 32 * ks + 8 * g4) * 2);
@@ -143,7 +248,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
                     f32x4 al = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < DK / 32; ++ks) {
-                        if (qlo) al = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qlf[ks], al);
+                        if (ROT || qlo) al = mfma16(frag_rowmajor_swz<QRB>(Ks, 16 * kt - kb0, 32 * ks, lane), qlf[ks], al);
                         if constexpr (KLO) al = mfma16(frag_rowmajor_swz<QRB>(Ks + KB * QRB, 16 * kt - kb0, 32 * ks, lane), qf[ks], al);
                     }
                     acc += al;
@@ -1278,7 +1383,7 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     if (!a.p_given && !a.no_pv) {
         hipLaunchKernelGGL(chunk_scores_kernel<DK>, dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream, a.H, a.N, C, nchunks, mp.q,
                            mp.qlo, mp.k, nullptr, const_cast<bf16*>(mp.P), const_cast<bf16*>(mp.Plo), static_cast<bf16*>(a.p_anti),
-                           a.hc, mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH);
+                           a.hc, mp.rev, mp.ldqk, mp.qcol_blk, mp.srcBH, NoRot{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1372,12 +1477,37 @@ hipError_t launch_chunkwise_bf16_scores(const LaunchArgs& a, const void* q, cons
     const dim3 grid(nchunks, a.B * a.H);
     const int BH = a.B * a.H;
     if (a.DK == 64) {
-        if (kl) hipLaunchKernelGGL((chunk_scores_kernel<64, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, kl, ph, pl, nullptr, a.hc, 0, 64, 0, BH);
-        else hipLaunchKernelGGL((chunk_scores_kernel<64, false>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, nullptr, ph, pl, nullptr, a.hc, 0, 64, 0, BH);
+        if (kl) hipLaunchKernelGGL((chunk_scores_kernel<64, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, kl, ph, pl, nullptr, a.hc, 0, 64, 0, BH, NoRot{});
+        else hipLaunchKernelGGL((chunk_scores_kernel<64, false>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, nullptr, ph, pl, nullptr, a.hc, 0, 64, 0, BH, NoRot{});
     } else {
-        if (kl) hipLaunchKernelGGL((chunk_scores_kernel<256, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, kl, ph, pl, nullptr, a.hc, 0, 256, 0, BH);
-        else hipLaunchKernelGGL((chunk_scores_kernel<256, false>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, nullptr, ph, pl, nullptr, a.hc, 0, 256, 0, BH);
+        if (kl) hipLaunchKernelGGL((chunk_scores_kernel<256, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, kl, ph, pl, nullptr, a.hc, 0, 256, 0, BH, NoRot{});
+        else hipLaunchKernelGGL((chunk_scores_kernel<256, false>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, ql, k_, nullptr, ph, pl, nullptr, a.hc, 0, 256, 0, BH, NoRot{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunkwise_bf16_scores_rot(const LaunchArgs& a, const void* q, const void* k, const RotConsts& rc, void* const planes[4],
+                                            void* P) {
+    const int C = a.chunk, nchunks = (a.N + C - 1) / C;
+    if (a.N <= 0 || a.B * a.H <= 0) return hipSuccess;
+    if (!(a.DK == 64 || a.DK == 256) || !p_lo_used(a.DK, C)) return hipErrorInvalidValue;
+    bf16* ph = static_cast<bf16*>(P);
+    bf16* pl = ph + (size_t)a.B * a.H * nchunks * C * C;
+    RotFuse rf;
+    rf.qh = static_cast<bf16*>(planes[0]);
+    rf.ql = static_cast<bf16*>(planes[1]);
+    rf.kh = static_cast<bf16*>(planes[2]);
+    rf.kl = static_cast<bf16*>(planes[3]);
+    rf.rc = rc;
+    const bf16 *q_ = static_cast<const bf16*>(q), *k_ = static_cast<const bf16*>(k);
+    const dim3 grid(nchunks, a.B * a.H);
+    const int BH = a.B * a.H;
+    if (a.DK == 64)
+        hipLaunchKernelGGL((chunk_scores_kernel<64, true, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, nullptr, k_,
+                           nullptr, ph, pl, nullptr, a.hc, 0, 64, 0, BH, rf);
+    else
+        hipLaunchKernelGGL((chunk_scores_kernel<256, true, true>), grid, dim3(256), 0, a.stream, a.H, a.N, C, nchunks, q_, nullptr, k_,
+                           nullptr, ph, pl, nullptr, a.hc, 0, 256, 0, BH, rf);
     return hipGetLastError();
 }
 

@@ -274,6 +274,11 @@ bool chunkwise_bf16_split2_supported(int DK, int chunk);
 // The scores kernel alone (plain operands, a.B, a.H, a.N, a.DK, a.chunk, a.hc): P = q k^T (+ qlo k^T
 // with qlo, + q klo^T with klo) as bf16 high and low planes at P (chunkwise_bf16_scores_bytes).
 hipError_t launch_chunkwise_bf16_scores(const LaunchArgs& a, const void* q, const void* qlo, const void* k, const void* klo, void* P);
+// The same scores of the rotated q and k from unrotated q and k (plain addressing): the kernel
+// turns them itself and also writes the rotated operands as bf16 high and low parts, planes =
+// {q_hi, q_lo, k_hi, k_lo}, each [B*H][N][DK].
+hipError_t launch_chunkwise_bf16_scores_rot(const LaunchArgs& a, const void* q, const void* k, const RotConsts& rc, void* const planes[4],
+                                            void* P);
 // The segmented bf16 chunkwise kernels (chunk_seg.hip): plain operands, an output, d_k 64 or 256,
 // chunk 64 or 128, d_v a multiple of 64. U: the segment states in the workspace; out: the call's
 // output, or fp32 pre-norm rows when out_f32 (a GroupNorm pass follows).
