@@ -242,8 +242,10 @@ hipError_t run_split(const ret::LaunchArgs& a, const void* qh, const void* ql, c
                    : ret::launch_chunkwise_bf16_scores(a, qh, ql, kh, kl, sc);
             if (e != hipSuccess) return e;
             c.q = qh; c.k = kl; c.p_given = sc; c.out = o; c.state_in = nullptr; c.state_out = a.state_out ? s2 : nullptr;
+            c.lo_state = 1;  // its state term is about 2^-8 of the result: single bf16 parts suffice
             if ((e = launch(c)) != hipSuccess) return e;
             c.p_given = nullptr;
+            c.lo_state = 0;
             c.addr.out_acc = 1;
             c.no_pv = 1;
             c.q = qh; c.qlo = ql; c.k = kh; c.state_in = a.state_in; c.state_out = a.state_out;

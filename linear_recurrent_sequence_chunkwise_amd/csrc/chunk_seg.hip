@@ -700,7 +700,7 @@ hipError_t seg_launch_dk(const LaunchArgs& a, float* U, void* out) {
 
 bool chunkwise_seg_supported(const LaunchArgs& a) {
     const bool plain = a.addr.rev == 0 && (a.addr.ldqk == 0 || a.addr.ldqk == a.DK) && a.addr.qcol_blk == 0 &&
-                       (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0 && a.qlo == nullptr && !a.p_anti && !a.p_given && a.vs.split == 0;
+                       (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0 && a.qlo == nullptr && !a.p_anti && !a.p_given && !a.lo_state && a.vs.split == 0;
     return plain && a.in_bf16 && a.out != nullptr && (a.DK == 64 || a.DK == 256) && (a.chunk == 64 || a.chunk == 128) &&
            seg_width(a.DV) != 0;
 }
@@ -708,7 +708,7 @@ bool chunkwise_seg_supported(const LaunchArgs& a) {
 // A state-only call (no output) with plain operands that the segment-state kernel serves.
 bool chunkwise_seg_state_supported(const LaunchArgs& a) {
     const bool plain = a.addr.rev == 0 && (a.addr.ldqk == 0 || a.addr.ldqk == a.DK) && a.addr.qcol_blk == 0 &&
-                       (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0 && a.qlo == nullptr && !a.p_anti && !a.p_given && a.vs.split == 0;
+                       (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0 && a.qlo == nullptr && !a.p_anti && !a.p_given && !a.lo_state && a.vs.split == 0;
     return plain && a.in_bf16 && a.out == nullptr && a.state_out != nullptr && (a.DK == 64 || a.DK == 256) && seg_width(a.DV) != 0;
 }
 

@@ -702,7 +702,11 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int C, typename TOUT, bool VSH, bool PLO, bool QLO = false, bool NOP = false>
+// LT: the state term of a correction call (the (q_hi, k_lo) call of a two-call split, whose k is
+// the low part of a k that bf16 does not hold, 2^-8 of it or less): V (.) zeta and R enter the
+// matrix cores as single bf16 values (about 2^-9 relative of a term that is itself about 2^-8 of
+// the result); P V keeps P as hi + lo.
+template <int DK, int C, typename TOUT, bool VSH, bool PLO, bool QLO = false, bool NOP = false, bool LT = false>
 __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts hc) {
     using G = WsGeom<DK, C, PLO, QLO, NOP>;
     constexpr int NB = G::NB;
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                     const int col = 16 * ct + c16, row = wl * (DK / 4) + 16 * rt + 4 * g4;
                     const int o = SwzTile<G::QRB>::off(col, row >> 3) + (row & 7) * 2;
                     *reinterpret_cast<bf16x4*>(b + o) = hi;
-                    *reinterpret_cast<bf16x4*>(b + G::OFF_K + o) = lo;
+                    if constexpr (!LT) *reinterpret_cast<bf16x4*>(b + G::OFF_K + o) = lo;
                 }
         };
         auto scale_R = [&](int L) __attribute__((always_inline)) {
@@ -942,10 +946,14 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                     const bf16x8 vv = lds_frag_kmajor(Vb, G::LV, 0, 16 * ct, lane);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        bf16 a, c;
-                        split_hi_lo((float)vv[j] * z[j], a, c);
-                        bhi[ct][j] = a;
-                        blo[ct][j] = c;
+                        if constexpr (LT) {
+                            bhi[ct][j] = (bf16)((float)vv[j] * z[j]);
+                        } else {
+                            bf16 a, c;
+                            split_hi_lo((float)vv[j] * z[j], a, c);
+                            bhi[ct][j] = a;
+                            blo[ct][j] = c;
+                        }
                     }
                 }
             }
@@ -960,7 +968,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     accR[rt][ct] = mfma16(ak[rt], bhi[ct], accR[rt][ct]);
-                    accR[rt][ct] = mfma16(ak[rt], blo[ct], accR[rt][ct]);
+                    if constexpr (!LT) accR[rt][ct] = mfma16(ak[rt], blo[ct], accR[rt][ct]);
                 }
             lds_barrier();  // stage g consumed; stage g+1 in LDS
             if (chunk_end && g + 1 < total) {
@@ -1009,7 +1017,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks) {
                     rfh[ks] = frag_rowmajor_swz<G::QRB>(Rb, 16 * ct_o, 32 * ks, lane);
-                    rfl[ks] = frag_rowmajor_swz<G::QRB>(Rb + G::OFF_K, 16 * ct_o, 32 * ks, lane);
+                    if constexpr (!LT) rfl[ks] = frag_rowmajor_swz<G::QRB>(Rb + G::OFF_K, 16 * ct_o, 32 * ks, lane);
                 }
                 lds_barrier();
             }
@@ -1036,7 +1044,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 qa[2 * (ks & 1)] = mfma16(qf[ks], rfh[ks], qa[2 * (ks & 1)]);
-                qa[2 * (ks & 1) + 1] = mfma16(qf[ks], rfl[ks], qa[2 * (ks & 1) + 1]);
+                if constexpr (!LT) qa[2 * (ks & 1) + 1] = mfma16(qf[ks], rfl[ks], qa[2 * (ks & 1) + 1]);
             }
             if constexpr (QLO) {
                 const char* Qls = buf(g) + G::OFF_QL;
@@ -1225,15 +1233,16 @@ bool p_lo_dk(int C) {
 // whether a call with an output at (DK, C) keeps the low part of P
 bool p_lo_used(int DK, int C) { return DK == 64 ? p_lo_dk<64>(C) : p_lo_dk<256>(C); }
 
-template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH, bool QLO = false, bool NOP = false>
+template <int DK, int C, typename TOUT, bool WANT_OUT, bool VSH, bool QLO = false, bool NOP = false, bool LT = false>
 hipError_t launch_main_v(const LaunchArgs& a, const MainParams& mp) {
     constexpr bool ws = use_ws<DK, C, WANT_OUT>();
     constexpr bool plo = WANT_OUT && p_lo<DK, C>();
     static_assert(!QLO || (ws && (NOP ? q_lo_nop_fits<DK, C>() : q_lo_fits<DK, C>())),
                   "q as two parts on the warp-specialised kernel only");
     static_assert(!NOP || QLO, "no intra-chunk term only with q as two parts");
+    static_assert(!LT || (ws && !QLO), "the correction call's single-part state on the warp-specialised kernel only");
     const void* kern;
-    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true, QLO, NOP>);
+    if constexpr (ws) kern = reinterpret_cast<const void*>(chunk_ws_kernel<DK, C, TOUT, VSH, true, QLO, NOP, LT>);
     else kern = reinterpret_cast<const void*>(chunk_main_kernel<DK, C, TOUT, WANT_OUT, VSH, plo>);
     size_t dyn;
     if constexpr (ws) dyn = WsGeom<DK, C, true, QLO, NOP>::BYTES;
@@ -1260,7 +1269,12 @@ hipError_t launch_main(const LaunchArgs& a, const MainParams& mp) {
             return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true, true>(a, mp)
                              : launch_main_v<DK, C, TOUT, WANT_OUT, false, true>(a, mp);
     }
-    if (mp.qlo || a.no_pv) return hipErrorInvalidValue;
+    if constexpr (WANT_OUT && sizeof(TOUT) == 4 && use_ws<DK, C, WANT_OUT>()) {
+        if (a.lo_state && !mp.qlo && !a.no_pv)
+            return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true, false, false, true>(a, mp)
+                             : launch_main_v<DK, C, TOUT, WANT_OUT, false, false, false, true>(a, mp);
+    }
+    if (mp.qlo || a.no_pv || a.lo_state) return hipErrorInvalidValue;
     return mp.vsplit ? launch_main_v<DK, C, TOUT, WANT_OUT, true>(a, mp) : launch_main_v<DK, C, TOUT, WANT_OUT, false>(a, mp);
 }
 
@@ -1309,7 +1323,7 @@ bool seg_preferred(const LaunchArgs& a) {
 bool intra_split_ok(const LaunchArgs& a, int DK) {
     const bool plain = a.addr.rev == 0 && (a.addr.ldqk == 0 || a.addr.ldqk == DK) && a.addr.qcol_blk == 0 &&
                        (a.addr.srcBH == 0 || a.addr.srcBH == a.B * a.H) && a.addr.out_acc == 0;
-    return plain && a.in_bf16 && a.out != nullptr && !a.qlo && !a.p_anti && !a.p_given && !a.no_pv && a.vs.split == 0 &&
+    return plain && a.in_bf16 && a.out != nullptr && !a.qlo && !a.p_anti && !a.p_given && !a.no_pv && !a.lo_state && a.vs.split == 0 &&
            parallel_bf16_supported(DK, a.DV);
 }
 
@@ -1372,6 +1386,7 @@ hipError_t launch_dk_c(const LaunchArgs& a) {
     if (a.p_anti && (!want_out || !plo || a.qlo || a.N % C != 0)) return hipErrorInvalidValue;
     if (a.p_given && (!want_out || !plo || a.qlo)) return hipErrorInvalidValue;
     if (a.no_pv && (!a.qlo || a.p_anti || a.p_given)) return hipErrorInvalidValue;
+    if (a.lo_state && (!want_out || a.gn.enabled || sizeof(TOUT) != 4 || a.qlo || a.no_pv || !use_ws<DK, C, true>())) return hipErrorInvalidValue;
     mp.q = (const bf16*)a.q;
     mp.qlo = (const bf16*)a.qlo; mp.k = (const bf16*)a.k; mp.v = (const bf16*)a.v;
     mp.vpre = (const bf16*)a.vs.pre; mp.vsplit = a.vs.split; mp.vshift = a.vs.shift;

@@ -73,6 +73,10 @@ struct LaunchArgs {
     // bf16 chunkwise, q as two parts (qlo), fp32 out: no intra-chunk term (no scores, no P V): the
     // output is g^(j+1) Q R alone, for a split call whose intra-chunk term another call carries
     int no_pv;
+    // bf16 chunkwise, fp32 out, no GroupNorm, chunks up to 256: the call is the correction term of a
+    // split whose k is the low part of a k that bf16 does not hold; its state term (V (.) zeta and R)
+    // enters the matrix cores as single bf16 values, P V as before
+    int lo_state;
     // bf16 parallel form: > 0 keeps only the keys of each query's own chunk of this many tokens (a
     // multiple of 64): the intra-chunk term of the chunkwise form
     int intra_chunk;
