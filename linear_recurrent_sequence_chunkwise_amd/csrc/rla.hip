@@ -12,7 +12,8 @@
 //                        used in place) and phi of the shifted key row, in the input dtype, with the
 //                        next row's loads in flight. d_k <= 256, a multiple of 4 (4 consecutive
 //                        features per lane, one 8- or 16-byte access); the softmax in double
-//                        precision.
+//                        precision for fp32 features, in single precision for bf16 features (stored
+//                        as high and low parts).
 // The retention itself runs in the chunkwise kernels (N > 1), which read value rows at and past the
 // split from v itself, shifted by w + 1 rows (VShift), or the decode-step kernel (N = 1).
 #include <algorithm>
@@ -142,6 +143,43 @@ __device__ __forceinline__ void softmax2(int d, int lane, float* a, float* b, co
 }
 
 
+__device__ __forceinline__ void wave_sum2f(float& a, float& b) {
+    a += dpp_f<0xB1>(a); b += dpp_f<0xB1>(b);
+    a += dpp_f<0x4E>(a); b += dpp_f<0x4E>(b);
+    a += dpp_f<0x141>(a); b += dpp_f<0x141>(b);
+    a += dpp_f<0x140>(a); b += dpp_f<0x140>(b);
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        const float x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
+        a += x;
+        b += y;
+    }
+}
+
+// phi over two rows in single precision, for features that are then stored as bf16 high and low
+// parts (about 2^-17 relative): exp(x - max) by the device library's expf (about 1 ulp), a
+// pairwise sum over the wave (8 levels, below 1e-6 relative), times the reciprocal of the sum.
+__device__ __forceinline__ void softmax2_f32(int d, int lane, float* a, float* b) {
+    float ma = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    float mb = fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
+    wave_max2(ma, mb);
+    float ea[4], eb[4];
+    const bool in = 4 * lane < d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ea[j] = in ? expf(a[j] - ma) : 0.f;
+        eb[j] = in ? expf(b[j] - mb) : 0.f;
+    }
+    float sa = (ea[0] + ea[1]) + (ea[2] + ea[3]), sb = (eb[0] + eb[1]) + (eb[2] + eb[3]);
+    wave_sum2f(sa, sb);
+    const float ia = 1.f / sa, ib = 1.f / sb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a[j] = ea[j] * ia;
+        b[j] = eb[j] * ib;
+    }
+}
+
 // The q and key features 4l .. 4l+3 of one row, as loaded (bf16x4 or f32x4).
 template <typename T> struct Raw4;
 template <> struct Raw4<bf16> { typedef bf16x4 type; };
@@ -209,7 +247,12 @@ __device__ __forceinline__ void finish_row(const RowAt<T>& r, const typename Raw
         fq[j] = live ? (float)xq[j] : -INFINITY;
         fk[j] = live && r.ks ? (float)xk[j] : -INFINITY;
     }
-    if (fmap == 1) softmax2(dk, lane, fq, fk, tab);
+    if (fmap == 1) {
+        if constexpr (sizeof(TO) == 2)
+            softmax2_f32(dk, lane, fq, fk);  // bf16 features with low parts
+        else
+            softmax2(dk, lane, fq, fk, tab);
+    }
     if (qo) store_row4(qo + (size_t)r.row * dk, dk, lane, fq);
     if (qlo) store_lo4(qlo + (size_t)r.row * dk, dk, lane, fq);
     if (!r.ks) {
