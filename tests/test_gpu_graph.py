@@ -169,3 +169,33 @@ def test_graph_parallel_and_rla(orc):
         assert all(torch.equal(a, b) for a, b in zip(o_rla, e_rla)), f"replay {r}: residual linear attention differs"
         eager_noise(noise)
     assert rel_err(o_par, orc.groupnorm(orc.parallel(q, k, v, gam), 1e-5)) <= 2e-2
+
+
+def test_graph_rotated_chunkwise(orc):
+    """The rotated bf16 chunkwise forward with GroupNorm and a state: the scores kernel that turns q
+    and k and writes their high and low parts, the two chunk passes adding into one fp32 buffer, the
+    state sum and the GroupNorm pass, as one graph (16 heads: the (b, h, slice) chunk kernels)."""
+    B, H, N, dk, dv = 1, 16, 1000, 256, 512
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=990)
+    s0 = I.make_state(B, H, dk, dv, seed=991, scale=0.02)
+    gam = I.multiscale_gammas(16)
+    rot = R.Rotation(10000.0, 321)
+    gn = R.GroupNorm(1e-5)
+    qd, kd, vd, s0d = (t.to(DEV) for t in (q, k, v, s0))
+    call = lambda: R.chunkwise_fwd(qd, kd, vd, gam, 128, state_in=s0d, groupnorm=gn, rotation=rot, out_dtype=torch.bfloat16)
+    eager = [t.clone() for t in call()]
+    torch.cuda.synchronize()
+    g, got = capture(call)
+    noise = [t.to(DEV) for t in I.make_qkv(1, 2, 300, 64, 64, "bf16", seed=992)]
+    for r in range(REPLAYS):
+        for t in got:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "state"), got, eager):
+            assert torch.equal(a, b), f"replay {r}: {name} differs from the eager call"
+        eager_noise(noise)
+    ro, rs = orc.recurrent_rot(q, k, v, gam, 10000.0, 321, state_in=s0)
+    assert rel_err(got[0], orc.groupnorm(ro, 1e-5)) <= 2e-2
+    assert rel_err(got[1], rs) <= 2e-2
