@@ -108,15 +108,17 @@ typedef struct {
  * Retention then runs on the rotated q and k, so scores depend on relative positions only.
  * offset is the absolute position of token 0 of this call (the number of tokens before it, e.g.
  * the prefill length for a decode step). Needs d_k even (d_k <= 256), base > 0 finite,
- * 0 <= offset < 2^31 and seq_len < 2^24. Pass NULL (or enabled = 0) for none. The rotated q and k are staged in the
+ * 0 <= offset < 2^31 and seq_len < 2^24. Pass NULL (or enabled = 0) for none. The rotated q and k are kept in the
  * workspace (flag RET_WS_ROTATION of retention_workspace_bytes). fp32 inputs: one fp32 copy each.
  * bf16 inputs: the turned values are not bf16 numbers, and rounding them once would move the
- * output by up to 2.4e-2 of its RMS, so the chunkwise and parallel forms and the backward stage
+ * output by up to 2.4e-2 of its RMS, so the chunkwise and parallel forms and the backward keep
  * them as bf16 high and low parts and run on (q_hi, k_hi), (q_hi, k_lo) and (q_lo, k_hi) (the
- * lo x lo term, about 2^-16 relative, is dropped); the chunkwise calls add their fp32 rows in
- * place (where the chunk kernel takes q as two parts, at chunk 64 and 128 and at chunk 256 with
- * d_k = 64, (q_hi, k_hi) and (q_lo, k_hi) are one call on q_hi + q_lo), the parallel and backward
- * calls keep fp32 partial results in the workspace and add them.
+ * lo x lo term, about 2^-16 relative, is dropped). The chunkwise forward with an output at chunks
+ * 64 to 256 forms the scores of the three products in one kernel, which also turns q and k and
+ * writes their parts to the workspace, then runs (q_hi, k_lo) on those scores and
+ * (q_hi + q_lo, k_hi) without an intra-chunk term, adding fp32 rows in place; its other calls
+ * (chunk 512, state only) turn q and k in a pass of their own first and run two or three calls. The
+ * parallel and backward calls keep fp32 partial results in the workspace and add them.
  * The decode step rounds the turned q and k to bf16 once.
  * Angles: the per-pair frequency theta_i / pi and the offset's phase are formed on the host in
  * double precision; the device adds n times the frequency with an exact two-product and
