@@ -543,6 +543,32 @@ def test_rotation_bf16_chunkwise(orc, dk, dv, N, C, off):
                ref_p, ex_p, TOL["bf16"])
 
 
+# The turned q and k that a rotated bf16 chunkwise call leaves at the front of its workspace (high
+# and low bf16 planes, q_hi, q_lo, k_hi, k_lo, each 256-byte aligned): written by the scores kernel
+# itself at chunks 64 to 256, by the rotation pass at chunk 512. hi + lo must equal the exact
+# rotation (fp64 cos and sin) to the two parts' resolution (about 2^-17 of a value) plus the
+# angles' error (about 1e-6 rad): at most 2e-5 of the largest value.
+@pytest.mark.parametrize("dk,C,N,off", [(64, 64, 300, 5), (256, 128, 1000, 123457), (256, 256, 700, 0), (256, 512, 700, 77)])
+def test_rotation_planes(orc, dk, C, N, off):
+    B, H, dv = 2, 3, 64
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=640 + N + dk)
+    gam = I.multiscale_gammas(H)
+    qd, kd, vd = dev(q, k, v)
+    need = R.workspace_bytes(R.RET_FN_CHUNKWISE, B, H, N, dk, dv, torch.bfloat16, torch.float32, C, rotation=True)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    R.chunkwise_fwd(qd, kd, vd, gam, C, rotation=R.Rotation(10000.0, off), workspace=ws, want_state=False)
+    torch.cuda.synchronize()
+    n = B * H * N * dk
+    A = (2 * n + 255) // 256 * 256
+    plane = [ws[i * A:i * A + 2 * n].view(torch.bfloat16).reshape(B, H, N, dk).double().cpu().numpy() for i in range(4)]
+    for name, x, hi, lo in (("q", q, plane[0], plane[1]), ("k", k, plane[2], plane[3])):
+        exact = orc.rotate(x, 10000.0, off)
+        err = float(np.max(np.abs(hi + lo - exact)) / np.max(np.abs(exact)))
+        report(f"turned {name} planes dk={dk} C={C} N={N} offset {off}", err, 2e-5)
+        # the high part is the bf16 rounding of the turned value (low part below half an ulp of it)
+        assert np.all(np.abs(lo) <= np.abs(hi) * 2.0 ** -8 + 1e-30), name
+
+
 # The N=8192 layer with rotation, GroupNorm and bf16 out (the launch configuration of the
 # benchmark's rotated call), against the oracle on every head; and, at full size, the property the
 # rotation exists for: with zero start state the output does not depend on the position offset
