@@ -543,6 +543,28 @@ def test_rotation_bf16_chunkwise(orc, dk, dv, N, C, off):
                ref_p, ex_p, TOL["bf16"])
 
 
+# Short and ragged sequences through the rotated two-call split (the scores kernel that turns q and
+# k, the (q_hi, k_lo) call with its single-part state term, the (q_hi + q_lo, k_hi) call): one
+# token, two, one short of a chunk and one past it, with a state and GroupNorm with bf16 out.
+@pytest.mark.parametrize("N", [1, 2, 63, 65])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
+def test_rotation_bf16_short(orc, N, dk, dv):
+    B, H, C, off = 1, 3, 64, 1234
+    q, k, v = I.make_qkv(B, H, N, dk, dv, "bf16", seed=650 + N + dk)
+    s0 = I.make_state(B, H, dk, dv, seed=651, scale=0.02)
+    gam = I.multiscale_gammas(H)
+    qd, kd, vd, s0d = dev(q, k, v, s0)
+    rot = R.Rotation(10000.0, off)
+    o, s = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, rotation=rot)
+    og, _ = R.chunkwise_fwd(qd, kd, vd, gam, C, state_in=s0d, rotation=rot, groupnorm=R.GroupNorm(1e-5),
+                            out_dtype=torch.float32, want_state=False)
+    ex, ex_s = orc.recurrent_rot(q, k, v, gam, 10000.0, off, state_in=s0)
+    tag = f"rotated bf16 short ({dk},{dv}) N={N}"
+    report(f"{tag} out", rel_err(o, ex), TOL["bf16"])
+    report(f"{tag} state", rel_err(s, ex_s), TOL["bf16"])
+    report(f"{tag} GroupNorm out", rel_err(og, orc.groupnorm(ex, 1e-5)), TOL["bf16"])
+
+
 # The turned q and k that a rotated bf16 chunkwise call leaves at the front of its workspace (high
 # and low bf16 planes, q_hi, q_lo, k_hi, k_lo, each 256-byte aligned): written by the scores kernel
 # itself at chunks 64 to 256, by the rotation pass at chunk 512. hi + lo must equal the exact
@@ -681,7 +703,7 @@ def test_rla_fp32(orc, fmap, w, C, plen):
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (256, 512)])
-@pytest.mark.parametrize("N,C,w", [(37, 64, 0), (900, 128, 100), (700, 256, 63), (1100, 512, 512)])
+@pytest.mark.parametrize("N,C,w", [(2, 64, 0), (37, 64, 0), (65, 64, 3), (900, 128, 100), (700, 256, 63), (1100, 512, 512)])
 def test_rla_bf16(orc, dk, dv, N, C, w):
     B, H = 1, 4
     q, k, v, kp, vp = _rla_inputs(B, H, N, dk, dv, "bf16", 710 + N + dk, P=w + 1)
