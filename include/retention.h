@@ -108,8 +108,9 @@ typedef struct {
  * Retention then runs on the rotated q and k, so scores depend on relative positions only.
  * offset is the absolute position of token 0 of this call (the number of tokens before it, e.g.
  * the prefill length for a decode step). Needs d_k even (d_k <= 256), base > 0 finite,
- * 0 <= offset < 2^31 and seq_len < 2^24. Pass NULL (or enabled = 0) for none. The rotated q and k are kept in the
- * workspace (flag RET_WS_ROTATION of retention_workspace_bytes). fp32 inputs: one fp32 copy each.
+ * 0 <= offset < 2^31 and seq_len < 2^24. Pass NULL (or enabled = 0) for none. The chunkwise, parallel and
+ * backward calls keep the rotated q and k in the workspace (flag RET_WS_ROTATION of
+ * retention_workspace_bytes); the decode step needs none. fp32 inputs: one fp32 copy each.
  * bf16 inputs: the turned values are not bf16 numbers, and rounding them once would move the
  * output by up to 2.4e-2 of its RMS, so the chunkwise and parallel forms and the backward keep
  * them as bf16 high and low parts and run on (q_hi, k_hi), (q_hi, k_lo) and (q_lo, k_hi) (the
@@ -119,7 +120,7 @@ typedef struct {
  * (q_hi + q_lo, k_hi) without an intra-chunk term, adding fp32 rows in place; its other calls
  * (chunk 512, state only) turn q and k in a pass of their own first and run two or three calls. The
  * parallel and backward calls keep fp32 partial results in the workspace and add them.
- * The decode step rounds the turned q and k to bf16 once.
+ * The decode step turns q and k in fp32 inside its kernel, with no rounding of the turned values.
  * Angles: the per-pair frequency theta_i / pi and the offset's phase are formed on the host in
  * double precision; the device adds n times the frequency with an exact two-product and
  * evaluates sin and cos of pi times the phase in fp32 (error about 1e-6 rad at any allowed
@@ -161,8 +162,9 @@ ret_status retention_chunkwise_fwd(const ret_shape* shape, int32_t chunk,
  * shape->seq_len must be 1. q, k: [B][H][d_k]; v: [B][H][d_v]; state: fp32 [B][H][d_k][d_v],
  * read and written in place; out: [B][H][d_v] (may be NULL to only advance the state).
  * Supported: d_v a multiple of 4 with d_v / 4 dividing 256 (d_v <= 1024), any d_k >= 1.
- * With a rotation, rotation->offset is the position of this token; the workspace holds the
- * rotated q and k.
+ * With a rotation, rotation->offset is the position of this token; the kernel turns q and k in
+ * fp32 as it reads them (no rounding of the turned values), so the step needs no workspace
+ * (workspace may be NULL; retention_workspace_bytes returns 0).
  */
 ret_status retention_recurrent_step(const ret_shape* shape,
                                     const void* q, const void* k, const void* v,

@@ -477,7 +477,7 @@ size_t retention_workspace_bytes(int32_t fn, const ret_shape* shape, int32_t chu
         case RET_FN_CHUNKWISE:
             if (chunk <= 0) return (size_t)-1;
             return rot ? chunkwise_rot_ws(shape, chunk, gn, 1) : chunkwise_ws(shape, chunk, gn, 1);
-        case RET_FN_RECURRENT_STEP: return rot;
+        case RET_FN_RECURRENT_STEP: return 0;  // a rotation is applied inside the step kernel
         case RET_FN_PARALLEL: return rot ? parallel_rot_ws(shape, gn) : parallel_ws(shape, gn);
         case RET_FN_CHUNKWISE_BWD:
             if (chunk <= 0) return (size_t)-1;
@@ -713,13 +713,11 @@ ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const
     ret::RotConsts rc;
     bool rot = false;
     RET_TRY(check_rotation(rotation, shape, &rc, &rot));
-    if (rot) {
-        RET_TRY(check_ws(rotation_ws(shape), workspace, workspace_bytes));
-        const hipError_t e = stage_rotation(shape, rc, &q, &k, &workspace, &workspace_bytes, reinterpret_cast<hipStream_t>(hip_stream));
-        if (e != hipSuccess) return device_status(e, "retention_recurrent_step rotation launch");
-    }
+    (void)workspace;
+    (void)workspace_bytes;  // the step needs none: a rotation is applied inside the kernel
     ret::LaunchArgs a = base_args(shape, 1, hc, gn, nullptr, 0, hip_stream);
     a.q = q; a.k = k; a.v = v; a.out = out; a.state_out = state;
+    a.step_rot = rot ? &rc : nullptr;
     return device_status(ret::launch_recurrent_step(a), "retention_recurrent_step launch");
 }
 

@@ -64,9 +64,6 @@ struct RotFuse {
     bf16 *qh, *ql, *kh, *kl;
     RotConsts rc;
 };
-struct NoRot {};
-template <bool ROT> struct RotSel { typedef NoRot type; };
-template <> struct RotSel<true> { typedef RotFuse type; };
 
 // Turns piece c (features 8c .. 8c+7, pairs 4c .. 4c+3) of rows r0 .. r0+nr-1 of a block in LDS
 // (rows of QRB bytes, swizzled as SwzTile<QRB>) holding sequence positions pos0 + r: high and low
@@ -116,7 +113,7 @@ __global__ __launch_bounds__(256) void chunk_scores_kernel(int H, int N, int C, 
                                                            const bf16* __restrict__ qlo, const bf16* __restrict__ k,
                                                            const bf16* __restrict__ klo, bf16* __restrict__ P,
                                                            bf16* __restrict__ Plo, bf16* __restrict__ Pa, HeadConsts hc, int rev,
-                                                           int ldqk, int qcol_blk, int srcBH, typename RotSel<ROT>::type rf) {
+                                                           int ldqk, int qcol_blk, int srcBH, typename IfRot<ROT, RotFuse>::type rf) {
     static_assert(!ROT || KLO, "the rotated scores use both parts of k");
     constexpr int KB = KLO ? 64 : 128;  // keys per LDS block
     constexpr int QRB = DK * 2;   // bytes per K row

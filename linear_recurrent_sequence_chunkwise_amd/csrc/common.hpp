@@ -56,6 +56,7 @@ struct VShift {
     int split, shift;
 };
 
+struct RotConsts;
 struct LaunchArgs {
     int B, H, N, DK, DV;
     int in_bf16, out_bf16;
@@ -77,6 +78,8 @@ struct LaunchArgs {
     // split whose k is the low part of a k that bf16 does not hold; its state term (V (.) zeta and R)
     // enters the matrix cores as single bf16 values, P V as before
     int lo_state;
+    // decode step: the rotation's constants (host memory; null: none); the kernel turns q and k
+    const RotConsts* step_rot;
     // bf16 parallel form: > 0 keeps only the keys of each query's own chunk of this many tokens (a
     // multiple of 64): the intra-chunk term of the chunkwise form
     int intra_chunk;
@@ -217,6 +220,12 @@ struct RotConsts {
     float flo[kMaxPairs];
     float ph[kMaxPairs];
 };
+
+// A kernel parameter that only instantiations with a rotation carry: IfRot<ROT, T>::type is T when
+// ROT, else an empty struct.
+struct NoRot {};
+template <bool ROT, typename T> struct IfRot { typedef NoRot type; };
+template <typename T> struct IfRot<true, T> { typedef T type; };
 
 // sin and cos of the angle of pair (fhi, flo, ph) at local position n (0 <= n < 2^24, exact in
 // fp32). The phase in half-turns is ph + n * (fhi + flo) mod 2: the product n * fhi is split into

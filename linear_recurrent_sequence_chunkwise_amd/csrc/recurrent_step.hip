@@ -48,10 +48,13 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // DV is a template parameter so that the row strides of the eight loads in flight are
 // compile-time constants: the loads are then issued in the order they are consumed and each
 // wait drains only the oldest one.
-template <typename TIN, typename TOUT, int DV>
+// ROT: q and k are turned by the positional rotation at this step's position (the offset) as they
+// come into LDS, in fp32 (pair (2i, 2i+1) by the angle of rot_sincos at local position 0), so the
+// turned values are never rounded to the input dtype.
+template <typename TIN, typename TOUT, int DV, bool ROT>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     int H, int DK, const TIN* __restrict__ q, const TIN* __restrict__ k, const TIN* __restrict__ v,
-    float* __restrict__ state, TOUT* __restrict__ out, HeadConsts hc, GnArgs gn) {
+    float* __restrict__ state, TOUT* __restrict__ out, HeadConsts hc, GnArgs gn, typename IfRot<ROT, RotConsts>::type rc) {
     extern __shared__ float smem[];
     __shared__ float red[kThreads / kWave];
     const int bh = blockIdx.x, h = bh % H, t = threadIdx.x;
@@ -61,9 +64,22 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     float* ks = smem + DK;
     float* part = smem + 2 * DK;  // [RG][DV]
 
-    for (int i = t; i < DK; i += kThreads) {
-        qs[i] = to_float(q[(size_t)bh * DK + i]);
-        ks[i] = to_float(k[(size_t)bh * DK + i]);
+    if constexpr (ROT) {
+        for (int i = t; i < DK / 2; i += kThreads) {
+            float sn, cs;
+            rot_sincos(0, rc.fhi[i], rc.flo[i], rc.ph[i], sn, cs);
+            const size_t e = (size_t)bh * DK + 2 * i;
+            const float qa = to_float(q[e]), qb = to_float(q[e + 1]), ka = to_float(k[e]), kb = to_float(k[e + 1]);
+            qs[2 * i] = qa * cs - qb * sn;
+            qs[2 * i + 1] = qa * sn + qb * cs;
+            ks[2 * i] = ka * cs - kb * sn;
+            ks[2 * i + 1] = ka * sn + kb * cs;
+        }
+    } else {
+        for (int i = t; i < DK; i += kThreads) {
+            qs[i] = to_float(q[(size_t)bh * DK + i]);
+            ks[i] = to_float(k[(size_t)bh * DK + i]);
+        }
     }
     const f32x4 vv = load4<TIN>(v + (size_t)bh * DV + 4 * cg);
     __syncthreads();
@@ -134,16 +150,25 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     }
 }
 
-template <typename TIN, typename TOUT, int DV>
-hipError_t launch_dv(const LaunchArgs& a) {
+template <typename TIN, typename TOUT, int DV, bool ROT>
+hipError_t launch_dv_r(const LaunchArgs& a, typename IfRot<ROT, RotConsts>::type rc) {
     constexpr int CG = DV / 4, RG = kThreads / CG;
     const size_t lds = (size_t)(2 * a.DK + RG * DV) * sizeof(float);
-    const void* kern = reinterpret_cast<const void*>(recurrent_step_kernel<TIN, TOUT, DV>);
+    const void* kern = reinterpret_cast<const void*>(recurrent_step_kernel<TIN, TOUT, DV, ROT>);
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((recurrent_step_kernel<TIN, TOUT, DV>), dim3(a.B * a.H), dim3(kThreads), lds, a.stream, a.H, a.DK,
-                       (const TIN*)a.q, (const TIN*)a.k, (const TIN*)a.v, a.state_out, (TOUT*)a.out, a.hc, a.gn);
+    hipLaunchKernelGGL((recurrent_step_kernel<TIN, TOUT, DV, ROT>), dim3(a.B * a.H), dim3(kThreads), lds, a.stream, a.H, a.DK,
+                       (const TIN*)a.q, (const TIN*)a.k, (const TIN*)a.v, a.state_out, (TOUT*)a.out, a.hc, a.gn, rc);
     return hipGetLastError();
+}
+
+template <typename TIN, typename TOUT, int DV>
+hipError_t launch_dv(const LaunchArgs& a) {
+    if (a.step_rot) {
+        if (a.DK % 2 || a.DK / 2 > kMaxPairs) return hipErrorInvalidValue;
+        return launch_dv_r<TIN, TOUT, DV, true>(a, *a.step_rot);
+    }
+    return launch_dv_r<TIN, TOUT, DV, false>(a, NoRot{});
 }
 
 // d_v / 4 divides 256 (checked by the caller): d_v in {4, 8, ..., 1024}
