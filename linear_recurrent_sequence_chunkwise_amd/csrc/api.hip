@@ -103,7 +103,9 @@ ret_status check_gn(const ret_groupnorm* gn, int in_bf16, ret::GnArgs* out) {
 
 // Rotation constants per feature pair, in double precision: theta_i / pi split into two floats,
 // and the offset's phase (offset * theta_i / pi mod 2) from an exact two-product and an exact fmod.
-ret_status check_rotation(const ret_rotation* r, const ret_shape* s, ret::RotConsts* rc, bool* on) {
+// step (optional): cos and sin of pi times that phase, for the decode step's single position.
+ret_status check_rotation(const ret_rotation* r, const ret_shape* s, ret::RotConsts* rc, bool* on,
+                          ret::StepRot* step = nullptr) {
     *on = false;
     if (!r || !r->enabled) return RET_OK;
     if (!(r->base > 0.0) || !std::isfinite(r->base)) return fail(RET_ERR_INVALID_ARG, "rotation base must be finite and > 0");
@@ -117,6 +119,7 @@ ret_status check_rotation(const ret_rotation* r, const ret_shape* s, ret::RotCon
     for (int i = 0; i < ret::kMaxPairs; ++i) {
         if (i >= d / 2) {
             rc->fhi[i] = rc->flo[i] = rc->ph[i] = 0.f;
+            if (step) step->cs[i] = step->sn[i] = 0.f;
             continue;
         }
         const double f = std::pow(r->base, -2.0 * i / d) / M_PI;
@@ -128,6 +131,10 @@ ret_status check_rotation(const ret_rotation* r, const ret_shape* s, ret::RotCon
         double ph = std::fmod(p, 2.0) + e;
         ph -= 2.0 * std::floor(0.5 * ph);
         rc->ph[i] = (float)ph;
+        if (step) {
+            step->cs[i] = (float)std::cos(M_PI * ph);
+            step->sn[i] = (float)std::sin(M_PI * ph);
+        }
     }
     *on = true;
     return RET_OK;
@@ -711,13 +718,14 @@ ret_status retention_recurrent_step(const ret_shape* shape, const void* q, const
     const size_t out_bytes = bh * dv * elem_size(shape->out_dtype);
     if (out && overlaps(out, out_bytes, state, st_bytes)) return fail(RET_ERR_INVALID_ARG, "out must not alias state");
     ret::RotConsts rc;
+    ret::StepRot sr;
     bool rot = false;
-    RET_TRY(check_rotation(rotation, shape, &rc, &rot));
+    RET_TRY(check_rotation(rotation, shape, &rc, &rot, &sr));
     (void)workspace;
     (void)workspace_bytes;  // the step needs none: a rotation is applied inside the kernel
     ret::LaunchArgs a = base_args(shape, 1, hc, gn, nullptr, 0, hip_stream);
     a.q = q; a.k = k; a.v = v; a.out = out; a.state_out = state;
-    a.step_rot = rot ? &rc : nullptr;
+    a.step_rot = rot ? &sr : nullptr;
     return device_status(ret::launch_recurrent_step(a), "retention_recurrent_step launch");
 }
 

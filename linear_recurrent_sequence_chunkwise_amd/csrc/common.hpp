@@ -57,6 +57,7 @@ struct VShift {
 };
 
 struct RotConsts;
+struct StepRot;
 struct LaunchArgs {
     int B, H, N, DK, DV;
     int in_bf16, out_bf16;
@@ -78,8 +79,9 @@ struct LaunchArgs {
     // split whose k is the low part of a k that bf16 does not hold; its state term (V (.) zeta and R)
     // enters the matrix cores as single bf16 values, P V as before
     int lo_state;
-    // decode step: the rotation's constants (host memory; null: none); the kernel turns q and k
-    const RotConsts* step_rot;
+    // decode step: cos and sin of each pair's angle at the step's position (host memory; null: no
+    // rotation); the kernel turns q and k with them
+    const StepRot* step_rot;
     // bf16 parallel form: > 0 keeps only the keys of each query's own chunk of this many tokens (a
     // multiple of 64): the intra-chunk term of the chunkwise form
     int intra_chunk;
@@ -219,6 +221,14 @@ struct RotConsts {
     float fhi[kMaxPairs];
     float flo[kMaxPairs];
     float ph[kMaxPairs];
+};
+
+// The decode step's rotation: one position (the offset) per call, so each pair's turn is a fixed
+// cos and sin, evaluated on the host in double precision from the same angle as RotConsts and
+// rounded once to float.
+struct StepRot {
+    float cs[kMaxPairs];
+    float sn[kMaxPairs];
 };
 
 // A kernel parameter that only instantiations with a rotation carry: IfRot<ROT, T>::type is T when

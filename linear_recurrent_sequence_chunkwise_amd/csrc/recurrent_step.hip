@@ -49,12 +49,40 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // compile-time constants: the loads are then issued in the order they are consumed and each
 // wait drains only the oldest one.
 // ROT: q and k are turned by the positional rotation at this step's position (the offset) as they
-// come into LDS, in fp32 (pair (2i, 2i+1) by the angle of rot_sincos at local position 0), so the
-// turned values are never rounded to the input dtype.
+// come into LDS, in fp32 (pair (2i, 2i+1) by the cos and sin that the host formed in double
+// precision), so the turned values are never rounded to the input dtype. Wave w turns pairs
+// 64 w + lane. The wave reads its 64 pairs' cos and sin out of the kernel arguments at
+// compile-time offsets (scalar loads) and writes each into its lane (v_writelane), in uniform
+// control flow: indexing the argument block by lane would make every workgroup fetch the whole
+// table with vector loads.
+template <bool ROT>
+__device__ __forceinline__ void pick_turn(const typename IfRot<ROT, StepRot>::type& rc, int w, float& cs, float& sn) {
+    if constexpr (ROT) {
+        static_assert(kMaxPairs == 2 * kWave, "two waves cover the pairs");
+        int c = 0, s = 0;
+        // the wave index made scalar, so that the branch and every offset below are wave-uniform
+        if (__builtin_amdgcn_readfirstlane(w) == 0) {
+#pragma unroll
+            for (int j = 0; j < kWave; ++j) {
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(c) : "s"(__builtin_bit_cast(int, rc.cs[j])), "i"(j));
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(s) : "s"(__builtin_bit_cast(int, rc.sn[j])), "i"(j));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kWave; ++j) {
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(c) : "s"(__builtin_bit_cast(int, rc.cs[kWave + j])), "i"(j));
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(s) : "s"(__builtin_bit_cast(int, rc.sn[kWave + j])), "i"(j));
+            }
+        }
+        cs = __builtin_bit_cast(float, c);
+        sn = __builtin_bit_cast(float, s);
+    }
+}
+
 template <typename TIN, typename TOUT, int DV, bool ROT>
 __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     int H, int DK, const TIN* __restrict__ q, const TIN* __restrict__ k, const TIN* __restrict__ v,
-    float* __restrict__ state, TOUT* __restrict__ out, HeadConsts hc, GnArgs gn, typename IfRot<ROT, RotConsts>::type rc) {
+    float* __restrict__ state, TOUT* __restrict__ out, HeadConsts hc, GnArgs gn, typename IfRot<ROT, StepRot>::type rc) {
     extern __shared__ float smem[];
     __shared__ float red[kThreads / kWave];
     const int bh = blockIdx.x, h = bh % H, t = threadIdx.x;
@@ -65,9 +93,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     float* part = smem + 2 * DK;  // [RG][DV]
 
     if constexpr (ROT) {
-        for (int i = t; i < DK / 2; i += kThreads) {
+        if (t < DK / 2) {  // DK / 2 <= kMaxPairs = 2 waves
+            const int i = t;
             float sn, cs;
-            rot_sincos(0, rc.fhi[i], rc.flo[i], rc.ph[i], sn, cs);
+            pick_turn<ROT>(rc, t >> 6, cs, sn);
             const size_t e = (size_t)bh * DK + 2 * i;
             const float qa = to_float(q[e]), qb = to_float(q[e + 1]), ka = to_float(k[e]), kb = to_float(k[e + 1]);
             qs[2 * i] = qa * cs - qb * sn;
@@ -85,8 +114,15 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
     __syncthreads();
 
     const float g = hc.gamma[h];
+    // The state's base address passes through readfirstlane: it is wave-uniform anyway, but after
+    // the rotation's lane-divergent prologue the compiler cannot prove it, and a descriptor it
+    // takes for divergent gets a readfirstlane loop around every buffer access (measured: the
+    // rotated step 14% slower than the plain one).
+    const uint64_t sb = reinterpret_cast<uint64_t>(state + (size_t)bh * DK * DV);
+    const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(sb >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(state + (size_t)bh * DK * DV), 0, (unsigned)(DK * DV * 4), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(sbu), 0, (unsigned)__builtin_amdgcn_readfirstlane(DK * DV * 4), 0x00020000);
     auto ld = [&](int r) __attribute__((always_inline)) {
         return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)((r * CG + cg) * 16), 0, kLoadNT));
     };
@@ -151,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_step_kernel(
 }
 
 template <typename TIN, typename TOUT, int DV, bool ROT>
-hipError_t launch_dv_r(const LaunchArgs& a, typename IfRot<ROT, RotConsts>::type rc) {
+hipError_t launch_dv_r(const LaunchArgs& a, typename IfRot<ROT, StepRot>::type rc) {
     constexpr int CG = DV / 4, RG = kThreads / CG;
     const size_t lds = (size_t)(2 * a.DK + RG * DV) * sizeof(float);
     const void* kern = reinterpret_cast<const void*>(recurrent_step_kernel<TIN, TOUT, DV, ROT>);
