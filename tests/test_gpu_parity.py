@@ -652,6 +652,25 @@ def test_rotation_decode_workload(orc):
     rot_report("rotated decode state", sd, rs, es, TOL["bf16"])
 
 
+# Turned decode steps at pair counts that leave lanes of a wave without a pair (each wave of the
+# step kernel turns 64 pairs with the cos and sin the host formed): 1, 33, 65 and 127 pairs, with
+# GroupNorm on two of them, at a position past 2^20.
+@pytest.mark.parametrize("dt,dk,dv,gn", [("bf16", 2, 64, False), ("f32", 66, 128, True), ("bf16", 130, 64, False),
+                                         ("bf16", 254, 32, True)])
+def test_rotation_decode_pair_counts(orc, dt, dk, dv, gn):
+    B, H, off = 2, 3, 1234567
+    q, k, v = I.make_qkv(B, H, 1, dk, dv, dt, seed=640 + dk)
+    state = I.make_state(B, H, dk, dv, seed=641, scale=0.05)
+    gam = [0.9, 0.99, 0.5]
+    qd, kd, vd, sd = dev(q[:, :, 0], k[:, :, 0], v[:, :, 0], state)
+    o = R.recurrent_step(qd, kd, vd, gam, sd, rotation=R.Rotation(10000.0, off), groupnorm=R.GroupNorm(1e-5) if gn else None)
+    eo, es = orc.step(orc.rotate(q, 10000.0, off)[:, :, 0], orc.rotate(k, 10000.0, off)[:, :, 0], v[:, :, 0], gam, state)
+    if gn:
+        eo = orc.groupnorm(eo[:, :, None, :], 1e-5)[:, :, 0, :]
+    report(f"rotated decode {dt} d_k={dk} d_v={dv}{' GroupNorm' if gn else ''} out (exact rotation)", rel_err(o, eo), TOL[dt])
+    report(f"rotated decode {dt} d_k={dk} d_v={dv} state (exact rotation)", rel_err(sd, es), TOL[dt])
+
+
 @pytest.mark.parametrize("dt,B,H,N,dk,dv,C,off", [
     ("f32", 1, 2, 256, 64, 64, 64, 11), ("bf16", 4, 8, 2048, 64, 64, 128, 0), ("bf16", 1, 4, 1000, 256, 512, 128, 4096)])
 def test_rotation_backward(orc, dt, B, H, N, dk, dv, C, off):
