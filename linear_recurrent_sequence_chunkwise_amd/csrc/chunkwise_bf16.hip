@@ -1080,13 +1080,16 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(MainParams p, HeadConsts 
                 const int j = kST * s + 16 * rt_o + 4 * g4 + i;  // row within the chunk
                 const float acc = qr[i] * (gs * row_decay[i]) + pv[i];
                 const unsigned off = (unsigned)((row_of(c0 + j) * DV + col0 + 16 * ct_o + c16) * (int)sizeof(TOUT));
+                // output rows with the non-temporal policy (2): they are not read again by this kernel,
+                // and the L2 keeps the lines of Q, K and P that the head's slices share (measured
+                // 4 us faster per call at the N=8192 layer, five interleaved runs each)
                 if constexpr (sizeof(TOUT) == 4) {
                     if (p.out_acc)
                         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc, ro, off, 0, 0);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc), ro, off, 0, 2);
                 } else
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_float<TOUT>(acc)), ro, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_float<TOUT>(acc)), ro, off, 0, 2);
             }
             lds_barrier();  // stage g consumed; stage g+1 in LDS
             if (chunk_end && g + 1 < total) lds_barrier();  // R of this chunk written
